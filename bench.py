@@ -1,0 +1,309 @@
+"""Benchmark: one decode step over a compressed long-context KV cache on one
+MI355X, plus the INT8 / QJL kernels on their own workloads.
+
+Workload (one step): batch 16 x 32 heads x 32768 tokens x head dim 128.
+The cache holds QJL-sketched keys (m = 256 sign bits + fp16 norm per token)
+and per-token INT8 values (codes + fp32 scale), built once before timing
+from fp16 N(0, 1) tensors.  A step
+  1. compresses the newest token of every head: INT8-quantizes its value and
+     QJL-sketches its key (kvq_quantize_int8, kvq_qjl_sketch), and writes the
+     compressed rows into cache position T - 1;
+  2. runs one decode query per head against all T tokens: QJL scores, fp32
+     softmax and the weighted sum of INT8 values (kvq_decode_qjl_int8).
+Throughput is scores per second (query-token pairs scored per step / time).
+
+Also reported (``components``): HBM GB/s of quantize / dequantize on the
+element-count sweep (2^28 and 2^30 fp32), the Llama-7B-layer INT8 path, and
+the QJL-cache sketch and score, each timed with HIP events on the stream the
+kernels run on.  ``cpu_baseline`` times the fp64 oracle on a bounded sample
+of the same decode workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-components]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_hbm_traffic.json")
+DECODE_SOURCES = ["decode_kernels.hip", "kvq_qjl_device.h", "kvq_device.h"]
+
+
+def parse_args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-components", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "kv_cache_compression_kvq_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(bytes_per_launch_alg: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current decode sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except OSError:
+        return None
+    if t.get("source_sha") != decode_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def event_times(fn, reps, warmup, stream=None):
+    """Durations (ms) of `reps` calls of fn, each bracketed by HIP events
+    recorded on the stream fn launches on."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def med(xs):
+    s = sorted(xs)
+    return s[len(s) // 2]
+
+
+def components(K, si, torch, np):
+    """GB/s of the INT8 and QJL kernels on their own workloads."""
+    res = {}
+    dev = "cuda"
+
+    def gbs(name, nbytes, fn, reps=20, flops=None):
+        ms = med(event_times(fn, reps, 3))
+        r = {"ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
+             "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 3), "bytes": int(nbytes)}
+        if flops:
+            r["TFLOP/s"] = round(flops / ms / 1e9, 1)
+            r["frac_mfma_f16"] = round(flops / ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 3)
+        res[name] = r
+        log(f"  {name}: {r}")
+
+    # element-count sweep, fp32 rows of d in {128, 1024, 8192}
+    for nlog in (28, 30):
+        n = 1 << nlog
+        x = torch.from_numpy(si.flat_rows(si.W_SWEEP, n, 128).reshape(-1)).to(dev)
+        for d in (128, 1024, 8192):
+            xv = x.view(n // d, d)
+            codes, scales = K.quantize_int8(xv)
+            rows = n // d
+            gbs(f"quantize_f32_2^{nlog}_d{d}", 4 * n + n + 4 * rows, lambda: K.quantize_int8(xv))
+            gbs(f"dequantize_f32_2^{nlog}_d{d}", n + 4 * rows + 4 * n,
+                lambda: K.dequantize_int8(codes, scales))
+            del codes, scales
+        del x
+        torch.cuda.empty_cache()
+
+    # Llama-7B-shaped layer, fp16: K and V quantized, dequantized, scored
+    W = si.W_LLAMA_LAYER
+    k = torch.from_numpy(si.kv_tensor(W, si.K, 1, 32, 4096, 128, "f16", outliers=True)).to(dev)
+    v = torch.from_numpy(si.kv_tensor(W, si.V, 1, 32, 4096, 128, "f16")).to(dev)
+    kv = torch.stack([k, v]).view(-1, 128)
+    R = kv.shape[0]
+    codes, scales = K.quantize_int8(kv)
+    gbs("llama_layer_quantize_kv_f16", 2 * R * 128 + R * 128 + 4 * R, lambda: K.quantize_int8(kv))
+    gbs("llama_layer_dequantize_kv_f16", R * 128 + 4 * R + 2 * R * 128,
+        lambda: K.dequantize_int8(codes, scales, torch.float16))
+    q = torch.from_numpy(si.queries(W, 32, 1, 128, "f16")).to(dev)
+    kc, ks = codes[: R // 2].view(32, 4096, 128), scales[: R // 2].view(32, 4096)
+    gbs("llama_layer_scores_int8", 32 * 4096 * (128 + 4 + 4) + 32 * 128 * 2,
+        lambda: K.scores_int8(q, kc, ks))
+    del k, v, kv, codes, scales
+
+    # QJL key cache: 8 x 32 x 8192 x 128 fp16, m = 256
+    W = si.W_QJL_CACHE
+    G, T, d, m = 256, 8192, 128, 256
+    kk = torch.from_numpy(si.kv_tensor(W, si.K, 8, 32, T, d, "f16", outliers=True)).to(dev).view(-1, d)
+    S = torch.from_numpy(si.projection(W, m, d, "f16")).to(dev)
+    R = kk.shape[0]
+    bits, norms = K.qjl_sketch(kk, S)
+    gbs("qjl_sketch_f16_m256", R * d * 2 + R * (m // 8) + 2 * R + m * d * 2,
+        lambda: K.qjl_sketch(kk, S), flops=2.0 * R * d * m)
+    q = torch.from_numpy(si.queries(W, G, 1, d, "f16")).to(dev)
+    b3, n3 = bits.view(G, T, m // 32), norms.view(G, T)
+    gbs("qjl_scores_f16_m256", R * (m // 8 + 2 + 4) + G * d * 2 + m * d * 2,
+        lambda: K.scores_qjl(q, S, b3, n3))
+    res["qjl_scores_f16_m256"]["scores/s"] = round(R / res["qjl_scores_f16_m256"]["ms"] * 1e3, 1)
+    del kk, bits, norms
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(si, np, seconds):
+    """The fp64 oracle's decode on one thread over whole groups of the same
+    workload, until `seconds` of compute have been timed (at least 2)."""
+    from threadpoolctl import threadpool_limits
+    from oracle import decode as OD, int8 as OI, qjl as OQ
+    W, B, H, T, d, m = si.W_DECODE, 16, 32, 32768, 128, 256
+    S = si.projection(W, m, d, "f16")
+    q = si.queries(W, B * H, 1, d, "f16")[:, 0]
+    lam = 1.0 / math.sqrt(d)
+    done, spent = 0, 0.0
+    while done < B * H and (spent < seconds or done < 2):
+        b, h = divmod(done, H)
+        k = si.kv_tensor(W, si.K, B, H, T, d, "f16", heads=range(h, h + 1)).reshape(B, T, d)[b]
+        v = si.kv_tensor(W, si.V, B, H, T, d, "f16", heads=range(h, h + 1)).reshape(B, T, d)[b]
+        kw, kn = OQ.qjl_sketch(k, S)                  # cache build (untimed)
+        vc, vs = OI.quantize_int8(v)
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            OD.decode_qjl_int8(q[done:done + 1], S, kw[None], kn[None], vc[None], vs[None], lam)
+            spent += time.perf_counter() - t0
+        done += 1
+    return {"value": round(done * T / spent, 1), "unit": "scores/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {B * H} (batch, head) groups x {T} tokens, one decode query each; "
+                      f"fp64 numpy oracle on one thread, {spent:.1f} s of compute timed"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kv_cache_compression_kvq_amd as K
+    import synth_inputs as si
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    W, B, H, T, d, m = si.W_DECODE, 16, 32, 32768, 128, 256
+    G = B * H
+    lam = 1.0 / math.sqrt(d)
+
+    log("bench: generating the decode cache (fp16 K, V ~ N(0,1), 16x32x32768x128)")
+    t0 = time.time()
+    k = torch.from_numpy(si.kv_tensor(W, si.K, B, H, T, d, "f16")).to(dev).view(G, T, d)
+    S = torch.from_numpy(si.projection(W, m, d, "f16")).to(dev)
+    kbits, knorms = K.qjl_sketch(k, S)
+    del k
+    v = torch.from_numpy(si.kv_tensor(W, si.V, B, H, T, d, "f16")).to(dev).view(G, T, d)
+    vcodes, vscales = K.quantize_int8(v)
+    del v
+    torch.cuda.empty_cache()
+    q = torch.from_numpy(si.queries(W, G, 1, d, "f16")).to(dev).view(G, d)
+    # the newest token of every head (its own streams: tensor ids 6, 7)
+    k_new = torch.from_numpy(si.stream(W, 6, G * d, "f16")).to(dev).view(G, d)
+    v_new = torch.from_numpy(si.stream(W, 7, G * d, "f16")).to(dev).view(G, d)
+    ws = torch.empty(max(16, K.decode_workspace_bytes(G, T, d)), dtype=torch.uint8, device=dev)
+    out = torch.empty((G, d), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"bench: cache ready in {time.time() - t0:.1f} s")
+
+    stream = torch.cuda.current_stream()
+    dec_events = []
+
+    def step(record=False):
+        vc_new, vs_new = K.quantize_int8(v_new)
+        kb_new, kn_new = K.qjl_sketch(k_new, S)
+        vcodes[:, T - 1].copy_(vc_new)
+        vscales[:, T - 1].copy_(vs_new)
+        kbits[:, T - 1].copy_(kb_new)
+        knorms[:, T - 1].copy_(kn_new)
+        if record:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+        K.decode_qjl_int8(q, S, kbits, knorms, vcodes, vscales, lam, workspace=ws, out=out)
+        if record:
+            b.record(stream)
+            dec_events.append((a, b))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(record=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_step = elapsed * 1e3 / args.steps
+    dec_ms = sum(a.elapsed_time(b) for a, b in dec_events) / len(dec_events)
+    scores = G * T
+    value = scores / (ms_step / 1e3)
+
+    alg_bytes = (G * T * (m // 8 + 2 + d + 4)       # sign words, norm, value codes, value scale
+                 + G * d * 2 + m * d * 2 + G * d * 4)  # queries, S, output
+    achieved = alg_bytes / (dec_ms / 1e3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(alg_bytes),
+                "kernel": "kvq_decode_qjl_int8 (decode_split_kernel + decode_merge_kernel)",
+                "alg_bytes_per_launch": alg_bytes, "avg_launch_ms": round(dec_ms, 4)}
+    log(f"bench: {args.steps} steps, {ms_step:.3f} ms/step, decode {dec_ms:.3f} ms "
+        f"({achieved:.0f} GB/s)")
+
+    comp = None
+    if not args.no_components:
+        del kbits, knorms, vcodes, vscales
+        torch.cuda.empty_cache()
+        log("bench: components")
+        comp = components(K, si, torch, np)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        cpu = cpu_baseline(si, np, args.cpu_seconds)
+
+    line = {
+        "metric": "KV quantize/dequant HBM GB/s (% of peak); QJL+INT8 decode scores/sec",
+        "value": round(value, 1),
+        "unit": "scores/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode step over a QJL-key / INT8-value cache: batch 16 x 32 heads "
+                               "x 32768 tokens x d 128, m 256, 1 fp16 query per head, newest token "
+                               "compressed in-step",
+                   "global_batch": 16, "seq_len": T, "heads": H, "head_dim": d, "qjl_m": m,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "components": comp,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,214 @@
+/*
+ * kvq.h - C ABI of libkvq, a KV-cache compressor for AMD Instinct MI355X
+ * (gfx950): per-row symmetric INT8 quantization and the QJL key sketch, with
+ * decode-time scoring and attention read straight from the compressed cache.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensor pointers are DEVICE pointers (HBM of the current HIP device).  The
+ *   caller allocates and owns every buffer; no call allocates, frees or
+ *   synchronises.  Work is enqueued on `stream` (NULL = the null stream) and
+ *   is complete when that stream is; calls are therefore capturable into a
+ *   HIP graph.
+ * - Layouts are row-major and contiguous.  A [B, H, T, d] cache is flattened
+ *   to rows = B*H*T (one row = one token of one head, d contiguous values)
+ *   and groups = B*H with T rows each.
+ * - Element types: KVQ_F32 = IEEE binary32, KVQ_F16 = IEEE binary16.  Codes
+ *   are int8, scales binary32, sign words uint32, norms binary16 stored as
+ *   uint16 bit patterns.
+ * - Validation happens on the host before any HIP call and returns a status
+ *   (never aborts, never throws); kvq_last_error() then describes the
+ *   failure.  rows == 0 (or groups == 0 or T == 0) is a successful no-op.
+ *   Base pointers must be 16-byte aligned.  A launch failure returns
+ *   KVQ_ERR_LAUNCH with the runtime's message; faults inside a kernel surface
+ *   at the caller's next synchronisation, as for any HIP kernel.
+ * - Inputs must be finite; results for NaN/Inf inputs are unspecified.
+ * - Calls are stateless and may be made from several host threads.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t, declared without the HIP headers. */
+typedef struct ihipStream_t* kvq_stream_t;
+
+typedef int32_t kvq_status;
+enum {
+  KVQ_OK = 0,
+  KVQ_ERR_NULL = 1,      /* a required pointer is NULL                       */
+  KVQ_ERR_SHAPE = 2,     /* a size is negative, zero where it must not be,
+                            or outside the supported range                   */
+  KVQ_ERR_ALIGN = 3,     /* a base pointer is not 16-byte aligned            */
+  KVQ_ERR_DTYPE = 4,     /* unsupported element type (or mismatched pair)    */
+  KVQ_ERR_WORKSPACE = 5, /* workspace pointer NULL or smaller than required  */
+  KVQ_ERR_LAUNCH = 6     /* the HIP runtime rejected a launch / device query */
+};
+
+typedef int32_t kvq_dtype;
+enum { KVQ_F32 = 0, KVQ_F16 = 1 };
+
+/*
+ * kvq_quantize_int8 - per-row symmetric INT8 quantization.
+ *
+ * Defined by the symmetric INT8 formula of the Q-TensorFormer model card
+ * (section 6, "Adaptive KV Cache Quantization & Attention-Sink Eviction"):
+ * scale = max|x| / 127; code = nearest integer of x / scale, clamped to
+ * [-128, 127]; and by the INT8 KV-cache paper (arXiv 2601.04719, Abstract).
+ * For each row r of x [rows, d]:
+ *   a_r = max_i |x_ri|
+ *   s_r = RN32(a_r / 127)                       (IEEE binary32 division)
+ *   c_ri = clamp(rne(RN32(x_ri / s_r)), -128, 127)
+ * with rne = round to nearest integer, ties to even.  A row whose s_r is +0
+ * gets s_r = +0 and all-zero codes.  Results are bit-identical to this
+ * definition (no fast-math; binary32 subnormals are honoured).
+ *
+ * x       [rows, d] KVQ_F32 or KVQ_F16 (x_dt)
+ * codes   [rows, d] int8, written
+ * scales  [rows]    binary32, written
+ * d       1 <= d <= 65536, d % 16 == 0
+ * Errors: NULL, ALIGN, SHAPE (rows < 0 or d outside the range), DTYPE.
+ */
+kvq_status kvq_quantize_int8(const void* x, kvq_dtype x_dt, int64_t rows, int32_t d,
+                             int8_t* codes, float* scales, kvq_stream_t stream);
+
+/*
+ * kvq_dequantize_int8 - reconstruction of quantized rows.
+ *
+ * Same source as kvq_quantize_int8 (the reconstruction multiplies the code
+ * back by its row scale):  out_ri = RN32(c_ri * s_r); for KVQ_F16 output,
+ * out_ri = RN16(RN32(c_ri * s_r)).  Bit-exact.
+ *
+ * codes  [rows, d] int8;  scales [rows] binary32
+ * out    [rows, d] KVQ_F32 or KVQ_F16 (out_dt), written
+ * Errors: NULL, ALIGN, SHAPE, DTYPE.
+ */
+kvq_status kvq_dequantize_int8(const int8_t* codes, const float* scales, int64_t rows,
+                               int32_t d, void* out, kvq_dtype out_dt, kvq_stream_t stream);
+
+/*
+ * kvq_scores_int8 - decode-query scores against INT8 keys, scale folded.
+ *
+ * The attention-score use of INT8 keys in the INT8 KV-cache paper (arXiv
+ * 2601.04719, Abstract: error of attention scores computed from quantized
+ * keys).  The query is not quantized; the row scale is pulled out of the dot
+ * product:
+ *   scores[g, j, t] = s_{g,t} * sum_i q[g, j, i] * c[g, t, i]
+ * accumulated in binary32.  Agrees with the exact value within
+ * 1e-5 * s_{g,t} * sum_i |q[g, j, i] * c[g, t, i]|.
+ *
+ * q       [groups, nq, d] KVQ_F32 or KVQ_F16 (q_dt)
+ * codes   [groups, T, d] int8;  scales [groups, T] binary32
+ * scores  [groups, nq, T] binary32, written
+ * 1 <= nq <= 64; d as for kvq_quantize_int8.
+ * Errors: NULL, ALIGN, SHAPE, DTYPE.
+ */
+kvq_status kvq_scores_int8(const void* q, kvq_dtype q_dt, int64_t groups, int32_t nq,
+                           const int8_t* codes, const float* scales, int64_t T, int32_t d,
+                           float* scores, kvq_stream_t stream);
+
+/*
+ * kvq_qjl_sketch - QJL sketch of key rows: sign bits of a JL projection plus
+ * the key norm.
+ *
+ * From the QJL paper (arXiv 2406.03482, abstract: a Johnson-Lindenstrauss
+ * transform followed by sign-bit quantization, no stored quantization
+ * constants).  For each row k_r of k [rows, d] and S [m, d]:
+ *   P_ri  = sum_j S_ij k_rj            (binary32 accumulation)
+ *   bit i = [P_ri >= 0], stored in word i / 32 at bit i % 32 (LSB first)
+ *   norm  = RN16(sqrt(sum_j k_rj^2))   (binary32 accumulation, correctly
+ *                                        rounded sqrt, then binary16)
+ * A bit may differ from the exact-arithmetic sign only where
+ * |P_ri| <= 1e-4 * ||S_i|| * ||k_r||; a norm may differ from RN16 of the
+ * exact norm by one binary16 ulp.  KVQ_F16 keys use fp16 matrix cores with
+ * binary32 accumulation (products of binary16 values are exact).
+ *
+ * k      [rows, d] (k_dt);  S [m, d] with the same element type as k
+ * bits   [rows, m / 32] uint32, written
+ * norms  [rows] binary16 bit patterns, written
+ * d as for kvq_quantize_int8; 32 <= m <= 1024, m % 32 == 0.
+ * Errors: NULL, ALIGN, SHAPE, DTYPE.
+ */
+kvq_status kvq_qjl_sketch(const void* k, kvq_dtype k_dt, int64_t rows, int32_t d,
+                          const void* S, int32_t m, uint32_t* bits, uint16_t* norms,
+                          kvq_stream_t stream);
+
+/*
+ * kvq_scores_qjl - asymmetric QJL inner-product estimate of decode queries
+ * against sketched keys.
+ *
+ * From the QJL paper (arXiv 2406.03482, abstract: the other vector gets the
+ * JL transform without quantization; the combination is an unbiased
+ * estimate of the inner product).  With y = S q (binary32, not quantized):
+ *   scores[g, j, t] = sqrt(pi/2) / m * norm_{g,t} * sum_i (2 b_{g,t,i} - 1) * y_i
+ * Given identical bits and norms, agrees with the exact value within
+ * 1e-4 * ||q|| * norm_{g,t}.
+ *
+ * q      [groups, nq, d] (q_dt);  S [m, d] (S_dt; KVQ_F32 or KVQ_F16)
+ * bits   [groups, T, m / 32] uint32;  norms [groups, T] binary16 patterns
+ * scores [groups, nq, T] binary32, written
+ * 1 <= nq <= 64; d, m as for kvq_qjl_sketch.
+ * Errors: NULL, ALIGN, SHAPE, DTYPE.
+ */
+kvq_status kvq_scores_qjl(const void* q, kvq_dtype q_dt, int64_t groups, int32_t nq,
+                          const void* S, kvq_dtype S_dt, int32_t m, const uint32_t* bits,
+                          const uint16_t* norms, int64_t T, int32_t d, float* scores,
+                          kvq_stream_t stream);
+
+/*
+ * kvq_decode_workspace_bytes - size of the scratch buffer kvq_decode_qjl_int8
+ * needs for `groups` groups of T tokens and head dimension d (0 when nothing
+ * is needed).  The value depends only on the arguments and on the number of
+ * compute units of the current device.
+ */
+size_t kvq_decode_workspace_bytes(int64_t groups, int64_t T, int32_t d);
+
+/*
+ * kvq_decode_qjl_int8 - one decode step of attention over a compressed
+ * cache: QJL-sketched keys and INT8 values, one query per group.
+ *
+ * Composes the QJL estimate (arXiv 2406.03482, abstract) for the keys with
+ * the INT8 reconstruction (Q-TensorFormer model card, section 6) for the
+ * values, consumed by scaled-dot-product attention (the attention engine of
+ * the same card's architecture diagram):
+ *   sigma_t = QJL estimate of <q, k_t>            (as kvq_scores_qjl)
+ *   p_t     = softmax_t(sm_scale * sigma_t)       (binary32)
+ *   out[g, :] = sum_t p_t * vscale_t * vcodes[t, :]
+ * Tokens are split across workgroups and merged with the log-sum-exp rule,
+ * so the result is independent of the split up to binary32 rounding.
+ * Given identical compressed inputs, each output agrees with the exact value
+ * within 1e-4 * sum_t p_t * |vscale_t * vcodes[t, j]| + 1e-6.
+ *
+ * q       [groups, d] (q_dt);  S [m, d] (S_dt)
+ * kbits   [groups, T, m / 32] uint32;  knorms [groups, T] binary16 patterns
+ * vcodes  [groups, T, d] int8;  vscales [groups, T] binary32
+ * ws      device scratch of ws_bytes >= kvq_decode_workspace_bytes(groups, T, d)
+ *         bytes (may be NULL when that size is 0); its contents on entry are
+ *         ignored and on exit unspecified; concurrent calls need distinct ws.
+ * out     [groups, d] binary32, written
+ * T >= 1 when groups > 0; d, m as for kvq_qjl_sketch.
+ * Errors: NULL, ALIGN, SHAPE, DTYPE, WORKSPACE.
+ */
+kvq_status kvq_decode_qjl_int8(const void* q, kvq_dtype q_dt, int64_t groups, const void* S,
+                               kvq_dtype S_dt, int32_t m, const uint32_t* kbits,
+                               const uint16_t* knorms, const int8_t* vcodes,
+                               const float* vscales, int64_t T, int32_t d, float sm_scale,
+                               void* ws, size_t ws_bytes, float* out, kvq_stream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* kvq_status_string(kvq_status status);
+
+/* Detail of the last non-OK status returned on the calling thread
+ * (thread-local; empty string if none). */
+const char* kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,18 @@
+"""kv_cache_compression_kvq_amd: KV-cache compression for AMD Instinct MI355X.
+
+Per-row symmetric INT8 quantization and the QJL key sketch, with decode-time
+scoring and attention over the compressed cache, implemented as hand-written
+gfx950 HIP kernels behind the C ABI of ``include/kvq.h`` (``libkvq.so``).
+This package is the thin Python binding: torch supplies device memory and
+streams; every step of the computation runs in libkvq.
+"""
+from ._lib import KvqError, LIB_PATH, lib  # noqa: F401
+from .ops import (  # noqa: F401
+    decode_qjl_int8,
+    decode_workspace_bytes,
+    dequantize_int8,
+    qjl_sketch,
+    quantize_int8,
+    scores_int8,
+    scores_qjl,
+)

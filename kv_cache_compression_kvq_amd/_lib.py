@@ -1,0 +1,68 @@
+"""ctypes loader for libkvq.so (the C ABI declared in include/kvq.h).
+
+The shared library is built in-tree by ``kv_cache_compression_kvq_amd.build``.
+Loading fails loudly when it is missing: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import c_float, c_int32, c_int64, c_size_t, c_void_p, c_char_p
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvq.so")
+
+KVQ_OK, KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_ALIGN = 0, 1, 2, 3
+KVQ_ERR_DTYPE, KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH = 4, 5, 6
+KVQ_F32, KVQ_F16 = 0, 1
+
+# name -> (restype, argtypes), mirroring include/kvq.h
+PROTOTYPES = {
+    "kvq_quantize_int8": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
+    "kvq_dequantize_int8": (c_int32, [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_int32, c_void_p]),
+    "kvq_scores_int8": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_void_p, c_void_p, c_int64,
+                                  c_int32, c_void_p, c_void_p]),
+    "kvq_qjl_sketch": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_void_p, c_int32, c_void_p,
+                                 c_void_p, c_void_p]),
+    "kvq_scores_qjl": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_void_p, c_int32, c_int32,
+                                 c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p]),
+    "kvq_decode_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int32]),
+    "kvq_decode_qjl_int8": (c_int32, [c_void_p, c_int32, c_int64, c_void_p, c_int32, c_int32,
+                                      c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32,
+                                      c_float, c_void_p, c_size_t, c_void_p, c_void_p]),
+    "kvq_status_string": (c_char_p, [c_int32]),
+    "kvq_last_error": (c_char_p, []),
+}
+
+
+class KvqError(RuntimeError):
+    """A non-OK status from libkvq (``status`` holds the code)."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is not built; run `python -m kv_cache_compression_kvq_amd.build` "
+                "(the library has no CPU fallback)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in PROTOTYPES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def check(status: int) -> None:
+    if status != KVQ_OK:
+        L = lib()
+        raise KvqError(status, f"{L.kvq_status_string(status).decode()}: {L.kvq_last_error().decode()}")

@@ -1,0 +1,321 @@
+// One decode step of attention over a compressed cache for gfx950: keys as
+// QJL sign sketches (arXiv 2406.03482, abstract: sign bits of a JL
+// projection, scored against the unquantized projection of the query),
+// values as per-row INT8 codes with a binary32 scale (symmetric INT8 formula
+// of the Q-TensorFormer model card, section 6), consumed by softmax
+// attention:
+//   sigma_t = sqrt(pi/2)/m * n_t * sum_i (2 b_ti - 1) (S q)_i
+//   out     = sum_t softmax_t(lam * sigma_t) * s_t * c_t
+//
+// Work split: the T tokens of a (batch, head) group are cut into `splits`
+// ranges; one workgroup per (group, range) builds y = S q and the byte tables
+// in LDS, streams its tokens once (sign words, norm, value codes, value
+// scale) and keeps a running max / sum / weighted value sum per wave
+// (online softmax).  The four waves are merged in LDS and the workgroup
+// writes (max, sum, o[d]) to the workspace; a second kernel merges the
+// ranges with the log-sum-exp rule.  Nothing is materialised per token.
+//
+// Value codes are read 16 per lane (one 16-byte load) with LPV = d / 16
+// lanes per token row, so a wave's load covers 64 / LPV whole rows (1 KiB);
+// they are issued at the top of each 64-token chunk, before the scores that
+// weight them are known, to keep HBM busy.
+#include "kvq_device.h"
+#include "kvq_launch.h"
+#include "kvq_qjl_device.h"
+
+#include <algorithm>
+#include <cmath>
+
+namespace kvq {
+
+constexpr int kDecodeChunk = 64;                       // tokens per wave step
+constexpr int kDecodeBlockTokens = 4 * kDecodeChunk;   // tokens per workgroup step
+constexpr int kDecodeMaxD = 1024;
+
+// DPP row rotate (lane i takes lane (i + n) % 16 of its 16-lane row).
+template <int N>
+__device__ __forceinline__ float dpp_ror_f32(float v) {
+  return dpp_f32<0x120 + N>(v);
+}
+
+// Sum over the lanes that share lane % LPV (the `slot` bits above it).
+template <int LPV>
+__device__ __forceinline__ float slot_sum(float v) {
+  if constexpr (LPV <= 4) v += dpp_ror_f32<4>(v);
+  if constexpr (LPV <= 8) v += dpp_ror_f32<8>(v);
+  if constexpr (LPV <= 16) v += swz_xor16_f32(v);
+  if constexpr (LPV <= 32) v += xor32_f32(v);
+  return v;
+}
+
+__device__ __forceinline__ float bcast_from(float v, int src_lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src_lane << 2, __builtin_bit_cast(int, v)));
+}
+
+template <typename TS, typename TQ, int W, int LPV>
+__global__ __launch_bounds__(256) void decode_split_kernel(
+    const TQ* __restrict__ q, const TS* __restrict__ S, int m_rt, int d,
+    const uint32_t* __restrict__ kbits, const uint16_t* __restrict__ knorms,
+    const int8_t* __restrict__ vcodes, const float* __restrict__ vscales, int64_t T,
+    int64_t splits, int64_t tps, float lam, float* __restrict__ partials) {
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  const int m = W > 0 ? 32 * W : m_rt;
+  const int words = m / 32;
+  float* y = reinterpret_cast<float*>(lds_raw);
+  float* lut = y + m;
+  float* wpart = lut + (m / 8) * 256;                  // [4][d + 2]
+
+  const int64_t g = blockIdx.x / splits;
+  const int64_t sp = blockIdx.x % splits;
+  const int64_t t_begin = sp * tps;
+  const int64_t t_end = std::min<int64_t>(T, t_begin + tps);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+
+  project_query(S, q + g * d, m, d, y);
+  __syncthreads();
+  build_byte_tables(y, m / 8, lut);
+  __syncthreads();
+
+  constexpr int SLOTS = kWave / LPV;      // value rows per wave load
+  constexpr int VSTEPS = kDecodeChunk / SLOTS;
+  constexpr bool PREFETCH = LPV <= 16;
+  const int sub = lane % LPV;
+  const int slot = lane / LPV;
+  const int cpr = d / 16;                  // 16-code chunks per value row
+  const bool sub_live = sub < cpr;         // LPV == 64 covers d < 1024 with idle lanes
+  const float c = kSqrtHalfPi / (float)m;
+  const uint32_t* bg = kbits + g * T * words;
+  const uint16_t* ng = knorms + g * T;
+  const int8_t* vg = vcodes + g * T * d;
+  const float* sg = vscales + g * T;
+
+  float M = -INFINITY, L = 0.0f;
+  float o[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) o[e] = 0.0f;
+
+  for (int64_t base = t_begin + wave * kDecodeChunk; base < t_end; base += kDecodeBlockTokens) {
+    const int64_t t = base + lane;
+    const bool valid = t < t_end;
+    // value codes of this chunk (independent of the scores)
+    u32x4 vc[PREFETCH ? VSTEPS : 1];
+    if constexpr (PREFETCH) {
+#pragma unroll
+      for (int i = 0; i < VSTEPS; ++i) {
+        const int64_t tv = base + i * SLOTS + slot;
+        vc[i] = (tv < t_end && sub_live) ? *reinterpret_cast<const u32x4*>(vg + tv * d + sub * 16)
+                                         : u32x4{};
+      }
+    }
+    // score of token t
+    float z = -INFINITY, vs = 0.0f;
+    if (valid) {
+      float acc;
+      if constexpr (W > 0) {
+        uint32_t wv[W];
+#pragma unroll
+        for (int i = 0; i < W; i += 4) {
+          const u32x4 v4 = *reinterpret_cast<const u32x4*>(bg + t * W + i);
+          wv[i] = v4[0]; wv[i + 1] = v4[1]; wv[i + 2] = v4[2]; wv[i + 3] = v4[3];
+        }
+        acc = lut_sum(lut, wv, W);
+      } else {
+        acc = 0.0f;
+        for (int i = 0; i < words; ++i) {
+          const uint32_t x = bg[t * words + i];
+          acc += lut_sum(lut + i * 1024, &x, 1);
+        }
+      }
+      const float n = (float)__builtin_bit_cast(_Float16, ng[t]);
+      z = lam * (c * n * acc);
+      vs = sg[t];
+    }
+    // online softmax update (lane 0 of every chunk is valid, so mx is finite)
+    const float mx = seg_max_f32<64>(z);
+    const float M_new = __builtin_fmaxf(M, mx);
+    const float alpha = (M == -INFINITY) ? 0.0f : __expf(M - M_new);
+    const float p = valid ? __expf(z - M_new) : 0.0f;
+    L = L * alpha + seg_sum_f32<64>(p);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[e] *= alpha;
+    M = M_new;
+    const float ps = p * vs;
+    // o += p_t * s_t * c_t over the chunk's value rows
+    if constexpr (PREFETCH) {
+#pragma unroll
+      for (int i = 0; i < VSTEPS; ++i) {
+        const float w = bcast_from(ps, i * SLOTS + slot);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[e] = __builtin_fmaf(w, i8_to_f32(vc[i][e >> 2], e & 3), o[e]);
+      }
+    } else {
+      for (int i = 0; i < VSTEPS; ++i) {
+        const float w = bcast_from(ps, i * SLOTS + slot);
+        const int64_t tv = base + i * SLOTS + slot;
+        const u32x4 cw = (tv < t_end && sub_live)
+                             ? *reinterpret_cast<const u32x4*>(vg + tv * d + sub * 16)
+                             : u32x4{};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[e] = __builtin_fmaf(w, i8_to_f32(cw[e >> 2], e & 3), o[e]);
+      }
+    }
+  }
+
+  // merge the slots of the wave, then the four waves of the workgroup
+#pragma unroll
+  for (int e = 0; e < 16; ++e) o[e] = slot_sum<LPV>(o[e]);
+  float* wp = wpart + wave * (d + 2);
+  if (lane == 0) {
+    wp[0] = M;
+    wp[1] = L;
+  }
+  if (slot == 0 && sub_live) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) wp[2 + sub * 16 + e] = o[e];
+  }
+  __syncthreads();
+  float Mw[4], Ms = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    Mw[w] = wpart[w * (d + 2)];
+    Ms = __builtin_fmaxf(Ms, Mw[w]);
+  }
+  float sc[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) sc[w] = (Mw[w] == -INFINITY) ? 0.0f : __expf(Mw[w] - Ms);
+  float* out = partials + (g * splits + sp) * (int64_t)(d + 2);
+  if (threadIdx.x == 0) {
+    float Ls = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) Ls += sc[w] * wpart[w * (d + 2) + 1];
+    out[0] = Ms;
+    out[1] = Ls;
+  }
+  for (int j = threadIdx.x; j < d; j += 256) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (sc[w] != 0.0f) acc += sc[w] * wpart[w * (d + 2) + 2 + j];
+    out[2 + j] = acc;
+  }
+}
+
+// out[g, j] = sum_k e^{M_k - M} o_k[j] / sum_k e^{M_k - M} L_k over the splits.
+__global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ partials,
+                                                           int64_t groups, int64_t splits, int d,
+                                                           float* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= groups * d) return;
+  const int64_t g = idx / d;
+  const int j = (int)(idx % d);
+  const float* pg = partials + g * splits * (int64_t)(d + 2);
+  float Ms = -INFINITY;
+  for (int64_t k = 0; k < splits; ++k) Ms = __builtin_fmaxf(Ms, pg[k * (d + 2)]);
+  float num = 0.0f, den = 0.0f;
+  for (int64_t k = 0; k < splits; ++k) {
+    const float Mk = pg[k * (d + 2)];
+    if (Mk == -INFINITY) continue;
+    const float wgt = __expf(Mk - Ms);
+    den += wgt * pg[k * (d + 2) + 1];
+    num += wgt * pg[k * (d + 2) + 2 + j];
+  }
+  out[idx] = num / den;
+}
+
+DecodeSplit decode_split(int64_t groups, int64_t T, const DeviceInfo& dev) {
+  DecodeSplit s;
+  const int64_t target_blocks = 8LL * std::max(1, dev.cus);
+  const int64_t max_splits = std::max<int64_t>(1, (T + kDecodeBlockTokens - 1) / kDecodeBlockTokens);
+  int64_t splits = std::min(max_splits, std::max<int64_t>(1, (target_blocks + groups - 1) / groups));
+  int64_t tps = (T + splits - 1) / splits;
+  tps = (tps + kDecodeBlockTokens - 1) / kDecodeBlockTokens * kDecodeBlockTokens;
+  s.tokens_per_split = tps;
+  s.splits = (T + tps - 1) / tps;
+  return s;
+}
+
+size_t decode_workspace_bytes(int64_t groups, int64_t T, int d, const DeviceInfo& dev) {
+  const DecodeSplit s = decode_split(groups, T, dev);
+  return (size_t)groups * (size_t)s.splits * (size_t)(d + 2) * sizeof(float);
+}
+
+static size_t decode_lds_bytes(int m, int d) {
+  return ((size_t)m + (size_t)(m / 8) * 256 + 4 * (size_t)(d + 2)) * sizeof(float);
+}
+
+template <typename TS, typename TQ, int W, int LPV>
+static hipError_t decode_launch(const TQ* q, int64_t groups, const TS* S, int m,
+                                const uint32_t* kbits, const uint16_t* knorms,
+                                const int8_t* vcodes, const float* vscales, int64_t T, int d,
+                                float lam, float* partials, const DecodeSplit& sp, hipStream_t st) {
+  const size_t lds = decode_lds_bytes(m, d);
+  hipError_t e0 = allow_dynamic_lds(decode_split_kernel<TS, TQ, W, LPV>, lds);
+  if (e0 != hipSuccess) return e0;
+  const int64_t max_groups = std::max<int64_t>(1, (int64_t(1) << 22) / sp.splits);
+  for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
+    const int64_t ng = std::min(max_groups, groups - g0);
+    hipLaunchKernelGGL((decode_split_kernel<TS, TQ, W, LPV>), dim3((unsigned)(ng * sp.splits)),
+                       dim3(256), lds, st, q + g0 * d, S, m, d, kbits + g0 * T * (m / 32),
+                       knorms + g0 * T, vcodes + g0 * T * d, vscales + g0 * T, T, sp.splits,
+                       sp.tokens_per_split, lam, partials + g0 * sp.splits * (d + 2));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename TS, typename TQ>
+static hipError_t decode_typed(const TQ* q, int64_t groups, const TS* S, int m,
+                               const uint32_t* kbits, const uint16_t* knorms, const int8_t* vcodes,
+                               const float* vscales, int64_t T, int d, float lam, float* partials,
+                               float* out, const DeviceInfo& dev, hipStream_t st) {
+  if (d > kDecodeMaxD || decode_lds_bytes(m, d) > dev.lds_per_block)
+    return hipErrorInvalidConfiguration;
+  const DecodeSplit sp = decode_split(groups, T, dev);
+  hipError_t e;
+  if (m == 256 && d == 128)
+    e = decode_launch<TS, TQ, 8, 8>(q, groups, S, m, kbits, knorms, vcodes, vscales, T, d, lam,
+                                    partials, sp, st);
+  else if (d == 64)
+    e = decode_launch<TS, TQ, 0, 4>(q, groups, S, m, kbits, knorms, vcodes, vscales, T, d, lam,
+                                    partials, sp, st);
+  else if (d == 128)
+    e = decode_launch<TS, TQ, 0, 8>(q, groups, S, m, kbits, knorms, vcodes, vscales, T, d, lam,
+                                    partials, sp, st);
+  else if (d == 256)
+    e = decode_launch<TS, TQ, 0, 16>(q, groups, S, m, kbits, knorms, vcodes, vscales, T, d, lam,
+                                     partials, sp, st);
+  else
+    e = decode_launch<TS, TQ, 0, 64>(q, groups, S, m, kbits, knorms, vcodes, vscales, T, d, lam,
+                                     partials, sp, st);
+  if (e != hipSuccess) return e;
+  const int64_t n = groups * d;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     partials, groups, sp.splits, d, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_qjl_int8(const void* q, int q_f16, int64_t groups, const void* S,
+                                  int S_f16, int m, const uint32_t* kbits, const uint16_t* knorms,
+                                  const int8_t* vcodes, const float* vscales, int64_t T, int d,
+                                  float sm_scale, void* ws, float* out, const DeviceInfo& dev,
+                                  hipStream_t st) {
+  float* partials = static_cast<float*>(ws);
+  if (S_f16) {
+    const _Float16* Sp = static_cast<const _Float16*>(S);
+    if (q_f16)
+      return decode_typed(static_cast<const _Float16*>(q), groups, Sp, m, kbits, knorms, vcodes,
+                          vscales, T, d, sm_scale, partials, out, dev, st);
+    return decode_typed(static_cast<const float*>(q), groups, Sp, m, kbits, knorms, vcodes,
+                        vscales, T, d, sm_scale, partials, out, dev, st);
+  }
+  const float* Sp = static_cast<const float*>(S);
+  if (q_f16)
+    return decode_typed(static_cast<const _Float16*>(q), groups, Sp, m, kbits, knorms, vcodes,
+                        vscales, T, d, sm_scale, partials, out, dev, st);
+  return decode_typed(static_cast<const float*>(q), groups, Sp, m, kbits, knorms, vcodes, vscales,
+                      T, d, sm_scale, partials, out, dev, st);
+}
+
+}  // namespace kvq

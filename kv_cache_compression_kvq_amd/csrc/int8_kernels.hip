@@ -1,0 +1,471 @@
+// Per-row symmetric INT8 quantize / dequantize / scale-folded score for gfx950.
+//
+// Method: the symmetric INT8 formula of the Q-TensorFormer model card
+// (section 6, "Adaptive KV Cache Quantization & Attention-Sink Eviction"):
+// the row scale is max|x| / 127, a code is the nearest integer of x / scale
+// clamped to [-128, 127], the reconstruction is code * scale; applied per
+// token as in the INT8 KV-cache paper (arXiv 2601.04719, Abstract).
+//
+// Arithmetic: s = a / 127 and t = x / s are IEEE binary32 divisions (the
+// compiler's correctly rounded sequence; no fast-math, denormals kept);
+// rint rounds half to even; the clamp is a med3.  A zero scale divides by 1
+// instead, which maps every value of such a row (all |x| < 127 * 2^-150) to
+// code 0.
+//
+// Memory: all three kernels are HBM streams.  Lanes are mapped so that each
+// load instruction of a wave reads 1 KiB of contiguous memory (16 B per
+// lane); rows are reduced across lanes with DPP/swizzle, never through LDS,
+// except for rows longer than one wave can hold (one row per workgroup).
+#include "kvq_device.h"
+#include "kvq_launch.h"
+
+#include <algorithm>
+
+namespace kvq {
+
+template <typename T> struct Chunk;
+template <> struct Chunk<float> {
+  static constexpr int N = 4;          // elements per 16-byte chunk
+  using V = f32x4;
+  using Codes = uint32_t;              // 4 codes
+};
+template <> struct Chunk<_Float16> {
+  static constexpr int N = 8;
+  using V = f16x8;
+  using Codes = u32x2;                 // 8 codes
+};
+
+__device__ __forceinline__ uint32_t code_of(float x, float sdiv) {
+  float t = x / sdiv;                                  // RN32(x / s)
+  float r = __builtin_rintf(t);                        // ties to even
+  r = __builtin_amdgcn_fmed3f(r, -128.0f, 127.0f);
+  return (uint32_t)(int)r & 0xFFu;
+}
+
+template <typename T>
+__device__ __forceinline__ typename Chunk<T>::Codes encode_chunk(const typename Chunk<T>::V& v,
+                                                                 float sdiv) {
+  if constexpr (Chunk<T>::N == 4) {
+    uint32_t c0 = code_of(v[0], sdiv), c1 = code_of(v[1], sdiv);
+    uint32_t c2 = code_of(v[2], sdiv), c3 = code_of(v[3], sdiv);
+    return c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+  } else {
+    u32x2 out;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t c0 = code_of((float)v[4 * h + 0], sdiv), c1 = code_of((float)v[4 * h + 1], sdiv);
+      uint32_t c2 = code_of((float)v[4 * h + 2], sdiv), c3 = code_of((float)v[4 * h + 3], sdiv);
+      out[h] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    }
+    return out;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ uint32_t chunk_absmax(const typename Chunk<T>::V& v) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int e = 0; e < Chunk<T>::N; ++e) m = max(m, abs_bits((float)v[e]));
+  return m;
+}
+
+// Scale from the row's max |x| (bit pattern of a non-negative float).
+__device__ __forceinline__ float row_scale(uint32_t amax_bits) {
+  return __builtin_bit_cast(float, amax_bits) / 127.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Quantize, rows shorter than a wave: LPR lanes per row, CPL 16-byte chunks
+// per lane and row, UNROLL independent row passes per wave for memory-level
+// parallelism.  d == LPR * CPL * N.
+template <typename T, int LPR, int CPL, int UNROLL>
+__global__ __launch_bounds__(256) void quantize_lanes_kernel(const T* __restrict__ x, int64_t rows,
+                                                             int8_t* __restrict__ codes,
+                                                             float* __restrict__ scales) {
+  using C = Chunk<T>;
+  constexpr int N = C::N;
+  constexpr int CPR = LPR * CPL;
+  constexpr int D = CPR * N;
+  constexpr int RPP = kWave / LPR;  // rows per pass
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int sub = lane % LPR;
+  const int rr = lane / LPR;
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * (RPP * UNROLL);
+
+  typename C::V v[UNROLL][CPL];
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const int64_t row = row0 + u * RPP + rr;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      if (row < rows)
+        v[u][j] = *reinterpret_cast<const typename C::V*>(x + row * D + (int64_t)(sub + LPR * j) * N);
+      else
+        v[u][j] = typename C::V{};
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const int64_t row = row0 + u * RPP + rr;
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) m = max(m, chunk_absmax<T>(v[u][j]));
+    m = seg_max_u32<LPR>(m);
+    const float s = row_scale(m);
+    const float sdiv = (s == 0.0f) ? 1.0f : s;
+    if (row < rows) {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        *reinterpret_cast<typename C::Codes*>(codes + row * D + (int64_t)(sub + LPR * j) * N) =
+            encode_chunk<T>(v[u][j], sdiv);
+      }
+      if (sub == 0) scales[row] = s;
+    }
+  }
+}
+
+// Quantize, one row per 256-thread workgroup held in registers:
+// d == 256 * CPL * N.
+template <typename T, int CPL>
+__global__ __launch_bounds__(256) void quantize_block_kernel(const T* __restrict__ x, int64_t rows,
+                                                             int8_t* __restrict__ codes,
+                                                             float* __restrict__ scales) {
+  using C = Chunk<T>;
+  constexpr int N = C::N;
+  constexpr int D = 256 * CPL * N;
+  __shared__ uint32_t wave_max[4];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const T* xr = x + row * D;
+  typename C::V v[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j)
+    v[j] = *reinterpret_cast<const typename C::V*>(xr + (int64_t)(tid + 256 * j) * N);
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) m = max(m, chunk_absmax<T>(v[j]));
+  m = seg_max_u32<64>(m);
+  if ((tid & 63) == 0) wave_max[tid >> 6] = m;
+  __syncthreads();
+  m = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
+  const float s = row_scale(m);
+  const float sdiv = (s == 0.0f) ? 1.0f : s;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j)
+    *reinterpret_cast<typename C::Codes*>(codes + row * D + (int64_t)(tid + 256 * j) * N) =
+        encode_chunk<T>(v[j], sdiv);
+  if (tid == 0) scales[row] = s;
+}
+
+// Quantize, any d % 16 == 0: one row per wave, a max pass and a code pass.
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_generic_kernel(const T* __restrict__ x, int64_t rows,
+                                                               int d, int8_t* __restrict__ codes,
+                                                               float* __restrict__ scales) {
+  using C = Chunk<T>;
+  constexpr int N = C::N;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // uniform per wave
+  const int cpr = d / N;
+  const T* xr = x + row * d;
+  uint32_t m = 0;
+  for (int c = lane; c < cpr; c += kWave)
+    m = max(m, chunk_absmax<T>(*reinterpret_cast<const typename C::V*>(xr + (int64_t)c * N)));
+  m = seg_max_u32<64>(m);
+  const float s = row_scale(m);
+  const float sdiv = (s == 0.0f) ? 1.0f : s;
+  for (int c = lane; c < cpr; c += kWave)
+    *reinterpret_cast<typename C::Codes*>(codes + row * d + (int64_t)c * N) =
+        encode_chunk<T>(*reinterpret_cast<const typename C::V*>(xr + (int64_t)c * N), sdiv);
+  if (lane == 0) scales[row] = s;
+}
+
+template <typename T>
+static hipError_t quantize_dispatch(const T* x, int64_t rows, int d, int8_t* codes, float* scales,
+                                    hipStream_t st) {
+  constexpr int N = Chunk<T>::N;
+  const int cpr = d / N;
+  const bool pow2 = (cpr & (cpr - 1)) == 0;
+  auto lanes = [&](auto kernel, int lpr, int unroll) {
+    const int64_t rows_per_block = 4LL * (kWave / lpr) * unroll;
+    const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, rows, codes, scales);
+    return hipGetLastError();
+  };
+  auto block = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)rows), dim3(256), 0, st, x, rows, codes, scales);
+    return hipGetLastError();
+  };
+  if (pow2) {
+    switch (cpr) {
+      case 1: return lanes(quantize_lanes_kernel<T, 1, 1, 8>, 1, 8);
+      case 2: return lanes(quantize_lanes_kernel<T, 2, 1, 8>, 2, 8);
+      case 4: return lanes(quantize_lanes_kernel<T, 4, 1, 8>, 4, 8);
+      case 8: return lanes(quantize_lanes_kernel<T, 8, 1, 8>, 8, 8);
+      case 16: return lanes(quantize_lanes_kernel<T, 16, 1, 8>, 16, 8);
+      case 32: return lanes(quantize_lanes_kernel<T, 32, 1, 8>, 32, 8);
+      case 64: return lanes(quantize_lanes_kernel<T, 64, 1, 4>, 64, 4);
+      case 128: return lanes(quantize_lanes_kernel<T, 64, 2, 4>, 64, 4);
+      case 256: return lanes(quantize_lanes_kernel<T, 64, 4, 2>, 64, 2);
+      case 512: return lanes(quantize_lanes_kernel<T, 64, 8, 1>, 64, 1);
+      case 1024: return block(quantize_block_kernel<T, 4>);
+      case 2048: return block(quantize_block_kernel<T, 8>);
+      case 4096: return block(quantize_block_kernel<T, 16>);
+      default: break;
+    }
+  }
+  const int64_t blocks = (rows + 3) / 4;
+  hipLaunchKernelGGL(quantize_generic_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, st, x, rows,
+                     d, codes, scales);
+  return hipGetLastError();
+}
+
+// Rows per launch: keeps every grid far below 2^32 threads.
+constexpr int64_t kRowsPerLaunch = int64_t(1) << 22;
+
+template <typename T>
+static hipError_t quantize_sliced(const T* x, int64_t rows, int d, int8_t* codes, float* scales,
+                                  hipStream_t s) {
+  for (int64_t r0 = 0; r0 < rows; r0 += kRowsPerLaunch) {
+    const int64_t nr = std::min(kRowsPerLaunch, rows - r0);
+    hipError_t e = quantize_dispatch(x + r0 * d, nr, d, codes + r0 * d, scales + r0, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_quantize_int8(const void* x, int x_f16, int64_t rows, int d, int8_t* codes,
+                                float* scales, hipStream_t s) {
+  if (x_f16) return quantize_sliced(static_cast<const _Float16*>(x), rows, d, codes, scales, s);
+  return quantize_sliced(static_cast<const float*>(x), rows, d, codes, scales, s);
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize: a flat stream of 16-byte output chunks; chunk i of the output
+// belongs to row i / (d / N).  UNROLL chunks per thread, consecutive threads
+// on consecutive chunks.
+template <typename TO> struct OutChunk;
+template <> struct OutChunk<float> {
+  static constexpr int N = 4;
+  using V = f32x4;
+  using Codes = uint32_t;
+};
+template <> struct OutChunk<_Float16> {
+  static constexpr int N = 8;
+  using V = f16x8;
+  using Codes = u32x2;
+};
+
+template <typename TO>
+__device__ __forceinline__ typename OutChunk<TO>::V decode_chunk(typename OutChunk<TO>::Codes c,
+                                                                 float s) {
+  typename OutChunk<TO>::V out;
+  if constexpr (OutChunk<TO>::N == 4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = i8_to_f32(c, e) * s;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (_Float16)(i8_to_f32(c[e >> 2], e & 3) * s);
+  }
+  return out;
+}
+
+template <typename TO, int UNROLL, bool POW2>
+__global__ __launch_bounds__(256) void dequantize_flat_kernel(const int8_t* __restrict__ codes,
+                                                              const float* __restrict__ scales,
+                                                              int64_t nchunks, int cpr_shift, int cpr,
+                                                              TO* __restrict__ out) {
+  using C = OutChunk<TO>;
+  constexpr int N = C::N;
+  const int64_t base = (int64_t)blockIdx.x * (256 * UNROLL) + threadIdx.x;
+  typename C::Codes cv[UNROLL];
+  float sv[UNROLL];
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const int64_t i = base + 256 * u;
+    if (i < nchunks) {
+      const int64_t row = POW2 ? (i >> cpr_shift) : (i / cpr);
+      cv[u] = *reinterpret_cast<const typename C::Codes*>(codes + i * N);
+      sv[u] = scales[row];
+    } else {
+      cv[u] = typename C::Codes{};
+      sv[u] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const int64_t i = base + 256 * u;
+    if (i < nchunks) *reinterpret_cast<typename C::V*>(out + i * N) = decode_chunk<TO>(cv[u], sv[u]);
+  }
+}
+
+template <typename TO>
+static hipError_t dequantize_dispatch(const int8_t* codes, const float* scales, int64_t rows, int d,
+                                      TO* out, hipStream_t st) {
+  constexpr int N = OutChunk<TO>::N;
+  constexpr int UNROLL = 4;
+  const int cpr = d / N;
+  const int64_t nchunks = rows * cpr;
+  const int64_t blocks = (nchunks + 256 * UNROLL - 1) / (256 * UNROLL);
+  if ((cpr & (cpr - 1)) == 0) {
+    const int shift = __builtin_ctz((unsigned)cpr);
+    hipLaunchKernelGGL((dequantize_flat_kernel<TO, UNROLL, true>), dim3((unsigned)blocks), dim3(256),
+                       0, st, codes, scales, nchunks, shift, cpr, out);
+  } else {
+    hipLaunchKernelGGL((dequantize_flat_kernel<TO, UNROLL, false>), dim3((unsigned)blocks),
+                       dim3(256), 0, st, codes, scales, nchunks, 0, cpr, out);
+  }
+  return hipGetLastError();
+}
+
+template <typename TO>
+static hipError_t dequantize_sliced(const int8_t* codes, const float* scales, int64_t rows, int d,
+                                    TO* out, hipStream_t s) {
+  for (int64_t r0 = 0; r0 < rows; r0 += kRowsPerLaunch) {
+    const int64_t nr = std::min(kRowsPerLaunch, rows - r0);
+    hipError_t e = dequantize_dispatch(codes + r0 * d, scales + r0, nr, d, out + r0 * d, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_dequantize_int8(const int8_t* codes, const float* scales, int64_t rows, int d,
+                                  void* out, int out_f16, hipStream_t s) {
+  if (out_f16)
+    return dequantize_sliced(codes, scales, rows, d, static_cast<_Float16*>(out), s);
+  return dequantize_sliced(codes, scales, rows, d, static_cast<float*>(out), s);
+}
+
+// ---------------------------------------------------------------------------
+// Scale-folded INT8 score: 8 lanes per token, 16 codes (one 16-byte chunk)
+// per lane and step; a wave covers 8 tokens per pass and UNROLL passes.  The
+// block's query rows sit in LDS as binary32; queries are processed NQC at a
+// time so every code chunk is converted once per NQC queries.
+constexpr int kScoreLpt = 8;
+constexpr int kScoreUnroll = 4;
+constexpr int kScoreNqc = 4;
+constexpr int kScoreTokensPerBlock = 4 * 8 * kScoreUnroll;  // 128
+constexpr int kScoreLdsFloats = 8192;                       // 32 KiB of queries per pass
+
+// Query values c*16 .. c*16+15 of query row jj, as binary32.
+template <typename TQ, bool QLDS>
+__device__ __forceinline__ void query_chunk(const float* qs, const TQ* qg, int d, int jj, int c,
+                                            float out[16]) {
+  if constexpr (QLDS) {
+    const f32x4* qv = reinterpret_cast<const f32x4*>(qs + jj * d + c * 16);
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const f32x4 v = qv[e4];
+      out[4 * e4 + 0] = v[0]; out[4 * e4 + 1] = v[1]; out[4 * e4 + 2] = v[2]; out[4 * e4 + 3] = v[3];
+    }
+  } else {
+    const TQ* p = qg + (int64_t)jj * d + c * 16;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) out[e] = to_f32(p[e]);
+  }
+}
+
+template <typename TQ, bool QLDS>
+__global__ __launch_bounds__(256) void scores_int8_kernel(const TQ* __restrict__ q, int nq,
+                                                          const int8_t* __restrict__ codes,
+                                                          const float* __restrict__ scales,
+                                                          int64_t T, int d, int64_t tiles,
+                                                          float* __restrict__ scores) {
+  __shared__ float qs[QLDS ? kScoreLdsFloats : 1];
+  const int64_t g = blockIdx.x / tiles;
+  const int64_t tile = blockIdx.x % tiles;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int sub = lane % kScoreLpt;
+  const int slot = lane / kScoreLpt;
+  const int cpr = d / 16;
+  const int64_t t0 = tile * kScoreTokensPerBlock + wave * (8 * kScoreUnroll);
+  const int8_t* cg = codes + g * T * d;
+  const int nq_pass = QLDS ? min(kScoreNqc, kScoreLdsFloats / d) : kScoreNqc;
+
+  for (int j0 = 0; j0 < nq; j0 += nq_pass) {
+    const int nqc = min(nq_pass, nq - j0);
+    const TQ* qg = q + ((int64_t)g * nq + j0) * d;
+    if constexpr (QLDS) {
+      __syncthreads();
+      for (int i = threadIdx.x; i < nqc * d; i += 256) qs[i] = to_f32(qg[i]);
+      __syncthreads();
+    }
+    float acc[kScoreUnroll][kScoreNqc];
+#pragma unroll
+    for (int u = 0; u < kScoreUnroll; ++u)
+#pragma unroll
+      for (int jj = 0; jj < kScoreNqc; ++jj) acc[u][jj] = 0.0f;
+
+    for (int c = sub; c < cpr; c += kScoreLpt) {
+      u32x4 w[kScoreUnroll];
+#pragma unroll
+      for (int u = 0; u < kScoreUnroll; ++u) {
+        const int64_t t = t0 + u * 8 + slot;
+        w[u] = (t < T) ? *reinterpret_cast<const u32x4*>(cg + t * d + (int64_t)c * 16) : u32x4{};
+      }
+#pragma unroll
+      for (int jj = 0; jj < kScoreNqc; ++jj) {
+        if (jj < nqc) {
+          float qv[16];
+          query_chunk<TQ, QLDS>(qs, qg, d, jj, c, qv);
+#pragma unroll
+          for (int u = 0; u < kScoreUnroll; ++u) {
+            float a = acc[u][jj];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) a = __builtin_fmaf(qv[e], i8_to_f32(w[u][e >> 2], e & 3), a);
+            acc[u][jj] = a;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kScoreUnroll; ++u) {
+      const int64_t t = t0 + u * 8 + slot;
+      const float st = (t < T) ? scales[g * T + t] : 0.0f;
+#pragma unroll
+      for (int jj = 0; jj < kScoreNqc; ++jj) {
+        const float tot = seg_sum_f32<kScoreLpt>(acc[u][jj]);
+        if (jj < nqc && sub == 0 && t < T) scores[((int64_t)g * nq + j0 + jj) * T + t] = tot * st;
+      }
+    }
+  }
+}
+
+template <typename TQ>
+static hipError_t scores_dispatch(const TQ* q, int64_t groups, int nq, const int8_t* codes,
+                                  const float* scales, int64_t T, int d, float* scores,
+                                  hipStream_t s) {
+  const int64_t tiles = (T + kScoreTokensPerBlock - 1) / kScoreTokensPerBlock;
+  // launch in slices of whole groups so grid.x stays far below 2^32
+  const int64_t max_groups = std::max<int64_t>(1, (int64_t(1) << 22) / tiles);
+  for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
+    const int64_t ng = std::min(max_groups, groups - g0);
+    const TQ* qp = q + g0 * nq * d;
+    const int8_t* cp = codes + g0 * T * d;
+    const float* sp = scales + g0 * T;
+    float* op = scores + g0 * nq * T;
+    if (d <= kScoreLdsFloats)
+      hipLaunchKernelGGL((scores_int8_kernel<TQ, true>), dim3((unsigned)(ng * tiles)), dim3(256), 0,
+                         s, qp, nq, cp, sp, T, d, tiles, op);
+    else
+      hipLaunchKernelGGL((scores_int8_kernel<TQ, false>), dim3((unsigned)(ng * tiles)), dim3(256),
+                         0, s, qp, nq, cp, sp, T, d, tiles, op);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_scores_int8(const void* q, int q_f16, int64_t groups, int nq,
+                              const int8_t* codes, const float* scales, int64_t T, int d,
+                              float* scores, hipStream_t s) {
+  if (q_f16)
+    return scores_dispatch(static_cast<const _Float16*>(q), groups, nq, codes, scales, T, d,
+                           scores, s);
+  return scores_dispatch(static_cast<const float*>(q), groups, nq, codes, scales, T, d, scores, s);
+}
+
+}  // namespace kvq

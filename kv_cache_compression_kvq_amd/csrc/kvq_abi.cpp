@@ -1,0 +1,259 @@
+// The C ABI of libkvq: argument validation (host only, before any HIP call),
+// status strings, thread-local error detail, and dispatch to the launchers.
+#include "../../include/kvq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "kvq_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kvq_status fail(kvq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+kvq_status ok() { return KVQ_OK; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define KVQ_CHECK_PTR(p)                                                              \
+  do {                                                                                \
+    if ((p) == nullptr) return fail(KVQ_ERR_NULL, "%s: %s is NULL", fn, #p);          \
+    if (!aligned16(p)) return fail(KVQ_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, #p); \
+  } while (0)
+
+kvq_status check_dtype(const char* fn, const char* name, kvq_dtype dt) {
+  if (dt != KVQ_F32 && dt != KVQ_F16)
+    return fail(KVQ_ERR_DTYPE, "%s: %s = %d is not KVQ_F32 (0) or KVQ_F16 (1)", fn, name, (int)dt);
+  return KVQ_OK;
+}
+
+kvq_status check_d(const char* fn, int32_t d) {
+  if (d < 16 || d > kvq::kMaxD || d % 16 != 0)
+    return fail(KVQ_ERR_SHAPE, "%s: d = %d must be a multiple of 16 in [16, %d]", fn, (int)d,
+                kvq::kMaxD);
+  return KVQ_OK;
+}
+
+kvq_status check_m(const char* fn, int32_t m) {
+  if (m < kvq::kMinM || m > kvq::kMaxM || m % 32 != 0)
+    return fail(KVQ_ERR_SHAPE, "%s: m = %d must be a multiple of 32 in [%d, %d]", fn, (int)m,
+                kvq::kMinM, kvq::kMaxM);
+  return KVQ_OK;
+}
+
+kvq_status check_nq(const char* fn, int32_t nq) {
+  if (nq < 1 || nq > kvq::kMaxNq)
+    return fail(KVQ_ERR_SHAPE, "%s: nq = %d must be in [1, %d]", fn, (int)nq, kvq::kMaxNq);
+  return KVQ_OK;
+}
+
+kvq_status check_count(const char* fn, const char* name, int64_t v) {
+  if (v < 0) return fail(KVQ_ERR_SHAPE, "%s: %s = %lld is negative", fn, name, (long long)v);
+  return KVQ_OK;
+}
+
+kvq_status launched(const char* fn, hipError_t e) {
+  if (e != hipSuccess)
+    return fail(KVQ_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  g_last_error.clear();
+  return KVQ_OK;
+}
+
+kvq_status device_info(const char* fn, kvq::DeviceInfo* info) {
+  hipError_t e = kvq::current_device_info(info);
+  if (e != hipSuccess)
+    return fail(KVQ_ERR_LAUNCH, "%s: device query failed: %s", fn, hipGetErrorString(e));
+  return KVQ_OK;
+}
+
+}  // namespace
+
+namespace kvq {
+
+hipError_t current_device_info(DeviceInfo* out) {
+  static std::mutex mu;
+  static DeviceInfo cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev].device != dev) {
+    DeviceInfo info;
+    info.device = dev;
+    e = hipDeviceGetAttribute(&info.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    int lds = 0;
+    e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) return e;
+    info.lds_per_block = (size_t)lds;
+    cache[dev] = info;
+  }
+  *out = cache[dev];
+  return hipSuccess;
+}
+
+}  // namespace kvq
+
+extern "C" {
+
+const char* kvq_status_string(kvq_status status) {
+  switch (status) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_ERR_NULL: return "KVQ_ERR_NULL";
+    case KVQ_ERR_SHAPE: return "KVQ_ERR_SHAPE";
+    case KVQ_ERR_ALIGN: return "KVQ_ERR_ALIGN";
+    case KVQ_ERR_DTYPE: return "KVQ_ERR_DTYPE";
+    case KVQ_ERR_WORKSPACE: return "KVQ_ERR_WORKSPACE";
+    case KVQ_ERR_LAUNCH: return "KVQ_ERR_LAUNCH";
+    default: return "KVQ_ERR_UNKNOWN";
+  }
+}
+
+const char* kvq_last_error(void) { return g_last_error.c_str(); }
+
+kvq_status kvq_quantize_int8(const void* x, kvq_dtype x_dt, int64_t rows, int32_t d,
+                             int8_t* codes, float* scales, kvq_stream_t stream) {
+  const char* fn = "kvq_quantize_int8";
+  kvq_status st;
+  if ((st = check_count(fn, "rows", rows)) || (st = check_d(fn, d)) ||
+      (st = check_dtype(fn, "x_dt", x_dt)))
+    return st;
+  if (rows == 0) return ok();
+  KVQ_CHECK_PTR(x);
+  KVQ_CHECK_PTR(codes);
+  KVQ_CHECK_PTR(scales);
+  return launched(fn, kvq::launch_quantize_int8(x, x_dt == KVQ_F16, rows, d, codes, scales,
+                                                reinterpret_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_dequantize_int8(const int8_t* codes, const float* scales, int64_t rows, int32_t d,
+                               void* out, kvq_dtype out_dt, kvq_stream_t stream) {
+  const char* fn = "kvq_dequantize_int8";
+  kvq_status st;
+  if ((st = check_count(fn, "rows", rows)) || (st = check_d(fn, d)) ||
+      (st = check_dtype(fn, "out_dt", out_dt)))
+    return st;
+  if (rows == 0) return ok();
+  KVQ_CHECK_PTR(codes);
+  KVQ_CHECK_PTR(scales);
+  KVQ_CHECK_PTR(out);
+  return launched(fn, kvq::launch_dequantize_int8(codes, scales, rows, d, out, out_dt == KVQ_F16,
+                                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_scores_int8(const void* q, kvq_dtype q_dt, int64_t groups, int32_t nq,
+                           const int8_t* codes, const float* scales, int64_t T, int32_t d,
+                           float* scores, kvq_stream_t stream) {
+  const char* fn = "kvq_scores_int8";
+  kvq_status st;
+  if ((st = check_count(fn, "groups", groups)) || (st = check_count(fn, "T", T)) ||
+      (st = check_nq(fn, nq)) || (st = check_d(fn, d)) || (st = check_dtype(fn, "q_dt", q_dt)))
+    return st;
+  if (groups == 0 || T == 0) return ok();
+  KVQ_CHECK_PTR(q);
+  KVQ_CHECK_PTR(codes);
+  KVQ_CHECK_PTR(scales);
+  KVQ_CHECK_PTR(scores);
+  return launched(fn, kvq::launch_scores_int8(q, q_dt == KVQ_F16, groups, nq, codes, scales, T, d,
+                                              scores, reinterpret_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_qjl_sketch(const void* k, kvq_dtype k_dt, int64_t rows, int32_t d, const void* S,
+                          int32_t m, uint32_t* bits, uint16_t* norms, kvq_stream_t stream) {
+  const char* fn = "kvq_qjl_sketch";
+  kvq_status st;
+  if ((st = check_count(fn, "rows", rows)) || (st = check_d(fn, d)) || (st = check_m(fn, m)) ||
+      (st = check_dtype(fn, "k_dt", k_dt)))
+    return st;
+  if (rows == 0) return ok();
+  KVQ_CHECK_PTR(k);
+  KVQ_CHECK_PTR(S);
+  KVQ_CHECK_PTR(bits);
+  KVQ_CHECK_PTR(norms);
+  kvq::DeviceInfo dev;
+  if ((st = device_info(fn, &dev))) return st;
+  return launched(fn, kvq::launch_qjl_sketch(k, k_dt == KVQ_F16, rows, d, S, m, bits, norms, dev,
+                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_scores_qjl(const void* q, kvq_dtype q_dt, int64_t groups, int32_t nq,
+                          const void* S, kvq_dtype S_dt, int32_t m, const uint32_t* bits,
+                          const uint16_t* norms, int64_t T, int32_t d, float* scores,
+                          kvq_stream_t stream) {
+  const char* fn = "kvq_scores_qjl";
+  kvq_status st;
+  if ((st = check_count(fn, "groups", groups)) || (st = check_count(fn, "T", T)) ||
+      (st = check_nq(fn, nq)) || (st = check_d(fn, d)) || (st = check_m(fn, m)) ||
+      (st = check_dtype(fn, "q_dt", q_dt)) || (st = check_dtype(fn, "S_dt", S_dt)))
+    return st;
+  if (groups == 0 || T == 0) return ok();
+  KVQ_CHECK_PTR(q);
+  KVQ_CHECK_PTR(S);
+  KVQ_CHECK_PTR(bits);
+  KVQ_CHECK_PTR(norms);
+  KVQ_CHECK_PTR(scores);
+  kvq::DeviceInfo dev;
+  if ((st = device_info(fn, &dev))) return st;
+  return launched(fn, kvq::launch_scores_qjl(q, q_dt == KVQ_F16, groups, nq, S, S_dt == KVQ_F16, m,
+                                             bits, norms, T, d, scores, dev,
+                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t kvq_decode_workspace_bytes(int64_t groups, int64_t T, int32_t d) {
+  if (groups <= 0 || T <= 0 || d < 16 || d > kvq::kMaxD || d % 16 != 0) return 0;
+  kvq::DeviceInfo dev;
+  if (kvq::current_device_info(&dev) != hipSuccess) return 0;
+  return kvq::decode_workspace_bytes(groups, T, d, dev);
+}
+
+kvq_status kvq_decode_qjl_int8(const void* q, kvq_dtype q_dt, int64_t groups, const void* S,
+                               kvq_dtype S_dt, int32_t m, const uint32_t* kbits,
+                               const uint16_t* knorms, const int8_t* vcodes,
+                               const float* vscales, int64_t T, int32_t d, float sm_scale,
+                               void* ws, size_t ws_bytes, float* out, kvq_stream_t stream) {
+  const char* fn = "kvq_decode_qjl_int8";
+  kvq_status st;
+  if ((st = check_count(fn, "groups", groups)) || (st = check_count(fn, "T", T)) ||
+      (st = check_d(fn, d)) || (st = check_m(fn, m)) || (st = check_dtype(fn, "q_dt", q_dt)) ||
+      (st = check_dtype(fn, "S_dt", S_dt)))
+    return st;
+  if (groups == 0) return ok();
+  if (T == 0) return fail(KVQ_ERR_SHAPE, "%s: T = 0 (attention over no tokens)", fn);
+  KVQ_CHECK_PTR(q);
+  KVQ_CHECK_PTR(S);
+  KVQ_CHECK_PTR(kbits);
+  KVQ_CHECK_PTR(knorms);
+  KVQ_CHECK_PTR(vcodes);
+  KVQ_CHECK_PTR(vscales);
+  KVQ_CHECK_PTR(out);
+  kvq::DeviceInfo dev;
+  if ((st = device_info(fn, &dev))) return st;
+  const size_t need = kvq::decode_workspace_bytes(groups, T, d, dev);
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need)
+      return fail(KVQ_ERR_WORKSPACE, "%s: workspace of %zu bytes at %p, need %zu", fn, ws_bytes, ws,
+                  need);
+    if (!aligned16(ws)) return fail(KVQ_ERR_ALIGN, "%s: ws is not 16-byte aligned", fn);
+  }
+  return launched(fn, kvq::launch_decode_qjl_int8(q, q_dt == KVQ_F16, groups, S, S_dt == KVQ_F16,
+                                                  m, kbits, knorms, vcodes, vscales, T, d,
+                                                  sm_scale, ws, out, dev,
+                                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Host-side launchers implemented in the .hip files and called by the C ABI
+// after validation.  Every launcher assumes validated arguments and returns
+// the HIP status of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvq {
+
+struct DeviceInfo {
+  int device = -1;
+  int cus = 0;              // compute units
+  size_t lds_per_block = 0; // bytes of LDS a workgroup may use
+};
+
+// Properties of the current device, cached per device id.
+hipError_t current_device_info(DeviceInfo* out);
+
+hipError_t launch_quantize_int8(const void* x, int x_f16, int64_t rows, int d, int8_t* codes,
+                                float* scales, hipStream_t s);
+hipError_t launch_dequantize_int8(const int8_t* codes, const float* scales, int64_t rows, int d,
+                                  void* out, int out_f16, hipStream_t s);
+hipError_t launch_scores_int8(const void* q, int q_f16, int64_t groups, int nq,
+                              const int8_t* codes, const float* scales, int64_t T, int d,
+                              float* scores, hipStream_t s);
+hipError_t launch_qjl_sketch(const void* k, int k_f16, int64_t rows, int d, const void* S, int m,
+                             uint32_t* bits, uint16_t* norms, const DeviceInfo& dev, hipStream_t s);
+hipError_t launch_scores_qjl(const void* q, int q_f16, int64_t groups, int nq, const void* S,
+                             int S_f16, int m, const uint32_t* bits, const uint16_t* norms,
+                             int64_t T, int d, float* scores, const DeviceInfo& dev, hipStream_t s);
+
+// Token split of the decode kernel: tokens per split and number of splits.
+struct DecodeSplit {
+  int64_t splits = 1;
+  int64_t tokens_per_split = 0;
+};
+DecodeSplit decode_split(int64_t groups, int64_t T, const DeviceInfo& dev);
+size_t decode_workspace_bytes(int64_t groups, int64_t T, int d, const DeviceInfo& dev);
+hipError_t launch_decode_qjl_int8(const void* q, int q_f16, int64_t groups, const void* S,
+                                  int S_f16, int m, const uint32_t* kbits, const uint16_t* knorms,
+                                  const int8_t* vcodes, const float* vscales, int64_t T, int d,
+                                  float sm_scale, void* ws, float* out, const DeviceInfo& dev,
+                                  hipStream_t s);
+
+// Raise a kernel's dynamic-LDS limit when it needs more than the default
+// 64 KiB (gfx950 workgroups may use up to 160 KiB).
+template <typename Kernel>
+inline hipError_t allow_dynamic_lds(Kernel kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+// Limits shared by validation and kernels.
+constexpr int kMaxD = 65536;
+constexpr int kMinM = 32;
+constexpr int kMaxM = 1024;
+constexpr int kMaxNq = 64;
+
+}  // namespace kvq

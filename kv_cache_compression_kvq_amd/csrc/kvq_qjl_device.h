@@ -1,0 +1,73 @@
+// Device helpers shared by the QJL score and decode kernels.
+#pragma once
+
+#include "kvq_device.h"
+
+namespace kvq {
+
+constexpr float kSqrtHalfPi = 1.2533141373155001f;  // sqrt(pi / 2)
+
+// Row of S that MFMA row i (0..31) of a 32-row tile reads.  The 32x32 MFMA
+// result puts tile row i = 8q + 4h + s in accumulator register 4q + s of the
+// lanes of half h; projection 16h + 4q + s is wanted there.
+__host__ __device__ constexpr int sketch_row_perm(int i) {
+  return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
+}
+
+// ---------------------------------------------------------------------------
+// Query projection and byte tables (shared by the score and decode kernels).
+
+// y[i] = sum_j S[i][j] q[j] for i < m, binary32, one row per thread.
+template <typename TS, typename TQ>
+__device__ void project_query(const TS* __restrict__ S, const TQ* __restrict__ q, int m, int d,
+                              float* y) {
+  for (int i = threadIdx.x; i < m; i += blockDim.x) {
+    const TS* sr = S + (int64_t)i * d;
+    float acc = 0.0f;
+    for (int j = 0; j < d; ++j) acc = __builtin_fmaf(to_f32(sr[j]), to_f32(q[j]), acc);
+    y[i] = acc;
+  }
+}
+
+// lut[p * 256 + v] = sum_{j<8} (bit j of v ? +1 : -1) * y[8p + j] for the
+// nt = m / 8 tables, written as lo-nibble + hi-nibble partial sums.
+__device__ void build_byte_tables(const float* y, int ntables, float* lut) {
+  for (int task = threadIdx.x; task < ntables * 8; task += blockDim.x) {
+    const int p = task >> 3;
+    const int sub = task & 7;                  // entries v = 32 sub .. 32 sub + 31
+    const float* yp = y + 8 * p;
+    float lo[16];
+    lo[0] = -(((yp[0] + yp[1]) + yp[2]) + yp[3]);
+#pragma unroll
+    for (int b = 1; b < 16; ++b) {
+      const int low = b & (-b);
+      const int j = __builtin_ctz(low);
+      lo[b] = lo[b ^ low] + 2.0f * yp[j];
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int a = 2 * sub + hh;              // high nibble
+      float hi = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hi += ((a >> j) & 1) ? yp[4 + j] : -yp[4 + j];
+#pragma unroll
+      for (int b = 0; b < 16; ++b) lut[p * 256 + a * 16 + b] = hi + lo[b];
+    }
+  }
+}
+
+// Sum of the table entries selected by the bytes of `nw` sign words.
+__device__ __forceinline__ float lut_sum(const float* lut, const uint32_t* w, int nw) {
+  float acc = 0.0f;
+  for (int i = 0; i < nw; ++i) {
+    const uint32_t x = w[i];
+    const float* t = lut + i * 1024;
+    acc += t[x & 0xFF];
+    acc += t[256 + ((x >> 8) & 0xFF)];
+    acc += t[512 + ((x >> 16) & 0xFF)];
+    acc += t[768 + (x >> 24)];
+  }
+  return acc;
+}
+
+}  // namespace kvq

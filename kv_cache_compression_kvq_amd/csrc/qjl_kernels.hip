@@ -1,0 +1,364 @@
+// QJL key sketch and asymmetric score for gfx950.
+//
+// Method: "QJL: 1-Bit Quantized JL Transform for KV Cache Quantization with
+// Zero Overhead" (arXiv 2406.03482), abstract: keys are compressed to the
+// signs of a Gaussian JL projection (no stored quantization constants) and a
+// query's inner product with a key is estimated from the query's unquantized
+// projection and the key's sign bits, which is unbiased.  With S [m, d],
+// y = S q and bits b of S k, the estimate is
+//   sqrt(pi/2) / m * ||k|| * sum_i (2 b_i - 1) y_i.
+//
+// Sketch (fp16 keys): P = K S^T is a dense contraction with K streamed from
+// HBM once and S (<= 64 KiB) resident in LDS, so it runs on fp16 matrix
+// cores: v_mfma_f32_32x32x16_f16 with S as the A operand (32 projections x
+// 16 channels) and K^T as the B operand (16 channels x 32 tokens).  Products
+// of binary16 values are exact in binary32 and the accumulation is binary32.
+// S rows are permuted inside each 32-row tile so that lane (token j, half h)
+// finds projections 16h .. 16h+15 of that tile in its accumulator registers
+// 0..15; its sign word is then built with shift-and-insert steps and one
+// exchange with the other half.
+//
+// Score: per (group, query) workgroup y = S q goes to LDS and is expanded
+// into one 256-entry table per byte of the sign words:
+//   T_p[v] = sum_{j<8} (bit j of v ? +1 : -1) * y_{8p+j},
+// so a token costs one table lookup per 8 bits.
+#include "kvq_device.h"
+#include "kvq_launch.h"
+#include "kvq_qjl_device.h"
+
+#include <algorithm>
+#include <cmath>
+
+namespace kvq {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// Sketch, fp16 keys on MFMA.  KS = d / 16 K-steps; MT = m / 32 projection
+// tiles, a multiple of 8 (MT == 0: runtime m, words stored as they are
+// produced).  Each wave
+// owns NT x 32 tokens per iteration and loops over token tiles.
+// Token tiles of 32 per wave iteration: two, or one when d = 256 would
+// otherwise spill.
+template <int KS> constexpr int sketch_nt() { return KS <= 8 ? 2 : 1; }
+
+constexpr int kSketchThreads = 512;
+constexpr int kSketchWaves = kSketchThreads / 64;
+
+template <int KS, int MT>
+__global__ __launch_bounds__(kSketchThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void sketch_mfma_kernel(const _Float16* __restrict__ k,
+                                                          int64_t rows,
+                                                          const _Float16* __restrict__ S,
+                                                          int m_rt, uint32_t* __restrict__ bits,
+                                                          uint16_t* __restrict__ norms) {
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  f16x8* sfrag = reinterpret_cast<f16x8*>(lds_raw);
+  constexpr int D = KS * 16;
+  const int mt_count = MT > 0 ? MT : m_rt / 32;
+  const int words = mt_count;  // sign words per token
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const int col = lane & 31;
+
+  // S -> LDS in fragment order: fragment (mt, ks), lane l holds
+  // S[32 mt + perm(l % 32)][16 ks + 8 (l / 32) .. + 8].
+  const int nfrag_lanes = mt_count * KS * 64;
+  for (int idx = tid; idx < nfrag_lanes; idx += kSketchThreads) {
+    const int l = idx & 63;
+    const int frag = idx >> 6;
+    const int mt = frag / KS, ks = frag % KS;
+    const int srow = 32 * mt + sketch_row_perm(l & 31);
+    sfrag[idx] = *reinterpret_cast<const f16x8*>(S + (int64_t)srow * D + 16 * ks + 8 * (l >> 5));
+  }
+  __syncthreads();
+
+  constexpr int kSketchNT = sketch_nt<KS>();
+  const int64_t tiles = (rows + 32 * kSketchNT - 1) / (32 * kSketchNT);
+  for (int64_t tile = (int64_t)blockIdx.x * kSketchWaves + wave; tile < tiles;
+       tile += (int64_t)gridDim.x * kSketchWaves) {
+    // S fragments are re-read from LDS for every tile: keeping all of them
+    // in registers would leave room for one wave per SIMD
+    asm volatile("" ::: "memory");
+    const int64_t tok0 = tile * (32 * kSketchNT);
+    f16x8 b[kSketchNT][KS];
+    float ss[kSketchNT];
+#pragma unroll
+    for (int nt = 0; nt < kSketchNT; ++nt) {
+      const int64_t tok = tok0 + 32 * nt + col;
+      const _Float16* kr = k + tok * D + 8 * h;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        b[nt][ks] = (tok < rows) ? *reinterpret_cast<const f16x8*>(kr + 16 * ks) : f16x8{};
+    }
+    // norms: this lane holds half of its token's channels
+#pragma unroll
+    for (int nt = 0; nt < kSketchNT; ++nt) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = (float)b[nt][ks][e];
+          acc = __builtin_fmaf(v, v, acc);
+        }
+      ss[nt] = acc;
+    }
+#pragma unroll
+    for (int nt = 0; nt < kSketchNT; ++nt) {
+      const float tot = ss[nt] + xor32_f32(ss[nt]);
+      const int64_t tok = tok0 + 32 * nt + col;
+      if (h == 0 && tok < rows) norms[tok] = f32_to_f16_bits(__builtin_sqrtf(tot));
+    }
+
+    // Half h of the wave stores words [h * MT/2, (h + 1) * MT/2) of each of
+    // its tokens; they are collected with selects so the projection-tile
+    // loop can stay rolled (an unrolled loop lets the scheduler hoist every
+    // S fragment into registers).
+    constexpr int HALF = MT > 0 ? MT / 2 : 1;
+    uint32_t wsel[kSketchNT][HALF];
+#pragma unroll
+    for (int nt = 0; nt < kSketchNT; ++nt)
+#pragma unroll
+      for (int j = 0; j < HALF; ++j) wsel[nt][j] = 0;
+#pragma unroll 1
+    for (int mt = 0; mt < mt_count; ++mt) {
+      f32x16 acc[kSketchNT];
+#pragma unroll
+      for (int nt = 0; nt < kSketchNT; ++nt) acc[nt] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const f16x8 a = sfrag[(mt * KS + ks) * 64 + lane];
+#pragma unroll
+        for (int nt = 0; nt < kSketchNT; ++nt)
+          acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[nt][ks], acc[nt], 0, 0, 0);
+      }
+      const int rel = mt - h * HALF;
+#pragma unroll
+      for (int nt = 0; nt < kSketchNT; ++nt) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int r = 15; r >= 0; --r) w = (w << 1) | (acc[nt][r] >= 0.0f ? 1u : 0u);
+        const uint32_t o = xor32_u32(w);
+        const uint32_t full = h == 0 ? (w | (o << 16)) : (o | (w << 16));
+        if constexpr (MT > 0) {
+#pragma unroll
+          for (int j = 0; j < HALF; ++j) wsel[nt][j] = (rel == j) ? full : wsel[nt][j];
+        } else {
+          const int64_t tok = tok0 + 32 * nt + col;
+          if (h == 0 && tok < rows) bits[tok * words + mt] = full;
+        }
+      }
+    }
+    if constexpr (MT > 0) {
+#pragma unroll
+      for (int nt = 0; nt < kSketchNT; ++nt) {
+        const int64_t tok = tok0 + 32 * nt + col;
+        if (tok < rows) {
+          uint32_t* dst = bits + tok * MT + h * HALF;
+#pragma unroll
+          for (int v4 = 0; v4 < HALF / 4; ++v4)
+            *reinterpret_cast<u32x4*>(dst + 4 * v4) =
+                u32x4{wsel[nt][4 * v4], wsel[nt][4 * v4 + 1], wsel[nt][4 * v4 + 2], wsel[nt][4 * v4 + 3]};
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Sketch, any shape (and fp32 keys): one thread per (row, sign word), 32
+// binary32 dot products each; the word-0 thread also writes the norm.
+template <typename T>
+__global__ __launch_bounds__(256) void sketch_generic_kernel(const T* __restrict__ k, int64_t rows,
+                                                             int d, const T* __restrict__ S, int m,
+                                                             uint32_t* __restrict__ bits,
+                                                             uint16_t* __restrict__ norms) {
+  const int words = m / 32;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid / words;
+  const int w = (int)(gid % words);
+  if (row >= rows) return;
+  const T* kr = k + row * d;
+  uint32_t word = 0;
+  for (int i = 0; i < 32; ++i) {
+    const T* sr = S + (int64_t)(32 * w + i) * d;
+    float p = 0.0f;
+    for (int j = 0; j < d; ++j) p = __builtin_fmaf(to_f32(sr[j]), to_f32(kr[j]), p);
+    word |= (p >= 0.0f ? 1u : 0u) << i;
+  }
+  bits[row * words + w] = word;
+  if (w == 0) {
+    float acc = 0.0f;
+    for (int j = 0; j < d; ++j) {
+      const float v = to_f32(kr[j]);
+      acc = __builtin_fmaf(v, v, acc);
+    }
+    norms[row] = f32_to_f16_bits(__builtin_sqrtf(acc));
+  }
+}
+
+template <int KS, int MT>
+static hipError_t sketch_mfma_launch(const _Float16* k, int64_t rows, const _Float16* S, int m,
+                                     uint32_t* bits, uint16_t* norms, const DeviceInfo& dev,
+                                     hipStream_t st) {
+  const size_t lds = (size_t)m * KS * 16 * sizeof(_Float16);
+  constexpr int kSketchNT = sketch_nt<KS>();
+  const int64_t tiles = (rows + 32 * kSketchNT - 1) / (32 * kSketchNT);
+  const int64_t want = (tiles + kSketchWaves - 1) / kSketchWaves;
+  const int64_t cap = (int64_t)dev.cus * std::max<int64_t>(1, (int64_t)(160 * 1024 / std::max<size_t>(lds, 1)));
+  const int64_t blocks = std::max<int64_t>(1, std::min(want, cap));
+  hipLaunchKernelGGL((sketch_mfma_kernel<KS, MT>), dim3((unsigned)blocks), dim3(kSketchThreads), lds, st, k,
+                     rows, S, m, bits, norms);
+  return hipGetLastError();
+}
+
+hipError_t launch_qjl_sketch(const void* k, int k_f16, int64_t rows, int d, const void* S, int m,
+                             uint32_t* bits, uint16_t* norms, const DeviceInfo& dev,
+                             hipStream_t st) {
+  if (k_f16) {
+    const size_t lds = (size_t)m * d * sizeof(_Float16);
+    const _Float16* kh = static_cast<const _Float16*>(k);
+    const _Float16* Sh = static_cast<const _Float16*>(S);
+    if (lds <= std::min<size_t>(dev.lds_per_block, 64 * 1024)) {
+      if (d == 128 && m == 256) return sketch_mfma_launch<8, 8>(kh, rows, Sh, m, bits, norms, dev, st);
+      switch (d) {
+        case 16: return sketch_mfma_launch<1, 0>(kh, rows, Sh, m, bits, norms, dev, st);
+        case 32: return sketch_mfma_launch<2, 0>(kh, rows, Sh, m, bits, norms, dev, st);
+        case 64: return sketch_mfma_launch<4, 0>(kh, rows, Sh, m, bits, norms, dev, st);
+        case 128: return sketch_mfma_launch<8, 0>(kh, rows, Sh, m, bits, norms, dev, st);
+        case 256: return sketch_mfma_launch<16, 0>(kh, rows, Sh, m, bits, norms, dev, st);
+        default: break;
+      }
+    }
+  }
+  const int64_t threads = rows * (m / 32);
+  const int64_t blocks = (threads + 255) / 256;
+  // the generic path is launched in row slices to bound the grid
+  const int64_t rows_per = std::max<int64_t>(1, (int64_t(1) << 30) / (m / 32));
+  for (int64_t r0 = 0; r0 < rows; r0 += rows_per) {
+    const int64_t nr = std::min(rows_per, rows - r0);
+    const int64_t nb = (nr * (m / 32) + 255) / 256;
+    if (k_f16)
+      hipLaunchKernelGGL(sketch_generic_kernel<_Float16>, dim3((unsigned)nb), dim3(256), 0, st,
+                         static_cast<const _Float16*>(k) + r0 * d, nr, d,
+                         static_cast<const _Float16*>(S), m, bits + r0 * (m / 32), norms + r0);
+    else
+      hipLaunchKernelGGL(sketch_generic_kernel<float>, dim3((unsigned)nb), dim3(256), 0, st,
+                         static_cast<const float*>(k) + r0 * d, nr, d,
+                         static_cast<const float*>(S), m, bits + r0 * (m / 32), norms + r0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  (void)blocks;
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// QJL scores: one workgroup per (group, query, tile of kScoreTok tokens).
+constexpr int kQjlTokPerThread = 8;
+constexpr int kQjlTok = 256 * kQjlTokPerThread;
+
+template <typename TS, typename TQ, int W>
+__global__ __launch_bounds__(256) void scores_qjl_kernel(const TQ* __restrict__ q, int nq,
+                                                         const TS* __restrict__ S, int m_rt, int d,
+                                                         const uint32_t* __restrict__ bits,
+                                                         const uint16_t* __restrict__ norms,
+                                                         int64_t T, int64_t tiles,
+                                                         float* __restrict__ scores) {
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  const int m = W > 0 ? 32 * W : m_rt;
+  const int words = m / 32;
+  float* y = reinterpret_cast<float*>(lds_raw);
+  float* lut = y + m;
+  const int64_t gj = blockIdx.x / tiles;           // (group, query) pair
+  const int64_t tile = blockIdx.x % tiles;
+  const int64_t g = gj / nq;
+  project_query(S, q + gj * d, m, d, y);
+  __syncthreads();
+  build_byte_tables(y, m / 8, lut);
+  __syncthreads();
+  const float c = kSqrtHalfPi / (float)m;
+  const uint32_t* bg = bits + g * T * words;
+  const uint16_t* ng = norms + g * T;
+  for (int u = 0; u < kQjlTokPerThread; ++u) {
+    const int64_t t = tile * kQjlTok + u * 256 + threadIdx.x;
+    if (t >= T) break;
+    float acc;
+    if constexpr (W > 0) {
+      uint32_t wv[W];
+#pragma unroll
+      for (int i = 0; i < W; i += 4) {
+        const u32x4 v4 = *reinterpret_cast<const u32x4*>(bg + t * W + i);
+        wv[i] = v4[0]; wv[i + 1] = v4[1]; wv[i + 2] = v4[2]; wv[i + 3] = v4[3];
+      }
+      acc = lut_sum(lut, wv, W);
+    } else {
+      acc = 0.0f;
+      for (int i = 0; i < words; ++i) {
+        const uint32_t x = bg[t * words + i];
+        acc += lut_sum(lut + i * 1024, &x, 1);
+      }
+    }
+    const float n = (float)__builtin_bit_cast(_Float16, ng[t]);
+    scores[gj * T + t] = c * n * acc;
+  }
+}
+
+template <typename TS, typename TQ>
+static hipError_t scores_qjl_typed(const TQ* q, int64_t groups, int nq, const TS* S, int m,
+                                   const uint32_t* bits, const uint16_t* norms, int64_t T, int d,
+                                   float* scores, const DeviceInfo& dev, hipStream_t st) {
+  const size_t lds = (size_t)m * sizeof(float) + (size_t)(m / 8) * 256 * sizeof(float);
+  if (lds > dev.lds_per_block) return hipErrorInvalidConfiguration;
+  const int64_t tiles = (T + kQjlTok - 1) / kQjlTok;
+  // launch in slices of whole groups so grid.x stays far below 2^32
+  const int64_t max_groups = std::max<int64_t>(1, (int64_t(1) << 22) / (tiles * nq));
+  for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
+    const int64_t ng = std::min(max_groups, groups - g0);
+    const TQ* qp = q + g0 * nq * d;
+    const uint32_t* bp = bits + g0 * T * (m / 32);
+    const uint16_t* np = norms + g0 * T;
+    float* sp = scores + g0 * nq * T;
+    const unsigned blocks = (unsigned)(ng * nq * tiles);
+    hipError_t e;
+    if (m == 256) {
+      e = allow_dynamic_lds(scores_qjl_kernel<TS, TQ, 8>, lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((scores_qjl_kernel<TS, TQ, 8>), dim3(blocks), dim3(256), lds, st, qp, nq,
+                         S, m, d, bp, np, T, tiles, sp);
+    } else {
+      e = allow_dynamic_lds(scores_qjl_kernel<TS, TQ, 0>, lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((scores_qjl_kernel<TS, TQ, 0>), dim3(blocks), dim3(256), lds, st, qp, nq,
+                         S, m, d, bp, np, T, tiles, sp);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_scores_qjl(const void* q, int q_f16, int64_t groups, int nq, const void* S,
+                             int S_f16, int m, const uint32_t* bits, const uint16_t* norms,
+                             int64_t T, int d, float* scores, const DeviceInfo& dev,
+                             hipStream_t st) {
+  if (S_f16) {
+    const _Float16* Sp = static_cast<const _Float16*>(S);
+    if (q_f16)
+      return scores_qjl_typed(static_cast<const _Float16*>(q), groups, nq, Sp, m, bits, norms, T, d,
+                              scores, dev, st);
+    return scores_qjl_typed(static_cast<const float*>(q), groups, nq, Sp, m, bits, norms, T, d,
+                            scores, dev, st);
+  }
+  const float* Sp = static_cast<const float*>(S);
+  if (q_f16)
+    return scores_qjl_typed(static_cast<const _Float16*>(q), groups, nq, Sp, m, bits, norms, T, d,
+                            scores, dev, st);
+  return scores_qjl_typed(static_cast<const float*>(q), groups, nq, Sp, m, bits, norms, T, d,
+                          scores, dev, st);
+}
+
+}  // namespace kvq

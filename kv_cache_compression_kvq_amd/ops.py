@@ -1,0 +1,149 @@
+"""Torch-facing wrappers of the libkvq C ABI.
+
+Argument marshalling only: dtype/device/contiguity checks, output allocation
+with torch, and the current HIP stream.  Every step of the computation runs
+in libkvq's kernels.  Sign words are returned as int32 tensors (the bytes of
+the ABI's uint32 words); norms as float16 tensors (the ABI's binary16 bits).
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib as L
+
+_DT = {torch.float32: L.KVQ_F32, torch.float16: L.KVQ_F16}
+
+
+def _dtype_code(t: torch.Tensor, what: str) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"{what}: expected float32 or float16, got {t.dtype}") from None
+
+
+def _dev(t: torch.Tensor, what: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a GPU tensor (libkvq has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t
+
+
+def _p(t: torch.Tensor):
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def quantize_int8(x: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """x [..., d] fp32/fp16 -> (codes int8 [..., d], scales fp32 [...])."""
+    _dev(x, "x")
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    codes = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    L.check(L.lib().kvq_quantize_int8(_p(x), _dtype_code(x, "x"), rows, d, _p(codes),
+                                      _p(scales), _stream(x)))
+    return codes, scales
+
+
+def dequantize_int8(codes: torch.Tensor, scales: torch.Tensor,
+                    out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """codes int8 [..., d], scales fp32 [...] -> [..., d] in out_dtype."""
+    _dev(codes, "codes"), _dev(scales, "scales")
+    if codes.dtype != torch.int8 or scales.dtype != torch.float32:
+        raise TypeError("codes must be int8 and scales float32")
+    d = codes.shape[-1]
+    rows = codes.numel() // d if d else 0
+    if scales.numel() != rows:
+        raise ValueError(f"scales has {scales.numel()} entries for {rows} rows")
+    out = torch.empty(codes.shape, dtype=out_dtype, device=codes.device)
+    L.check(L.lib().kvq_dequantize_int8(_p(codes), _p(scales), rows, d, _p(out),
+                                        _dtype_code(out, "out_dtype"), _stream(codes)))
+    return out
+
+
+def scores_int8(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
+    """q [G, nq, d]; codes [G, T, d] int8; scales [G, T] -> scores [G, nq, T] fp32."""
+    _dev(q, "q"), _dev(codes, "codes"), _dev(scales, "scales")
+    G, nq, d = q.shape
+    if codes.shape[0] != G or codes.shape[2] != d or tuple(scales.shape) != tuple(codes.shape[:2]):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, codes {tuple(codes.shape)}, "
+                         f"scales {tuple(scales.shape)}")
+    T = codes.shape[1]
+    out = torch.empty((G, nq, T), dtype=torch.float32, device=q.device)
+    L.check(L.lib().kvq_scores_int8(_p(q), _dtype_code(q, "q"), G, nq, _p(codes), _p(scales), T, d,
+                                    _p(out), _stream(q)))
+    return out
+
+
+def qjl_sketch(k: torch.Tensor, S: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """k [..., d] and S [m, d] of the same dtype -> (sign words int32 [..., m // 32],
+    norms fp16 [...])."""
+    _dev(k, "k"), _dev(S, "S")
+    if S.dtype != k.dtype:
+        raise TypeError("S must have the keys' dtype")
+    m, d = S.shape
+    if k.shape[-1] != d:
+        raise ValueError(f"k has d = {k.shape[-1]}, S has d = {d}")
+    rows = k.numel() // d if d else 0
+    bits = torch.empty((*k.shape[:-1], m // 32), dtype=torch.int32, device=k.device)
+    norms = torch.empty(k.shape[:-1], dtype=torch.float16, device=k.device)
+    L.check(L.lib().kvq_qjl_sketch(_p(k), _dtype_code(k, "k"), rows, d, _p(S), m, _p(bits),
+                                   _p(norms), _stream(k)))
+    return bits, norms
+
+
+def scores_qjl(q: torch.Tensor, S: torch.Tensor, bits: torch.Tensor,
+               norms: torch.Tensor) -> torch.Tensor:
+    """q [G, nq, d]; S [m, d]; bits [G, T, m // 32]; norms [G, T] -> [G, nq, T] fp32."""
+    for t, n in ((q, "q"), (S, "S"), (bits, "bits"), (norms, "norms")):
+        _dev(t, n)
+    G, nq, d = q.shape
+    m = S.shape[0]
+    T = bits.shape[1]
+    if bits.shape != (G, T, m // 32) or norms.shape != (G, T) or S.shape[1] != d:
+        raise ValueError("shape mismatch between q, S, bits and norms")
+    out = torch.empty((G, nq, T), dtype=torch.float32, device=q.device)
+    L.check(L.lib().kvq_scores_qjl(_p(q), _dtype_code(q, "q"), G, nq, _p(S), _dtype_code(S, "S"), m,
+                                   _p(bits), _p(norms), T, d, _p(out), _stream(q)))
+    return out
+
+
+def decode_workspace_bytes(groups: int, T: int, d: int) -> int:
+    return int(L.lib().kvq_decode_workspace_bytes(groups, T, d))
+
+
+def decode_qjl_int8(q: torch.Tensor, S: torch.Tensor, kbits: torch.Tensor, knorms: torch.Tensor,
+                    vcodes: torch.Tensor, vscales: torch.Tensor, sm_scale: float | None = None,
+                    workspace: torch.Tensor | None = None,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
+    """One decode step: q [G, d] against QJL keys (kbits [G, T, m // 32],
+    knorms [G, T]) and INT8 values (vcodes [G, T, d], vscales [G, T]).
+    Returns out [G, d] fp32.  ``workspace`` (uint8, >= decode_workspace_bytes)
+    and ``out`` may be passed to avoid allocations."""
+    for t, n in ((q, "q"), (S, "S"), (kbits, "kbits"), (knorms, "knorms"), (vcodes, "vcodes"),
+                 (vscales, "vscales")):
+        _dev(t, n)
+    G, d = q.shape
+    m = S.shape[0]
+    T = kbits.shape[1]
+    if (kbits.shape != (G, T, m // 32) or knorms.shape != (G, T) or vcodes.shape != (G, T, d)
+            or vscales.shape != (G, T) or S.shape[1] != d):
+        raise ValueError("shape mismatch between q, S and the cache tensors")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    need = decode_workspace_bytes(G, T, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((G, d), dtype=torch.float32, device=q.device)
+    L.check(L.lib().kvq_decode_qjl_int8(
+        _p(q), _dtype_code(q, "q"), G, _p(S), _dtype_code(S, "S"), m, _p(kbits), _p(knorms),
+        _p(vcodes), _p(vscales), T, d, float(sm_scale), _p(workspace), workspace.numel(), _p(out),
+        _stream(q)))
+    return out

@@ -1,0 +1,142 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/kvq.h declares, and rejects invalid arguments with a status and a
+message before making any HIP call (so no GPU is needed here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from kv_cache_compression_kvq_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+A = 0x10000          # an aligned fake device address; never dereferenced
+MIS = 0x10004        # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    assert set(names) == set(L.PROTOTYPES), names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True)
+    exported = set(re.findall(r"\bT (kvq_[a-z0-9_]+)", out.stdout))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings():
+    lib = L.lib()
+    names = ["KVQ_OK", "KVQ_ERR_NULL", "KVQ_ERR_SHAPE", "KVQ_ERR_ALIGN", "KVQ_ERR_DTYPE",
+             "KVQ_ERR_WORKSPACE", "KVQ_ERR_LAUNCH"]
+    for code, name in enumerate(names):
+        assert lib.kvq_status_string(code).decode() == name
+    assert lib.kvq_status_string(99).decode() == "KVQ_ERR_UNKNOWN"
+
+
+def _err(status, expect):
+    assert status == expect, (status, L.lib().kvq_last_error())
+    assert L.lib().kvq_last_error().decode()
+
+
+def test_quantize_validation():
+    f = L.lib().kvq_quantize_int8
+    _err(f(None, L.KVQ_F32, 4, 128, A, A, None), L.KVQ_ERR_NULL)
+    _err(f(A, L.KVQ_F32, 4, 128, None, A, None), L.KVQ_ERR_NULL)
+    _err(f(A, L.KVQ_F32, 4, 128, A, None, None), L.KVQ_ERR_NULL)
+    _err(f(MIS, L.KVQ_F32, 4, 128, A, A, None), L.KVQ_ERR_ALIGN)
+    _err(f(A, L.KVQ_F32, 4, 128, MIS, A, None), L.KVQ_ERR_ALIGN)
+    _err(f(A, L.KVQ_F32, -1, 128, A, A, None), L.KVQ_ERR_SHAPE)
+    for d in (0, 8, 120, 65552, -16):
+        _err(f(A, L.KVQ_F32, 4, d, A, A, None), L.KVQ_ERR_SHAPE)
+    _err(f(A, 7, 4, 128, A, A, None), L.KVQ_ERR_DTYPE)
+    # zero rows is a no-op, even with NULL pointers
+    assert f(None, L.KVQ_F32, 0, 128, None, None, None) == L.KVQ_OK
+
+
+def test_dequantize_validation():
+    f = L.lib().kvq_dequantize_int8
+    _err(f(None, A, 4, 128, A, L.KVQ_F32, None), L.KVQ_ERR_NULL)
+    _err(f(A, A, 4, 128, None, L.KVQ_F16, None), L.KVQ_ERR_NULL)
+    _err(f(A, MIS, 4, 128, A, L.KVQ_F32, None), L.KVQ_ERR_ALIGN)
+    _err(f(A, A, 4, 100, A, L.KVQ_F32, None), L.KVQ_ERR_SHAPE)
+    _err(f(A, A, 4, 128, A, 2, None), L.KVQ_ERR_DTYPE)
+    assert f(None, None, 0, 128, None, L.KVQ_F32, None) == L.KVQ_OK
+
+
+def test_scores_int8_validation():
+    f = L.lib().kvq_scores_int8
+    _err(f(A, L.KVQ_F16, 2, 0, A, A, 16, 128, A, None), L.KVQ_ERR_SHAPE)
+    _err(f(A, L.KVQ_F16, 2, 65, A, A, 16, 128, A, None), L.KVQ_ERR_SHAPE)
+    _err(f(A, L.KVQ_F16, -2, 1, A, A, 16, 128, A, None), L.KVQ_ERR_SHAPE)
+    _err(f(A, L.KVQ_F16, 2, 1, A, A, -16, 128, A, None), L.KVQ_ERR_SHAPE)
+    _err(f(A, L.KVQ_F16, 2, 1, A, A, 16, 128, None, None), L.KVQ_ERR_NULL)
+    _err(f(A, 5, 2, 1, A, A, 16, 128, A, None), L.KVQ_ERR_DTYPE)
+    assert f(None, L.KVQ_F16, 0, 1, None, None, 16, 128, None, None) == L.KVQ_OK
+    assert f(None, L.KVQ_F16, 2, 1, None, None, 0, 128, None, None) == L.KVQ_OK
+
+
+def test_sketch_validation():
+    f = L.lib().kvq_qjl_sketch
+    for m in (0, 16, 48, 1056, 2048):
+        _err(f(A, L.KVQ_F16, 4, 128, A, m, A, A, None), L.KVQ_ERR_SHAPE)
+    _err(f(A, L.KVQ_F16, 4, 128, None, 256, A, A, None), L.KVQ_ERR_NULL)
+    _err(f(A, L.KVQ_F16, 4, 128, A, 256, A, MIS, None), L.KVQ_ERR_ALIGN)
+    _err(f(A, 3, 4, 128, A, 256, A, A, None), L.KVQ_ERR_DTYPE)
+    assert f(None, L.KVQ_F16, 0, 128, None, 256, None, None, None) == L.KVQ_OK
+
+
+def test_scores_qjl_validation():
+    f = L.lib().kvq_scores_qjl
+    _err(f(A, L.KVQ_F16, 2, 1, A, L.KVQ_F16, 40, A, A, 16, 128, A, None), L.KVQ_ERR_SHAPE)
+    _err(f(A, L.KVQ_F16, 2, 1, A, 9, 256, A, A, 16, 128, A, None), L.KVQ_ERR_DTYPE)
+    _err(f(A, L.KVQ_F16, 2, 1, A, L.KVQ_F16, 256, None, A, 16, 128, A, None), L.KVQ_ERR_NULL)
+    assert f(None, L.KVQ_F16, 2, 1, None, L.KVQ_F16, 256, None, None, 0, 128, None, None) == L.KVQ_OK
+
+
+def test_decode_validation():
+    f = L.lib().kvq_decode_qjl_int8
+    args = [A, L.KVQ_F16, 2, A, L.KVQ_F16, 256, A, A, A, A, 16, 128, 0.1, A, 1 << 20, A, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["q", "q_dt", "groups", "S", "S_dt", "m", "kbits", "knorms", "vcodes", "vscales",
+                 "T", "d", "sm", "ws", "ws_bytes", "out", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    _err(call(T=0), L.KVQ_ERR_SHAPE)
+    _err(call(m=33), L.KVQ_ERR_SHAPE)
+    _err(call(d=24), L.KVQ_ERR_SHAPE)
+    _err(call(vcodes=None), L.KVQ_ERR_NULL)
+    _err(call(out=MIS), L.KVQ_ERR_ALIGN)
+    _err(call(q_dt=4), L.KVQ_ERR_DTYPE)
+    assert call(groups=0, q=None, S=None, kbits=None, knorms=None, vcodes=None, vscales=None,
+                ws=None, out=None) == L.KVQ_OK
+
+
+def test_workspace_query_rejects_bad_shapes_without_a_device():
+    f = L.lib().kvq_decode_workspace_bytes
+    assert f(0, 16, 128) == 0
+    assert f(4, 0, 128) == 0
+    assert f(4, 16, 100) == 0
+
+
+def test_python_binding_requires_gpu_tensors():
+    import torch
+    from kv_cache_compression_kvq_amd import ops
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ops.quantize_int8(torch.zeros(4, 128))

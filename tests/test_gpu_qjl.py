@@ -1,0 +1,145 @@
+"""GPU parity of the QJL path against the oracle: sign bits bit-exact except
+inside the 1e-4 * ||S_i|| * ||k|| band, norms within one binary16 ulp, and
+scores within 1e-4 * ||q|| * ||k|| given identical bits and norms (the
+oracle's own bits and norms are uploaded for the score checks)."""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_kvq_amd as K
+import synth_inputs as si
+from oracle import qjl as O
+from gpu_common import (assert_bits_within_band, assert_norms_within_ulp, assert_qjl_scores, down,
+                        log, up)
+
+pytestmark = pytest.mark.gpu
+
+
+def sketch_check(k: np.ndarray, S: np.ndarray, label: str):
+    log(f"[qjl] {label}: k {k.shape} {k.dtype}, m={S.shape[0]}")
+    bits_g, norms_g = K.qjl_sketch(up(k), up(S))
+    words_o, norms_o = O.qjl_sketch(k.reshape(-1, k.shape[-1]), S)
+    flips = assert_bits_within_band(down(bits_g, np.uint32), words_o, k, S)
+    nd = assert_norms_within_ulp(down(norms_g), norms_o)
+    log(f"[qjl] {label}: {flips} sign bits inside the band differ, {nd} norms one ulp apart")
+    return words_o, norms_o
+
+
+def scores_check(q, S, words, norms, label):
+    sc = down(K.scores_qjl(up(q), up(S), up(words), up(norms)))
+    ora = O.scores_qjl(q, S, words, norms)
+    worst = assert_qjl_scores(sc, q, norms, ora)
+    log(f"[qjl] {label}: worst err / tol = {worst:.3g}")
+
+
+def test_tiny_fp32_keys():
+    W = si.W_TINY
+    k = si.kv_tensor(W, si.K, 1, 1, 512, 128, "f32").reshape(512, 128)
+    S = si.projection(W, 256, 128, "f32")
+    words, norms = sketch_check(k, S, "tiny fp32")
+    q = si.queries(W, 1, 4, 128, "f32")
+    scores_check(q, S, words.reshape(1, 512, 8), norms.reshape(1, 512), "tiny scores")
+
+
+def test_qjl_cache_reduced_ragged():
+    """The QJL-cache shape with fewer tokens (1000: ragged against every tile)."""
+    W = si.W_QJL_CACHE
+    B, H, T, d, m = 2, 32, 1000, 128, 256
+    k = si.kv_tensor(W, si.K, B, H, T, d, "f16", outliers=True)
+    S = si.projection(W, m, d, "f16")
+    words, norms = sketch_check(k.reshape(-1, d), S, "qjl cache T=1000")
+    q = si.queries(W, B * H, 1, d, "f16")
+    scores_check(q, S, words.reshape(B * H, T, m // 32), norms.reshape(B * H, T), "T=1000 scores")
+
+
+def test_qjl_cache_full_size_sampled():
+    """8 x 32 x 8192 x 128 fp16 keys, S 256 x 128: the whole cache is sketched
+    and scored on the GPU (the bench's launch configuration); 16384 sampled
+    rows are checked against the oracle's sketch, and three groups get the
+    oracle's bits and norms before the full-size score launch, whose scores
+    for those groups are then checked."""
+    W = si.W_QJL_CACHE
+    B, H, T, d, m = 8, 32, 8192, 128, 256
+    G = B * H
+    k = si.kv_tensor(W, si.K, B, H, T, d, "f16", outliers=True).reshape(G * T, d)
+    S = si.projection(W, m, d, "f16")
+    kd, Sd = up(k), up(S)
+    log("[qjl] full size: sketch")
+    bits, norms = K.qjl_sketch(kd, Sd)
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([[0, G * T - 1], rng.integers(0, G * T, 16384)]))
+    idx = torch.from_numpy(rows).to("cuda")
+    wo, no = O.qjl_sketch(k[rows], S)
+    assert_bits_within_band(down(bits.index_select(0, idx), np.uint32), wo, k[rows], S)
+    assert_norms_within_ulp(down(norms.index_select(0, idx)), no)
+    groups = [0, 137, G - 1]
+    bits3 = bits.view(G, T, m // 32)
+    norms3 = norms.view(G, T)
+    for g in groups:
+        wg, ng = O.qjl_sketch(k[g * T:(g + 1) * T], S)
+        bits3[g].copy_(up(wg))
+        norms3[g].copy_(up(ng))
+    q = si.queries(W, G, 1, d, "f16")
+    log("[qjl] full size: scores")
+    sc = down(K.scores_qjl(up(q), Sd, bits3, norms3))
+    for g in groups:
+        wg, ng = O.qjl_sketch(k[g * T:(g + 1) * T], S)
+        ora = O.scores_qjl(q[g:g + 1], S, wg[None], ng[None])
+        assert_qjl_scores(sc[g:g + 1], q[g:g + 1], ng[None], ora)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("d,m", [(16, 32), (64, 64), (128, 256), (128, 512), (256, 256), (96, 128),
+                                 (128, 96), (256, 1024), (48, 64)])
+def test_sketch_shapes(dtype, d, m):
+    rng = np.random.default_rng(d * 7 + m)
+    npdt = np.float16 if dtype == "f16" else np.float32
+    for rows in (1, 31, 65, 1000):
+        k = rng.standard_normal((rows, d)).astype(npdt)
+        S = rng.standard_normal((m, d)).astype(npdt)
+        sketch_check(k, S, f"{dtype} d={d} m={m} rows={rows}")
+
+
+def test_sketch_zero_and_scaled_keys():
+    rng = np.random.default_rng(5)
+    d, m = 128, 256
+    S = rng.standard_normal((m, d)).astype(np.float16)
+    k = rng.standard_normal((64, d)).astype(np.float16)
+    k[0] = 0
+    k[1] = -0.0
+    k[2] = k[3] * np.float16(4)
+    words, norms = sketch_check(k, S, "zero / scaled keys")
+    bits_g, norms_g = K.qjl_sketch(up(k), up(S))
+    wg = down(bits_g, np.uint32)
+    assert np.all(wg[0] == 0xFFFFFFFF) and np.all(wg[1] == 0xFFFFFFFF)
+    assert down(norms_g)[0] == 0
+
+
+@pytest.mark.parametrize("qdt,sdt", [("f16", "f16"), ("f32", "f32"), ("f16", "f32"), ("f32", "f16")])
+@pytest.mark.parametrize("nq,T,m,d", [(1, 1, 256, 128), (3, 2049, 256, 128), (8, 300, 64, 64),
+                                      (2, 513, 512, 128), (1, 100, 1024, 256), (4, 77, 96, 48)])
+def test_scores_shapes(qdt, sdt, nq, T, m, d):
+    rng = np.random.default_rng(nq + T + m)
+    G = 3
+    S = rng.standard_normal((m, d)).astype(np.float16 if sdt == "f16" else np.float32)
+    k = rng.standard_normal((G * T, d)).astype(np.float32)
+    words, norms = O.qjl_sketch(k, S)
+    q = rng.standard_normal((G, nq, d)).astype(np.float16 if qdt == "f16" else np.float32)
+    scores_check(q, S, words.reshape(G, T, m // 32), norms.reshape(G, T), f"scores nq={nq} T={T} m={m}")
+
+
+def test_bit_order_matches_fixture_on_gpu():
+    """S = identity: the GPU sign words equal the hand-derived fixture."""
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "qjl_bit_order.txt")
+    keys, want = [], []
+    for line in open(path):
+        if line.startswith("#") or not line.strip():
+            continue
+        pat, words = [p.strip() for p in line.split("|")]
+        keys.append([{"+": 1.0, "-": -1.0, "0": 0.0}[c] for c in pat])
+        want.append([int(w, 16) for w in words.split()])
+    for dt in (np.float16, np.float32):
+        k = np.array(keys, dt)
+        bits, _ = K.qjl_sketch(up(k), up(np.eye(64, dtype=dt)))
+        assert down(bits, np.uint32).tolist() == want
