@@ -47,6 +47,9 @@ def parse_args():
     p.add_argument("--no-components", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a 1 GiB device-to-device copy 3 times (the known-size "
+                        "kernel used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return p.parse_args()
 
 
@@ -173,9 +176,9 @@ def cpu_baseline(si, np, seconds):
     lam = 1.0 / math.sqrt(d)
     done, spent = 0, 0.0
     while done < B * H and (spent < seconds or done < 2):
-        b, h = divmod(done, H)
-        k = si.kv_tensor(W, si.K, B, H, T, d, "f16", heads=range(h, h + 1)).reshape(B, T, d)[b]
-        v = si.kv_tensor(W, si.V, B, H, T, d, "f16", heads=range(h, h + 1)).reshape(B, T, d)[b]
+        # group `done` is rows [done * T, (done + 1) * T) of the [B*H*T, d] tensors
+        k = si.stream(W, si.K, T * d, "f16", start=done * T * d).reshape(T, d)
+        v = si.stream(W, si.V, T * d, "f16", start=done * T * d).reshape(T, d)
         kw, kn = OQ.qjl_sketch(k, S)                  # cache build (untimed)
         vc, vs = OI.quantize_int8(v)
         with threadpool_limits(1):
@@ -197,6 +200,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = 1 << 28                                   # 2^28 fp32 = 1 GiB each way
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
+        return
 
     import kv_cache_compression_kvq_amd as K
     import synth_inputs as si
