@@ -234,7 +234,7 @@ def main():
     # the newest token of every head (its own streams: tensor ids 6, 7)
     k_new = torch.from_numpy(si.stream(W, 6, G * d, "f16")).to(dev).view(G, d)
     v_new = torch.from_numpy(si.stream(W, 7, G * d, "f16")).to(dev).view(G, d)
-    ws = torch.empty(max(16, K.decode_workspace_bytes(G, T, d)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(16, K.decode_workspace_bytes(G, T, d, m)), dtype=torch.uint8, device=dev)
     out = torch.empty((G, d), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     log(f"bench: cache ready in {time.time() - t0:.1f} s")

@@ -162,11 +162,13 @@ kvq_status kvq_scores_qjl(const void* q, kvq_dtype q_dt, int64_t groups, int32_t
 
 /*
  * kvq_decode_workspace_bytes - size of the scratch buffer kvq_decode_qjl_int8
- * needs for `groups` groups of T tokens and head dimension d (0 when nothing
- * is needed).  The value depends only on the arguments and on the number of
- * compute units of the current device.
+ * needs for `groups` groups of T tokens, head dimension d and sketch size m
+ * (0 for invalid arguments).  It holds the projected queries S q (groups * m
+ * binary32) and the per-token-range softmax partials.  The value depends
+ * only on the arguments and on the number of compute units of the current
+ * device.
  */
-size_t kvq_decode_workspace_bytes(int64_t groups, int64_t T, int32_t d);
+size_t kvq_decode_workspace_bytes(int64_t groups, int64_t T, int32_t d, int32_t m);
 
 /*
  * kvq_decode_qjl_int8 - one decode step of attention over a compressed
@@ -187,11 +189,11 @@ size_t kvq_decode_workspace_bytes(int64_t groups, int64_t T, int32_t d);
  * q       [groups, d] (q_dt);  S [m, d] (S_dt)
  * kbits   [groups, T, m / 32] uint32;  knorms [groups, T] binary16 patterns
  * vcodes  [groups, T, d] int8;  vscales [groups, T] binary32
- * ws      device scratch of ws_bytes >= kvq_decode_workspace_bytes(groups, T, d)
- *         bytes (may be NULL when that size is 0); its contents on entry are
+ * ws      device scratch of ws_bytes >= kvq_decode_workspace_bytes(groups, T, d, m)
+ *         bytes; its contents on entry are
  *         ignored and on exit unspecified; concurrent calls need distinct ws.
  * out     [groups, d] binary32, written
- * T >= 1 when groups > 0; d, m as for kvq_qjl_sketch.
+ * T >= 1 when groups > 0; 16 <= d <= 1024, d % 16 == 0; m as for kvq_qjl_sketch.
  * Errors: NULL, ALIGN, SHAPE, DTYPE, WORKSPACE.
  */
 kvq_status kvq_decode_qjl_int8(const void* q, kvq_dtype q_dt, int64_t groups, const void* S,

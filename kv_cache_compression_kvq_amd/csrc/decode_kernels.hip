@@ -30,7 +30,6 @@ namespace kvq {
 
 constexpr int kDecodeChunk = 64;                       // tokens per wave step
 constexpr int kDecodeBlockTokens = 4 * kDecodeChunk;   // tokens per workgroup step
-constexpr int kDecodeMaxD = 1024;
 
 // DPP row rotate (lane i takes lane (i + n) % 16 of its 16-lane row).
 template <int N>
@@ -52,10 +51,20 @@ __device__ __forceinline__ float bcast_from(float v, int src_lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src_lane << 2, __builtin_bit_cast(int, v)));
 }
 
-template <typename TS, typename TQ, int W, int LPV>
+// y[g] = S q[g] for every group, once per decode step (the split kernels of a
+// group all read it from the workspace).
+template <typename TS, typename TQ>
+__global__ __launch_bounds__(256) void qjl_project_kernel(const TQ* __restrict__ q,
+                                                          const TS* __restrict__ S, int m, int d,
+                                                          float* __restrict__ y) {
+  __shared__ __align__(16) float qs[kProjQChunk];
+  const int64_t g = blockIdx.x;
+  project_query_block(S, q + g * d, m, d, qs, y + g * m);
+}
+
+template <int W, int LPV>
 __global__ __launch_bounds__(256) void decode_split_kernel(
-    const TQ* __restrict__ q, const TS* __restrict__ S, int m_rt, int d,
-    const uint32_t* __restrict__ kbits, const uint16_t* __restrict__ knorms,
+    const float* __restrict__ yall, int m_rt, int d, const uint32_t* __restrict__ kbits, const uint16_t* __restrict__ knorms,
     const int8_t* __restrict__ vcodes, const float* __restrict__ vscales, int64_t T,
     int64_t splits, int64_t tps, float lam, float* __restrict__ partials) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
@@ -72,7 +81,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
-  project_query(S, q + g * d, m, d, y);
+  for (int i = threadIdx.x; i < m; i += 256) y[i] = yall[g * m + i];
   __syncthreads();
   build_byte_tables(y, m / 8, lut);
   __syncthreads();
@@ -235,28 +244,33 @@ DecodeSplit decode_split(int64_t groups, int64_t T, const DeviceInfo& dev) {
   return s;
 }
 
-size_t decode_workspace_bytes(int64_t groups, int64_t T, int d, const DeviceInfo& dev) {
-  const DecodeSplit s = decode_split(groups, T, dev);
-  return (size_t)groups * (size_t)s.splits * (size_t)(d + 2) * sizeof(float);
+// Workspace: y [groups][m] (padded to 256 B), then partials [groups][splits][d + 2].
+static size_t decode_y_bytes(int64_t groups, int m) {
+  return ((size_t)groups * (size_t)m * sizeof(float) + 255) / 256 * 256;
 }
 
-static size_t decode_lds_bytes(int m, int d) {
+size_t decode_workspace_bytes(int64_t groups, int64_t T, int d, int m, const DeviceInfo& dev) {
+  const DecodeSplit s = decode_split(groups, T, dev);
+  return decode_y_bytes(groups, m) + (size_t)groups * (size_t)s.splits * (size_t)(d + 2) * sizeof(float);
+}
+
+size_t decode_lds_bytes(int m, int d) {
   return ((size_t)m + (size_t)(m / 8) * 256 + 4 * (size_t)(d + 2)) * sizeof(float);
 }
 
-template <typename TS, typename TQ, int W, int LPV>
-static hipError_t decode_launch(const TQ* q, int64_t groups, const TS* S, int m,
-                                const uint32_t* kbits, const uint16_t* knorms,
-                                const int8_t* vcodes, const float* vscales, int64_t T, int d,
-                                float lam, float* partials, const DecodeSplit& sp, hipStream_t st) {
+template <int W, int LPV>
+static hipError_t decode_launch(const float* y, int64_t groups, int m, const uint32_t* kbits,
+                                const uint16_t* knorms, const int8_t* vcodes,
+                                const float* vscales, int64_t T, int d, float lam, float* partials,
+                                const DecodeSplit& sp, hipStream_t st) {
   const size_t lds = decode_lds_bytes(m, d);
-  hipError_t e0 = allow_dynamic_lds(decode_split_kernel<TS, TQ, W, LPV>, lds);
+  hipError_t e0 = allow_dynamic_lds(decode_split_kernel<W, LPV>, lds);
   if (e0 != hipSuccess) return e0;
   const int64_t max_groups = std::max<int64_t>(1, (int64_t(1) << 22) / sp.splits);
   for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
     const int64_t ng = std::min(max_groups, groups - g0);
-    hipLaunchKernelGGL((decode_split_kernel<TS, TQ, W, LPV>), dim3((unsigned)(ng * sp.splits)),
-                       dim3(256), lds, st, q + g0 * d, S, m, d, kbits + g0 * T * (m / 32),
+    hipLaunchKernelGGL((decode_split_kernel<W, LPV>), dim3((unsigned)(ng * sp.splits)),
+                       dim3(256), lds, st, y + g0 * m, m, d, kbits + g0 * T * (m / 32),
                        knorms + g0 * T, vcodes + g0 * T * d, vscales + g0 * T, T, sp.splits,
                        sp.tokens_per_split, lam, partials + g0 * sp.splits * (d + 2));
     hipError_t e = hipGetLastError();
@@ -268,27 +282,30 @@ static hipError_t decode_launch(const TQ* q, int64_t groups, const TS* S, int m,
 template <typename TS, typename TQ>
 static hipError_t decode_typed(const TQ* q, int64_t groups, const TS* S, int m,
                                const uint32_t* kbits, const uint16_t* knorms, const int8_t* vcodes,
-                               const float* vscales, int64_t T, int d, float lam, float* partials,
+                               const float* vscales, int64_t T, int d, float lam, void* ws,
                                float* out, const DeviceInfo& dev, hipStream_t st) {
-  if (d > kDecodeMaxD || decode_lds_bytes(m, d) > dev.lds_per_block)
-    return hipErrorInvalidConfiguration;
   const DecodeSplit sp = decode_split(groups, T, dev);
+  float* y = static_cast<float*>(ws);
+  float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + decode_y_bytes(groups, m));
+  const int64_t max_groups = int64_t(1) << 22;
+  for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
+    const int64_t ng = std::min(max_groups, groups - g0);
+    hipLaunchKernelGGL((qjl_project_kernel<TS, TQ>), dim3((unsigned)ng), dim3(256), 0, st,
+                       q + g0 * d, S, m, d, y + g0 * m);
+    hipError_t e1 = hipGetLastError();
+    if (e1 != hipSuccess) return e1;
+  }
   hipError_t e;
   if (m == 256 && d == 128)
-    e = decode_launch<TS, TQ, 8, 8>(q, groups, S, m, kbits, knorms, vcodes, vscales, T, d, lam,
-                                    partials, sp, st);
+    e = decode_launch<8, 8>(y, groups, m, kbits, knorms, vcodes, vscales, T, d, lam, partials, sp, st);
   else if (d == 64)
-    e = decode_launch<TS, TQ, 0, 4>(q, groups, S, m, kbits, knorms, vcodes, vscales, T, d, lam,
-                                    partials, sp, st);
+    e = decode_launch<0, 4>(y, groups, m, kbits, knorms, vcodes, vscales, T, d, lam, partials, sp, st);
   else if (d == 128)
-    e = decode_launch<TS, TQ, 0, 8>(q, groups, S, m, kbits, knorms, vcodes, vscales, T, d, lam,
-                                    partials, sp, st);
+    e = decode_launch<0, 8>(y, groups, m, kbits, knorms, vcodes, vscales, T, d, lam, partials, sp, st);
   else if (d == 256)
-    e = decode_launch<TS, TQ, 0, 16>(q, groups, S, m, kbits, knorms, vcodes, vscales, T, d, lam,
-                                     partials, sp, st);
+    e = decode_launch<0, 16>(y, groups, m, kbits, knorms, vcodes, vscales, T, d, lam, partials, sp, st);
   else
-    e = decode_launch<TS, TQ, 0, 64>(q, groups, S, m, kbits, knorms, vcodes, vscales, T, d, lam,
-                                     partials, sp, st);
+    e = decode_launch<0, 64>(y, groups, m, kbits, knorms, vcodes, vscales, T, d, lam, partials, sp, st);
   if (e != hipSuccess) return e;
   const int64_t n = groups * d;
   hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
@@ -301,21 +318,20 @@ hipError_t launch_decode_qjl_int8(const void* q, int q_f16, int64_t groups, cons
                                   const int8_t* vcodes, const float* vscales, int64_t T, int d,
                                   float sm_scale, void* ws, float* out, const DeviceInfo& dev,
                                   hipStream_t st) {
-  float* partials = static_cast<float*>(ws);
   if (S_f16) {
     const _Float16* Sp = static_cast<const _Float16*>(S);
     if (q_f16)
       return decode_typed(static_cast<const _Float16*>(q), groups, Sp, m, kbits, knorms, vcodes,
-                          vscales, T, d, sm_scale, partials, out, dev, st);
+                          vscales, T, d, sm_scale, ws, out, dev, st);
     return decode_typed(static_cast<const float*>(q), groups, Sp, m, kbits, knorms, vcodes,
-                        vscales, T, d, sm_scale, partials, out, dev, st);
+                        vscales, T, d, sm_scale, ws, out, dev, st);
   }
   const float* Sp = static_cast<const float*>(S);
   if (q_f16)
     return decode_typed(static_cast<const _Float16*>(q), groups, Sp, m, kbits, knorms, vcodes,
-                        vscales, T, d, sm_scale, partials, out, dev, st);
+                        vscales, T, d, sm_scale, ws, out, dev, st);
   return decode_typed(static_cast<const float*>(q), groups, Sp, m, kbits, knorms, vcodes, vscales,
-                      T, d, sm_scale, partials, out, dev, st);
+                      T, d, sm_scale, ws, out, dev, st);
 }
 
 }  // namespace kvq

@@ -214,11 +214,13 @@ kvq_status kvq_scores_qjl(const void* q, kvq_dtype q_dt, int64_t groups, int32_t
                                              reinterpret_cast<hipStream_t>(stream)));
 }
 
-size_t kvq_decode_workspace_bytes(int64_t groups, int64_t T, int32_t d) {
-  if (groups <= 0 || T <= 0 || d < 16 || d > kvq::kMaxD || d % 16 != 0) return 0;
+size_t kvq_decode_workspace_bytes(int64_t groups, int64_t T, int32_t d, int32_t m) {
+  if (groups <= 0 || T <= 0 || d < 16 || d > kvq::kMaxDecodeD || d % 16 != 0 || m < kvq::kMinM ||
+      m > kvq::kMaxM || m % 32 != 0)
+    return 0;
   kvq::DeviceInfo dev;
   if (kvq::current_device_info(&dev) != hipSuccess) return 0;
-  return kvq::decode_workspace_bytes(groups, T, d, dev);
+  return kvq::decode_workspace_bytes(groups, T, d, m, dev);
 }
 
 kvq_status kvq_decode_qjl_int8(const void* q, kvq_dtype q_dt, int64_t groups, const void* S,
@@ -232,6 +234,8 @@ kvq_status kvq_decode_qjl_int8(const void* q, kvq_dtype q_dt, int64_t groups, co
       (st = check_d(fn, d)) || (st = check_m(fn, m)) || (st = check_dtype(fn, "q_dt", q_dt)) ||
       (st = check_dtype(fn, "S_dt", S_dt)))
     return st;
+  if (d > kvq::kMaxDecodeD)
+    return fail(KVQ_ERR_SHAPE, "%s: d = %d exceeds %d", fn, (int)d, kvq::kMaxDecodeD);
   if (groups == 0) return ok();
   if (T == 0) return fail(KVQ_ERR_SHAPE, "%s: T = 0 (attention over no tokens)", fn);
   KVQ_CHECK_PTR(q);
@@ -243,13 +247,14 @@ kvq_status kvq_decode_qjl_int8(const void* q, kvq_dtype q_dt, int64_t groups, co
   KVQ_CHECK_PTR(out);
   kvq::DeviceInfo dev;
   if ((st = device_info(fn, &dev))) return st;
-  const size_t need = kvq::decode_workspace_bytes(groups, T, d, dev);
-  if (need > 0) {
-    if (ws == nullptr || ws_bytes < need)
-      return fail(KVQ_ERR_WORKSPACE, "%s: workspace of %zu bytes at %p, need %zu", fn, ws_bytes, ws,
-                  need);
-    if (!aligned16(ws)) return fail(KVQ_ERR_ALIGN, "%s: ws is not 16-byte aligned", fn);
-  }
+  const size_t need = kvq::decode_workspace_bytes(groups, T, d, m, dev);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(KVQ_ERR_WORKSPACE, "%s: workspace of %zu bytes at %p, need %zu", fn, ws_bytes, ws,
+                need);
+  if (!aligned16(ws)) return fail(KVQ_ERR_ALIGN, "%s: ws is not 16-byte aligned", fn);
+  if (kvq::decode_lds_bytes(m, d) > dev.lds_per_block)
+    return fail(KVQ_ERR_SHAPE, "%s: m = %d, d = %d need %zu bytes of LDS, the device has %zu", fn,
+                (int)m, (int)d, kvq::decode_lds_bytes(m, d), dev.lds_per_block);
   return launched(fn, kvq::launch_decode_qjl_int8(q, q_dt == KVQ_F16, groups, S, S_dt == KVQ_F16,
                                                   m, kbits, knorms, vcodes, vscales, T, d,
                                                   sm_scale, ws, out, dev,

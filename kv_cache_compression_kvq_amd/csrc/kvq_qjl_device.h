@@ -17,15 +17,72 @@ __host__ __device__ constexpr int sketch_row_perm(int i) {
 // ---------------------------------------------------------------------------
 // Query projection and byte tables (shared by the score and decode kernels).
 
-// y[i] = sum_j S[i][j] q[j] for i < m, binary32, one row per thread.
+// 16 values of type T from 16-byte-aligned memory, widened to binary32.
+template <typename T>
+__device__ __forceinline__ void load16_f32(const T* p, float out[16]);
+template <>
+__device__ __forceinline__ void load16_f32<float>(const float* p, float out[16]) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const f32x4 x = reinterpret_cast<const f32x4*>(p)[v];
+    out[4 * v] = x[0]; out[4 * v + 1] = x[1]; out[4 * v + 2] = x[2]; out[4 * v + 3] = x[3];
+  }
+}
+template <>
+__device__ __forceinline__ void load16_f32<_Float16>(const _Float16* p, float out[16]) {
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    const f16x8 x = reinterpret_cast<const f16x8*>(p)[v];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[8 * v + e] = (float)x[e];
+  }
+}
+
+constexpr int kProjQChunk = 2048;   // query values staged in LDS per pass
+constexpr int kProjMaxRowsPerThread = 4;
+
+// y[i] = sum_j S[i][j] q[j] for i < m (m <= 1024), binary32 fused
+// multiply-adds in j order, computed by the whole 256-thread workgroup:
+// thread t owns rows t, t + 256, ...; q is staged through LDS (qs, at least
+// kProjQChunk floats) and S rows are read 16 values at a time.
 template <typename TS, typename TQ>
-__device__ void project_query(const TS* __restrict__ S, const TQ* __restrict__ q, int m, int d,
-                              float* y) {
-  for (int i = threadIdx.x; i < m; i += blockDim.x) {
-    const TS* sr = S + (int64_t)i * d;
-    float acc = 0.0f;
-    for (int j = 0; j < d; ++j) acc = __builtin_fmaf(to_f32(sr[j]), to_f32(q[j]), acc);
-    y[i] = acc;
+__device__ void project_query_block(const TS* __restrict__ S, const TQ* __restrict__ q, int m,
+                                    int d, float* qs, float* y) {
+  float acc[kProjMaxRowsPerThread];
+#pragma unroll
+  for (int r = 0; r < kProjMaxRowsPerThread; ++r) acc[r] = 0.0f;
+  for (int j0 = 0; j0 < d; j0 += kProjQChunk) {
+    const int len = min(kProjQChunk, d - j0);
+    __syncthreads();
+    for (int j = threadIdx.x; j < len; j += blockDim.x) qs[j] = to_f32(q[j0 + j]);
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kProjMaxRowsPerThread; ++r) {
+      const int i = threadIdx.x + r * (int)blockDim.x;
+      if (i < m) {
+        const TS* sr = S + (int64_t)i * d + j0;
+        float a = acc[r];
+        for (int j = 0; j < len; j += 16) {
+          float sv[16];
+          load16_f32<TS>(sr + j, sv);
+          const f32x4* qv = reinterpret_cast<const f32x4*>(qs + j);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const f32x4 qq = qv[v];
+            a = __builtin_fmaf(sv[4 * v + 0], qq[0], a);
+            a = __builtin_fmaf(sv[4 * v + 1], qq[1], a);
+            a = __builtin_fmaf(sv[4 * v + 2], qq[2], a);
+            a = __builtin_fmaf(sv[4 * v + 3], qq[3], a);
+          }
+        }
+        acc[r] = a;
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kProjMaxRowsPerThread; ++r) {
+    const int i = threadIdx.x + r * (int)blockDim.x;
+    if (i < m) y[i] = acc[r];
   }
 }
 

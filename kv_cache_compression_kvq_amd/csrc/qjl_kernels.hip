@@ -257,9 +257,20 @@ hipError_t launch_qjl_sketch(const void* k, int k_f16, int64_t rows, int d, cons
 }
 
 // ---------------------------------------------------------------------------
-// QJL scores: one workgroup per (group, query, tile of kScoreTok tokens).
-constexpr int kQjlTokPerThread = 8;
+// QJL scores: one workgroup per (group, query, tile of kQjlTok tokens).  Each
+// thread owns kQjlTokPerThread tokens and loads kQjlBatch of them (sign
+// words and norm) before scoring any, so every wave keeps 8 x 34 bytes per
+// lane in flight.
+constexpr int kQjlBatch = 8;
+constexpr int kQjlTokPerThread = 16;
 constexpr int kQjlTok = 256 * kQjlTokPerThread;
+
+// LDS: y [m] | byte tables [m / 8][256] (also the query staging area of the
+// projection, which ends before the tables are built).
+__host__ __device__ inline size_t qjl_table_lds_floats(int m) {
+  const size_t tables = (size_t)(m / 8) * 256;
+  return (size_t)m + (tables > (size_t)kProjQChunk ? tables : (size_t)kProjQChunk);
+}
 
 template <typename TS, typename TQ, int W>
 __global__ __launch_bounds__(256) void scores_qjl_kernel(const TQ* __restrict__ q, int nq,
@@ -276,34 +287,53 @@ __global__ __launch_bounds__(256) void scores_qjl_kernel(const TQ* __restrict__ 
   const int64_t gj = blockIdx.x / tiles;           // (group, query) pair
   const int64_t tile = blockIdx.x % tiles;
   const int64_t g = gj / nq;
-  project_query(S, q + gj * d, m, d, y);
+  project_query_block(S, q + gj * d, m, d, lut, y);
   __syncthreads();
   build_byte_tables(y, m / 8, lut);
   __syncthreads();
   const float c = kSqrtHalfPi / (float)m;
   const uint32_t* bg = bits + g * T * words;
   const uint16_t* ng = norms + g * T;
-  for (int u = 0; u < kQjlTokPerThread; ++u) {
-    const int64_t t = tile * kQjlTok + u * 256 + threadIdx.x;
-    if (t >= T) break;
-    float acc;
-    if constexpr (W > 0) {
-      uint32_t wv[W];
+  float* sg = scores + gj * T;
+  const int64_t t0 = tile * kQjlTok + threadIdx.x;
+  if constexpr (W > 0) {
+    for (int b0 = 0; b0 < kQjlTokPerThread; b0 += kQjlBatch) {
+      uint32_t wv[kQjlBatch][W];
+      float nv[kQjlBatch];
 #pragma unroll
-      for (int i = 0; i < W; i += 4) {
-        const u32x4 v4 = *reinterpret_cast<const u32x4*>(bg + t * W + i);
-        wv[i] = v4[0]; wv[i + 1] = v4[1]; wv[i + 2] = v4[2]; wv[i + 3] = v4[3];
+      for (int u = 0; u < kQjlBatch; ++u) {
+        const int64_t t = t0 + (int64_t)(b0 + u) * 256;
+        if (t < T) {
+#pragma unroll
+          for (int i = 0; i < W; i += 4) {
+            const u32x4 v4 = *reinterpret_cast<const u32x4*>(bg + t * W + i);
+            wv[u][i] = v4[0]; wv[u][i + 1] = v4[1]; wv[u][i + 2] = v4[2]; wv[u][i + 3] = v4[3];
+          }
+          nv[u] = (float)__builtin_bit_cast(_Float16, ng[t]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < W; ++i) wv[u][i] = 0;
+          nv[u] = 0.0f;
+        }
       }
-      acc = lut_sum(lut, wv, W);
-    } else {
-      acc = 0.0f;
+#pragma unroll
+      for (int u = 0; u < kQjlBatch; ++u) {
+        const int64_t t = t0 + (int64_t)(b0 + u) * 256;
+        const float acc = lut_sum(lut, wv[u], W);
+        if (t < T) sg[t] = c * nv[u] * acc;
+      }
+    }
+  } else {
+    for (int u = 0; u < kQjlTokPerThread; ++u) {
+      const int64_t t = t0 + (int64_t)u * 256;
+      if (t >= T) break;
+      float acc = 0.0f;
       for (int i = 0; i < words; ++i) {
         const uint32_t x = bg[t * words + i];
         acc += lut_sum(lut + i * 1024, &x, 1);
       }
+      sg[t] = c * (float)__builtin_bit_cast(_Float16, ng[t]) * acc;
     }
-    const float n = (float)__builtin_bit_cast(_Float16, ng[t]);
-    scores[gj * T + t] = c * n * acc;
   }
 }
 
@@ -311,7 +341,7 @@ template <typename TS, typename TQ>
 static hipError_t scores_qjl_typed(const TQ* q, int64_t groups, int nq, const TS* S, int m,
                                    const uint32_t* bits, const uint16_t* norms, int64_t T, int d,
                                    float* scores, const DeviceInfo& dev, hipStream_t st) {
-  const size_t lds = (size_t)m * sizeof(float) + (size_t)(m / 8) * 256 * sizeof(float);
+  const size_t lds = qjl_table_lds_floats(m) * sizeof(float);
   if (lds > dev.lds_per_block) return hipErrorInvalidConfiguration;
   const int64_t tiles = (T + kQjlTok - 1) / kQjlTok;
   // launch in slices of whole groups so grid.x stays far below 2^32

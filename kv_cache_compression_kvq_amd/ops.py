@@ -114,8 +114,8 @@ def scores_qjl(q: torch.Tensor, S: torch.Tensor, bits: torch.Tensor,
     return out
 
 
-def decode_workspace_bytes(groups: int, T: int, d: int) -> int:
-    return int(L.lib().kvq_decode_workspace_bytes(groups, T, d))
+def decode_workspace_bytes(groups: int, T: int, d: int, m: int) -> int:
+    return int(L.lib().kvq_decode_workspace_bytes(groups, T, d, m))
 
 
 def decode_qjl_int8(q: torch.Tensor, S: torch.Tensor, kbits: torch.Tensor, knorms: torch.Tensor,
@@ -137,7 +137,7 @@ def decode_qjl_int8(q: torch.Tensor, S: torch.Tensor, kbits: torch.Tensor, knorm
         raise ValueError("shape mismatch between q, S and the cache tensors")
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
-    need = decode_workspace_bytes(G, T, d)
+    need = decode_workspace_bytes(G, T, d, m)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if out is None:

@@ -130,9 +130,11 @@ def test_decode_validation():
 
 def test_workspace_query_rejects_bad_shapes_without_a_device():
     f = L.lib().kvq_decode_workspace_bytes
-    assert f(0, 16, 128) == 0
-    assert f(4, 0, 128) == 0
-    assert f(4, 16, 100) == 0
+    assert f(0, 16, 128, 256) == 0
+    assert f(4, 0, 128, 256) == 0
+    assert f(4, 16, 100, 256) == 0
+    assert f(4, 16, 128, 48) == 0
+    assert f(4, 16, 2048, 256) == 0
 
 
 def test_python_binding_requires_gpu_tensors():

@@ -94,7 +94,7 @@ def test_split_invariance():
     alone = down(K.decode_qjl_int8(up(q[:1]), up(S), up(kw[:1]), up(kn[:1]), up(vc[:1]), up(vs[:1])))
     rep = lambda a: np.ascontiguousarray(np.repeat(a[:1], G, axis=0))
     many = down(K.decode_qjl_int8(up(rep(q)), up(S), up(rep(kw)), up(rep(kn)), up(rep(vc)), up(rep(vs))))
-    assert K.decode_workspace_bytes(1, T, d) // (d + 2) // 4 != K.decode_workspace_bytes(G, T, d) // G // (d + 2) // 4
+    assert K.decode_workspace_bytes(1, T, d, m) // (d + 2) // 4 != K.decode_workspace_bytes(G, T, d, m) // G // (d + 2) // 4
     assert np.allclose(many, alone[0][None, :], rtol=2e-5, atol=1e-6)
 
 
