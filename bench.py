@@ -100,34 +100,48 @@ def med(xs):
     return s[len(s) // 2]
 
 
+COLD_BYTES = 1 << 30     # rotate inputs over > 1 GiB: 4x the 256 MB last-level cache (MALL)
+
+
 def components(K, si, torch, np):
-    """GB/s of the INT8 and QJL kernels on their own workloads."""
+    """GB/s of the INT8 and QJL kernels on their own workloads, cold: each
+    timed call reads a different copy of its inputs, and the copies together
+    exceed 1 GiB, so no call finds its inputs in the MALL or L2."""
     res = {}
     dev = "cuda"
 
-    def gbs(name, nbytes, fn, reps=20, flops=None):
+    def gbs(name, nbytes, calls, reps=20, flops=None):
+        """calls: list of zero-argument launches, one per input copy."""
+        it = iter(range(10 ** 9))
+        fn = lambda: calls[next(it) % len(calls)]()
         ms = med(event_times(fn, reps, 3))
         r = {"ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
-             "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 3), "bytes": int(nbytes)}
+             "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 3), "bytes": int(nbytes),
+             "copies": len(calls)}
         if flops:
             r["TFLOP/s"] = round(flops / ms / 1e9, 1)
             r["frac_mfma_f16"] = round(flops / ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 3)
         res[name] = r
         log(f"  {name}: {r}")
 
+    def ncopies(bytes_per_call):
+        return max(1, -(-COLD_BYTES // int(bytes_per_call)) + 1)
+
     # element-count sweep, fp32 rows of d in {128, 1024, 8192}
     for nlog in (28, 30):
         n = 1 << nlog
         x = torch.from_numpy(si.flat_rows(si.W_SWEEP, n, 128).reshape(-1)).to(dev)
+        xs = [x] + [x.clone() for _ in range(ncopies(4 * n) - 1)] if nlog < 30 else [x]
         for d in (128, 1024, 8192):
-            xv = x.view(n // d, d)
-            codes, scales = K.quantize_int8(xv)
             rows = n // d
-            gbs(f"quantize_f32_2^{nlog}_d{d}", 4 * n + n + 4 * rows, lambda: K.quantize_int8(xv))
+            views = [t.view(rows, d) for t in xs]
+            cs = [K.quantize_int8(v) for v in views]
+            gbs(f"quantize_f32_2^{nlog}_d{d}", 4 * n + n + 4 * rows,
+                [lambda v=v: K.quantize_int8(v) for v in views])
             gbs(f"dequantize_f32_2^{nlog}_d{d}", n + 4 * rows + 4 * n,
-                lambda: K.dequantize_int8(codes, scales))
-            del codes, scales
-        del x
+                [lambda c=c: K.dequantize_int8(c[0], c[1]) for c in cs])
+            del cs
+        del x, xs
         torch.cuda.empty_cache()
 
     # Llama-7B-shaped layer, fp16: K and V quantized, dequantized, scored
@@ -136,15 +150,19 @@ def components(K, si, torch, np):
     v = torch.from_numpy(si.kv_tensor(W, si.V, 1, 32, 4096, 128, "f16")).to(dev)
     kv = torch.stack([k, v]).view(-1, 128)
     R = kv.shape[0]
-    codes, scales = K.quantize_int8(kv)
-    gbs("llama_layer_quantize_kv_f16", 2 * R * 128 + R * 128 + 4 * R, lambda: K.quantize_int8(kv))
+    nc = ncopies(2 * R * 128)
+    kvs = [kv] + [kv.clone() for _ in range(nc - 1)]
+    cs = [K.quantize_int8(t) for t in kvs]
+    gbs("llama_layer_quantize_kv_f16", 2 * R * 128 + R * 128 + 4 * R,
+        [lambda t=t: K.quantize_int8(t) for t in kvs])
     gbs("llama_layer_dequantize_kv_f16", R * 128 + 4 * R + 2 * R * 128,
-        lambda: K.dequantize_int8(codes, scales, torch.float16))
+        [lambda c=c: K.dequantize_int8(c[0], c[1], torch.float16) for c in cs])
     q = torch.from_numpy(si.queries(W, 32, 1, 128, "f16")).to(dev)
-    kc, ks = codes[: R // 2].view(32, 4096, 128), scales[: R // 2].view(32, 4096)
+    halves = [(c[0][: R // 2].view(32, 4096, 128), c[1][: R // 2].view(32, 4096)) for c in cs]
     gbs("llama_layer_scores_int8", 32 * 4096 * (128 + 4 + 4) + 32 * 128 * 2,
-        lambda: K.scores_int8(q, kc, ks))
-    del k, v, kv, codes, scales
+        [lambda h=h: K.scores_int8(q, h[0], h[1]) for h in halves])
+    del k, v, kv, kvs, cs, halves
+    torch.cuda.empty_cache()
 
     # QJL key cache: 8 x 32 x 8192 x 128 fp16, m = 256
     W = si.W_QJL_CACHE
@@ -152,15 +170,19 @@ def components(K, si, torch, np):
     kk = torch.from_numpy(si.kv_tensor(W, si.K, 8, 32, T, d, "f16", outliers=True)).to(dev).view(-1, d)
     S = torch.from_numpy(si.projection(W, m, d, "f16")).to(dev)
     R = kk.shape[0]
-    bits, norms = K.qjl_sketch(kk, S)
+    kks = [kk] + [kk.clone() for _ in range(ncopies(R * d * 2) - 1)]
+    sk = [K.qjl_sketch(t, S) for t in kks]
     gbs("qjl_sketch_f16_m256", R * d * 2 + R * (m // 8) + 2 * R + m * d * 2,
-        lambda: K.qjl_sketch(kk, S), flops=2.0 * R * d * m)
+        [lambda t=t: K.qjl_sketch(t, S) for t in kks], flops=2.0 * R * d * m)
+    del kks
     q = torch.from_numpy(si.queries(W, G, 1, d, "f16")).to(dev)
-    b3, n3 = bits.view(G, T, m // 32), norms.view(G, T)
+    b3 = [(b.view(G, T, m // 32), n.view(G, T)) for b, n in sk]
+    while len(b3) < ncopies(R * (m // 8 + 2)):
+        b3.append((b3[0][0].clone(), b3[0][1].clone()))
     gbs("qjl_scores_f16_m256", R * (m // 8 + 2 + 4) + G * d * 2 + m * d * 2,
-        lambda: K.scores_qjl(q, S, b3, n3))
+        [lambda bn=bn: K.scores_qjl(q, S, bn[0], bn[1]) for bn in b3])
     res["qjl_scores_f16_m256"]["scores/s"] = round(R / res["qjl_scores_f16_m256"]["ms"] * 1e3, 1)
-    del kk, bits, norms
+    del kk, sk, b3
     torch.cuda.empty_cache()
     return res
 

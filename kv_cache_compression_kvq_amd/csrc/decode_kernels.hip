@@ -8,10 +8,10 @@
 //   out     = sum_t softmax_t(lam * sigma_t) * s_t * c_t
 //
 // Work split: the T tokens of a (batch, head) group are cut into `splits`
-// ranges; one workgroup per (group, range) builds y = S q and the byte tables
+// ranges; one workgroup per (group, range) builds the byte tables from y = S q
 // in LDS, streams its tokens once (sign words, norm, value codes, value
 // scale) and keeps a running max / sum / weighted value sum per wave
-// (online softmax).  The four waves are merged in LDS and the workgroup
+// (online softmax).  The eight waves are merged in LDS and the workgroup
 // writes (max, sum, o[d]) to the workspace; a second kernel merges the
 // ranges with the log-sum-exp rule.  Nothing is materialised per token.
 //
@@ -28,8 +28,10 @@
 
 namespace kvq {
 
+constexpr int kDecodeWaves = 8;                        // waves per workgroup
+constexpr int kDecodeThreads = 64 * kDecodeWaves;
 constexpr int kDecodeChunk = 64;                       // tokens per wave step
-constexpr int kDecodeBlockTokens = 4 * kDecodeChunk;   // tokens per workgroup step
+constexpr int kDecodeBlockTokens = kDecodeWaves * kDecodeChunk;   // tokens per workgroup step
 
 // DPP row rotate (lane i takes lane (i + n) % 16 of its 16-lane row).
 template <int N>
@@ -63,7 +65,7 @@ __global__ __launch_bounds__(256) void qjl_project_kernel(const TQ* __restrict__
 }
 
 template <int W, int LPV>
-__global__ __launch_bounds__(256) void decode_split_kernel(
+__global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     const float* __restrict__ yall, int m_rt, int d, const uint32_t* __restrict__ kbits, const uint16_t* __restrict__ knorms,
     const int8_t* __restrict__ vcodes, const float* __restrict__ vscales, int64_t T,
     int64_t splits, int64_t tps, float lam, float* __restrict__ partials) {
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const int words = m / 32;
   float* y = reinterpret_cast<float*>(lds_raw);
   float* lut = y + m;
-  float* wpart = lut + (m / 8) * 256;                  // [4][d + 2]
+  float* wpart = lut + (m / 8) * 256;                  // [kDecodeWaves][d + 2]
 
   const int64_t g = blockIdx.x / splits;
   const int64_t sp = blockIdx.x % splits;
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
-  for (int i = threadIdx.x; i < m; i += 256) y[i] = yall[g * m + i];
+  for (int i = threadIdx.x; i < m; i += kDecodeThreads) y[i] = yall[g * m + i];
   __syncthreads();
   build_byte_tables(y, m / 8, lut);
   __syncthreads();
@@ -89,62 +91,65 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   constexpr int SLOTS = kWave / LPV;      // value rows per wave load
   constexpr int VSTEPS = kDecodeChunk / SLOTS;
   constexpr bool PREFETCH = LPV <= 16;
+  constexpr int DV = PREFETCH ? 16 * LPV : 0;   // compile-time d when LPV fixes it
+  const int dd = DV > 0 ? DV : d;
   const int sub = lane % LPV;
   const int slot = lane / LPV;
-  const int cpr = d / 16;                  // 16-code chunks per value row
+  const int cpr = dd / 16;                 // 16-code chunks per value row
   const bool sub_live = sub < cpr;         // LPV == 64 covers d < 1024 with idle lanes
   const float c = kSqrtHalfPi / (float)m;
-  const uint32_t* bg = kbits + g * T * words;
-  const uint16_t* ng = knorms + g * T;
-  const int8_t* vg = vcodes + g * T * d;
-  const float* sg = vscales + g * T;
+  // Per-workgroup bases; everything below is a 32-bit offset from them (a
+  // token range holds at most 2^31 / (d + m / 8) tokens, checked on launch).
+  const int64_t row0 = g * T + t_begin;
+  const uint32_t* bblk = kbits + row0 * words;
+  const uint16_t* nblk = knorms + row0;
+  const int8_t* vblk = vcodes + row0 * dd + sub * 16;
+  const float* sblk = vscales + row0;
+  const int ntok = (int)(t_end - t_begin);
 
   float M = -INFINITY, L = 0.0f;
   float o[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) o[e] = 0.0f;
 
-  for (int64_t base = t_begin + wave * kDecodeChunk; base < t_end; base += kDecodeBlockTokens) {
-    const int64_t t = base + lane;
-    const bool valid = t < t_end;
-    // value codes of this chunk (independent of the scores)
+  for (int base = wave * kDecodeChunk; base < ntok; base += kDecodeBlockTokens) {
+    // Tokens past the range are clamped to its last token: their loads stay
+    // in bounds and their softmax weight is forced to 0 below.
+    const int t = base + lane;
+    const bool valid = t < ntok;
+    const int tc = min(t, ntok - 1);
     u32x4 vc[PREFETCH ? VSTEPS : 1];
     if constexpr (PREFETCH) {
 #pragma unroll
       for (int i = 0; i < VSTEPS; ++i) {
-        const int64_t tv = base + i * SLOTS + slot;
-        vc[i] = (tv < t_end && sub_live) ? *reinterpret_cast<const u32x4*>(vg + tv * d + sub * 16)
-                                         : u32x4{};
+        const int tv = min(base + i * SLOTS + slot, ntok - 1);
+        vc[i] = ld_stream(reinterpret_cast<const u32x4*>(vblk + tv * DV));
       }
     }
-    // score of token t
-    float z = -INFINITY, vs = 0.0f;
-    if (valid) {
-      float acc;
-      if constexpr (W > 0) {
-        uint32_t wv[W];
+    float acc;
+    if constexpr (W > 0) {
+      uint32_t wv[W];
 #pragma unroll
-        for (int i = 0; i < W; i += 4) {
-          const u32x4 v4 = *reinterpret_cast<const u32x4*>(bg + t * W + i);
-          wv[i] = v4[0]; wv[i + 1] = v4[1]; wv[i + 2] = v4[2]; wv[i + 3] = v4[3];
-        }
-        acc = lut_sum(lut, wv, W);
-      } else {
-        acc = 0.0f;
-        for (int i = 0; i < words; ++i) {
-          const uint32_t x = bg[t * words + i];
-          acc += lut_sum(lut + i * 1024, &x, 1);
-        }
+      for (int i = 0; i < W; i += 4) {
+        const u32x4 v4 = ld_stream(reinterpret_cast<const u32x4*>(bblk + tc * W + i));
+        wv[i] = v4[0]; wv[i + 1] = v4[1]; wv[i + 2] = v4[2]; wv[i + 3] = v4[3];
       }
-      const float n = (float)__builtin_bit_cast(_Float16, ng[t]);
-      z = lam * (c * n * acc);
-      vs = sg[t];
+      acc = lut_sum(lut, wv, W);
+    } else {
+      acc = 0.0f;
+      for (int i = 0; i < words; ++i) {
+        const uint32_t x = bblk[tc * words + i];
+        acc += lut_sum(lut + i * 1024, &x, 1);
+      }
     }
+    const float n = (float)__builtin_bit_cast(_Float16, ld_stream(nblk + tc));
+    const float vs = ld_stream(sblk + tc);
+    const float z = valid ? lam * (c * n * acc) : -INFINITY;
     // online softmax update (lane 0 of every chunk is valid, so mx is finite)
     const float mx = seg_max_f32<64>(z);
     const float M_new = __builtin_fmaxf(M, mx);
-    const float alpha = (M == -INFINITY) ? 0.0f : __expf(M - M_new);
-    const float p = valid ? __expf(z - M_new) : 0.0f;
+    const float alpha = __expf(M - M_new);        // 0 on the first chunk (M = -inf)
+    const float p = __expf(z - M_new);            // 0 for invalid tokens (z = -inf)
     L = L * alpha + seg_sum_f32<64>(p);
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[e] *= alpha;
@@ -161,10 +166,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     } else {
       for (int i = 0; i < VSTEPS; ++i) {
         const float w = bcast_from(ps, i * SLOTS + slot);
-        const int64_t tv = base + i * SLOTS + slot;
-        const u32x4 cw = (tv < t_end && sub_live)
-                             ? *reinterpret_cast<const u32x4*>(vg + tv * d + sub * 16)
-                             : u32x4{};
+        const int tv = min(base + i * SLOTS + slot, ntok - 1);
+        const u32x4 cw = sub_live ? *reinterpret_cast<const u32x4*>(vblk + tv * dd) : u32x4{};
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[e] = __builtin_fmaf(w, i8_to_f32(cw[e >> 2], e & 3), o[e]);
       }
@@ -184,27 +187,27 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     for (int e = 0; e < 16; ++e) wp[2 + sub * 16 + e] = o[e];
   }
   __syncthreads();
-  float Mw[4], Ms = -INFINITY;
+  float Mw[kDecodeWaves], Ms = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < kDecodeWaves; ++w) {
     Mw[w] = wpart[w * (d + 2)];
     Ms = __builtin_fmaxf(Ms, Mw[w]);
   }
-  float sc[4];
+  float sc[kDecodeWaves];
 #pragma unroll
-  for (int w = 0; w < 4; ++w) sc[w] = (Mw[w] == -INFINITY) ? 0.0f : __expf(Mw[w] - Ms);
+  for (int w = 0; w < kDecodeWaves; ++w) sc[w] = (Mw[w] == -INFINITY) ? 0.0f : __expf(Mw[w] - Ms);
   float* out = partials + (g * splits + sp) * (int64_t)(d + 2);
   if (threadIdx.x == 0) {
     float Ls = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) Ls += sc[w] * wpart[w * (d + 2) + 1];
+    for (int w = 0; w < kDecodeWaves; ++w) Ls += sc[w] * wpart[w * (d + 2) + 1];
     out[0] = Ms;
     out[1] = Ls;
   }
-  for (int j = threadIdx.x; j < d; j += 256) {
+  for (int j = threadIdx.x; j < d; j += kDecodeThreads) {
     float acc = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
+    for (int w = 0; w < kDecodeWaves; ++w)
       if (sc[w] != 0.0f) acc += sc[w] * wpart[w * (d + 2) + 2 + j];
     out[2 + j] = acc;
   }
@@ -234,9 +237,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
 
 DecodeSplit decode_split(int64_t groups, int64_t T, const DeviceInfo& dev) {
   DecodeSplit s;
-  const int64_t target_blocks = 8LL * std::max(1, dev.cus);
+  const int64_t target_blocks = 6LL * std::max(1, dev.cus);
   const int64_t max_splits = std::max<int64_t>(1, (T + kDecodeBlockTokens - 1) / kDecodeBlockTokens);
   int64_t splits = std::min(max_splits, std::max<int64_t>(1, (target_blocks + groups - 1) / groups));
+  // token ranges of at most 2^20 tokens keep every in-kernel offset in 32 bits
+  splits = std::max<int64_t>(splits, (T + (int64_t(1) << 20) - 1) >> 20);
   int64_t tps = (T + splits - 1) / splits;
   tps = (tps + kDecodeBlockTokens - 1) / kDecodeBlockTokens * kDecodeBlockTokens;
   s.tokens_per_split = tps;
@@ -255,7 +260,7 @@ size_t decode_workspace_bytes(int64_t groups, int64_t T, int d, int m, const Dev
 }
 
 size_t decode_lds_bytes(int m, int d) {
-  return ((size_t)m + (size_t)(m / 8) * 256 + 4 * (size_t)(d + 2)) * sizeof(float);
+  return ((size_t)m + (size_t)(m / 8) * 256 + kDecodeWaves * (size_t)(d + 2)) * sizeof(float);
 }
 
 template <int W, int LPV>
@@ -270,7 +275,7 @@ static hipError_t decode_launch(const float* y, int64_t groups, int m, const uin
   for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
     const int64_t ng = std::min(max_groups, groups - g0);
     hipLaunchKernelGGL((decode_split_kernel<W, LPV>), dim3((unsigned)(ng * sp.splits)),
-                       dim3(256), lds, st, y + g0 * m, m, d, kbits + g0 * T * (m / 32),
+                       dim3(kDecodeThreads), lds, st, y + g0 * m, m, d, kbits + g0 * T * (m / 32),
                        knorms + g0 * T, vcodes + g0 * T * d, vscales + g0 * T, T, sp.splits,
                        sp.tokens_per_split, lam, partials + g0 * sp.splits * (d + 2));
     hipError_t e = hipGetLastError();

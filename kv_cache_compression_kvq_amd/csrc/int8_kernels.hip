@@ -8,9 +8,7 @@
 //
 // Arithmetic: s = a / 127 and t = x / s are IEEE binary32 divisions (the
 // compiler's correctly rounded sequence; no fast-math, denormals kept);
-// rint rounds half to even; the clamp is a med3.  A zero scale divides by 1
-// instead, which maps every value of such a row (all |x| < 127 * 2^-150) to
-// code 0.
+// rint rounds half to even; the clamp is a med3.
 //
 // Memory: all three kernels are HBM streams.  Lanes are mapped so that each
 // load instruction of a wave reads 1 KiB of contiguous memory (16 B per
@@ -35,10 +33,15 @@ template <> struct Chunk<_Float16> {
   using Codes = u32x2;                 // 8 codes
 };
 
+// Row divisor: the scale, or 1 for a zero scale (every value of such a row
+// has |x| < 127 * 2^-150 and maps to code 0).
+__device__ __forceinline__ float row_divisor(float s) { return (s == 0.0f) ? 1.0f : s; }
+
+// One code: rint(RN32(x / s)) clamped to [-128, 127].  x / s is the
+// compiler's IEEE binary32 division; rint rounds half to even.
 __device__ __forceinline__ uint32_t code_of(float x, float sdiv) {
-  float t = x / sdiv;                                  // RN32(x / s)
-  float r = __builtin_rintf(t);                        // ties to even
-  r = __builtin_amdgcn_fmed3f(r, -128.0f, 127.0f);
+  const float t = x / sdiv;
+  const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(t), -128.0f, 127.0f);
   return (uint32_t)(int)r & 0xFFu;
 }
 
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(256) void quantize_lanes_kernel(const T* __restrict
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       if (row < rows)
-        v[u][j] = *reinterpret_cast<const typename C::V*>(x + row * D + (int64_t)(sub + LPR * j) * N);
+        v[u][j] = ld_stream(reinterpret_cast<const typename C::V*>(x + row * D + (int64_t)(sub + LPR * j) * N));
       else
         v[u][j] = typename C::V{};
     }
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(256) void quantize_lanes_kernel(const T* __restrict
     for (int j = 0; j < CPL; ++j) m = max(m, chunk_absmax<T>(v[u][j]));
     m = seg_max_u32<LPR>(m);
     const float s = row_scale(m);
-    const float sdiv = (s == 0.0f) ? 1.0f : s;
+    const float sdiv = row_divisor(s);
     if (row < rows) {
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(256) void quantize_block_kernel(const T* __restrict
   typename C::V v[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j)
-    v[j] = *reinterpret_cast<const typename C::V*>(xr + (int64_t)(tid + 256 * j) * N);
+    v[j] = ld_stream(reinterpret_cast<const typename C::V*>(xr + (int64_t)(tid + 256 * j) * N));
   uint32_t m = 0;
 #pragma unroll
   for (int j = 0; j < CPL; ++j) m = max(m, chunk_absmax<T>(v[j]));
@@ -150,7 +153,7 @@ __global__ __launch_bounds__(256) void quantize_block_kernel(const T* __restrict
   __syncthreads();
   m = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
   const float s = row_scale(m);
-  const float sdiv = (s == 0.0f) ? 1.0f : s;
+  const float sdiv = row_divisor(s);
 #pragma unroll
   for (int j = 0; j < CPL; ++j)
     *reinterpret_cast<typename C::Codes*>(codes + row * D + (int64_t)(tid + 256 * j) * N) =
@@ -175,7 +178,7 @@ __global__ __launch_bounds__(256) void quantize_generic_kernel(const T* __restri
     m = max(m, chunk_absmax<T>(*reinterpret_cast<const typename C::V*>(xr + (int64_t)c * N)));
   m = seg_max_u32<64>(m);
   const float s = row_scale(m);
-  const float sdiv = (s == 0.0f) ? 1.0f : s;
+  const float sdiv = row_divisor(s);
   for (int c = lane; c < cpr; c += kWave)
     *reinterpret_cast<typename C::Codes*>(codes + row * d + (int64_t)c * N) =
         encode_chunk<T>(*reinterpret_cast<const typename C::V*>(xr + (int64_t)c * N), sdiv);
@@ -287,7 +290,7 @@ __global__ __launch_bounds__(256) void dequantize_flat_kernel(const int8_t* __re
     const int64_t i = base + 256 * u;
     if (i < nchunks) {
       const int64_t row = POW2 ? (i >> cpr_shift) : (i / cpr);
-      cv[u] = *reinterpret_cast<const typename C::Codes*>(codes + i * N);
+      cv[u] = ld_stream(reinterpret_cast<const typename C::Codes*>(codes + i * N));
       sv[u] = scales[row];
     } else {
       cv[u] = typename C::Codes{};
@@ -404,7 +407,7 @@ __global__ __launch_bounds__(256) void scores_int8_kernel(const TQ* __restrict__
 #pragma unroll
       for (int u = 0; u < kScoreUnroll; ++u) {
         const int64_t t = t0 + u * 8 + slot;
-        w[u] = (t < T) ? *reinterpret_cast<const u32x4*>(cg + t * d + (int64_t)c * 16) : u32x4{};
+        w[u] = (t < T) ? ld_stream(reinterpret_cast<const u32x4*>(cg + t * d + (int64_t)c * 16)) : u32x4{};
       }
 #pragma unroll
       for (int jj = 0; jj < kScoreNqc; ++jj) {

@@ -82,6 +82,20 @@ __device__ __forceinline__ float seg_max_f32(float v) {
   return v;
 }
 
+// --- streaming memory access ----------------------------------------------------
+// Loads and stores of data touched once: nontemporal, so streams do not
+// displace reused lines in L2 / MALL (measured on MI355X: a 16-byte-per-lane
+// read stream reaches ~7.0 TB/s nontemporal vs ~6.25 TB/s with default
+// caching).
+template <typename V>
+__device__ __forceinline__ V ld_stream(const V* p) {
+  return __builtin_nontemporal_load(p);
+}
+template <typename V>
+__device__ __forceinline__ void st_stream(V* p, const V& v) {
+  __builtin_nontemporal_store(v, p);
+}
+
 // --- element access -----------------------------------------------------------
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(_Float16 v) { return (float)v; }

@@ -306,10 +306,10 @@ __global__ __launch_bounds__(256) void scores_qjl_kernel(const TQ* __restrict__ 
         if (t < T) {
 #pragma unroll
           for (int i = 0; i < W; i += 4) {
-            const u32x4 v4 = *reinterpret_cast<const u32x4*>(bg + t * W + i);
+            const u32x4 v4 = ld_stream(reinterpret_cast<const u32x4*>(bg + t * W + i));
             wv[u][i] = v4[0]; wv[u][i + 1] = v4[1]; wv[u][i + 2] = v4[2]; wv[u][i + 3] = v4[3];
           }
-          nv[u] = (float)__builtin_bit_cast(_Float16, ng[t]);
+          nv[u] = (float)__builtin_bit_cast(_Float16, ld_stream(ng + t));
         } else {
 #pragma unroll
           for (int i = 0; i < W; ++i) wv[u][i] = 0;
