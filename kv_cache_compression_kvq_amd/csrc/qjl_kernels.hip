@@ -32,6 +32,7 @@
 namespace kvq {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // Sketch, fp16 keys on MFMA.  KS = d / 16 K-steps; MT = m / 32 projection
@@ -42,11 +43,45 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // otherwise spill.
 template <int KS> constexpr int sketch_nt() { return KS <= 8 ? 2 : 1; }
 
+// Sign words of projection tile mt (32 projections) for the NT x 32 tokens
+// of a wave: P = S_tile K^T on fp16 MFMA, then bit = [P >= 0].  Accumulator
+// r of lane (token j, half h) holds projection 32 mt + 16 h + r (the rows of
+// S are permuted in LDS); each step shifts the sign bit of one accumulator in
+// (v_alignbit), MSB first, and the bits are inverted at the end.  A zero
+// projection is +0 here (the accumulation starts from +0), so it gives bit 1.
+// Both halves of the wave return the token's full 32-bit word.
+template <int KS, int NT>
+__device__ __forceinline__ void sketch_tile_words(const f16x8* sfrag, int mt, int lane, int h,
+                                                  const f16x8 (&b)[NT][KS], uint32_t (&full)[NT]) {
+  f32x16 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const f16x8 a = sfrag[(mt * KS + ks) * 64 + lane];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[nt][ks], acc[nt], 0, 0, 0);
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    uint32_t sb = 0;
+#pragma unroll
+    for (int r = 15; r >= 0; --r) {
+      const float pr = acc[nt][r];   // copy first: bit-casting the vector element in place reads element 0
+      sb = __builtin_amdgcn_alignbit(sb, __builtin_bit_cast(uint32_t, pr), 31);
+    }
+    const uint32_t w = ~sb & 0xFFFFu;
+    const uint32_t o = xor32_u32(w);
+    full[nt] = h == 0 ? (w | (o << 16)) : (o | (w << 16));
+  }
+}
+
 constexpr int kSketchThreads = 512;
 constexpr int kSketchWaves = kSketchThreads / 64;
 
 template <int KS, int MT>
-__global__ __launch_bounds__(kSketchThreads) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(kSketchThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void sketch_mfma_kernel(const _Float16* __restrict__ k,
                                                           int64_t rows,
                                                           const _Float16* __restrict__ S,
@@ -77,14 +112,11 @@ void sketch_mfma_kernel(const _Float16* __restrict__ k,
 
   constexpr int kSketchNT = sketch_nt<KS>();
   const int64_t tiles = (rows + 32 * kSketchNT - 1) / (32 * kSketchNT);
-  for (int64_t tile = (int64_t)blockIdx.x * kSketchWaves + wave; tile < tiles;
-       tile += (int64_t)gridDim.x * kSketchWaves) {
-    // S fragments are re-read from LDS for every tile: keeping all of them
-    // in registers would leave room for one wave per SIMD
-    asm volatile("" ::: "memory");
+
+  // B fragments of one token tile: lane (token j, half h) holds channels
+  // 16 ks + 8 h .. + 8 of token 32 nt + j.
+  auto load = [&](f16x8 (&b)[kSketchNT][KS], int64_t tile) {
     const int64_t tok0 = tile * (32 * kSketchNT);
-    f16x8 b[kSketchNT][KS];
-    float ss[kSketchNT];
 #pragma unroll
     for (int nt = 0; nt < kSketchNT; ++nt) {
       const int64_t tok = tok0 + 32 * nt + col;
@@ -93,16 +125,27 @@ void sketch_mfma_kernel(const _Float16* __restrict__ k,
       for (int ks = 0; ks < KS; ++ks)
         b[nt][ks] = (tok < rows) ? *reinterpret_cast<const f16x8*>(kr + 16 * ks) : f16x8{};
     }
-    // norms: this lane holds half of its token's channels
+  };
+
+  auto process = [&](const f16x8 (&b)[kSketchNT][KS], int64_t tile) {
+    const int64_t tok0 = tile * (32 * kSketchNT);
+    // S fragments are re-read from LDS for every tile (an opaque offset
+    // stops the compiler from hoisting all of them into registers)
+    int off = 0;
+    asm volatile("" : "+v"(off));
+    const f16x8* sf = sfrag + off;
+    // norms: this lane holds half of its token's channels; packed fp16
+    // products (exact in binary32) summed in binary32
+    float ss[kSketchNT];
 #pragma unroll
     for (int nt = 0; nt < kSketchNT; ++nt) {
       float acc = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = (float)b[nt][ks][e];
-          acc = __builtin_fmaf(v, v, acc);
+        for (int e = 0; e < 4; ++e) {
+          const f16x2 v2 = {b[nt][ks][2 * e], b[nt][ks][2 * e + 1]};
+          acc = __builtin_amdgcn_fdot2(v2, v2, acc, false);
         }
       ss[nt] = acc;
     }
@@ -112,59 +155,67 @@ void sketch_mfma_kernel(const _Float16* __restrict__ k,
       const int64_t tok = tok0 + 32 * nt + col;
       if (h == 0 && tok < rows) norms[tok] = f32_to_f16_bits(__builtin_sqrtf(tot));
     }
-
-    // Half h of the wave stores words [h * MT/2, (h + 1) * MT/2) of each of
-    // its tokens; they are collected with selects so the projection-tile
-    // loop can stay rolled (an unrolled loop lets the scheduler hoist every
-    // S fragment into registers).
-    constexpr int HALF = MT > 0 ? MT / 2 : 1;
-    uint32_t wsel[kSketchNT][HALF];
-#pragma unroll
-    for (int nt = 0; nt < kSketchNT; ++nt)
-#pragma unroll
-      for (int j = 0; j < HALF; ++j) wsel[nt][j] = 0;
-#pragma unroll 1
-    for (int mt = 0; mt < mt_count; ++mt) {
-      f32x16 acc[kSketchNT];
-#pragma unroll
-      for (int nt = 0; nt < kSketchNT; ++nt) acc[nt] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const f16x8 a = sfrag[(mt * KS + ks) * 64 + lane];
-#pragma unroll
-        for (int nt = 0; nt < kSketchNT; ++nt)
-          acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[nt][ks], acc[nt], 0, 0, 0);
-      }
-      const int rel = mt - h * HALF;
-#pragma unroll
-      for (int nt = 0; nt < kSketchNT; ++nt) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int r = 15; r >= 0; --r) w = (w << 1) | (acc[nt][r] >= 0.0f ? 1u : 0u);
-        const uint32_t o = xor32_u32(w);
-        const uint32_t full = h == 0 ? (w | (o << 16)) : (o | (w << 16));
-        if constexpr (MT > 0) {
-#pragma unroll
-          for (int j = 0; j < HALF; ++j) wsel[nt][j] = (rel == j) ? full : wsel[nt][j];
-        } else {
-          const int64_t tok = tok0 + 32 * nt + col;
-          if (h == 0 && tok < rows) bits[tok * words + mt] = full;
-        }
-      }
-    }
     if constexpr (MT > 0) {
+      // unrolled so the words stay in registers; the scheduling barrier
+      // keeps each tile's S-fragment reads inside its own iteration
+      uint32_t wbuf[kSketchNT][MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t f[kSketchNT];
+        sketch_tile_words<KS, kSketchNT>(sf, mt, lane, h, b, f);
+#pragma unroll
+        for (int nt = 0; nt < kSketchNT; ++nt) wbuf[nt][mt] = f[nt];
+      }
+      // half h stores words [h * MT/2, (h + 1) * MT/2) of its token
+      constexpr int HALF = MT / 2;
 #pragma unroll
       for (int nt = 0; nt < kSketchNT; ++nt) {
         const int64_t tok = tok0 + 32 * nt + col;
         if (tok < rows) {
           uint32_t* dst = bits + tok * MT + h * HALF;
+          // lane-mask blend rather than a select, which the compiler would
+          // turn into a dynamically indexed (scratch) load of wbuf
+          const uint32_t lo_mask = h == 0 ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-          for (int v4 = 0; v4 < HALF / 4; ++v4)
-            *reinterpret_cast<u32x4*>(dst + 4 * v4) =
-                u32x4{wsel[nt][4 * v4], wsel[nt][4 * v4 + 1], wsel[nt][4 * v4 + 2], wsel[nt][4 * v4 + 3]};
+          for (int v4 = 0; v4 < HALF / 4; ++v4) {
+            u32x4 val;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              val[j] = (wbuf[nt][4 * v4 + j] & lo_mask) | (wbuf[nt][HALF + 4 * v4 + j] & ~lo_mask);
+            *reinterpret_cast<u32x4*>(dst + 4 * v4) = val;
+          }
+        }
+      }
+    } else {
+#pragma unroll 1
+      for (int mt = 0; mt < mt_count; ++mt) {
+        uint32_t f[kSketchNT];
+        sketch_tile_words<KS, kSketchNT>(sf, mt, lane, h, b, f);
+#pragma unroll
+        for (int nt = 0; nt < kSketchNT; ++nt) {
+          const int64_t tok = tok0 + 32 * nt + col;
+          if (h == 0 && tok < rows) bits[tok * words + mt] = f[nt];
         }
       }
     }
+  };
+
+  // Two token tiles in flight per wave: the keys of the next tile load while
+  // the current one is multiplied (ping-pong buffers, no register copies).
+  const int64_t stride = (int64_t)gridDim.x * kSketchWaves;
+  int64_t tile = (int64_t)blockIdx.x * kSketchWaves + wave;
+  f16x8 b0[kSketchNT][KS], b1[kSketchNT][KS];
+  if (tile < tiles) load(b0, tile);
+  while (tile < tiles) {
+    const int64_t t1 = tile + stride;
+    if (t1 < tiles) load(b1, t1);
+    process(b0, tile);
+    if (t1 >= tiles) break;
+    const int64_t t2 = t1 + stride;
+    if (t2 < tiles) load(b0, t2);
+    process(b1, t1);
+    tile = t2;
   }
 }
 
@@ -200,6 +251,152 @@ __global__ __launch_bounds__(256) void sketch_generic_kernel(const T* __restrict
   }
 }
 
+// ---------------------------------------------------------------------------
+// Sketch, fp16 keys, d = 128, m = 64 * NW (the key-cache shape): wave w owns
+// projection tiles 2w and 2w + 1 and keeps their S fragments in registers
+// for the whole kernel; the workgroup streams 64-token key tiles through
+// padded, double-buffered LDS.  Per tile:
+//   load   - every thread reads 16 contiguous bytes per chunk (a wave reads
+//            1 KiB per instruction), for the tile after the current one, so
+//            the loads are in flight while the current tile is multiplied;
+//   stage  - the staged chunks give the key norms (16 chunks of a token sit
+//            in 16 consecutive lanes: packed fp16 squares, 16-lane DPP sum)
+//            and are written to LDS rows padded to 272 bytes (conflict-free
+//            B-fragment reads);
+//   compute- 8 K-steps x (2 projection tiles x 2 token tiles) MFMAs, i.e.
+//            four independent accumulation chains, then the sign words.
+constexpr int kTileTok = 64;
+constexpr int kTileRowBytes = 128 * 2 + 16;
+constexpr int kTileBytes = kTileTok * kTileRowBytes;
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void sketch_tiles_kernel(const _Float16* __restrict__ k,
+                                                               int64_t rows,
+                                                               const _Float16* __restrict__ S,
+                                                               uint32_t* __restrict__ bits,
+                                                               uint16_t* __restrict__ norms) {
+  constexpr int KS = 8, D = 128, W = 2 * NW, NTHR = 64 * NW;
+  constexpr int CHUNKS = kTileTok * D * 2 / 16;   // 16-byte chunks per tile
+  constexpr int CPT = CHUNKS / NTHR;              // chunks per thread
+  __shared__ __align__(16) unsigned char tl[2][kTileBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const int col = lane & 31;
+
+  // this wave's two projection tiles, A-fragment order (rows permuted so a
+  // lane's accumulators hold 16 consecutive projections)
+  f16x8 a[2][KS];
+#pragma unroll
+  for (int mtl = 0; mtl < 2; ++mtl) {
+    const int srow = 32 * (2 * wave + mtl) + sketch_row_perm(col);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      a[mtl][ks] = *reinterpret_cast<const f16x8*>(S + (int64_t)srow * D + 16 * ks + 8 * h);
+  }
+
+  const int64_t ntiles = (rows + kTileTok - 1) / kTileTok;
+  int64_t tile = blockIdx.x;
+  if (tile >= ntiles) return;  // uniform per workgroup
+
+  f16x8 st[CPT];
+  auto load = [&](int64_t t) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = tid + u * NTHR;
+      const int64_t tok = t * kTileTok + (c >> 4);
+      st[u] = tok < rows ? ld_stream(reinterpret_cast<const f16x8*>(k + tok * D + (c & 15) * 8))
+                         : f16x8{};
+    }
+  };
+  auto stage = [&](int64_t t, int buf) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = tid + u * NTHR;
+      float ss = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f16x2 v2 = {st[u][2 * e], st[u][2 * e + 1]};
+        ss = __builtin_amdgcn_fdot2(v2, v2, ss, false);
+      }
+      ss = seg_sum_f32<16>(ss);
+      const int64_t tok = t * kTileTok + (c >> 4);
+      if ((c & 15) == 0 && tok < rows) norms[tok] = f32_to_f16_bits(__builtin_sqrtf(ss));
+      *reinterpret_cast<f16x8*>(tl[buf] + (c >> 4) * kTileRowBytes + (c & 15) * 16) = st[u];
+    }
+  };
+  auto compute = [&](int64_t t, int buf) {
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int mtl = 0; mtl < 2; ++mtl)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[mtl][nt] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      f16x8 b[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        b[nt] = *reinterpret_cast<const f16x8*>(tl[buf] + (32 * nt + col) * kTileRowBytes +
+                                                 (16 * ks + 8 * h) * 2);
+#pragma unroll
+      for (int mtl = 0; mtl < 2; ++mtl)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          acc[mtl][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mtl][ks], b[nt], acc[mtl][nt], 0, 0, 0);
+    }
+    uint32_t full[2][2];
+#pragma unroll
+    for (int mtl = 0; mtl < 2; ++mtl)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        uint32_t sb = 0;
+#pragma unroll
+        for (int r = 15; r >= 0; --r) {
+          const float pr = acc[mtl][nt][r];   // copy first: see sketch_tile_words
+          sb = __builtin_amdgcn_alignbit(sb, __builtin_bit_cast(uint32_t, pr), 31);
+        }
+        const uint32_t w = ~sb & 0xFFFFu;
+        const uint32_t o = xor32_u32(w);
+        full[mtl][nt] = h == 0 ? (w | (o << 16)) : (o | (w << 16));
+      }
+    // lane (token j, half h) stores word 2 * wave + h of its token
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int64_t tok = t * kTileTok + 32 * nt + col;
+      if (tok < rows) bits[tok * W + 2 * wave + h] = h == 0 ? full[0][nt] : full[1][nt];
+    }
+  };
+
+  load(tile);
+  stage(tile, 0);
+  __syncthreads();
+  int buf = 0;
+  while (true) {
+    const int64_t next = tile + gridDim.x;
+    const bool more = next < ntiles;   // uniform per workgroup
+    if (more) load(next);
+    compute(tile, buf);
+    if (!more) break;
+    stage(next, buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    tile = next;
+  }
+}
+
+template <int NW>
+static hipError_t sketch_tiles_launch(const _Float16* k, int64_t rows, const _Float16* S,
+                                      uint32_t* bits, uint16_t* norms, const DeviceInfo& dev,
+                                      hipStream_t st) {
+  const int64_t ntiles = (rows + kTileTok - 1) / kTileTok;
+  const int64_t per_cu = std::max(1, 8 / NW);
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(ntiles, per_cu * dev.cus));
+  hipLaunchKernelGGL((sketch_tiles_kernel<NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, st, k,
+                     rows, S, bits, norms);
+  return hipGetLastError();
+}
+
 template <int KS, int MT>
 static hipError_t sketch_mfma_launch(const _Float16* k, int64_t rows, const _Float16* S, int m,
                                      uint32_t* bits, uint16_t* norms, const DeviceInfo& dev,
@@ -207,8 +404,14 @@ static hipError_t sketch_mfma_launch(const _Float16* k, int64_t rows, const _Flo
   const size_t lds = (size_t)m * KS * 16 * sizeof(_Float16);
   constexpr int kSketchNT = sketch_nt<KS>();
   const int64_t tiles = (rows + 32 * kSketchNT - 1) / (32 * kSketchNT);
+  // persistent grid: exactly the workgroups that fit on the device at once
+  // (registers and LDS both limit it), each striding over the token tiles
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sketch_mfma_kernel<KS, MT>,
+                                                              kSketchThreads, lds);
+  if (e != hipSuccess) return e;
   const int64_t want = (tiles + kSketchWaves - 1) / kSketchWaves;
-  const int64_t cap = (int64_t)dev.cus * std::max<int64_t>(1, (int64_t)(160 * 1024 / std::max<size_t>(lds, 1)));
+  const int64_t cap = (int64_t)dev.cus * std::max(1, per_cu);
   const int64_t blocks = std::max<int64_t>(1, std::min(want, cap));
   hipLaunchKernelGGL((sketch_mfma_kernel<KS, MT>), dim3((unsigned)blocks), dim3(kSketchThreads), lds, st, k,
                      rows, S, m, bits, norms);
