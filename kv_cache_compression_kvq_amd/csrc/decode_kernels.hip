@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
   const int words = m / 32;
   float* y = reinterpret_cast<float*>(lds_raw);
   float* lut = y + m;
-  float* wpart = lut + (m / 8) * 256;                  // [kDecodeWaves][d + 2]
+  float* wpart = lut + byte_table_floats(m, W == 8);  // [kDecodeWaves][d + 2]
 
   const int64_t g = blockIdx.x / splits;
   const int64_t sp = blockIdx.x % splits;
@@ -85,7 +85,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
 
   for (int i = threadIdx.x; i < m; i += kDecodeThreads) y[i] = yall[g * m + i];
   __syncthreads();
-  build_byte_tables(y, m / 8, lut);
+  if constexpr (W == 8)
+    build_rot_tables(y, lut);
+  else
+    build_byte_tables(y, m / 8, lut);
   __syncthreads();
 
   constexpr int SLOTS = kWave / LPV;      // value rows per wave load
@@ -127,14 +130,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
       }
     }
     float acc;
-    if constexpr (W > 0) {
-      uint32_t wv[W];
-#pragma unroll
-      for (int i = 0; i < W; i += 4) {
-        const u32x4 v4 = ld_stream(reinterpret_cast<const u32x4*>(bblk + tc * W + i));
-        wv[i] = v4[0]; wv[i + 1] = v4[1]; wv[i + 2] = v4[2]; wv[i + 3] = v4[3];
-      }
-      acc = lut_sum(lut, wv, W);
+    if constexpr (W == 8) {
+      uint32_t wv[8];
+      load_rot_words(bblk + tc * 8, lane & 31, wv);
+      acc = rot_lut_sum(lut, wv, lane & 31, 4u * (uint32_t)(lane & 31));
     } else {
       acc = 0.0f;
       for (int i = 0; i < words; ++i) {
@@ -259,8 +258,12 @@ size_t decode_workspace_bytes(int64_t groups, int64_t T, int d, int m, const Dev
   return decode_y_bytes(groups, m) + (size_t)groups * (size_t)s.splits * (size_t)(d + 2) * sizeof(float);
 }
 
+// The specialised kernel (m = 256, d = 128) reads the rotated byte tables.
+static bool decode_rotated(int m, int d) { return m == 256 && d == 128; }
+
 size_t decode_lds_bytes(int m, int d) {
-  return ((size_t)m + (size_t)(m / 8) * 256 + kDecodeWaves * (size_t)(d + 2)) * sizeof(float);
+  return ((size_t)m + byte_table_floats(m, decode_rotated(m, d)) + kDecodeWaves * (size_t)(d + 2)) *
+         sizeof(float);
 }
 
 template <int W, int LPV>
@@ -301,7 +304,7 @@ static hipError_t decode_typed(const TQ* q, int64_t groups, const TS* S, int m,
     if (e1 != hipSuccess) return e1;
   }
   hipError_t e;
-  if (m == 256 && d == 128)
+  if (decode_rotated(m, d))
     e = decode_launch<8, 8>(y, groups, m, kbits, knorms, vcodes, vscales, T, d, lam, partials, sp, st);
   else if (d == 64)
     e = decode_launch<0, 4>(y, groups, m, kbits, knorms, vcodes, vscales, T, d, lam, partials, sp, st);

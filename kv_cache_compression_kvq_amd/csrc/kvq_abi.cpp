@@ -1,6 +1,6 @@
 // The C ABI of libkvq: argument validation (host only, before any HIP call),
 // status strings, thread-local error detail, and dispatch to the launchers.
-#include "../../include/kvq.h"
+#include "kvq.h"
 
 #include <hip/hip_runtime.h>
 

@@ -113,6 +113,106 @@ __device__ void build_byte_tables(const float* y, int ntables, float* lut) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Bank-conflict-free byte tables for m = 256 (32 tables, one per byte of a
+// token's 256 sign bits).
+//
+// A lookup of the plain layout (lut[p * 256 + v]) by 64 lanes with random
+// bytes v hits ~4 lanes per LDS bank.  Here row v (one per byte value, 64
+// floats = 256 bytes, bank aligned) holds entry e = T_{e mod 32}[v], every
+// table twice.  Lane L first rotates its 32 sign bytes by r = L mod 32, so at
+// step i (0..31) it needs table (r + i) mod 32 and reads entry r + i of the
+// row of its byte: the bank is (r + i) mod 64, different for every lane of a
+// 32-lane half whatever the bytes are.  The lane's part of the address,
+// 256 v + 4 r, is one byte permute; 4 i is the instruction's offset.
+constexpr int kRotRowFloats = 64;
+constexpr int kRotLutFloats = 256 * kRotRowFloats;
+
+// Tables for projections of size m in floats, rotated layout or plain.
+__host__ __device__ inline size_t byte_table_floats(int m, bool rotated) {
+  return rotated ? (size_t)kRotLutFloats : (size_t)(m / 8) * 256;
+}
+
+// Rotated layout of the 32 tables of y[0..255]; entries hold the same
+// binary32 values as build_byte_tables.
+__device__ void build_rot_tables(const float* y, float* lut) {
+  for (int task = threadIdx.x; task < 32 * 16; task += blockDim.x) {
+    const int p = task & 31;                   // table
+    const int a = task >> 5;                   // high nibble of v
+    const float* yp = y + 8 * p;
+    float lo[16];
+    lo[0] = -(((yp[0] + yp[1]) + yp[2]) + yp[3]);
+#pragma unroll
+    for (int b = 1; b < 16; ++b) {
+      const int low = b & (-b);
+      const int j = __builtin_ctz(low);
+      lo[b] = lo[b ^ low] + 2.0f * yp[j];
+    }
+    float hi = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hi += ((a >> j) & 1) ? yp[4 + j] : -yp[4 + j];
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      const float val = hi + lo[b];
+      float* row = lut + (16 * a + b) * kRotRowFloats;
+      row[p] = val;
+      row[p + 32] = val;
+    }
+  }
+}
+
+// The 8 sign words of one token, as two 16-byte loads ordered by bit 4 of r
+// (the first load starts at byte 16 * ((r >> 4) & 1)).
+__device__ __forceinline__ void load_rot_words(const uint32_t* p, int r, uint32_t w[8]) {
+  const int h = (r >> 4) & 1;
+  const u32x4 a = ld_stream(reinterpret_cast<const u32x4*>(p + 4 * h));
+  const u32x4 b = ld_stream(reinterpret_cast<const u32x4*>(p + 4 * (h ^ 1)));
+  w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
+  w[4] = b[0]; w[5] = b[1]; w[6] = b[2]; w[7] = b[3];
+}
+
+// Sum over the 32 bytes of one token of the rotated tables' entries, for
+// words loaded by load_rot_words with the same r (= lane % 32); rq = 4 r.
+__device__ __forceinline__ float rot_lut_sum(const float* lut, const uint32_t wl[8], int r,
+                                             uint32_t rq) {
+  // rotate the remaining 4 (r >> 2 & 3) words, then r & 3 bytes; the word
+  // moves are bit blends with all-ones / all-zero lane masks (a select would
+  // become an indexed array in scratch)
+  uint32_t x[8], w[8];
+  const uint32_t m2 = 0u - ((uint32_t)r >> 3 & 1u), m1 = 0u - ((uint32_t)r >> 2 & 1u);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = wl[j] ^ ((wl[(j + 2) & 7] ^ wl[j]) & m2);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w[j] = x[j] ^ ((x[(j + 1) & 7] ^ x[j]) & m1);
+  const uint32_t sh = 8u * (uint32_t)(r & 3);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = __builtin_amdgcn_alignbit(w[(j + 1) & 7], w[j], sh);
+  const char* base = reinterpret_cast<const char*>(lut);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    // (byte i & 3 of word i >> 2) * 256 + 4 r
+    const uint32_t off =
+        __builtin_amdgcn_perm(rq, x[i >> 2], 0x0C0C0004u | ((uint32_t)(i & 3) << 8));
+    v[i] = *reinterpret_cast<const float*>(base + off + 4 * i);
+  }
+  // Keep the 32 reads in flight together: left to itself the scheduler
+  // waits for each read before issuing the next.
+#pragma unroll
+  for (int g = 0; g < 32; g += 8)
+    asm volatile("" ::"v"(v[g]), "v"(v[g + 1]), "v"(v[g + 2]), "v"(v[g + 3]), "v"(v[g + 4]),
+                 "v"(v[g + 5]), "v"(v[g + 6]), "v"(v[g + 7]));
+  float part[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float a = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a += v[8 * c + k];
+    part[c] = a;
+  }
+  return (part[0] + part[1]) + (part[2] + part[3]);
+}
+
 // Sum of the table entries selected by the bytes of `nw` sign words.
 __device__ __forceinline__ float lut_sum(const float* lut, const uint32_t* w, int nw) {
   float acc = 0.0f;

@@ -21,7 +21,8 @@
 // Score: per (group, query) workgroup y = S q goes to LDS and is expanded
 // into one 256-entry table per byte of the sign words:
 //   T_p[v] = sum_{j<8} (bit j of v ? +1 : -1) * y_{8p+j},
-// so a token costs one table lookup per 8 bits.
+// so a token costs one table lookup per 8 bits (for m = 256 in a layout
+// whose lookups never share an LDS bank within a half-wave).
 #include "kvq_device.h"
 #include "kvq_launch.h"
 #include "kvq_qjl_device.h"
@@ -251,152 +252,6 @@ __global__ __launch_bounds__(256) void sketch_generic_kernel(const T* __restrict
   }
 }
 
-// ---------------------------------------------------------------------------
-// Sketch, fp16 keys, d = 128, m = 64 * NW (the key-cache shape): wave w owns
-// projection tiles 2w and 2w + 1 and keeps their S fragments in registers
-// for the whole kernel; the workgroup streams 64-token key tiles through
-// padded, double-buffered LDS.  Per tile:
-//   load   - every thread reads 16 contiguous bytes per chunk (a wave reads
-//            1 KiB per instruction), for the tile after the current one, so
-//            the loads are in flight while the current tile is multiplied;
-//   stage  - the staged chunks give the key norms (16 chunks of a token sit
-//            in 16 consecutive lanes: packed fp16 squares, 16-lane DPP sum)
-//            and are written to LDS rows padded to 272 bytes (conflict-free
-//            B-fragment reads);
-//   compute- 8 K-steps x (2 projection tiles x 2 token tiles) MFMAs, i.e.
-//            four independent accumulation chains, then the sign words.
-constexpr int kTileTok = 64;
-constexpr int kTileRowBytes = 128 * 2 + 16;
-constexpr int kTileBytes = kTileTok * kTileRowBytes;
-
-template <int NW>
-__global__ __launch_bounds__(64 * NW) void sketch_tiles_kernel(const _Float16* __restrict__ k,
-                                                               int64_t rows,
-                                                               const _Float16* __restrict__ S,
-                                                               uint32_t* __restrict__ bits,
-                                                               uint16_t* __restrict__ norms) {
-  constexpr int KS = 8, D = 128, W = 2 * NW, NTHR = 64 * NW;
-  constexpr int CHUNKS = kTileTok * D * 2 / 16;   // 16-byte chunks per tile
-  constexpr int CPT = CHUNKS / NTHR;              // chunks per thread
-  __shared__ __align__(16) unsigned char tl[2][kTileBytes];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int h = lane >> 5;
-  const int col = lane & 31;
-
-  // this wave's two projection tiles, A-fragment order (rows permuted so a
-  // lane's accumulators hold 16 consecutive projections)
-  f16x8 a[2][KS];
-#pragma unroll
-  for (int mtl = 0; mtl < 2; ++mtl) {
-    const int srow = 32 * (2 * wave + mtl) + sketch_row_perm(col);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      a[mtl][ks] = *reinterpret_cast<const f16x8*>(S + (int64_t)srow * D + 16 * ks + 8 * h);
-  }
-
-  const int64_t ntiles = (rows + kTileTok - 1) / kTileTok;
-  int64_t tile = blockIdx.x;
-  if (tile >= ntiles) return;  // uniform per workgroup
-
-  f16x8 st[CPT];
-  auto load = [&](int64_t t) {
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = tid + u * NTHR;
-      const int64_t tok = t * kTileTok + (c >> 4);
-      st[u] = tok < rows ? ld_stream(reinterpret_cast<const f16x8*>(k + tok * D + (c & 15) * 8))
-                         : f16x8{};
-    }
-  };
-  auto stage = [&](int64_t t, int buf) {
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = tid + u * NTHR;
-      float ss = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const f16x2 v2 = {st[u][2 * e], st[u][2 * e + 1]};
-        ss = __builtin_amdgcn_fdot2(v2, v2, ss, false);
-      }
-      ss = seg_sum_f32<16>(ss);
-      const int64_t tok = t * kTileTok + (c >> 4);
-      if ((c & 15) == 0 && tok < rows) norms[tok] = f32_to_f16_bits(__builtin_sqrtf(ss));
-      *reinterpret_cast<f16x8*>(tl[buf] + (c >> 4) * kTileRowBytes + (c & 15) * 16) = st[u];
-    }
-  };
-  auto compute = [&](int64_t t, int buf) {
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int mtl = 0; mtl < 2; ++mtl)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[mtl][nt] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      f16x8 b[2];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        b[nt] = *reinterpret_cast<const f16x8*>(tl[buf] + (32 * nt + col) * kTileRowBytes +
-                                                 (16 * ks + 8 * h) * 2);
-#pragma unroll
-      for (int mtl = 0; mtl < 2; ++mtl)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          acc[mtl][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mtl][ks], b[nt], acc[mtl][nt], 0, 0, 0);
-    }
-    uint32_t full[2][2];
-#pragma unroll
-    for (int mtl = 0; mtl < 2; ++mtl)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        uint32_t sb = 0;
-#pragma unroll
-        for (int r = 15; r >= 0; --r) {
-          const float pr = acc[mtl][nt][r];   // copy first: see sketch_tile_words
-          sb = __builtin_amdgcn_alignbit(sb, __builtin_bit_cast(uint32_t, pr), 31);
-        }
-        const uint32_t w = ~sb & 0xFFFFu;
-        const uint32_t o = xor32_u32(w);
-        full[mtl][nt] = h == 0 ? (w | (o << 16)) : (o | (w << 16));
-      }
-    // lane (token j, half h) stores word 2 * wave + h of its token
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int64_t tok = t * kTileTok + 32 * nt + col;
-      if (tok < rows) bits[tok * W + 2 * wave + h] = h == 0 ? full[0][nt] : full[1][nt];
-    }
-  };
-
-  load(tile);
-  stage(tile, 0);
-  __syncthreads();
-  int buf = 0;
-  while (true) {
-    const int64_t next = tile + gridDim.x;
-    const bool more = next < ntiles;   // uniform per workgroup
-    if (more) load(next);
-    compute(tile, buf);
-    if (!more) break;
-    stage(next, buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    tile = next;
-  }
-}
-
-template <int NW>
-static hipError_t sketch_tiles_launch(const _Float16* k, int64_t rows, const _Float16* S,
-                                      uint32_t* bits, uint16_t* norms, const DeviceInfo& dev,
-                                      hipStream_t st) {
-  const int64_t ntiles = (rows + kTileTok - 1) / kTileTok;
-  const int64_t per_cu = std::max(1, 8 / NW);
-  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(ntiles, per_cu * dev.cus));
-  hipLaunchKernelGGL((sketch_tiles_kernel<NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, st, k,
-                     rows, S, bits, norms);
-  return hipGetLastError();
-}
-
 template <int KS, int MT>
 static hipError_t sketch_mfma_launch(const _Float16* k, int64_t rows, const _Float16* S, int m,
                                      uint32_t* bits, uint16_t* norms, const DeviceInfo& dev,
@@ -468,10 +323,11 @@ constexpr int kQjlBatch = 8;
 constexpr int kQjlTokPerThread = 16;
 constexpr int kQjlTok = 256 * kQjlTokPerThread;
 
-// LDS: y [m] | byte tables [m / 8][256] (also the query staging area of the
-// projection, which ends before the tables are built).
+// LDS: y [m] | byte tables (rotated layout for m = 256, else [m / 8][256]);
+// the table area is also the query staging area of the projection, which
+// ends before the tables are built.
 __host__ __device__ inline size_t qjl_table_lds_floats(int m) {
-  const size_t tables = (size_t)(m / 8) * 256;
+  const size_t tables = byte_table_floats(m, m == 256);
   return (size_t)m + (tables > (size_t)kProjQChunk ? tables : (size_t)kProjQChunk);
 }
 
@@ -492,37 +348,38 @@ __global__ __launch_bounds__(256) void scores_qjl_kernel(const TQ* __restrict__ 
   const int64_t g = gj / nq;
   project_query_block(S, q + gj * d, m, d, lut, y);
   __syncthreads();
-  build_byte_tables(y, m / 8, lut);
+  if constexpr (W == 8)
+    build_rot_tables(y, lut);
+  else
+    build_byte_tables(y, m / 8, lut);
   __syncthreads();
   const float c = kSqrtHalfPi / (float)m;
   const uint32_t* bg = bits + g * T * words;
   const uint16_t* ng = norms + g * T;
   float* sg = scores + gj * T;
   const int64_t t0 = tile * kQjlTok + threadIdx.x;
-  if constexpr (W > 0) {
+  if constexpr (W == 8) {
+    const int r = threadIdx.x & 31;
+    const uint32_t rq = 4u * (uint32_t)r;
     for (int b0 = 0; b0 < kQjlTokPerThread; b0 += kQjlBatch) {
-      uint32_t wv[kQjlBatch][W];
+      uint32_t wv[kQjlBatch][8];
       float nv[kQjlBatch];
 #pragma unroll
       for (int u = 0; u < kQjlBatch; ++u) {
         const int64_t t = t0 + (int64_t)(b0 + u) * 256;
         if (t < T) {
-#pragma unroll
-          for (int i = 0; i < W; i += 4) {
-            const u32x4 v4 = ld_stream(reinterpret_cast<const u32x4*>(bg + t * W + i));
-            wv[u][i] = v4[0]; wv[u][i + 1] = v4[1]; wv[u][i + 2] = v4[2]; wv[u][i + 3] = v4[3];
-          }
+          load_rot_words(bg + t * 8, r, wv[u]);
           nv[u] = (float)__builtin_bit_cast(_Float16, ld_stream(ng + t));
         } else {
 #pragma unroll
-          for (int i = 0; i < W; ++i) wv[u][i] = 0;
+          for (int i = 0; i < 8; ++i) wv[u][i] = 0;
           nv[u] = 0.0f;
         }
       }
 #pragma unroll
       for (int u = 0; u < kQjlBatch; ++u) {
         const int64_t t = t0 + (int64_t)(b0 + u) * 256;
-        const float acc = lut_sum(lut, wv[u], W);
+        const float acc = rot_lut_sum(lut, wv[u], r, rq);
         if (t < T) sg[t] = c * nv[u] * acc;
       }
     }
