@@ -202,6 +202,33 @@ kvq_status kvq_decode_qjl_int8(const void* q, kvq_dtype q_dt, int64_t groups, co
                                const float* vscales, int64_t T, int32_t d, float sm_scale,
                                void* ws, size_t ws_bytes, float* out, kvq_stream_t stream);
 
+/*
+ * kvq_cache_append - compress-on-write for one decode step: the newest key
+ * and value of every group are compressed and written into token position
+ * `pos` of the group's compressed cache (the cache layout of
+ * kvq_decode_qjl_int8), in one launch.
+ *
+ * Keys follow the QJL sketch (arXiv 2406.03482, abstract) as kvq_qjl_sketch
+ * does: bit i of the key's row is [ (S k)_i >= 0 ], LSB-first in 32-bit
+ * words, and its norm is the binary16 rounding of ||k||.  Values follow the
+ * symmetric INT8 formula (Q-TensorFormer model card, section 6) exactly as
+ * kvq_quantize_int8 does: codes and scale are bit-identical to it.  Sign
+ * bits equal the exact signs except where |(S k)_i| <= 1e-4 ||S_i|| ||k||;
+ * norms are within one binary16 ulp.  Only row `pos` of each group is
+ * written.
+ *
+ * k, v    [groups, d] (kv_dt);  S [m, d] (kv_dt)
+ * kbits   [groups, T, m / 32] uint32;  knorms [groups, T] binary16 patterns
+ * vcodes  [groups, T, d] int8;  vscales [groups, T] binary32
+ * 0 <= pos < T; 16 <= d <= 1024, d % 16 == 0; m as for kvq_qjl_sketch.
+ * groups == 0 is a no-op.
+ * Errors: NULL, ALIGN, SHAPE, DTYPE.
+ */
+kvq_status kvq_cache_append(const void* k, const void* v, kvq_dtype kv_dt, int64_t groups,
+                            int32_t d, const void* S, int32_t m, int64_t T, int64_t pos,
+                            uint32_t* kbits, uint16_t* knorms, int8_t* vcodes, float* vscales,
+                            kvq_stream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* kvq_status_string(kvq_status status);
 

@@ -8,6 +8,7 @@ streams; every step of the computation runs in libkvq.
 """
 from ._lib import KvqError, LIB_PATH, lib  # noqa: F401
 from .ops import (  # noqa: F401
+    cache_append,
     decode_qjl_int8,
     decode_workspace_bytes,
     dequantize_int8,

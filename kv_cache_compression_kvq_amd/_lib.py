@@ -30,6 +30,9 @@ PROTOTYPES = {
     "kvq_decode_qjl_int8": (c_int32, [c_void_p, c_int32, c_int64, c_void_p, c_int32, c_int32,
                                       c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32,
                                       c_float, c_void_p, c_size_t, c_void_p, c_void_p]),
+    "kvq_cache_append": (c_int32, [c_void_p, c_void_p, c_int32, c_int64, c_int32, c_void_p, c_int32,
+                                   c_int64, c_int64, c_void_p, c_void_p, c_void_p, c_void_p,
+                                   c_void_p]),
     "kvq_status_string": (c_char_p, [c_int32]),
     "kvq_last_error": (c_char_p, []),
 }

@@ -15,6 +15,7 @@
 // lane); rows are reduced across lanes with DPP/swizzle, never through LDS,
 // except for rows longer than one wave can hold (one row per workgroup).
 #include "kvq_device.h"
+#include "kvq_int8_device.h"
 #include "kvq_launch.h"
 
 #include <algorithm>
@@ -32,18 +33,6 @@ template <> struct Chunk<_Float16> {
   using V = f16x8;
   using Codes = u32x2;                 // 8 codes
 };
-
-// Row divisor: the scale, or 1 for a zero scale (every value of such a row
-// has |x| < 127 * 2^-150 and maps to code 0).
-__device__ __forceinline__ float row_divisor(float s) { return (s == 0.0f) ? 1.0f : s; }
-
-// One code: rint(RN32(x / s)) clamped to [-128, 127].  x / s is the
-// compiler's IEEE binary32 division; rint rounds half to even.
-__device__ __forceinline__ uint32_t code_of(float x, float sdiv) {
-  const float t = x / sdiv;
-  const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(t), -128.0f, 127.0f);
-  return (uint32_t)(int)r & 0xFFu;
-}
 
 template <typename T>
 __device__ __forceinline__ typename Chunk<T>::Codes encode_chunk(const typename Chunk<T>::V& v,
@@ -70,11 +59,6 @@ __device__ __forceinline__ uint32_t chunk_absmax(const typename Chunk<T>::V& v) 
 #pragma unroll
   for (int e = 0; e < Chunk<T>::N; ++e) m = max(m, abs_bits((float)v[e]));
   return m;
-}
-
-// Scale from the row's max |x| (bit pattern of a non-negative float).
-__device__ __forceinline__ float row_scale(uint32_t amax_bits) {
-  return __builtin_bit_cast(float, amax_bits) / 127.0f;
 }
 
 // ---------------------------------------------------------------------------

@@ -261,4 +261,31 @@ kvq_status kvq_decode_qjl_int8(const void* q, kvq_dtype q_dt, int64_t groups, co
                                                   reinterpret_cast<hipStream_t>(stream)));
 }
 
+kvq_status kvq_cache_append(const void* k, const void* v, kvq_dtype kv_dt, int64_t groups,
+                            int32_t d, const void* S, int32_t m, int64_t T, int64_t pos,
+                            uint32_t* kbits, uint16_t* knorms, int8_t* vcodes, float* vscales,
+                            kvq_stream_t stream) {
+  const char* fn = "kvq_cache_append";
+  kvq_status st;
+  if ((st = check_count(fn, "groups", groups)) || (st = check_count(fn, "T", T)) ||
+      (st = check_d(fn, d)) || (st = check_m(fn, m)) || (st = check_dtype(fn, "kv_dt", kv_dt)))
+    return st;
+  if (d > kvq::kMaxDecodeD)
+    return fail(KVQ_ERR_SHAPE, "%s: d = %d exceeds %d", fn, (int)d, kvq::kMaxDecodeD);
+  if (groups == 0) return ok();
+  if (pos < 0 || pos >= T)
+    return fail(KVQ_ERR_SHAPE, "%s: pos = %lld is outside [0, T = %lld)", fn, (long long)pos,
+                (long long)T);
+  KVQ_CHECK_PTR(k);
+  KVQ_CHECK_PTR(v);
+  KVQ_CHECK_PTR(S);
+  KVQ_CHECK_PTR(kbits);
+  KVQ_CHECK_PTR(knorms);
+  KVQ_CHECK_PTR(vcodes);
+  KVQ_CHECK_PTR(vscales);
+  return launched(fn, kvq::launch_cache_append(k, v, kv_dt == KVQ_F16, groups, d, S, m, T, pos,
+                                               kbits, knorms, vcodes, vscales,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -45,6 +45,10 @@ hipError_t launch_decode_qjl_int8(const void* q, int q_f16, int64_t groups, cons
                                   float sm_scale, void* ws, float* out, const DeviceInfo& dev,
                                   hipStream_t s);
 
+hipError_t launch_cache_append(const void* k, const void* v, int kv_f16, int64_t groups, int d,
+                               const void* S, int m, int64_t T, int64_t pos, uint32_t* kbits,
+                               uint16_t* knorms, int8_t* vcodes, float* vscales, hipStream_t s);
+
 // Raise a kernel's dynamic-LDS limit when it needs more than the default
 // 64 KiB (gfx950 workgroups may use up to 160 KiB).
 template <typename Kernel>

@@ -41,6 +41,43 @@ __device__ __forceinline__ void load16_f32<_Float16>(const _Float16* p, float ou
 constexpr int kProjQChunk = 2048;   // query values staged in LDS per pass
 constexpr int kProjMaxRowsPerThread = 4;
 
+// a = fma chain of sr[j] * x[j] over j < len (len % 16 == 0) in j order, with
+// the S loads of 64 channels issued together (one memory latency per 64
+// channels instead of one per 16).  x is in LDS.
+template <typename TS>
+__device__ __forceinline__ float row_dot(const TS* __restrict__ sr, const float* x, int len,
+                                         float a) {
+  int j = 0;
+  for (; j + 64 <= len; j += 64) {
+    float sv[64];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) load16_f32<TS>(sr + j + 16 * c, sv + 16 * c);
+    const f32x4* xv = reinterpret_cast<const f32x4*>(x + j);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const f32x4 xx = xv[v];
+      a = __builtin_fmaf(sv[4 * v + 0], xx[0], a);
+      a = __builtin_fmaf(sv[4 * v + 1], xx[1], a);
+      a = __builtin_fmaf(sv[4 * v + 2], xx[2], a);
+      a = __builtin_fmaf(sv[4 * v + 3], xx[3], a);
+    }
+  }
+  for (; j < len; j += 16) {
+    float sv[16];
+    load16_f32<TS>(sr + j, sv);
+    const f32x4* xv = reinterpret_cast<const f32x4*>(x + j);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const f32x4 xx = xv[v];
+      a = __builtin_fmaf(sv[4 * v + 0], xx[0], a);
+      a = __builtin_fmaf(sv[4 * v + 1], xx[1], a);
+      a = __builtin_fmaf(sv[4 * v + 2], xx[2], a);
+      a = __builtin_fmaf(sv[4 * v + 3], xx[3], a);
+    }
+  }
+  return a;
+}
+
 // y[i] = sum_j S[i][j] q[j] for i < m (m <= 1024), binary32 fused
 // multiply-adds in j order, computed by the whole 256-thread workgroup:
 // thread t owns rows t, t + 256, ...; q is staged through LDS (qs, at least
@@ -59,24 +96,7 @@ __device__ void project_query_block(const TS* __restrict__ S, const TQ* __restri
 #pragma unroll
     for (int r = 0; r < kProjMaxRowsPerThread; ++r) {
       const int i = threadIdx.x + r * (int)blockDim.x;
-      if (i < m) {
-        const TS* sr = S + (int64_t)i * d + j0;
-        float a = acc[r];
-        for (int j = 0; j < len; j += 16) {
-          float sv[16];
-          load16_f32<TS>(sr + j, sv);
-          const f32x4* qv = reinterpret_cast<const f32x4*>(qs + j);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const f32x4 qq = qv[v];
-            a = __builtin_fmaf(sv[4 * v + 0], qq[0], a);
-            a = __builtin_fmaf(sv[4 * v + 1], qq[1], a);
-            a = __builtin_fmaf(sv[4 * v + 2], qq[2], a);
-            a = __builtin_fmaf(sv[4 * v + 3], qq[3], a);
-          }
-        }
-        acc[r] = a;
-      }
+      if (i < m) acc[r] = row_dot<TS>(S + (int64_t)i * d + j0, qs, len, acc[r]);
     }
   }
 #pragma unroll

@@ -147,3 +147,28 @@ def decode_qjl_int8(q: torch.Tensor, S: torch.Tensor, kbits: torch.Tensor, knorm
         _p(vcodes), _p(vscales), T, d, float(sm_scale), _p(workspace), workspace.numel(), _p(out),
         _stream(q)))
     return out
+
+
+def cache_append(k: torch.Tensor, v: torch.Tensor, S: torch.Tensor, kbits: torch.Tensor,
+                 knorms: torch.Tensor, vcodes: torch.Tensor, vscales: torch.Tensor,
+                 pos: int) -> None:
+    """Compress the newest key k [G, d] and value v [G, d] of every group into
+    token position ``pos`` of the cache (kbits [G, T, m // 32], knorms [G, T],
+    vcodes [G, T, d], vscales [G, T]), in place."""
+    for t, n in ((k, "k"), (v, "v"), (S, "S"), (kbits, "kbits"), (knorms, "knorms"),
+                 (vcodes, "vcodes"), (vscales, "vscales")):
+        _dev(t, n)
+    if v.dtype != k.dtype or S.dtype != k.dtype:
+        raise TypeError("k, v and S must have one dtype")
+    G, d = k.shape
+    m = S.shape[0]
+    T = kbits.shape[1] if kbits.dim() == 3 else 0
+    if (v.shape != (G, d) or S.shape[1] != d or kbits.shape != (G, T, m // 32)
+            or knorms.shape != (G, T) or vcodes.shape != (G, T, d) or vscales.shape != (G, T)):
+        raise ValueError("shape mismatch between k, v, S and the cache tensors")
+    if (kbits.dtype != torch.int32 or knorms.dtype != torch.float16 or vcodes.dtype != torch.int8
+            or vscales.dtype != torch.float32):
+        raise TypeError("cache dtypes: kbits int32, knorms float16, vcodes int8, vscales float32")
+    L.check(L.lib().kvq_cache_append(_p(k), _p(v), _dtype_code(k, "k"), G, d, _p(S), m, T,
+                                     int(pos), _p(kbits), _p(knorms), _p(vcodes), _p(vscales),
+                                     _stream(k)))

@@ -128,6 +128,33 @@ def test_decode_validation():
                 ws=None, out=None) == L.KVQ_OK
 
 
+def test_cache_append_validation():
+    f = L.lib().kvq_cache_append
+    args = [A, A, L.KVQ_F16, 4, 128, A, 256, 16, 15, A, A, A, A, None]
+    names = ["k", "v", "dt", "groups", "d", "S", "m", "T", "pos", "kbits", "knorms", "vcodes",
+             "vscales", "stream"]
+
+    def call(**kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    _err(call(pos=16), L.KVQ_ERR_SHAPE)
+    _err(call(pos=-1), L.KVQ_ERR_SHAPE)
+    _err(call(T=0), L.KVQ_ERR_SHAPE)
+    _err(call(d=2048), L.KVQ_ERR_SHAPE)
+    _err(call(d=120), L.KVQ_ERR_SHAPE)
+    _err(call(m=48), L.KVQ_ERR_SHAPE)
+    _err(call(groups=-1), L.KVQ_ERR_SHAPE)
+    _err(call(dt=2), L.KVQ_ERR_DTYPE)
+    _err(call(v=None), L.KVQ_ERR_NULL)
+    _err(call(kbits=None), L.KVQ_ERR_NULL)
+    _err(call(vscales=MIS), L.KVQ_ERR_ALIGN)
+    assert call(groups=0, k=None, v=None, S=None, kbits=None, knorms=None, vcodes=None,
+                vscales=None) == L.KVQ_OK
+
+
 def test_workspace_query_rejects_bad_shapes_without_a_device():
     f = L.lib().kvq_decode_workspace_bytes
     assert f(0, 16, 128, 256) == 0
