@@ -80,21 +80,26 @@ def measured_traffic(bytes_per_launch_alg: float):
     return t.get("hbm_bytes_per_launch")
 
 
-def event_times(fn, reps, warmup, stream=None):
-    """Durations (ms) of `reps` calls of fn, each bracketed by HIP events
-    recorded on the stream fn launches on."""
+def block_times(fn, calls_per_block, blocks, warmup, stream=None):
+    """Mean duration (ms) of one call of fn, for each of `blocks` blocks of
+    `calls_per_block` back-to-back calls bracketed by one pair of HIP events
+    on the stream fn launches on.  (A timing event recorded between two
+    launches idles the GPU for ~10-15 us on this stack, so events never sit
+    between the calls being timed.)"""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    for a, b in evs:
+    out = []
+    for _ in range(blocks):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        fn()
+        for _ in range(calls_per_block):
+            fn()
         b.record(stream)
-    torch.cuda.synchronize()
-    return [a.elapsed_time(b) for a, b in evs]
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) / calls_per_block)
+    return out
 
 
 def med(xs):
@@ -108,7 +113,9 @@ COLD_BYTES = 1 << 30     # rotate inputs over > 1 GiB: 4x the 256 MB last-level 
 def components(K, si, torch, np):
     """GB/s of the INT8 and QJL kernels on their own workloads, cold: each
     timed call reads a different copy of its inputs, and the copies together
-    exceed 1 GiB, so no call finds its inputs in the MALL or L2."""
+    exceed 1 GiB, so no call finds its inputs in the MALL or L2.  Calls run
+    back to back in blocks timed by one pair of HIP events; the median block's
+    mean per call is reported."""
     res = {}
     dev = "cuda"
 
@@ -116,7 +123,7 @@ def components(K, si, torch, np):
         """calls: list of zero-argument launches, one per input copy."""
         it = iter(range(10 ** 9))
         fn = lambda: calls[next(it) % len(calls)]()
-        ms = med(event_times(fn, reps, 3))
+        ms = med(block_times(fn, max(reps, len(calls)), 5, 3))
         r = {"ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
              "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 3), "bytes": int(nbytes),
              "copies": len(calls)}

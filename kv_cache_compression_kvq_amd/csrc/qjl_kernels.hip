@@ -43,6 +43,8 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // Token tiles of 32 per wave iteration: two, or one when d = 256 would
 // otherwise spill.
 template <int KS> constexpr int sketch_nt() { return KS <= 8 ? 2 : 1; }
+// Key tiles in flight per wave (a ring of register buffers).
+template <int NT> constexpr int sketch_ring() { return NT == 1 ? 4 : 2; }
 
 // Sign words of projection tile mt (32 projections) for the NT x 32 tokens
 // of a wave: P = S_tile K^T on fp16 MFMA, then bit = [P >= 0].  Accumulator
@@ -50,9 +52,19 @@ template <int KS> constexpr int sketch_nt() { return KS <= 8 ? 2 : 1; }
 // S are permuted in LDS); each step shifts the sign bit of one accumulator in
 // (v_alignbit), MSB first, and the bits are inverted at the end.  A zero
 // projection is +0 here (the accumulation starts from +0), so it gives bit 1.
-// Both halves of the wave return the token's full 32-bit word.
+// Both halves of the wave return the token's full 32-bit word (the halves'
+// 16-bit parts are exchanged with v_permlane32_swap).
+// Both halves' values of a 64-lane register: lo = the value of lane l % 32,
+// hi = that of lane 32 + l % 32, in every lane (v_permlane32_swap of the
+// register with itself; no LDS traffic).
+__device__ __forceinline__ void halves_u32(uint32_t v, uint32_t& lo, uint32_t& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  lo = r[0];
+  hi = r[1];
+}
+
 template <int KS, int NT>
-__device__ __forceinline__ void sketch_tile_words(const f16x8* sfrag, int mt, int lane, int h,
+__device__ __forceinline__ void sketch_tile_words(const f16x8* sfrag, int mt, int lane,
                                                   const f16x8 (&b)[NT][KS], uint32_t (&full)[NT]) {
   f32x16 acc[NT];
 #pragma unroll
@@ -72,9 +84,9 @@ __device__ __forceinline__ void sketch_tile_words(const f16x8* sfrag, int mt, in
       const float pr = acc[nt][r];   // copy first: bit-casting the vector element in place reads element 0
       sb = __builtin_amdgcn_alignbit(sb, __builtin_bit_cast(uint32_t, pr), 31);
     }
-    const uint32_t w = ~sb & 0xFFFFu;
-    const uint32_t o = xor32_u32(w);
-    full[nt] = h == 0 ? (w | (o << 16)) : (o | (w << 16));
+    uint32_t lo, hi;
+    halves_u32(~sb & 0xFFFFu, lo, hi);
+    full[nt] = lo | (hi << 16);
   }
 }
 
@@ -115,16 +127,18 @@ void sketch_mfma_kernel(const _Float16* __restrict__ k,
   const int64_t tiles = (rows + 32 * kSketchNT - 1) / (32 * kSketchNT);
 
   // B fragments of one token tile: lane (token j, half h) holds channels
-  // 16 ks + 8 h .. + 8 of token 32 nt + j.
+  // 16 ks + 8 h .. + 8 of token 32 nt + j.  The loads are unconditional
+  // (tokens past the end re-read the last row and are not stored): a load
+  // under a branch would make the compiler's wait counts conservative and
+  // serialise the prefetch with the multiplies.
   auto load = [&](f16x8 (&b)[kSketchNT][KS], int64_t tile) {
     const int64_t tok0 = tile * (32 * kSketchNT);
 #pragma unroll
     for (int nt = 0; nt < kSketchNT; ++nt) {
-      const int64_t tok = tok0 + 32 * nt + col;
+      const int64_t tok = std::min<int64_t>(tok0 + 32 * nt + col, rows - 1);
       const _Float16* kr = k + tok * D + 8 * h;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        b[nt][ks] = (tok < rows) ? *reinterpret_cast<const f16x8*>(kr + 16 * ks) : f16x8{};
+      for (int ks = 0; ks < KS; ++ks) b[nt][ks] = *reinterpret_cast<const f16x8*>(kr + 16 * ks);
     }
   };
 
@@ -152,7 +166,9 @@ void sketch_mfma_kernel(const _Float16* __restrict__ k,
     }
 #pragma unroll
     for (int nt = 0; nt < kSketchNT; ++nt) {
-      const float tot = ss[nt] + xor32_f32(ss[nt]);
+      uint32_t slo, shi;
+      halves_u32(__builtin_bit_cast(uint32_t, ss[nt]), slo, shi);
+      const float tot = __builtin_bit_cast(float, slo) + __builtin_bit_cast(float, shi);
       const int64_t tok = tok0 + 32 * nt + col;
       if (h == 0 && tok < rows) norms[tok] = f32_to_f16_bits(__builtin_sqrtf(tot));
     }
@@ -164,7 +180,7 @@ void sketch_mfma_kernel(const _Float16* __restrict__ k,
       for (int mt = 0; mt < MT; ++mt) {
         __builtin_amdgcn_sched_barrier(0);
         uint32_t f[kSketchNT];
-        sketch_tile_words<KS, kSketchNT>(sf, mt, lane, h, b, f);
+        sketch_tile_words<KS, kSketchNT>(sf, mt, lane, b, f);
 #pragma unroll
         for (int nt = 0; nt < kSketchNT; ++nt) wbuf[nt][mt] = f[nt];
       }
@@ -192,7 +208,7 @@ void sketch_mfma_kernel(const _Float16* __restrict__ k,
 #pragma unroll 1
       for (int mt = 0; mt < mt_count; ++mt) {
         uint32_t f[kSketchNT];
-        sketch_tile_words<KS, kSketchNT>(sf, mt, lane, h, b, f);
+        sketch_tile_words<KS, kSketchNT>(sf, mt, lane, b, f);
 #pragma unroll
         for (int nt = 0; nt < kSketchNT; ++nt) {
           const int64_t tok = tok0 + 32 * nt + col;
@@ -202,21 +218,24 @@ void sketch_mfma_kernel(const _Float16* __restrict__ k,
     }
   };
 
-  // Two token tiles in flight per wave: the keys of the next tile load while
-  // the current one is multiplied (ping-pong buffers, no register copies).
+  // RING token tiles in flight per wave: a ring of register buffers, each
+  // refilled (unconditionally, clamped past the end) right after its tile's
+  // multiplies are issued.
+  constexpr int RING = sketch_ring<kSketchNT>();
   const int64_t stride = (int64_t)gridDim.x * kSketchWaves;
-  int64_t tile = (int64_t)blockIdx.x * kSketchWaves + wave;
-  f16x8 b0[kSketchNT][KS], b1[kSketchNT][KS];
-  if (tile < tiles) load(b0, tile);
-  while (tile < tiles) {
-    const int64_t t1 = tile + stride;
-    if (t1 < tiles) load(b1, t1);
-    process(b0, tile);
-    if (t1 >= tiles) break;
-    const int64_t t2 = t1 + stride;
-    if (t2 < tiles) load(b0, t2);
-    process(b1, t1);
-    tile = t2;
+  const int64_t first = (int64_t)blockIdx.x * kSketchWaves + wave;
+  if (first >= tiles) return;
+  f16x8 bq[RING][kSketchNT][KS];
+#pragma unroll
+  for (int r = 0; r < RING; ++r) load(bq[r], std::min(first + r * stride, tiles - 1));
+  for (int64_t t0 = first;; t0 += RING * stride) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) {
+      const int64_t t = t0 + r * stride;
+      process(bq[r], t);
+      if (t + stride >= tiles) return;
+      load(bq[r], std::min(t + RING * stride, tiles - 1));
+    }
   }
 }
 
