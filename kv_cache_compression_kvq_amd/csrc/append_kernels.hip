@@ -8,11 +8,14 @@
 // encoded with the same helpers as the standalone quantizer, so the codes
 // and scale are bit-identical to kvq_quantize_int8 of the same row.
 //
-// A workgroup takes kAppendTok groups.  Their keys are staged in LDS as
-// binary32; each thread owns up to four projection rows of S (read once from
-// global memory / L2 for all kAppendTok keys) and accumulates binary32 fused
-// multiply-adds in channel order; a wave ballot turns 64 projections into
-// two sign words.  Values are quantized one row per wave in registers.
+// A workgroup takes kAppendTok groups; their keys are staged in LDS as
+// binary32 and their values are quantized one row per wave in registers.
+// Projections (fp16 S, d <= 128, m <= 256): each wave reads 64 rows of S with
+// coalesced 1 KiB loads (4 rows per instruction, 16 lanes per row), forms
+// each lane's 8 products per key and sums a row's 16 lanes with DPP; a wave
+// ballot turns 64 projection signs into two sign words.  Other shapes: each
+// thread owns up to four rows of S and accumulates binary32 fused
+// multiply-adds in channel order.
 #include "kvq_device.h"
 #include "kvq_int8_device.h"
 #include "kvq_launch.h"
@@ -22,7 +25,7 @@
 
 namespace kvq {
 
-constexpr int kAppendTok = 8;
+constexpr int kAppendTok = 4;
 constexpr int kAppendThreads = 256;
 constexpr int kAppendWaves = kAppendThreads / 64;
 constexpr int kAppendVals = kMaxDecodeD / 64;   // value elements per lane
@@ -38,6 +41,24 @@ __global__ __launch_bounds__(kAppendThreads) void cache_append_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int words = m / 32;
+
+  // fp16 S with d <= 128 and m <= 256: coalesced projection (see below); its
+  // S loads are issued first so they overlap the staging of keys and values
+  constexpr bool kHalf = sizeof(T) == 2;
+  const bool fast = kHalf && d <= 128 && m <= kAppendThreads;
+  const int c = lane & 15;
+  const int r4 = lane >> 4;
+  const int cc = min(c, d / 8 - 1);
+  f16x8 raw[16];
+  if constexpr (kHalf) {
+    if (fast) {
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int row = min(64 * wave + 16 * r4 + it, m - 1);
+        raw[it] = *reinterpret_cast<const f16x8*>(S + (int64_t)row * d + 8 * cc);
+      }
+    }
+  }
 
   for (int i = threadIdx.x; i < ntok * d; i += kAppendThreads) ks[i] = to_f32(k[g0 * d + i]);
 
@@ -72,6 +93,48 @@ __global__ __launch_bounds__(kAppendThreads) void cache_append_kernel(
     for (int j = lane; j < d; j += 64) ss = __builtin_fmaf(kr[j], kr[j], ss);
     ss = seg_sum_f32<64>(ss);
     if (lane == 0) knorms[(g0 + tok) * Tcap + pos] = f32_to_f16_bits(__builtin_sqrtf(ss));
+  }
+
+  if constexpr (kHalf) {
+    if (fast) {
+      // Iteration it: the wave's load read rows 64 w + 16 r4 + it (lanes of
+      // segment r4, 16 bytes each); the 16 lanes of a segment sum the row's
+      // products with DPP, and lane c keeps the sign of the row it == c.  A
+      // ballot then yields the signs of rows 64 w .. 64 w + 63 in lane order,
+      // i.e. two sign words.
+      const bool live_c = 8 * c < d;
+      bool sgn[kAppendTok];
+#pragma unroll
+      for (int u = 0; u < kAppendTok; ++u) sgn[u] = false;
+#pragma unroll
+      for (int u = 0; u < kAppendTok; ++u) {
+        if (u >= ntok) break;
+        float kv[8];
+        const f32x4* p4 = reinterpret_cast<const f32x4*>(ks + u * d + 8 * cc);
+        const f32x4 k0 = p4[0], k1 = p4[1];
+        kv[0] = k0[0]; kv[1] = k0[1]; kv[2] = k0[2]; kv[3] = k0[3];
+        kv[4] = k1[0]; kv[5] = k1[1]; kv[6] = k1[2]; kv[7] = k1[3];
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+          float part = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)raw[it][e], kv[e], part);
+          part = seg_sum_f32<16>(live_c ? part : 0.0f);
+          sgn[u] = (it == c) ? (part >= 0.0f) : sgn[u];
+        }
+      }
+      const int row = 64 * wave + 16 * r4 + c;
+      const int w0 = 2 * wave;
+#pragma unroll
+      for (int u = 0; u < kAppendTok; ++u) {
+        if (u >= ntok) break;
+        const uint64_t bal = __ballot(row < m && sgn[u]);
+        uint32_t* dst = kbits + ((g0 + u) * Tcap + pos) * words;
+        if (lane == 0 && w0 < words) dst[w0] = (uint32_t)bal;
+        if (lane == 1 && w0 + 1 < words) dst[w0 + 1] = (uint32_t)(bal >> 32);
+      }
+      return;
+    }
   }
 
   // projections: thread t owns rows t + 256 r

@@ -72,9 +72,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
   extern __shared__ __align__(16) unsigned char lds_raw[];
   const int m = W > 0 ? 32 * W : m_rt;
   const int words = m / 32;
-  float* y = reinterpret_cast<float*>(lds_raw);
-  float* lut = y + m;
-  float* wpart = lut + byte_table_floats(m, W == 8);  // [kDecodeWaves][d + 2]
+  // tables first: at LDS address 0 a lookup's address needs no base added
+  float* lut = reinterpret_cast<float*>(lds_raw);
+  float* y = lut + byte_table_floats(m, W == 8);
+  float* wpart = y + m;                                // [kDecodeWaves][d + 2]
 
   const int64_t g = blockIdx.x / splits;
   const int64_t sp = blockIdx.x % splits;
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
     if constexpr (W == 8) {
       uint32_t wv[8];
       load_rot_words(bblk + tc * 8, lane & 31, wv);
-      acc = rot_lut_sum(lut, wv, lane & 31, 4u * (uint32_t)(lane & 31));
+      acc = rot_lut_sum(lut, wv, lane & 31, rot_lane_base(lut, lane & 31));
     } else {
       acc = 0.0f;
       for (int i = 0; i < words; ++i) {

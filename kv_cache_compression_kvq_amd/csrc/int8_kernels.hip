@@ -372,6 +372,23 @@ __global__ __launch_bounds__(256) void scores_int8_kernel(const TQ* __restrict__
   const int8_t* cg = codes + g * T * d;
   const int nq_pass = QLDS ? min(kScoreNqc, kScoreLdsFloats / d) : kScoreNqc;
 
+  // Every load is unconditional (tokens past T re-read token T - 1, chunks
+  // past the row re-read its last chunk; neither is used): loads under a
+  // branch make the compiler wait for each one.  The scales and the first
+  // chunk of codes are requested before the query is staged.
+  int64_t tc[kScoreUnroll];
+  float st[kScoreUnroll];
+#pragma unroll
+  for (int u = 0; u < kScoreUnroll; ++u) {
+    tc[u] = std::min<int64_t>(t0 + u * 8 + slot, T - 1);
+    st[u] = scales[g * T + tc[u]];
+  }
+  const int c_first = min(sub, cpr - 1);
+  u32x4 w_first[kScoreUnroll];
+#pragma unroll
+  for (int u = 0; u < kScoreUnroll; ++u)
+    w_first[u] = ld_stream(reinterpret_cast<const u32x4*>(cg + tc[u] * d + (int64_t)c_first * 16));
+
   for (int j0 = 0; j0 < nq; j0 += nq_pass) {
     const int nqc = min(nq_pass, nq - j0);
     const TQ* qg = q + ((int64_t)g * nq + j0) * d;
@@ -389,10 +406,10 @@ __global__ __launch_bounds__(256) void scores_int8_kernel(const TQ* __restrict__
     for (int c = sub; c < cpr; c += kScoreLpt) {
       u32x4 w[kScoreUnroll];
 #pragma unroll
-      for (int u = 0; u < kScoreUnroll; ++u) {
-        const int64_t t = t0 + u * 8 + slot;
-        w[u] = (t < T) ? ld_stream(reinterpret_cast<const u32x4*>(cg + t * d + (int64_t)c * 16)) : u32x4{};
-      }
+      for (int u = 0; u < kScoreUnroll; ++u)
+        w[u] = (j0 == 0 && c == sub)
+                   ? w_first[u]
+                   : ld_stream(reinterpret_cast<const u32x4*>(cg + tc[u] * d + (int64_t)c * 16));
 #pragma unroll
       for (int jj = 0; jj < kScoreNqc; ++jj) {
         if (jj < nqc) {
@@ -411,11 +428,10 @@ __global__ __launch_bounds__(256) void scores_int8_kernel(const TQ* __restrict__
 #pragma unroll
     for (int u = 0; u < kScoreUnroll; ++u) {
       const int64_t t = t0 + u * 8 + slot;
-      const float st = (t < T) ? scales[g * T + t] : 0.0f;
 #pragma unroll
       for (int jj = 0; jj < kScoreNqc; ++jj) {
         const float tot = seg_sum_f32<kScoreLpt>(acc[u][jj]);
-        if (jj < nqc && sub == 0 && t < T) scores[((int64_t)g * nq + j0 + jj) * T + t] = tot * st;
+        if (jj < nqc && sub == 0 && t < T) scores[((int64_t)g * nq + j0 + jj) * T + t] = tot * st[u];
       }
     }
   }

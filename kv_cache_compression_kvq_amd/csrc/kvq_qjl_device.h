@@ -82,9 +82,87 @@ __device__ __forceinline__ float row_dot(const TS* __restrict__ sr, const float*
 // multiply-adds in j order, computed by the whole 256-thread workgroup:
 // thread t owns rows t, t + 256, ...; q is staged through LDS (qs, at least
 // kProjQChunk floats) and S rows are read 16 values at a time.
+// y = S q for fp16 S with d <= 128 and m <= 64 * waves, coalesced: a wave
+// load instruction reads 4 whole rows (16 lanes x 16 bytes each, 1 KiB
+// contiguous); lane (row r4, chunk c) forms the 8 products of its chunk and
+// the 16 lanes of a row are summed with DPP.  Two phases, so a caller can
+// issue other loads between them: issue() requests the wave's rows of S and
+// the thread's element of q (all unconditionally, so the compiler's wait
+// counts stay exact), finish() stages q in LDS and writes y (callers
+// synchronise before reading y).
+template <typename TQ>
+struct QueryProj16 {
+  f16x8 raw[16];
+  TQ qreg;                          // converted in finish(), not here: a use
+                                    // would make the compiler wait for the load
+  int rpw;                          // rows per wave, a multiple of 4
+
+  __device__ __forceinline__ static bool fits(int m, int d) {
+    const int nw = (int)blockDim.x / 64;
+    return d <= 128 && (int)blockDim.x >= d && ((m + nw - 1) / nw + 3) / 4 * 4 <= 64;
+  }
+
+  __device__ __forceinline__ void issue(const _Float16* __restrict__ S, const TQ* __restrict__ q,
+                                        int m, int d) {
+    const int nw = (int)blockDim.x / 64;
+    rpw = ((m + nw - 1) / nw + 3) & ~3;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int c = lane & 15;
+    const int r4 = lane >> 4;
+    const int cc = min(c, d / 8 - 1);          // chunks past the row: reloaded, unused
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int row = min(wave * rpw + 4 * min(it, rpw / 4 - 1) + r4, m - 1);
+      raw[it] = *reinterpret_cast<const f16x8*>(S + (int64_t)row * d + 8 * cc);
+    }
+    qreg = q[min((int)threadIdx.x, d - 1)];
+  }
+
+  __device__ __forceinline__ void finish(float* qs, float* y, int m, int d) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int c = lane & 15;
+    const int r4 = lane >> 4;
+    const int cc = min(c, d / 8 - 1);
+    // every thread writes (qs holds at least kProjQChunk >= blockDim.x floats;
+    // entries past d are not read): a store under a branch would let the
+    // compiler sink the q load next to it, behind the caller's later loads
+    qs[threadIdx.x] = to_f32(qreg);
+    __syncthreads();
+    const bool live_c = 8 * c < d;
+    float qv[8];
+    const f32x4* p4 = reinterpret_cast<const f32x4*>(qs + 8 * cc);
+    const f32x4 q0 = p4[0], q1 = p4[1];
+    qv[0] = q0[0]; qv[1] = q0[1]; qv[2] = q0[2]; qv[3] = q0[3];
+    qv[4] = q1[0]; qv[5] = q1[1]; qv[6] = q1[2]; qv[7] = q1[3];
+    // all 16 row groups are formed (past rpw they repeat the last one and are
+    // not stored): a use under a branch would let the compiler sink the S
+    // loads of issue() next to it
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      float part = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)raw[it][e], qv[e], part);
+      part = seg_sum_f32<16>(live_c ? part : 0.0f);
+      const int row = wave * rpw + 4 * it + r4;
+      if (c == 0 && 4 * it < rpw && row < m) y[row] = part;
+    }
+  }
+};
+
 template <typename TS, typename TQ>
-__device__ void project_query_block(const TS* __restrict__ S, const TQ* __restrict__ q, int m,
-                                    int d, float* qs, float* y) {
+__device__ __forceinline__ void project_query_block(const TS* __restrict__ S,
+                                                    const TQ* __restrict__ q, int m, int d,
+                                                    float* qs, float* y) {
+  if constexpr (sizeof(TS) == 2) {
+    if (QueryProj16<TQ>::fits(m, d)) {
+      QueryProj16<TQ> pj;
+      pj.issue(S, q, m, d);
+      pj.finish(qs, y, m, d);
+      return;
+    }
+  }
   float acc[kProjMaxRowsPerThread];
 #pragma unroll
   for (int r = 0; r < kProjMaxRowsPerThread; ++r) acc[r] = 0.0f;
@@ -191,8 +269,20 @@ __device__ __forceinline__ void load_rot_words(const uint32_t* p, int r, uint32_
   w[4] = b[0]; w[5] = b[1]; w[6] = b[2]; w[7] = b[3];
 }
 
+typedef __attribute__((address_space(3))) const float* lds_cfloat_ptr;
+
+// The lane's constant part of a rotated-table address: the tables' LDS
+// address plus 4 r.  The byte permute below keeps bytes 0, 2 and 3 of it and
+// puts the token's byte in byte 1, so the tables must start at an LDS address
+// whose bits 8..15 are zero and whose low byte leaves room for 4 r (the
+// kernels place them at the start of their LDS, address 0).
+__device__ __forceinline__ uint32_t rot_lane_base(const float* lut, int r) {
+  return (uint32_t)(uintptr_t)(lds_cfloat_ptr)lut + 4u * (uint32_t)r;
+}
+
 // Sum over the 32 bytes of one token of the rotated tables' entries, for
-// words loaded by load_rot_words with the same r (= lane % 32); rq = 4 r.
+// words loaded by load_rot_words with the same r (= lane % 32); rq is
+// rot_lane_base(lut, r).
 __device__ __forceinline__ float rot_lut_sum(const float* lut, const uint32_t wl[8], int r,
                                              uint32_t rq) {
   // rotate the remaining 4 (r >> 2 & 3) words, then r & 3 bytes; the word
@@ -207,14 +297,15 @@ __device__ __forceinline__ float rot_lut_sum(const float* lut, const uint32_t wl
   const uint32_t sh = 8u * (uint32_t)(r & 3);
 #pragma unroll
   for (int j = 0; j < 8; ++j) x[j] = __builtin_amdgcn_alignbit(w[(j + 1) & 7], w[j], sh);
-  const char* base = reinterpret_cast<const char*>(lut);
+  (void)lut;
   float v[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    // (byte i & 3 of word i >> 2) * 256 + 4 r
+    // LDS address: tables + (byte i & 3 of word i >> 2) * 256 + 4 r, + 4 i
+    // as the instruction offset
     const uint32_t off =
-        __builtin_amdgcn_perm(rq, x[i >> 2], 0x0C0C0004u | ((uint32_t)(i & 3) << 8));
-    v[i] = *reinterpret_cast<const float*>(base + off + 4 * i);
+        __builtin_amdgcn_perm(rq, x[i >> 2], 0x07060004u | ((uint32_t)(i & 3) << 8));
+    v[i] = *(lds_cfloat_ptr)(uintptr_t)(off + 4u * (uint32_t)i);
   }
   // Keep the 32 reads in flight together: left to itself the scheduler
   // waits for each read before issuing the next.

@@ -335,14 +335,14 @@ hipError_t launch_qjl_sketch(const void* k, int k_f16, int64_t rows, int d, cons
 
 // ---------------------------------------------------------------------------
 // QJL scores: one workgroup per (group, query, tile of kQjlTok tokens).  Each
-// thread owns kQjlTokPerThread tokens and loads kQjlBatch of them (sign
-// words and norm) before scoring any, so every wave keeps 8 x 34 bytes per
-// lane in flight.
+// thread owns kQjlTokPerThread tokens, kQjlThreads apart, loaded in batches
+// of kQjlBatch (sign words and norm) before any of them is scored.
 constexpr int kQjlBatch = 8;
+constexpr int kQjlThreads = 256;
 constexpr int kQjlTokPerThread = 16;
-constexpr int kQjlTok = 256 * kQjlTokPerThread;
+constexpr int kQjlTok = kQjlThreads * kQjlTokPerThread;
 
-// LDS: y [m] | byte tables (rotated layout for m = 256, else [m / 8][256]);
+// LDS: byte tables (rotated layout for m = 256, else [m / 8][256]) | y [m];
 // the table area is also the query staging area of the projection, which
 // ends before the tables are built.
 __host__ __device__ inline size_t qjl_table_lds_floats(int m) {
@@ -351,7 +351,7 @@ __host__ __device__ inline size_t qjl_table_lds_floats(int m) {
 }
 
 template <typename TS, typename TQ, int W>
-__global__ __launch_bounds__(256) void scores_qjl_kernel(const TQ* __restrict__ q, int nq,
+__global__ __launch_bounds__(kQjlThreads) void scores_qjl_kernel(const TQ* __restrict__ q, int nq,
                                                          const TS* __restrict__ S, int m_rt, int d,
                                                          const uint32_t* __restrict__ bits,
                                                          const uint16_t* __restrict__ norms,
@@ -360,59 +360,81 @@ __global__ __launch_bounds__(256) void scores_qjl_kernel(const TQ* __restrict__ 
   extern __shared__ __align__(16) unsigned char lds_raw[];
   const int m = W > 0 ? 32 * W : m_rt;
   const int words = m / 32;
-  float* y = reinterpret_cast<float*>(lds_raw);
-  float* lut = y + m;
+  // tables first: at LDS address 0 a lookup's address is the byte permute's
+  // result plus the instruction offset, with no base to add
+  float* lut = reinterpret_cast<float*>(lds_raw);
+  const size_t tfl = byte_table_floats(m, m == 256);
+  float* y = lut + (tfl > (size_t)kProjQChunk ? tfl : (size_t)kProjQChunk);
   const int64_t gj = blockIdx.x / tiles;           // (group, query) pair
   const int64_t tile = blockIdx.x % tiles;
   const int64_t g = gj / nq;
-  project_query_block(S, q + gj * d, m, d, lut, y);
-  __syncthreads();
-  if constexpr (W == 8)
-    build_rot_tables(y, lut);
-  else
-    build_byte_tables(y, m / 8, lut);
-  __syncthreads();
   const float c = kSqrtHalfPi / (float)m;
   const uint32_t* bg = bits + g * T * words;
   const uint16_t* ng = norms + g * T;
   float* sg = scores + gj * T;
   const int64_t t0 = tile * kQjlTok + threadIdx.x;
   if constexpr (W == 8) {
+    static_assert(kQjlTokPerThread == 2 * kQjlBatch, "two batches per thread");
+    // The first batch of tokens is requested right after the projection's own
+    // loads (so those can be waited for alone), the second before the first
+    // batch is scored.  The loads are
+    // unconditional (tokens past T re-read token T - 1 and are not stored):
+    // loads under a branch make the compiler wait for each one.
     const int r = threadIdx.x & 31;
-    const uint32_t rq = 4u * (uint32_t)r;
-    for (int b0 = 0; b0 < kQjlTokPerThread; b0 += kQjlBatch) {
-      uint32_t wv[kQjlBatch][8];
-      float nv[kQjlBatch];
+    uint32_t wv[2][kQjlBatch][8];
+    float nv[2][kQjlBatch];
+    auto load_batch = [&](int bi) {
 #pragma unroll
       for (int u = 0; u < kQjlBatch; ++u) {
-        const int64_t t = t0 + (int64_t)(b0 + u) * 256;
-        if (t < T) {
-          load_rot_words(bg + t * 8, r, wv[u]);
-          nv[u] = (float)__builtin_bit_cast(_Float16, ld_stream(ng + t));
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) wv[u][i] = 0;
-          nv[u] = 0.0f;
-        }
+        const int64_t t = std::min(t0 + (int64_t)(bi * kQjlBatch + u) * kQjlThreads, T - 1);
+        load_rot_words(bg + t * 8, r, wv[bi][u]);
+        nv[bi][u] = (float)__builtin_bit_cast(_Float16, ld_stream(ng + t));
       }
+    };
+    if constexpr (sizeof(TS) == 2) {
+      if (QueryProj16<TQ>::fits(m, d)) {
+        QueryProj16<TQ> pj;
+        pj.issue(S, q + gj * d, m, d);
+        __builtin_amdgcn_sched_barrier(0);   // keep the projection's loads first
+        load_batch(0);
+        __builtin_amdgcn_sched_barrier(0);
+        pj.finish(lut, y, m, d);
+      } else {
+        load_batch(0);
+        project_query_block(S, q + gj * d, m, d, lut, y);
+      }
+    } else {
+      load_batch(0);
+      project_query_block(S, q + gj * d, m, d, lut, y);
+    }
+    __syncthreads();
+    build_rot_tables(y, lut);
+    __syncthreads();
+    load_batch(1);
+    const uint32_t rq = rot_lane_base(lut, r);
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
       for (int u = 0; u < kQjlBatch; ++u) {
-        const int64_t t = t0 + (int64_t)(b0 + u) * 256;
-        const float acc = rot_lut_sum(lut, wv[u], r, rq);
-        if (t < T) sg[t] = c * nv[u] * acc;
+        const int64_t t = t0 + (int64_t)(bi * kQjlBatch + u) * kQjlThreads;
+        const float acc = rot_lut_sum(lut, wv[bi][u], r, rq);
+        if (t < T) sg[t] = c * nv[bi][u] * acc;
       }
+    return;
+  }
+  project_query_block(S, q + gj * d, m, d, lut, y);
+  __syncthreads();
+  build_byte_tables(y, m / 8, lut);
+  __syncthreads();
+  for (int u = 0; u < kQjlTokPerThread; ++u) {
+    const int64_t t = t0 + (int64_t)u * kQjlThreads;
+    if (t >= T) break;
+    float acc = 0.0f;
+    for (int i = 0; i < words; ++i) {
+      const uint32_t x = bg[t * words + i];
+      acc += lut_sum(lut + i * 1024, &x, 1);
     }
-  } else {
-    for (int u = 0; u < kQjlTokPerThread; ++u) {
-      const int64_t t = t0 + (int64_t)u * 256;
-      if (t >= T) break;
-      float acc = 0.0f;
-      for (int i = 0; i < words; ++i) {
-        const uint32_t x = bg[t * words + i];
-        acc += lut_sum(lut + i * 1024, &x, 1);
-      }
-      sg[t] = c * (float)__builtin_bit_cast(_Float16, ng[t]) * acc;
-    }
+    sg[t] = c * (float)__builtin_bit_cast(_Float16, ng[t]) * acc;
   }
 }
 
@@ -436,12 +458,12 @@ static hipError_t scores_qjl_typed(const TQ* q, int64_t groups, int nq, const TS
     if (m == 256) {
       e = allow_dynamic_lds(scores_qjl_kernel<TS, TQ, 8>, lds);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((scores_qjl_kernel<TS, TQ, 8>), dim3(blocks), dim3(256), lds, st, qp, nq,
+      hipLaunchKernelGGL((scores_qjl_kernel<TS, TQ, 8>), dim3(blocks), dim3(kQjlThreads), lds, st, qp, nq,
                          S, m, d, bp, np, T, tiles, sp);
     } else {
       e = allow_dynamic_lds(scores_qjl_kernel<TS, TQ, 0>, lds);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((scores_qjl_kernel<TS, TQ, 0>), dim3(blocks), dim3(256), lds, st, qp, nq,
+      hipLaunchKernelGGL((scores_qjl_kernel<TS, TQ, 0>), dim3(blocks), dim3(kQjlThreads), lds, st, qp, nq,
                          S, m, d, bp, np, T, tiles, sp);
     }
     e = hipGetLastError();
