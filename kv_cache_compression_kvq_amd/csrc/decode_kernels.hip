@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void qjl_project_kernel(const TQ* __restrict__
 }
 
 template <int W, int LPV>
-__global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
+__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(4))) void decode_split_kernel(
     const float* __restrict__ yall, int m_rt, int d, const uint32_t* __restrict__ kbits, const uint16_t* __restrict__ knorms,
     const int8_t* __restrict__ vcodes, const float* __restrict__ vscales, int64_t T,
     int64_t splits, int64_t tps, float lam, float* __restrict__ partials) {
@@ -83,14 +83,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
   const int64_t t_end = std::min<int64_t>(T, t_begin + tps);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-
-  for (int i = threadIdx.x; i < m; i += kDecodeThreads) y[i] = yall[g * m + i];
-  __syncthreads();
-  if constexpr (W == 8)
-    build_rot_tables(y, lut);
-  else
-    build_byte_tables(y, m / 8, lut);
-  __syncthreads();
 
   constexpr int SLOTS = kWave / LPV;      // value rows per wave load
   constexpr int VSTEPS = kDecodeChunk / SLOTS;
@@ -116,60 +108,148 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
 #pragma unroll
   for (int e = 0; e < 16; ++e) o[e] = 0.0f;
 
-  for (int base = wave * kDecodeChunk; base < ntok; base += kDecodeBlockTokens) {
-    // Tokens past the range are clamped to its last token: their loads stay
-    // in bounds and their softmax weight is forced to 0 below.
-    const int t = base + lane;
-    const bool valid = t < ntok;
-    const int tc = min(t, ntok - 1);
-    u32x4 vc[PREFETCH ? VSTEPS : 1];
-    if constexpr (PREFETCH) {
+  if constexpr (W == 8 && PREFETCH) {
+    // Software pipeline over the wave's 64-token chunks: the loads of the
+    // next chunk (value codes, sign words, norm, value scale) are issued
+    // before the current chunk is scored and accumulated, and the first
+    // chunk's before the byte tables are built.  Every load is unconditional
+    // (past the range: the last token, weight 0), so the compiler's wait
+    // counts leave the next chunk in flight.
+    // Sign words, norm and value scale of a chunk (needed first, for the
+    // scores) and its value codes (needed last) are loaded separately, so
+    // the next chunk's value codes are requested only once the current
+    // chunk's score temporaries are dead.
+    struct Keys {
+      uint32_t wv[8];
+      uint16_t nb;
+      float vs;
+    };
+    struct Vals {
+      u32x4 vc[VSTEPS];
+    };
+    const int r = lane & 31;
+    auto load_keys = [&](Keys& kk, int base) {
+      const int tc = min(base + lane, ntok - 1);
+      load_rot_words(bblk + tc * 8, r, kk.wv);
+      kk.nb = ld_stream(nblk + tc);
+      kk.vs = ld_stream(sblk + tc);
+    };
+    auto load_vals = [&](Vals& vv, int base) {
 #pragma unroll
       for (int i = 0; i < VSTEPS; ++i) {
         const int tv = min(base + i * SLOTS + slot, ntok - 1);
-        vc[i] = ld_stream(reinterpret_cast<const u32x4*>(vblk + tv * DV));
+        vv.vc[i] = ld_stream(reinterpret_cast<const u32x4*>(vblk + tv * DV));
+      }
+    };
+    // softmax weight times value scale of this lane's token
+    auto score = [&](const Keys& kk, int base) -> float {
+      const bool valid = base + lane < ntok;
+      const float acc = rot_lut_sum(lut, kk.wv, r, rot_lane_base(lut, r));
+      const float n = (float)__builtin_bit_cast(_Float16, kk.nb);
+      const float z = valid ? lam * (c * n * acc) : -INFINITY;
+      // online softmax update (lane 0 of every chunk is valid, so mx is finite)
+      const float mx = seg_max_f32<64>(z);
+      const float M_new = __builtin_fmaxf(M, mx);
+      const float alpha = __expf(M - M_new);        // 0 on the first chunk (M = -inf)
+      const float p = __expf(z - M_new);            // 0 for invalid tokens (z = -inf)
+      L = L * alpha + seg_sum_f32<64>(p);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[e] *= alpha;
+      M = M_new;
+      return p * kk.vs;
+    };
+    auto accumulate = [&](const Vals& vv, float ps) {
+#pragma unroll
+      for (int i = 0; i < VSTEPS; ++i) {
+        const float w = bcast_from(ps, i * SLOTS + slot);
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          o[e] = __builtin_fmaf(w, i8_to_f32(vv.vc[i][e >> 2], e & 3), o[e]);
+      }
+    };
+
+    // y first (so its wait leaves the chunk loads in flight); every thread
+    // writes, past m into the merge area, which is written again later
+    const float yv = yall[g * m + min((int)threadIdx.x, m - 1)];
+    const int first = wave * kDecodeChunk;
+    Keys ka, kb;
+    Vals va, vb;
+    __builtin_amdgcn_sched_barrier(0);
+    load_keys(ka, first);
+    load_vals(va, first);
+    __builtin_amdgcn_sched_barrier(0);
+    y[threadIdx.x] = yv;
+    __syncthreads();
+    build_rot_tables(y, lut);
+    __syncthreads();
+    if (first < ntok) {
+      for (int base = first;; base += 2 * kDecodeBlockTokens) {
+        const int nb1 = base + kDecodeBlockTokens, nb2 = base + 2 * kDecodeBlockTokens;
+        load_keys(kb, nb1);
+        const float psa = score(ka, base);
+        accumulate(va, psa);
+        load_vals(vb, nb1);
+        if (nb1 >= ntok) break;
+        load_keys(ka, nb2);
+        const float psb = score(kb, nb1);
+        accumulate(vb, psb);
+        load_vals(va, nb2);
+        if (nb2 >= ntok) break;
       }
     }
-    float acc;
-    if constexpr (W == 8) {
-      uint32_t wv[8];
-      load_rot_words(bblk + tc * 8, lane & 31, wv);
-      acc = rot_lut_sum(lut, wv, lane & 31, rot_lane_base(lut, lane & 31));
-    } else {
-      acc = 0.0f;
+  } else {
+    for (int i = threadIdx.x; i < m; i += kDecodeThreads) y[i] = yall[g * m + i];
+    __syncthreads();
+    build_byte_tables(y, m / 8, lut);
+    __syncthreads();
+    for (int base = wave * kDecodeChunk; base < ntok; base += kDecodeBlockTokens) {
+      // Tokens past the range are clamped to its last token: their loads stay
+      // in bounds and their softmax weight is forced to 0 below.
+      const int t = base + lane;
+      const bool valid = t < ntok;
+      const int tc = min(t, ntok - 1);
+      u32x4 vc[PREFETCH ? VSTEPS : 1];
+      if constexpr (PREFETCH) {
+  #pragma unroll
+        for (int i = 0; i < VSTEPS; ++i) {
+          const int tv = min(base + i * SLOTS + slot, ntok - 1);
+          vc[i] = ld_stream(reinterpret_cast<const u32x4*>(vblk + tv * DV));
+        }
+      }
+      float acc = 0.0f;
       for (int i = 0; i < words; ++i) {
         const uint32_t x = bblk[tc * words + i];
         acc += lut_sum(lut + i * 1024, &x, 1);
       }
-    }
-    const float n = (float)__builtin_bit_cast(_Float16, ld_stream(nblk + tc));
-    const float vs = ld_stream(sblk + tc);
-    const float z = valid ? lam * (c * n * acc) : -INFINITY;
-    // online softmax update (lane 0 of every chunk is valid, so mx is finite)
-    const float mx = seg_max_f32<64>(z);
-    const float M_new = __builtin_fmaxf(M, mx);
-    const float alpha = __expf(M - M_new);        // 0 on the first chunk (M = -inf)
-    const float p = __expf(z - M_new);            // 0 for invalid tokens (z = -inf)
-    L = L * alpha + seg_sum_f32<64>(p);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[e] *= alpha;
-    M = M_new;
-    const float ps = p * vs;
-    // o += p_t * s_t * c_t over the chunk's value rows
-    if constexpr (PREFETCH) {
-#pragma unroll
-      for (int i = 0; i < VSTEPS; ++i) {
-        const float w = bcast_from(ps, i * SLOTS + slot);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[e] = __builtin_fmaf(w, i8_to_f32(vc[i][e >> 2], e & 3), o[e]);
-      }
-    } else {
-      for (int i = 0; i < VSTEPS; ++i) {
-        const float w = bcast_from(ps, i * SLOTS + slot);
-        const int tv = min(base + i * SLOTS + slot, ntok - 1);
-        const u32x4 cw = sub_live ? *reinterpret_cast<const u32x4*>(vblk + tv * dd) : u32x4{};
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[e] = __builtin_fmaf(w, i8_to_f32(cw[e >> 2], e & 3), o[e]);
+      const float n = (float)__builtin_bit_cast(_Float16, ld_stream(nblk + tc));
+      const float vs = ld_stream(sblk + tc);
+      const float z = valid ? lam * (c * n * acc) : -INFINITY;
+      // online softmax update (lane 0 of every chunk is valid, so mx is finite)
+      const float mx = seg_max_f32<64>(z);
+      const float M_new = __builtin_fmaxf(M, mx);
+      const float alpha = __expf(M - M_new);        // 0 on the first chunk (M = -inf)
+      const float p = __expf(z - M_new);            // 0 for invalid tokens (z = -inf)
+      L = L * alpha + seg_sum_f32<64>(p);
+  #pragma unroll
+      for (int e = 0; e < 16; ++e) o[e] *= alpha;
+      M = M_new;
+      const float ps = p * vs;
+      // o += p_t * s_t * c_t over the chunk's value rows
+      if constexpr (PREFETCH) {
+  #pragma unroll
+        for (int i = 0; i < VSTEPS; ++i) {
+          const float w = bcast_from(ps, i * SLOTS + slot);
+  #pragma unroll
+          for (int e = 0; e < 16; ++e) o[e] = __builtin_fmaf(w, i8_to_f32(vc[i][e >> 2], e & 3), o[e]);
+        }
+      } else {
+        for (int i = 0; i < VSTEPS; ++i) {
+          const float w = bcast_from(ps, i * SLOTS + slot);
+          const int tv = min(base + i * SLOTS + slot, ntok - 1);
+          const u32x4 cw = sub_live ? *reinterpret_cast<const u32x4*>(vblk + tv * dd) : u32x4{};
+  #pragma unroll
+          for (int e = 0; e < 16; ++e) o[e] = __builtin_fmaf(w, i8_to_f32(cw[e >> 2], e & 3), o[e]);
+        }
       }
     }
   }

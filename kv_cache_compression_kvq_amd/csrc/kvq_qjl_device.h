@@ -298,28 +298,33 @@ __device__ __forceinline__ float rot_lut_sum(const float* lut, const uint32_t wl
 #pragma unroll
   for (int j = 0; j < 8; ++j) x[j] = __builtin_amdgcn_alignbit(w[(j + 1) & 7], w[j], sh);
   (void)lut;
-  float v[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    // LDS address: tables + (byte i & 3 of word i >> 2) * 256 + 4 r, + 4 i
-    // as the instruction offset
-    const uint32_t off =
-        __builtin_amdgcn_perm(rq, x[i >> 2], 0x07060004u | ((uint32_t)(i & 3) << 8));
-    v[i] = *(lds_cfloat_ptr)(uintptr_t)(off + 4u * (uint32_t)i);
-  }
-  // Keep the 32 reads in flight together: left to itself the scheduler
-  // waits for each read before issuing the next.
-#pragma unroll
-  for (int g = 0; g < 32; g += 8)
-    asm volatile("" ::"v"(v[g]), "v"(v[g + 1]), "v"(v[g + 2]), "v"(v[g + 3]), "v"(v[g + 4]),
-                 "v"(v[g + 5]), "v"(v[g + 6]), "v"(v[g + 7]));
+  // Two halves of 16 reads, each kept in flight together (left to itself the
+  // scheduler waits for each read before issuing the next); the sum is four
+  // chains of 8 added pairwise.
   float part[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    float a = 0.0f;
+  for (int hf = 0; hf < 2; ++hf) {
+    float v[16];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) a += v[8 * c + k];
-    part[c] = a;
+    for (int k = 0; k < 16; ++k) {
+      const int i = 16 * hf + k;
+      // LDS address: tables + (byte i & 3 of word i >> 2) * 256 + 4 r, + 4 i
+      // as the instruction offset
+      const uint32_t off =
+          __builtin_amdgcn_perm(rq, x[i >> 2], 0x07060004u | ((uint32_t)(i & 3) << 8));
+      v[k] = *(lds_cfloat_ptr)(uintptr_t)(off + 4u * (uint32_t)i);
+    }
+#pragma unroll
+    for (int g = 0; g < 16; g += 8)
+      asm volatile("" ::"v"(v[g]), "v"(v[g + 1]), "v"(v[g + 2]), "v"(v[g + 3]), "v"(v[g + 4]),
+                   "v"(v[g + 5]), "v"(v[g + 6]), "v"(v[g + 7]));
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc += v[8 * c2 + k];
+      part[2 * hf + c2] = acc;
+    }
   }
   return (part[0] + part[1]) + (part[2] + part[3]);
 }
