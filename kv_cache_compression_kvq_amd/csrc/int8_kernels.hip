@@ -192,10 +192,10 @@ static hipError_t quantize_dispatch(const T* x, int64_t rows, int d, int8_t* cod
       case 4: return lanes(quantize_lanes_kernel<T, 4, 1, 8>, 4, 8);
       case 8: return lanes(quantize_lanes_kernel<T, 8, 1, 8>, 8, 8);
       case 16: return lanes(quantize_lanes_kernel<T, 16, 1, 8>, 16, 8);
-      case 32: return lanes(quantize_lanes_kernel<T, 32, 1, 8>, 32, 8);
+      case 32: return lanes(quantize_lanes_kernel<T, 32, 1, 16>, 32, 16);
       case 64: return lanes(quantize_lanes_kernel<T, 64, 1, 4>, 64, 4);
       case 128: return lanes(quantize_lanes_kernel<T, 64, 2, 4>, 64, 4);
-      case 256: return lanes(quantize_lanes_kernel<T, 64, 4, 2>, 64, 2);
+      case 256: return lanes(quantize_lanes_kernel<T, 64, 4, 4>, 64, 4);
       case 512: return lanes(quantize_lanes_kernel<T, 64, 8, 1>, 64, 1);
       case 1024: return block(quantize_block_kernel<T, 4>);
       case 2048: return block(quantize_block_kernel<T, 8>);
