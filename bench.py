@@ -170,6 +170,10 @@ def components(K, si, torch, np):
     halves = [(c[0][: R // 2].view(32, 4096, 128), c[1][: R // 2].view(32, 4096)) for c in cs]
     gbs("llama_layer_scores_int8", 32 * 4096 * (128 + 4 + 4) + 32 * 128 * 2,
         [lambda h=h: K.scores_int8(q, h[0], h[1]) for h in halves])
+    # grouped-query attention, 4 query heads per KV head: one pass over the codes
+    q4 = torch.from_numpy(si.queries(W, 32, 4, 128, "f16")).to(dev)
+    gbs("llama_layer_scores_int8_gqa4", 32 * 4096 * (128 + 4 + 4 * 4) + 32 * 4 * 128 * 2,
+        [lambda h=h: K.scores_int8(q4, h[0], h[1]) for h in halves])
     del k, v, kv, kvs, cs, halves
     torch.cuda.empty_cache()
 
@@ -191,6 +195,12 @@ def components(K, si, torch, np):
     gbs("qjl_scores_f16_m256", R * (m // 8 + 2 + 4) + G * d * 2 + m * d * 2,
         [lambda bn=bn: K.scores_qjl(q, S, bn[0], bn[1]) for bn in b3])
     res["qjl_scores_f16_m256"]["scores/s"] = round(R / res["qjl_scores_f16_m256"]["ms"] * 1e3, 1)
+    # grouped-query attention, 4 query heads per KV head: one pass over the sign words
+    q4 = torch.from_numpy(si.queries(W, G, 4, d, "f16")).to(dev)
+    gbs("qjl_scores_gqa4_f16_m256", R * (m // 8 + 2 + 4 * 4) + G * 4 * d * 2 + m * d * 2,
+        [lambda bn=bn: K.scores_qjl(q4, S, bn[0], bn[1]) for bn in b3])
+    res["qjl_scores_gqa4_f16_m256"]["scores/s"] = round(
+        4 * R / res["qjl_scores_gqa4_f16_m256"]["ms"] * 1e3, 1)
     del kk, sk, b3
     torch.cuda.empty_cache()
     return res

@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
     // softmax weight times value scale of this lane's token
     auto score = [&](const Keys& kk, int base) -> float {
       const bool valid = base + lane < ntok;
-      const float acc = rot_lut_sum(lut, kk.wv, r, rot_lane_base(lut, r));
+      const float acc = rot_lut_sum(kk.wv, r, rot_lane_base(lut, r));
       const float n = (float)__builtin_bit_cast(_Float16, kk.nb);
       const float z = valid ? lam * (c * n * acc) : -INFINITY;
       // online softmax update (lane 0 of every chunk is valid, so mx is finite)

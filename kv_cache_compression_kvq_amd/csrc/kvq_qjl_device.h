@@ -151,6 +151,48 @@ struct QueryProj16 {
   }
 };
 
+// The same y = S q as QueryProj16 (same arithmetic, bit for bit) with only
+// 4 row groups of S in registers at a time, for callers that hold many
+// registers across it.  Starts with the q staging (the caller synchronises
+// before, if qs is in use).
+template <typename TQ>
+__device__ __forceinline__ void project16_lite(const _Float16* __restrict__ S,
+                                               const TQ* __restrict__ q, int m, int d, float* qs,
+                                               float* y) {
+  const int nw = (int)blockDim.x / 64;
+  const int rpw = ((m + nw - 1) / nw + 3) & ~3;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c = lane & 15;
+  const int r4 = lane >> 4;
+  const int cc = min(c, d / 8 - 1);
+  qs[threadIdx.x] = to_f32(q[min((int)threadIdx.x, d - 1)]);
+  __syncthreads();
+  const bool live_c = 8 * c < d;
+  float qv[8];
+  const f32x4* p4 = reinterpret_cast<const f32x4*>(qs + 8 * cc);
+  const f32x4 q0 = p4[0], q1 = p4[1];
+  qv[0] = q0[0]; qv[1] = q0[1]; qv[2] = q0[2]; qv[3] = q0[3];
+  qv[4] = q1[0]; qv[5] = q1[1]; qv[6] = q1[2]; qv[7] = q1[3];
+  for (int it0 = 0; 4 * it0 < rpw; it0 += 4) {
+    f16x8 raw[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int row = min(wave * rpw + 4 * min(it0 + k, rpw / 4 - 1) + r4, m - 1);
+      raw[k] = *reinterpret_cast<const f16x8*>(S + (int64_t)row * d + 8 * cc);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float part = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)raw[k][e], qv[e], part);
+      part = seg_sum_f32<16>(live_c ? part : 0.0f);
+      const int row = wave * rpw + 4 * (it0 + k) + r4;
+      if (c == 0 && 4 * (it0 + k) < rpw && row < m) y[row] = part;
+    }
+  }
+}
+
 template <typename TS, typename TQ>
 __device__ __forceinline__ void project_query_block(const TS* __restrict__ S,
                                                     const TQ* __restrict__ q, int m, int d,
@@ -280,15 +322,13 @@ __device__ __forceinline__ uint32_t rot_lane_base(const float* lut, int r) {
   return (uint32_t)(uintptr_t)(lds_cfloat_ptr)lut + 4u * (uint32_t)r;
 }
 
-// Sum over the 32 bytes of one token of the rotated tables' entries, for
-// words loaded by load_rot_words with the same r (= lane % 32); rq is
-// rot_lane_base(lut, r).
-__device__ __forceinline__ float rot_lut_sum(const float* lut, const uint32_t wl[8], int r,
-                                             uint32_t rq) {
-  // rotate the remaining 4 (r >> 2 & 3) words, then r & 3 bytes; the word
-  // moves are bit blends with all-ones / all-zero lane masks (a select would
-  // become an indexed array in scratch)
-  uint32_t x[8], w[8];
+// The 8 words from load_rot_words rotated by the remaining 4 ((r >> 2) & 3)
+// words and then r & 3 bytes, so that byte i of the result is byte (r + i)
+// mod 32 of the token's sign bytes.  The word moves are bit blends with
+// all-ones / all-zero lane masks (a select would become an indexed array in
+// scratch).
+__device__ __forceinline__ void rot_words(const uint32_t wl[8], int r, uint32_t x[8]) {
+  uint32_t w[8];
   const uint32_t m2 = 0u - ((uint32_t)r >> 3 & 1u), m1 = 0u - ((uint32_t)r >> 2 & 1u);
 #pragma unroll
   for (int j = 0; j < 8; ++j) x[j] = wl[j] ^ ((wl[(j + 2) & 7] ^ wl[j]) & m2);
@@ -297,7 +337,11 @@ __device__ __forceinline__ float rot_lut_sum(const float* lut, const uint32_t wl
   const uint32_t sh = 8u * (uint32_t)(r & 3);
 #pragma unroll
   for (int j = 0; j < 8; ++j) x[j] = __builtin_amdgcn_alignbit(w[(j + 1) & 7], w[j], sh);
-  (void)lut;
+}
+
+// Sum over the 32 bytes of one token of the rotated tables' entries, for
+// words already rotated by rot_words; rq is rot_lane_base(tables, r).
+__device__ __forceinline__ float rot_lut_sum_rotated(const uint32_t x[8], uint32_t rq) {
   // Two halves of 16 reads, each kept in flight together (left to itself the
   // scheduler waits for each read before issuing the next); the sum is four
   // chains of 8 added pairwise.
@@ -327,6 +371,15 @@ __device__ __forceinline__ float rot_lut_sum(const float* lut, const uint32_t wl
     }
   }
   return (part[0] + part[1]) + (part[2] + part[3]);
+}
+
+// Sum over the 32 bytes of one token of the rotated tables' entries, for
+// words loaded by load_rot_words with the same r (= lane % 32); rq is
+// rot_lane_base(tables, r).
+__device__ __forceinline__ float rot_lut_sum(const uint32_t wl[8], int r, uint32_t rq) {
+  uint32_t x[8];
+  rot_words(wl, r, x);
+  return rot_lut_sum_rotated(x, rq);
 }
 
 // Sum of the table entries selected by the bytes of `nw` sign words.

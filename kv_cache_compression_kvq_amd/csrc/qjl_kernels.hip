@@ -334,9 +334,10 @@ hipError_t launch_qjl_sketch(const void* k, int k_f16, int64_t rows, int d, cons
 }
 
 // ---------------------------------------------------------------------------
-// QJL scores: one workgroup per (group, query, tile of kQjlTok tokens).  Each
-// thread owns kQjlTokPerThread tokens, kQjlThreads apart, loaded in batches
-// of kQjlBatch (sign words and norm) before any of them is scored.
+// QJL scores: one workgroup per (group, tile of kQjlTok tokens) for m = 256
+// (all of the group's queries), else per (group, query, tile).  Each thread
+// owns kQjlTokPerThread tokens, kQjlThreads apart, loaded in batches of
+// kQjlBatch (sign words and norm) before any of them is scored.
 constexpr int kQjlBatch = 8;
 constexpr int kQjlThreads = 256;
 constexpr int kQjlTokPerThread = 16;
@@ -350,8 +351,11 @@ __host__ __device__ inline size_t qjl_table_lds_floats(int m) {
   return (size_t)m + (tables > (size_t)kProjQChunk ? tables : (size_t)kProjQChunk);
 }
 
-template <typename TS, typename TQ, int W>
-__global__ __launch_bounds__(kQjlThreads) void scores_qjl_kernel(const TQ* __restrict__ q, int nq,
+// NB: batches of kQjlBatch tokens per thread in the m = 256 kernel (2 for a
+// single query per group; 1 when the group's queries share the pass, whose
+// tokens stay in registers across the queries).
+template <typename TS, typename TQ, int W, int NB>
+__global__ __launch_bounds__(kQjlThreads) __attribute__((amdgpu_waves_per_eu(2))) void scores_qjl_kernel(const TQ* __restrict__ q, int nq,
                                                          const TS* __restrict__ S, int m_rt, int d,
                                                          const uint32_t* __restrict__ bits,
                                                          const uint16_t* __restrict__ norms,
@@ -365,24 +369,27 @@ __global__ __launch_bounds__(kQjlThreads) void scores_qjl_kernel(const TQ* __res
   float* lut = reinterpret_cast<float*>(lds_raw);
   const size_t tfl = byte_table_floats(m, m == 256);
   float* y = lut + (tfl > (size_t)kProjQChunk ? tfl : (size_t)kProjQChunk);
-  const int64_t gj = blockIdx.x / tiles;           // (group, query) pair
-  const int64_t tile = blockIdx.x % tiles;
-  const int64_t g = gj / nq;
   const float c = kSqrtHalfPi / (float)m;
-  const uint32_t* bg = bits + g * T * words;
-  const uint16_t* ng = norms + g * T;
-  float* sg = scores + gj * T;
-  const int64_t t0 = tile * kQjlTok + threadIdx.x;
   if constexpr (W == 8) {
-    static_assert(kQjlTokPerThread == 2 * kQjlBatch, "two batches per thread");
-    // The first batch of tokens is requested right after the projection's own
-    // loads (so those can be waited for alone), the second before the first
-    // batch is scored.  The loads are
-    // unconditional (tokens past T re-read token T - 1 and are not stored):
-    // loads under a branch make the compiler wait for each one.
+    static_assert(NB == 1 || NB == 2, "one or two batches per thread");
+    constexpr int kTile = kQjlThreads * kQjlBatch * NB;
+    // One workgroup per (group, tile) scores all nq queries of the group
+    // (grouped-query attention: the queries of a KV head share one pass over
+    // its sign words and norms, which stay in registers).  Per query: y = S q
+    // and the byte tables are rebuilt in LDS, then the tokens are scored.
+    // The first batch of tokens is requested right after the first
+    // projection's own loads (so those can be waited for alone), the second
+    // before the first batch is scored.  The loads are unconditional (tokens
+    // past T re-read token T - 1 and are not stored): loads under a branch
+    // make the compiler wait for each one.
+    const int64_t g = blockIdx.x / tiles;
+    const int64_t tile = blockIdx.x % tiles;
+    const uint32_t* bg = bits + g * T * words;
+    const uint16_t* ng = norms + g * T;
+    const int64_t t0 = tile * kTile + threadIdx.x;
     const int r = threadIdx.x & 31;
-    uint32_t wv[2][kQjlBatch][8];
-    float nv[2][kQjlBatch];
+    uint32_t wv[NB][kQjlBatch][8];
+    float nv[NB][kQjlBatch];
     auto load_batch = [&](int bi) {
 #pragma unroll
       for (int u = 0; u < kQjlBatch; ++u) {
@@ -391,37 +398,69 @@ __global__ __launch_bounds__(kQjlThreads) void scores_qjl_kernel(const TQ* __res
         nv[bi][u] = (float)__builtin_bit_cast(_Float16, ld_stream(ng + t));
       }
     };
+    // the words are rotated in place once (rot_words) and serve every query
+    auto rotate_all = [&]() {
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+        for (int u = 0; u < kQjlBatch; ++u) {
+          uint32_t xr[8];
+          rot_words(wv[bi][u], r, xr);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) wv[bi][u][k] = xr[k];
+        }
+    };
+    auto score_all = [&](float* sg) {
+      // opaque per call: the lookup addresses depend only on the words and
+      // r, and hoisting all of them out of the query loop would need 256
+      // registers
+      uint32_t rq = rot_lane_base(lut, r);
+      asm volatile("" : "+v"(rq));
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+        for (int u = 0; u < kQjlBatch; ++u) {
+          const int64_t t = t0 + (int64_t)(bi * kQjlBatch + u) * kQjlThreads;
+          const float acc = rot_lut_sum_rotated(wv[bi][u], rq);
+          if (t < T) sg[t] = c * nv[bi][u] * acc;
+        }
+    };
+    // query 0 (this kernel is launched for fp16 S with d <= 128 only)
+    const TQ* q0 = q + g * nq * d;
     if constexpr (sizeof(TS) == 2) {
-      if (QueryProj16<TQ>::fits(m, d)) {
-        QueryProj16<TQ> pj;
-        pj.issue(S, q + gj * d, m, d);
-        __builtin_amdgcn_sched_barrier(0);   // keep the projection's loads first
-        load_batch(0);
-        __builtin_amdgcn_sched_barrier(0);
-        pj.finish(lut, y, m, d);
-      } else {
-        load_batch(0);
-        project_query_block(S, q + gj * d, m, d, lut, y);
-      }
-    } else {
+      QueryProj16<TQ> pj;
+      pj.issue(S, q0, m, d);
+      __builtin_amdgcn_sched_barrier(0);   // keep the projection's loads first
       load_batch(0);
-      project_query_block(S, q + gj * d, m, d, lut, y);
-    }
-    __syncthreads();
-    build_rot_tables(y, lut);
-    __syncthreads();
-    load_batch(1);
-    const uint32_t rq = rot_lane_base(lut, r);
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-      for (int u = 0; u < kQjlBatch; ++u) {
-        const int64_t t = t0 + (int64_t)(bi * kQjlBatch + u) * kQjlThreads;
-        const float acc = rot_lut_sum(lut, wv[bi][u], r, rq);
-        if (t < T) sg[t] = c * nv[bi][u] * acc;
+      __builtin_amdgcn_sched_barrier(0);
+      pj.finish(lut, y, m, d);
+      __syncthreads();
+      build_rot_tables(y, lut);
+      __syncthreads();
+      if constexpr (NB == 2) load_batch(1);
+      rotate_all();
+      score_all(scores + g * nq * T);
+      // queries 1 .. nq - 1: the tokens are already in registers (the
+      // two-batch kernel is launched for one query per group only)
+      if constexpr (NB == 1)
+      for (int j = 1; j < nq; ++j) {
+        __syncthreads();                       // every lookup of query j - 1 is done
+        project16_lite(S, q0 + (int64_t)j * d, m, d, lut, y);
+        __syncthreads();
+        build_rot_tables(y, lut);
+        __syncthreads();
+        score_all(scores + (g * nq + j) * T);
       }
+    }
     return;
   }
+  const int64_t gj = blockIdx.x / tiles;           // (group, query) pair
+  const int64_t tile = blockIdx.x % tiles;
+  const int64_t g = gj / nq;
+  const uint32_t* bg = bits + g * T * words;
+  const uint16_t* ng = norms + g * T;
+  float* sg = scores + gj * T;
+  const int64_t t0 = tile * kQjlTok + threadIdx.x;
   project_query_block(S, q + gj * d, m, d, lut, y);
   __syncthreads();
   build_byte_tables(y, m / 8, lut);
@@ -444,27 +483,38 @@ static hipError_t scores_qjl_typed(const TQ* q, int64_t groups, int nq, const TS
                                    float* scores, const DeviceInfo& dev, hipStream_t st) {
   const size_t lds = qjl_table_lds_floats(m) * sizeof(float);
   if (lds > dev.lds_per_block) return hipErrorInvalidConfiguration;
-  const int64_t tiles = (T + kQjlTok - 1) / kQjlTok;
+  // m = 256 with fp16 S and d <= 128: one workgroup per (group, tile) scores
+  // all nq queries; else one per (group, query, tile)
+  const bool grouped = m == 256 && sizeof(TS) == 2 && d <= 128;
+  const int64_t tile_tokens = grouped ? (int64_t)kQjlThreads * kQjlBatch * (nq == 1 ? 2 : 1)
+                                      : (int64_t)kQjlTok;
+  const int64_t tiles = (T + tile_tokens - 1) / tile_tokens;
+  const int64_t per_group = grouped ? tiles : tiles * nq;
   // launch in slices of whole groups so grid.x stays far below 2^32
-  const int64_t max_groups = std::max<int64_t>(1, (int64_t(1) << 22) / (tiles * nq));
+  const int64_t max_groups = std::max<int64_t>(1, (int64_t(1) << 22) / per_group);
   for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
     const int64_t ng = std::min(max_groups, groups - g0);
     const TQ* qp = q + g0 * nq * d;
     const uint32_t* bp = bits + g0 * T * (m / 32);
     const uint16_t* np = norms + g0 * T;
     float* sp = scores + g0 * nq * T;
-    const unsigned blocks = (unsigned)(ng * nq * tiles);
+    const unsigned blocks = (unsigned)(ng * per_group);
     hipError_t e;
-    if (m == 256) {
-      e = allow_dynamic_lds(scores_qjl_kernel<TS, TQ, 8>, lds);
+    if (grouped && nq == 1) {
+      e = allow_dynamic_lds(scores_qjl_kernel<TS, TQ, 8, 2>, lds);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((scores_qjl_kernel<TS, TQ, 8>), dim3(blocks), dim3(kQjlThreads), lds, st, qp, nq,
-                         S, m, d, bp, np, T, tiles, sp);
+      hipLaunchKernelGGL((scores_qjl_kernel<TS, TQ, 8, 2>), dim3(blocks), dim3(kQjlThreads), lds,
+                         st, qp, nq, S, m, d, bp, np, T, tiles, sp);
+    } else if (grouped) {
+      e = allow_dynamic_lds(scores_qjl_kernel<TS, TQ, 8, 1>, lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((scores_qjl_kernel<TS, TQ, 8, 1>), dim3(blocks), dim3(kQjlThreads), lds,
+                         st, qp, nq, S, m, d, bp, np, T, tiles, sp);
     } else {
-      e = allow_dynamic_lds(scores_qjl_kernel<TS, TQ, 0>, lds);
+      e = allow_dynamic_lds(scores_qjl_kernel<TS, TQ, 0, 2>, lds);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((scores_qjl_kernel<TS, TQ, 0>), dim3(blocks), dim3(kQjlThreads), lds, st, qp, nq,
-                         S, m, d, bp, np, T, tiles, sp);
+      hipLaunchKernelGGL((scores_qjl_kernel<TS, TQ, 0, 2>), dim3(blocks), dim3(kQjlThreads), lds,
+                         st, qp, nq, S, m, d, bp, np, T, tiles, sp);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;

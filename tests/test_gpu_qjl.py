@@ -117,7 +117,8 @@ def test_sketch_zero_and_scaled_keys():
 
 @pytest.mark.parametrize("qdt,sdt", [("f16", "f16"), ("f32", "f32"), ("f16", "f32"), ("f32", "f16")])
 @pytest.mark.parametrize("nq,T,m,d", [(1, 1, 256, 128), (3, 2049, 256, 128), (8, 300, 64, 64),
-                                      (2, 513, 512, 128), (1, 100, 1024, 256), (4, 77, 96, 48)])
+                                      (2, 513, 512, 128), (1, 100, 1024, 256), (4, 77, 96, 48),
+                                      (4, 4100, 256, 128), (8, 1000, 256, 64), (2, 5, 256, 16)])
 def test_scores_shapes(qdt, sdt, nq, T, m, d):
     rng = np.random.default_rng(nq + T + m)
     G = 3
@@ -143,3 +144,20 @@ def test_bit_order_matches_fixture_on_gpu():
         k = np.array(keys, dt)
         bits, _ = K.qjl_sketch(up(k), up(np.eye(64, dtype=dt)))
         assert down(bits, np.uint32).tolist() == want
+
+
+@pytest.mark.parametrize("nq,T,d", [(4, 4100, 128), (8, 999, 64)])
+def test_grouped_queries_equal_single_query_runs(nq, T, d):
+    """Grouped-query scoring (one pass over a KV head's sign words for all of
+    its queries) gives, bit for bit, what scoring each query alone gives."""
+    rng = np.random.default_rng(nq * T)
+    G, m = 3, 256
+    S = rng.standard_normal((m, d)).astype(np.float16)
+    k = rng.standard_normal((G * T, d)).astype(np.float16)
+    words, norms = O.qjl_sketch(k, S)
+    q = rng.standard_normal((G, nq, d)).astype(np.float16)
+    w, n, Sd = up(words.reshape(G, T, m // 32)), up(norms.reshape(G, T)), up(S)
+    grouped = down(K.scores_qjl(up(q), Sd, w, n))
+    for j in range(nq):
+        alone = down(K.scores_qjl(up(np.ascontiguousarray(q[:, j:j + 1])), Sd, w, n))
+        assert np.array_equal(grouped[:, j:j + 1].view(np.uint32), alone.view(np.uint32)), j
