@@ -28,7 +28,9 @@ Readings taken where the passage is open
 * Storage: codes two per byte, the even-indexed value of a pair in the low
   nibble (LSB-first, as the QJL sign bits); steps and offsets binary32,
   [rows, d / g] each.
-* Non-finite input is outside the domain: the reference raises.
+* Non-finite input is outside the domain, and so is a group whose range
+  max - min overflows binary32 (its step would be infinite): the reference
+  raises for both.
 
 Why fp64 gives the binary32 results exactly: every operand is binary32 (or
 binary16 widened exactly); one fp64 operation followed by a cast to binary32
@@ -66,7 +68,10 @@ def group_params(x: np.ndarray, g: int) -> tuple[np.ndarray, np.ndarray]:
     grp = xw.reshape(R, d // g, g)
     mx = grp.max(axis=2)
     mn = grp.min(axis=2)
-    rng = (mx - mn).astype(np.float32)                       # RN32(max - min)
+    with np.errstate(over="ignore"):
+        rng = (mx - mn).astype(np.float32)                   # RN32(max - min)
+    if not np.all(np.isfinite(rng)):
+        raise ValueError("a group's range max - min overflows binary32")
     s = (rng.astype(np.float64) / LEVELS).astype(np.float32)  # RN32(range / 15)
     z = mn.astype(np.float32)                                 # exact
     return s, z

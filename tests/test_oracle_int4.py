@@ -131,6 +131,8 @@ def test_rejects_bad_groups_and_inputs():
         O.quantize_int4(np.zeros((1, 48), np.float32), 8)
     with pytest.raises(ValueError):
         O.quantize_int4(np.array([[np.nan] * 16], np.float32), 16)
+    with pytest.raises(ValueError):
+        O.quantize_int4(np.linspace(3e38, -3e38, 16, dtype=np.float32)[None, :], 16)
 
 
 def test_storage_bits():
