@@ -111,7 +111,7 @@ COLD_BYTES = 1 << 30     # rotate inputs over > 1 GiB: 4x the 256 MB last-level 
 
 
 def components(K, si, torch, np):
-    """GB/s of the INT8 and QJL kernels on their own workloads, cold: each
+    """GB/s of the INT8, INT4 and QJL kernels on their own workloads, cold: each
     timed call reads a different copy of its inputs, and the copies together
     exceed 1 GiB, so no call finds its inputs in the MALL or L2.  Calls run
     back to back in blocks timed by one pair of HIP events; the median block's
@@ -150,6 +150,15 @@ def components(K, si, torch, np):
             gbs(f"dequantize_f32_2^{nlog}_d{d}", n + 4 * rows + 4 * n,
                 [lambda c=c: K.dequantize_int8(c[0], c[1]) for c in cs])
             del cs
+            if d == 128:
+                # asymmetric group-wise INT4, groups of 32 and 128
+                for g in (32, 128):
+                    c4 = [K.quantize_int4(v, g) for v in views]
+                    gbs(f"quantize_int4_f32_2^{nlog}_d{d}_g{g}", 4 * n + n // 2 + 8 * (n // g),
+                        [lambda v=v: K.quantize_int4(v, g) for v in views])
+                    gbs(f"dequantize_int4_f32_2^{nlog}_d{d}_g{g}", n // 2 + 8 * (n // g) + 4 * n,
+                        [lambda c=c: K.dequantize_int4(c[0], c[1], c[2], g) for c in c4])
+                    del c4
         del x, xs
         torch.cuda.empty_cache()
 
@@ -166,6 +175,13 @@ def components(K, si, torch, np):
         [lambda t=t: K.quantize_int8(t) for t in kvs])
     gbs("llama_layer_dequantize_kv_f16", R * 128 + 4 * R + 2 * R * 128,
         [lambda c=c: K.dequantize_int8(c[0], c[1], torch.float16) for c in cs])
+    for g in (32, 128):
+        c4 = [K.quantize_int4(t, g) for t in kvs]
+        gbs(f"llama_layer_quantize_int4_kv_f16_g{g}", 2 * R * 128 + R * 64 + 8 * R * (128 // g),
+            [lambda t=t: K.quantize_int4(t, g) for t in kvs])
+        gbs(f"llama_layer_dequantize_int4_kv_f16_g{g}", R * 64 + 8 * R * (128 // g) + 2 * R * 128,
+            [lambda c=c: K.dequantize_int4(c[0], c[1], c[2], g, torch.float16) for c in c4])
+        del c4
     q = torch.from_numpy(si.queries(W, 32, 1, 128, "f16")).to(dev)
     halves = [(c[0][: R // 2].view(32, 4096, 128), c[1][: R // 2].view(32, 4096)) for c in cs]
     gbs("llama_layer_scores_int8", 32 * 4096 * (128 + 4 + 4) + 32 * 128 * 2,

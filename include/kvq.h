@@ -1,7 +1,8 @@
 /*
  * kvq.h - C ABI of libkvq, a KV-cache compressor for AMD Instinct MI355X
- * (gfx950): per-row symmetric INT8 quantization and the QJL key sketch, with
- * decode-time scoring and attention read straight from the compressed cache.
+ * (gfx950): per-row symmetric INT8 quantization, asymmetric group-wise INT4
+ * quantization and the QJL key sketch, with decode-time scoring and attention
+ * read straight from the compressed cache.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -13,9 +14,10 @@
  * - Layouts are row-major and contiguous.  A [B, H, T, d] cache is flattened
  *   to rows = B*H*T (one row = one token of one head, d contiguous values)
  *   and groups = B*H with T rows each.
- * - Element types: KVQ_F32 = IEEE binary32, KVQ_F16 = IEEE binary16.  Codes
- *   are int8, scales binary32, sign words uint32, norms binary16 stored as
- *   uint16 bit patterns.
+ * - Element types: KVQ_F32 = IEEE binary32, KVQ_F16 = IEEE binary16.  INT8
+ *   codes are int8, INT4 codes two per uint8, scales / steps / offsets
+ *   binary32, sign words uint32, norms binary16 stored as uint16 bit
+ *   patterns.
  * - Validation happens on the host before any HIP call and returns a status
  *   (never aborts, never throws); kvq_last_error() then describes the
  *   failure.  rows == 0 (or groups == 0 or T == 0) is a successful no-op.
@@ -111,6 +113,49 @@ kvq_status kvq_dequantize_int8(const int8_t* codes, const float* scales, int64_t
 kvq_status kvq_scores_int8(const void* q, kvq_dtype q_dt, int64_t groups, int32_t nq,
                            const int8_t* codes, const float* scales, int64_t T, int32_t d,
                            float* scores, kvq_stream_t stream);
+
+/*
+ * kvq_quantize_int4 - asymmetric group-wise INT4 quantization.
+ *
+ * Defined by the asymmetric group-wise INT4 formula of the Q-TensorFormer
+ * model card (section 6, "Adaptive KV Cache Quantization & Attention-Sink
+ * Eviction"): step = (max - min) / 15 and offset = min over a group; code =
+ * nearest integer of (x - offset) / step, clamped to [0, 15].  A group is g
+ * consecutive values of one row; row r has d / g groups.  For group (r, j):
+ *   z_rj = min of the group                      (exact)
+ *   s_rj = RN32(RN32(max - z_rj) / 15)           (IEEE binary32)
+ *   c_ri = clamp(rne(RN32(RN32(x_ri - z_rj) / s_rj)), 0, 15)
+ * with rne = round to nearest integer, ties to even.  A group whose s is +0
+ * gets all-zero codes.  Codes, steps and offsets are bit-identical to this
+ * definition, except that the sign of a zero offset is unspecified.  A group
+ * whose max - min overflows binary32 is outside the domain (its results are
+ * unspecified), as is non-finite input.
+ *
+ * x        [rows, d] KVQ_F32 or KVQ_F16 (x_dt)
+ * codes    [rows, d / 2] uint8, written: value 2i in the low nibble of
+ *          byte i, value 2i + 1 in the high nibble
+ * steps    [rows, d / g] binary32, written
+ * offsets  [rows, d / g] binary32, written
+ * d as for kvq_quantize_int8; 16 <= g, g % 16 == 0, d % g == 0.
+ * Errors: NULL, ALIGN, SHAPE (rows < 0, d or g outside the range), DTYPE.
+ */
+kvq_status kvq_quantize_int4(const void* x, kvq_dtype x_dt, int64_t rows, int32_t d, int32_t g,
+                             uint8_t* codes, float* steps, float* offsets, kvq_stream_t stream);
+
+/*
+ * kvq_dequantize_int4 - reconstruction of INT4-quantized rows.
+ *
+ * Same source as kvq_quantize_int4 (code times step plus offset), rounded
+ * twice, never fused: out_ri = RN32(RN32(c_ri * s_rj) + z_rj); for KVQ_F16
+ * output, RN16 of that binary32 value.  Bit-exact.
+ *
+ * codes, steps, offsets as written by kvq_quantize_int4 for the same d, g
+ * out    [rows, d] KVQ_F32 or KVQ_F16 (out_dt), written
+ * Errors: NULL, ALIGN, SHAPE, DTYPE.
+ */
+kvq_status kvq_dequantize_int4(const uint8_t* codes, const float* steps, const float* offsets,
+                               int64_t rows, int32_t d, int32_t g, void* out, kvq_dtype out_dt,
+                               kvq_stream_t stream);
 
 /*
  * kvq_qjl_sketch - QJL sketch of key rows: sign bits of a JL projection plus

@@ -1,7 +1,8 @@
 """kv_cache_compression_kvq_amd: KV-cache compression for AMD Instinct MI355X.
 
-Per-row symmetric INT8 quantization and the QJL key sketch, with decode-time
-scoring and attention over the compressed cache, implemented as hand-written
+Per-row symmetric INT8 quantization, asymmetric group-wise INT4 quantization
+and the QJL key sketch, with decode-time scoring and attention over the
+compressed cache, implemented as hand-written
 gfx950 HIP kernels behind the C ABI of ``include/kvq.h`` (``libkvq.so``).
 This package is the thin Python binding: torch supplies device memory and
 streams; every step of the computation runs in libkvq.
@@ -11,8 +12,10 @@ from .ops import (  # noqa: F401
     cache_append,
     decode_qjl_int8,
     decode_workspace_bytes,
+    dequantize_int4,
     dequantize_int8,
     qjl_sketch,
+    quantize_int4,
     quantize_int8,
     scores_int8,
     scores_qjl,

@@ -80,6 +80,13 @@ kvq_status device_info(const char* fn, kvq::DeviceInfo* info) {
   return KVQ_OK;
 }
 
+kvq_status check_group(const char* fn, int32_t d, int32_t g) {
+  if (g < 16 || g % 16 != 0 || d % g != 0)
+    return fail(KVQ_ERR_SHAPE, "%s: g = %d must be a multiple of 16 that divides d = %d", fn,
+                (int)g, (int)d);
+  return KVQ_OK;
+}
+
 }  // namespace
 
 namespace kvq {
@@ -171,6 +178,40 @@ kvq_status kvq_scores_int8(const void* q, kvq_dtype q_dt, int64_t groups, int32_
   KVQ_CHECK_PTR(scores);
   return launched(fn, kvq::launch_scores_int8(q, q_dt == KVQ_F16, groups, nq, codes, scales, T, d,
                                               scores, reinterpret_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_quantize_int4(const void* x, kvq_dtype x_dt, int64_t rows, int32_t d, int32_t g,
+                             uint8_t* codes, float* steps, float* offsets, kvq_stream_t stream) {
+  const char* fn = "kvq_quantize_int4";
+  kvq_status st;
+  if ((st = check_count(fn, "rows", rows)) || (st = check_d(fn, d)) ||
+      (st = check_group(fn, d, g)) || (st = check_dtype(fn, "x_dt", x_dt)))
+    return st;
+  if (rows == 0) return ok();
+  KVQ_CHECK_PTR(x);
+  KVQ_CHECK_PTR(codes);
+  KVQ_CHECK_PTR(steps);
+  KVQ_CHECK_PTR(offsets);
+  return launched(fn, kvq::launch_quantize_int4(x, x_dt == KVQ_F16, rows, d, g, codes, steps,
+                                                offsets, reinterpret_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_dequantize_int4(const uint8_t* codes, const float* steps, const float* offsets,
+                               int64_t rows, int32_t d, int32_t g, void* out, kvq_dtype out_dt,
+                               kvq_stream_t stream) {
+  const char* fn = "kvq_dequantize_int4";
+  kvq_status st;
+  if ((st = check_count(fn, "rows", rows)) || (st = check_d(fn, d)) ||
+      (st = check_group(fn, d, g)) || (st = check_dtype(fn, "out_dt", out_dt)))
+    return st;
+  if (rows == 0) return ok();
+  KVQ_CHECK_PTR(codes);
+  KVQ_CHECK_PTR(steps);
+  KVQ_CHECK_PTR(offsets);
+  KVQ_CHECK_PTR(out);
+  return launched(fn, kvq::launch_dequantize_int4(codes, steps, offsets, rows, d, g, out,
+                                                  out_dt == KVQ_F16,
+                                                  reinterpret_cast<hipStream_t>(stream)));
 }
 
 kvq_status kvq_qjl_sketch(const void* k, kvq_dtype k_dt, int64_t rows, int32_t d, const void* S,

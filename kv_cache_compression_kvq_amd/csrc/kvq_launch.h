@@ -25,6 +25,11 @@ hipError_t launch_dequantize_int8(const int8_t* codes, const float* scales, int6
 hipError_t launch_scores_int8(const void* q, int q_f16, int64_t groups, int nq,
                               const int8_t* codes, const float* scales, int64_t T, int d,
                               float* scores, hipStream_t s);
+hipError_t launch_quantize_int4(const void* x, int x_f16, int64_t rows, int d, int g,
+                                uint8_t* codes, float* steps, float* offsets, hipStream_t s);
+hipError_t launch_dequantize_int4(const uint8_t* codes, const float* steps, const float* offsets,
+                                  int64_t rows, int d, int g, void* out, int out_f16,
+                                  hipStream_t s);
 hipError_t launch_qjl_sketch(const void* k, int k_f16, int64_t rows, int d, const void* S, int m,
                              uint32_t* bits, uint16_t* norms, const DeviceInfo& dev, hipStream_t s);
 hipError_t launch_scores_qjl(const void* q, int q_f16, int64_t groups, int nq, const void* S,

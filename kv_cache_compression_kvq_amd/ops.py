@@ -67,6 +67,38 @@ def dequantize_int8(codes: torch.Tensor, scales: torch.Tensor,
     return out
 
 
+def quantize_int4(x: torch.Tensor, g: int) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """x [..., d] fp32/fp16, group size g -> (codes uint8 [..., d/2] two per
+    byte, steps fp32 [..., d/g], offsets fp32 [..., d/g])."""
+    _dev(x, "x")
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    ng = d // g if g > 0 else 0
+    codes = torch.empty((*x.shape[:-1], d // 2), dtype=torch.uint8, device=x.device)
+    steps = torch.empty((*x.shape[:-1], ng), dtype=torch.float32, device=x.device)
+    offsets = torch.empty((*x.shape[:-1], ng), dtype=torch.float32, device=x.device)
+    L.check(L.lib().kvq_quantize_int4(_p(x), _dtype_code(x, "x"), rows, d, g, _p(codes), _p(steps),
+                                      _p(offsets), _stream(x)))
+    return codes, steps, offsets
+
+
+def dequantize_int4(codes: torch.Tensor, steps: torch.Tensor, offsets: torch.Tensor, g: int,
+                    out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """codes uint8 [..., d/2], steps / offsets fp32 [..., d/g] -> [..., d]."""
+    _dev(codes, "codes"), _dev(steps, "steps"), _dev(offsets, "offsets")
+    if codes.dtype != torch.uint8 or steps.dtype != torch.float32 or offsets.dtype != torch.float32:
+        raise TypeError("codes must be uint8, steps and offsets float32")
+    d = 2 * codes.shape[-1]
+    rows = codes.numel() * 2 // d if d else 0
+    if g <= 0 or d % g != 0 or steps.shape != offsets.shape or steps.numel() != rows * (d // g):
+        raise ValueError(f"shape mismatch: codes {tuple(codes.shape)}, g {g}, "
+                         f"steps {tuple(steps.shape)}, offsets {tuple(offsets.shape)}")
+    out = torch.empty((*codes.shape[:-1], d), dtype=out_dtype, device=codes.device)
+    L.check(L.lib().kvq_dequantize_int4(_p(codes), _p(steps), _p(offsets), rows, d, g, _p(out),
+                                        _dtype_code(out, "out_dtype"), _stream(codes)))
+    return out
+
+
 def scores_int8(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
     """q [G, nq, d]; codes [G, T, d] int8; scales [G, T] -> scores [G, nq, T] fp32."""
     _dev(q, "q"), _dev(codes, "codes"), _dev(scales, "scales")

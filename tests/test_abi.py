@@ -76,6 +76,25 @@ def test_dequantize_validation():
     assert f(None, None, 0, 128, None, L.KVQ_F32, None) == L.KVQ_OK
 
 
+def test_int4_validation():
+    q = L.lib().kvq_quantize_int4
+    _err(q(None, L.KVQ_F32, 4, 128, 32, A, A, A, None), L.KVQ_ERR_NULL)
+    _err(q(A, L.KVQ_F32, 4, 128, 32, A, A, None, None), L.KVQ_ERR_NULL)
+    _err(q(A, L.KVQ_F32, 4, 128, 32, A, MIS, A, None), L.KVQ_ERR_ALIGN)
+    _err(q(A, L.KVQ_F32, -1, 128, 32, A, A, A, None), L.KVQ_ERR_SHAPE)
+    for g in (0, 8, 24, 48, 256, -32):      # not a multiple of 16 dividing 128
+        _err(q(A, L.KVQ_F32, 4, 128, g, A, A, A, None), L.KVQ_ERR_SHAPE)
+    _err(q(A, L.KVQ_F32, 4, 100, 20, A, A, A, None), L.KVQ_ERR_SHAPE)
+    _err(q(A, 2, 4, 128, 32, A, A, A, None), L.KVQ_ERR_DTYPE)
+    assert q(None, L.KVQ_F16, 0, 96, 48, None, None, None, None) == L.KVQ_OK
+    dq = L.lib().kvq_dequantize_int4
+    _err(dq(A, A, None, 4, 128, 32, A, L.KVQ_F32, None), L.KVQ_ERR_NULL)
+    _err(dq(A, A, A, 4, 128, 32, MIS, L.KVQ_F32, None), L.KVQ_ERR_ALIGN)
+    _err(dq(A, A, A, 4, 128, 40, A, L.KVQ_F32, None), L.KVQ_ERR_SHAPE)
+    _err(dq(A, A, A, 4, 128, 32, A, 3, None), L.KVQ_ERR_DTYPE)
+    assert dq(None, None, None, 0, 128, 32, None, L.KVQ_F16, None) == L.KVQ_OK
+
+
 def test_scores_int8_validation():
     f = L.lib().kvq_scores_int8
     _err(f(A, L.KVQ_F16, 2, 0, A, A, 16, 128, A, None), L.KVQ_ERR_SHAPE)

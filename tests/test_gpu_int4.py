@@ -1,0 +1,174 @@
+"""GPU parity of the asymmetric group-wise INT4 path against the oracle:
+codes (bytes), steps and dequantised values bit-exact, offsets equal (the
+sign of a zero offset aside).  Every call goes through the C ABI
+(libkvq.so)."""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_kvq_amd as K
+import synth_inputs as si
+from oracle import int4 as O
+from gpu_common import down, log, up
+
+pytestmark = pytest.mark.gpu
+
+
+def _cmp_offsets(zg: np.ndarray, zo: np.ndarray, label: str):
+    assert np.array_equal(zg, zo), f"{label}: offsets differ"
+    nz = zo != 0
+    assert np.array_equal(zg[nz].view(np.uint32), zo[nz].view(np.uint32)), f"{label}: offset bits differ"
+
+
+def roundtrip_check(x: np.ndarray, g: int, label: str):
+    """Quantize + dequantize x [R, d] with group g on the GPU; compare with
+    the oracle bit-exactly (both output types of the dequantizer)."""
+    log(f"[int4] {label}: x {x.shape} {x.dtype} g={g}")
+    cg_t, sg_t, zg_t = K.quantize_int4(up(x), g)
+    co, so, zo = O.quantize_int4(x, g)
+    cg, sg, zg = down(cg_t), down(sg_t), down(zg_t)
+    assert np.array_equal(sg.view(np.uint32), so.view(np.uint32)), f"{label}: steps differ"
+    _cmp_offsets(zg, zo, label)
+    if not np.array_equal(cg, co):
+        r, c = np.nonzero(cg != co)
+        raise AssertionError(f"{label}: {len(r)} code bytes differ, first at row {r[0]} byte {c[0]}: "
+                             f"x={x[r[0], 2 * c[0]:2 * c[0] + 2]!r} gpu={cg[r[0], c[0]]:#04x} "
+                             f"oracle={co[r[0], c[0]]:#04x}")
+    for out_dt, name, u in ((torch.float32, "f32", np.uint32), (torch.float16, "f16", np.uint16)):
+        dg = down(K.dequantize_int4(cg_t, sg_t, zg_t, g, out_dt))
+        do = O.dequantize_int4(co, so, zo, g, name)
+        assert np.array_equal(dg.view(u), do.view(u)), f"{label}: {name} reconstruction differs"
+    return co, so, zo
+
+
+# --- Llama-7B-shaped layer: 32 heads x 4096 tokens x 128, fp16, outliers --------
+
+@pytest.mark.parametrize("g", [32, 128])
+def test_llama_layer_full_size(g):
+    W = si.W_LLAMA_LAYER
+    k = si.kv_tensor(W, si.K, 1, 32, 4096, 128, "f16", outliers=True)
+    v = si.kv_tensor(W, si.V, 1, 32, 4096, 128, "f16")
+    roundtrip_check(k.reshape(-1, 128), g, "llama K")
+    roundtrip_check(v.reshape(-1, 128), g, "llama V")
+
+
+# --- element-count sweep ---------------------------------------------------------
+
+@pytest.mark.parametrize("g", [16, 32, 64, 128])
+@pytest.mark.parametrize("d", [128, 1024])
+def test_sweep_2p24_full_compare(d, g):
+    x = si.flat_rows(si.W_SWEEP, 1 << 24, d)
+    roundtrip_check(x, g, f"sweep 2^24 d={d}")
+
+
+def test_sweep_2p28_sampled():
+    """2^28 fp32 elements, d = 128, g = 32: every group is quantized on the
+    GPU; 4096 sampled rows plus the first and last are compared bit-exactly
+    with the oracle; on every group the minimum code is 0 and the maximum 15
+    (or the step is 0), checked on the device."""
+    n, d, g = 1 << 28, 128, 32
+    x_host = si.flat_rows(si.W_SWEEP, n, d)
+    x = up(x_host)
+    rows = n // d
+    codes, steps, offsets = K.quantize_int4(x, g)
+    deq = K.dequantize_int4(codes, steps, offsets, g)
+    rng = np.random.default_rng(28)
+    sample = np.unique(np.concatenate([[0, rows - 1], rng.integers(0, rows, 4096)]))
+    idx = torch.from_numpy(sample).to(x.device)
+    co, so, zo = O.quantize_int4(x_host[sample], g)
+    assert np.array_equal(down(codes.index_select(0, idx)), co)
+    assert np.array_equal(down(steps.index_select(0, idx)).view(np.uint32), so.view(np.uint32))
+    _cmp_offsets(down(offsets.index_select(0, idx)), zo, "2^28 sample")
+    do = O.dequantize_int4(co, so, zo, g)
+    assert np.array_equal(down(deq.index_select(0, idx)).view(np.uint32), do.view(np.uint32))
+    lo = (codes & 0xF).to(torch.int32)
+    hi = (codes >> 4).to(torch.int32)
+    both = torch.stack([lo, hi], dim=-1).reshape(rows, d // g, g)
+    live = steps != 0
+    assert bool((both.amin(dim=2)[live] == 0).all()) and bool((both.amax(dim=2)[live] == 15).all())
+    err = (x - deq).abs().reshape(rows, d // g, g).amax(dim=2)
+    assert bool((err <= steps * 0.50001 + 1e-6 * x.abs().reshape(rows, d // g, g).amax(dim=2)).all())
+    log(f"[int4] 2^28: max|x-x_hat| {float(err.max()):.4g}")
+
+
+# --- edge cases -------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("d,g", [(16, 16), (32, 16), (48, 48), (48, 16), (96, 32), (128, 64),
+                                 (256, 256), (1024, 1024), (2048, 2048), (4096, 4096),
+                                 (1040, 80), (1040, 16), (8192, 512), (160, 160)])
+def test_shapes_and_ragged_rows(dtype, d, g):
+    rng = np.random.default_rng(d * 7 + g)
+    for rows in (1, 3, 63, 129, 1000):
+        x = rng.standard_normal((rows, d)).astype(np.float32)
+        x *= np.exp(rng.uniform(-8, 8, (rows, 1))).astype(np.float32)
+        x += rng.uniform(-4, 4, (rows, 1)).astype(np.float32) * np.abs(x).max(axis=1, keepdims=True)
+        if dtype == "f16":
+            x = np.clip(x, -6e4, 6e4).astype(np.float16)
+        roundtrip_check(x, g, f"{dtype} d={d} g={g} rows={rows}")
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float16])
+def test_special_groups(dtype):
+    g = 16
+    groups = [np.zeros(g), -np.zeros(g), np.full(g, 0.3), np.full(g, -7.25)]
+    z = np.zeros(g); z[5] = -0.0; z[9] = 1.0; groups.append(z)            # +-0 with a positive max
+    z = np.zeros(g); z[3] = 1e4 if dtype == np.float16 else 1e30; groups.append(z)  # one spike
+    groups.append(np.arange(g, dtype=np.float64))                          # steps of 1 exactly
+    groups.append(np.arange(g) * 0.5 + 0.25)                               # ties everywhere
+    groups.append(np.array([0, 15] + [k + 0.5 for k in range(14)]))        # x.5 quotients
+    groups.append(-np.arange(g, dtype=np.float64) - 100)                   # negative only
+    if dtype == np.float32:
+        z = np.zeros(g); z[0] = 2.0 ** -149; groups.append(z)             # step underflows to 0
+        z = np.zeros(g); z[0] = 2.0 ** -130; z[1] = -2.0 ** -131; groups.append(z)  # subnormal step
+        groups.append(np.linspace(-1e-38, 1e-38, g))                       # subnormal inputs
+        groups.append(np.linspace(1.6e38, -1.6e38, g))                     # range near the top
+    else:
+        z = np.zeros(g); z[0] = 2.0 ** -24; groups.append(z)              # smallest fp16 subnormal
+        groups.append(np.linspace(-65504, 65504, g))
+    x = np.concatenate(groups).astype(dtype).reshape(1, -1)
+    # also as many short rows of one group each
+    roundtrip_check(x, g, f"special groups {np.dtype(dtype).name}")
+    roundtrip_check(x.reshape(-1, g), g, f"special groups as rows {np.dtype(dtype).name}")
+
+
+def test_exhaustive_fp16_values():
+    """Every finite binary16 value inside groups of 64 whose range is set by
+    the extremes 0 and 65504, or by -1 and 1."""
+    allf = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    allf = allf[np.isfinite(allf)]
+    pad = (-len(allf)) % 62
+    vals = np.concatenate([allf, np.zeros(pad, np.float16)]).reshape(-1, 62)
+    a = np.abs(vals)
+    big = np.concatenate([np.zeros((len(vals), 1), np.float16), a,
+                          np.full((len(vals), 1), 65504, np.float16)], axis=1)
+    roundtrip_check(big, 64, "all |fp16| values, range [0, 65504]")
+    small = np.where(np.abs(vals.astype(np.float32)) <= 1.0, vals, np.float16(0.5))
+    small = np.concatenate([np.full((len(vals), 1), -1, np.float16), small,
+                            np.ones((len(vals), 1), np.float16)], axis=1)
+    roundtrip_check(small, 64, "all fp16 values in [-1, 1]")
+
+
+def test_near_tie_quotients():
+    """Groups where (x - z) / s lands within a few ulps of half-integers."""
+    rng = np.random.default_rng(44)
+    R, g = 4096, 32
+    z = rng.standard_normal(R).astype(np.float32)
+    s = (np.abs(rng.standard_normal(R)) * 10.0 ** rng.integers(-4, 4, R) + 1e-6).astype(np.float32)
+    top = (z.astype(np.float64) + 15.0 * s).astype(np.float32)
+    k = rng.integers(0, 15, (R, g)) + 0.5
+    base = (z.astype(np.float64)[:, None] + k * s.astype(np.float64)[:, None]).astype(np.float32)
+    nudge = rng.integers(-2, 3, (R, g)).astype(np.int32)
+    x = (base.view(np.int32) + nudge * np.sign(base).astype(np.int32)).view(np.float32)
+    x = np.clip(x, z[:, None], top[:, None])
+    x[:, 0] = z
+    x[:, 1] = top
+    roundtrip_check(x.astype(np.float32), g, "near ties")
+
+
+def test_empty_input_is_a_noop():
+    x = torch.empty((0, 128), dtype=torch.float16, device="cuda")
+    c, s, z = K.quantize_int4(x, 32)
+    assert c.shape == (0, 64) and s.shape == (0, 4) and z.shape == (0, 4)
+    out = K.dequantize_int4(c, s, z, 32, torch.float16)
+    assert out.shape == (0, 128)
