@@ -8,7 +8,9 @@
 //
 // Arithmetic: s = a / 127 and t = x / s are IEEE binary32 divisions (the
 // compiler's correctly rounded sequence; no fast-math, denormals kept);
-// rint rounds half to even; the clamp is a med3.
+// rint rounds half to even; the clamp is a med3.  The quantizers multiply by
+// a reciprocal and divide only where the quotient's rounding could change a
+// code (encode_chunk below): the codes are those of the division.
 //
 // Memory: all three kernels are HBM streams.  Lanes are mapped so that each
 // load instruction of a wave reads 1 KiB of contiguous memory (16 B per
@@ -34,22 +36,43 @@ template <> struct Chunk<_Float16> {
   using Codes = u32x2;                 // 8 codes
 };
 
+// Codes of one chunk: rint(RN32(x / s)) clamped to [-128, 127].  For s in
+// [2^-120, 2^120], q = RN32(x * rcp(s)) (v_rcp_f32: within 1 ulp) differs
+// from RN32(x / s) by at most 127 * (2^-23 + 2^-24) + 2^-18 < 2.7e-5
+// (|x / s| <= 127 + 2^-16), so both round to the same integer unless q lies
+// within 2^-14 of a half-integer; lanes with such a q, or rows whose scale
+// is outside the range, divide.
 template <typename T>
 __device__ __forceinline__ typename Chunk<T>::Codes encode_chunk(const typename Chunk<T>::V& v,
                                                                  float sdiv) {
-  if constexpr (Chunk<T>::N == 4) {
-    uint32_t c0 = code_of(v[0], sdiv), c1 = code_of(v[1], sdiv);
-    uint32_t c2 = code_of(v[2], sdiv), c3 = code_of(v[3], sdiv);
-    return c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
-  } else {
-    u32x2 out;
+  constexpr int N = Chunk<T>::N;
+  const float r = __builtin_amdgcn_rcpf(sdiv);
+  bool near = !(sdiv >= 0x1p-120f && sdiv <= 0x1p120f);
+  float c[N];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint32_t c0 = code_of((float)v[4 * h + 0], sdiv), c1 = code_of((float)v[4 * h + 1], sdiv);
-      uint32_t c2 = code_of((float)v[4 * h + 2], sdiv), c3 = code_of((float)v[4 * h + 3], sdiv);
-      out[h] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
-    }
-    return out;
+  for (int e = 0; e < N; ++e) {
+    const float q = (float)v[e] * r;
+    c[e] = __builtin_rintf(q);
+    near |= __builtin_fabsf(q - c[e]) > 0.5f - 0x1p-14f;
+  }
+  if (near) {
+    // (an opaque statement keeps the divisions behind the branch)
+    __asm__ volatile("");
+#pragma unroll
+    for (int e = 0; e < N; ++e) c[e] = __builtin_rintf((float)v[e] / sdiv);
+  }
+  uint32_t w[N / 4];
+#pragma unroll
+  for (int h = 0; h < N / 4; ++h) {
+    w[h] = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[h] |= ((uint32_t)(int)__builtin_amdgcn_fmed3f(c[4 * h + e], -128.0f, 127.0f) & 0xFFu) << (8 * e);
+  }
+  if constexpr (N == 4) {
+    return w[0];
+  } else {
+    return u32x2{w[0], w[1]};
   }
 }
 
