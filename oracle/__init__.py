@@ -18,9 +18,10 @@ qjl     QJL key sketch (JL projection, sign bits, key norm) and the
 decode  one decode step over a QJL-key / INT8-value cache: scores, softmax,
         weighted sum of dequantised values
 int4    asymmetric group-wise INT4 quantize / dequantize
+residual  QJL sketch of the INT4 residual and the two-stage score
 
 Every function is pinned by CPU tests (``tests/test_oracle_*.py``) against
 exact rational arithmetic, brute force on tiny inputs, closed forms and
 hand-derived fixtures; none is "parity unpinned".
 """
-from . import int8, int4, qjl, decode  # noqa: F401
+from . import int8, int4, qjl, decode, residual  # noqa: F401
