@@ -206,6 +206,35 @@ kvq_status kvq_scores_qjl(const void* q, kvq_dtype q_dt, int64_t groups, int32_t
                           kvq_stream_t stream);
 
 /*
+ * kvq_residual_sketch - two-stage key compression: INT4, then the QJL sketch
+ * of the INT4 residual.
+ *
+ * From the TurboQuant news item (after ArsTechnica: a first quantizer whose
+ * residual error a 1-bit QJL layer corrects), with the asymmetric group-wise
+ * INT4 formula of the Q-TensorFormer model card (section 6) as the first
+ * stage and the QJL sketch (arXiv 2406.03482, abstract) as the second.  For
+ * each row k_r of k [rows, d]:
+ *   codes, steps, offsets  exactly as kvq_quantize_int4 (bit-identical)
+ *   khat_ri = RN32(RN32(c_ri * s) + z),  r_ri = RN32(k_ri - khat_ri)
+ *   bit i   = [sum_j S_ij r_rj >= 0]   (LSB-first words, as kvq_qjl_sketch)
+ *   norm    = RN16(||r_r||)
+ * A bit may differ from the exact sign only where |sum_j S_ij r_rj| <=
+ * 1e-4 * ||S_i|| * ||r_r||; a norm may differ from RN16 of the exact norm by
+ * one binary16 ulp.  A row with r = 0 gets all bits 1 and norm 0.
+ *
+ * k        [rows, d] (k_dt);  S [m, d] (S_dt)
+ * codes    [rows, d / 2] uint8;  steps, offsets [rows, d / g] binary32
+ * bits     [rows, m / 32] uint32;  norms [rows] binary16 patterns; all written
+ * 16 <= d <= 1024, d % 16 == 0; g as for kvq_quantize_int4; m as for
+ * kvq_qjl_sketch.
+ * Errors: NULL, ALIGN, SHAPE, DTYPE, LAUNCH.
+ */
+kvq_status kvq_residual_sketch(const void* k, kvq_dtype k_dt, int64_t rows, int32_t d, int32_t g,
+                               const void* S, kvq_dtype S_dt, int32_t m, uint8_t* codes,
+                               float* steps, float* offsets, uint32_t* bits, uint16_t* norms,
+                               kvq_stream_t stream);
+
+/*
  * kvq_decode_workspace_bytes - size of the scratch buffer kvq_decode_qjl_int8
  * needs for `groups` groups of T tokens, head dimension d and sketch size m
  * (0 for invalid arguments).  It holds the projected queries S q (groups * m

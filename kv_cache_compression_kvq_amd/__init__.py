@@ -15,6 +15,7 @@ from .ops import (  # noqa: F401
     dequantize_int4,
     dequantize_int8,
     qjl_sketch,
+    residual_sketch,
     quantize_int4,
     quantize_int8,
     scores_int8,

@@ -20,6 +20,9 @@ KVQ_F32, KVQ_F16 = 0, 1
 PROTOTYPES = {
     "kvq_quantize_int8": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
     "kvq_dequantize_int8": (c_int32, [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_int32, c_void_p]),
+    "kvq_residual_sketch": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_int32, c_void_p, c_int32,
+                                      c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_void_p]),
     "kvq_quantize_int4": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_int32, c_void_p, c_void_p,
                                     c_void_p, c_void_p]),
     "kvq_dequantize_int4": (c_int32, [c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_int32, c_void_p,

@@ -24,6 +24,7 @@
 // so every load instruction of a wave reads 1 KiB; group min/max are reduced
 // across the lanes of a group with DPP/swizzle moves, never through LDS.
 #include "kvq_device.h"
+#include "kvq_int4_device.h"
 #include "kvq_launch.h"
 
 #include <algorithm>
@@ -42,23 +43,6 @@ template <> struct In4<_Float16> {
   using Codes = uint32_t;          // 8 nibbles
 };
 
-template <int SEG>
-__device__ __forceinline__ float seg_min_f32(float v) {
-  if constexpr (SEG >= 2) v = __builtin_fminf(v, dpp_f32<kDppXor1>(v));
-  if constexpr (SEG >= 4) v = __builtin_fminf(v, dpp_f32<kDppXor2>(v));
-  if constexpr (SEG >= 8) v = __builtin_fminf(v, dpp_f32<kDppHalfMirror>(v));
-  if constexpr (SEG >= 16) v = __builtin_fminf(v, dpp_f32<kDppMirror>(v));
-  if constexpr (SEG >= 32) v = __builtin_fminf(v, swz_xor16_f32(v));
-  if constexpr (SEG >= 64) v = __builtin_fminf(v, xor32_f32(v));
-  return v;
-}
-
-// One code: rint(RN32(RN32(x - z) / sdiv)) in [0, 15].
-__device__ __forceinline__ uint32_t nibble_of(float x, float z, float sdiv) {
-  const float t = (x - z) / sdiv;
-  return (uint32_t)(int)__builtin_amdgcn_fmed3f(__builtin_rintf(t), 0.0f, 15.0f);
-}
-
 template <typename T>
 __device__ __forceinline__ typename In4<T>::Codes encode4(const typename In4<T>::V& v, float z,
                                                           float sdiv) {
@@ -68,42 +52,17 @@ __device__ __forceinline__ typename In4<T>::Codes encode4(const typename In4<T>:
   return (typename In4<T>::Codes)w;
 }
 
-// Whether q = t * rcp(s) may stand in for RN32(t / s): s in [2^-120, 2^120].
-__device__ __forceinline__ bool rcp_ok(float sdiv) {
-  return sdiv >= 0x1p-120f && sdiv <= 0x1p120f;
-}
-
-// Same codes as encode4 with one multiply per value instead of a division.
-// For s in [2^-120, 2^120], v_rcp_f32 is within 1 ulp, so q = RN32(t * r)
-// differs from RN32(t / s) by at most 15 * (2^-23 + 2^-24) + 2^-21 < 3.3e-6
-// (t / s <= 15 + 2^-19): both round to the same integer unless q lies
-// within 2^-16 of a half-integer.  Lanes with such a q (or a step outside
-// the range) divide, as encode4 does.
+// Same codes as encode4 with one multiply per value instead of a division
+// (codes_rcp).
 template <typename T>
 __device__ __forceinline__ typename In4<T>::Codes encode4_rcp(const typename In4<T>::V& v, float z,
                                                               float sdiv, float r, bool divide) {
   constexpr int N = In4<T>::N;
-  float t[N], c[N];
-  bool near = divide;
+  float x[N], c[N];
 #pragma unroll
-  for (int e = 0; e < N; ++e) {
-    t[e] = (float)v[e] - z;
-    const float q = t[e] * r;
-    c[e] = __builtin_rintf(q);
-    near |= __builtin_fabsf(q - c[e]) > 0.5f - 0x1p-16f;
-  }
-  if (near) {
-    // (an opaque statement keeps the divisions behind the branch instead of
-    // being computed for every lane and selected)
-    __asm__ volatile("");
-#pragma unroll
-    for (int e = 0; e < N; ++e) c[e] = __builtin_rintf(t[e] / sdiv);
-  }
-  uint32_t w = 0;
-#pragma unroll
-  for (int e = 0; e < N; ++e)
-    w |= (uint32_t)(int)__builtin_amdgcn_fmed3f(c[e], 0.0f, 15.0f) << (4 * e);
-  return (typename In4<T>::Codes)w;
+  for (int e = 0; e < N; ++e) x[e] = (float)v[e];
+  codes_rcp<N>(x, z, sdiv, r, divide, c);
+  return (typename In4<T>::Codes)pack_nibbles<N>(c);
 }
 
 template <typename T>
@@ -114,10 +73,6 @@ __device__ __forceinline__ void chunk_minmax(const typename In4<T>::V& v, float&
     mx = __builtin_fmaxf(mx, (float)v[e]);
   }
 }
-
-// Step and divisor from the group's min and max.
-__device__ __forceinline__ float group_step(float mn, float mx) { return (mx - mn) / 15.0f; }
-__device__ __forceinline__ float step_divisor(float s) { return (s == 0.0f) ? 1.0f : s; }
 
 // ---------------------------------------------------------------------------
 // Quantize, power-of-two groups: LPG lanes per group, CPL chunks per lane and
@@ -274,17 +229,11 @@ template <> struct Out4<_Float16> {
   using Codes = uint32_t;
 };
 
-// RN32(RN32(c * s) + z), kept as two roundings.
-__device__ __forceinline__ float recon4(uint32_t c, float s, float z) {
-#pragma clang fp contract(off)
-  return (float)c * s + z;
-}
-
 template <typename TO>
 __device__ __forceinline__ typename Out4<TO>::V decode4(uint32_t w, float s, float z) {
   typename Out4<TO>::V out;
 #pragma unroll
-  for (int e = 0; e < Out4<TO>::N; ++e) out[e] = (TO)recon4((w >> (4 * e)) & 0xFu, s, z);
+  for (int e = 0; e < Out4<TO>::N; ++e) out[e] = (TO)recon4((float)((w >> (4 * e)) & 0xFu), s, z);
   return out;
 }
 

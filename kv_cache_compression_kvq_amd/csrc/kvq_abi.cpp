@@ -214,6 +214,33 @@ kvq_status kvq_dequantize_int4(const uint8_t* codes, const float* steps, const f
                                                   reinterpret_cast<hipStream_t>(stream)));
 }
 
+kvq_status kvq_residual_sketch(const void* k, kvq_dtype k_dt, int64_t rows, int32_t d, int32_t g,
+                               const void* S, kvq_dtype S_dt, int32_t m, uint8_t* codes,
+                               float* steps, float* offsets, uint32_t* bits, uint16_t* norms,
+                               kvq_stream_t stream) {
+  const char* fn = "kvq_residual_sketch";
+  kvq_status st;
+  if ((st = check_count(fn, "rows", rows)) || (st = check_d(fn, d)) ||
+      (st = check_group(fn, d, g)) || (st = check_m(fn, m)) ||
+      (st = check_dtype(fn, "k_dt", k_dt)) || (st = check_dtype(fn, "S_dt", S_dt)))
+    return st;
+  if (d > kvq::kMaxDecodeD)
+    return fail(KVQ_ERR_SHAPE, "%s: d = %d exceeds %d", fn, (int)d, kvq::kMaxDecodeD);
+  if (rows == 0) return ok();
+  KVQ_CHECK_PTR(k);
+  KVQ_CHECK_PTR(S);
+  KVQ_CHECK_PTR(codes);
+  KVQ_CHECK_PTR(steps);
+  KVQ_CHECK_PTR(offsets);
+  KVQ_CHECK_PTR(bits);
+  KVQ_CHECK_PTR(norms);
+  kvq::DeviceInfo dev;
+  if ((st = device_info(fn, &dev))) return st;
+  return launched(fn, kvq::launch_residual_sketch(k, k_dt == KVQ_F16, rows, d, g, S, S_dt == KVQ_F16,
+                                                  m, codes, steps, offsets, bits, norms, dev,
+                                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
 kvq_status kvq_qjl_sketch(const void* k, kvq_dtype k_dt, int64_t rows, int32_t d, const void* S,
                           int32_t m, uint32_t* bits, uint16_t* norms, kvq_stream_t stream) {
   const char* fn = "kvq_qjl_sketch";

@@ -46,6 +46,15 @@ __device__ __forceinline__ float xor32_f32(float v) {
   return __builtin_bit_cast(float, (int)xor32_u32(__builtin_bit_cast(uint32_t, v)));
 }
 
+// Both halves' values of a 64-lane register: lo = the value of lane l % 32,
+// hi = that of lane 32 + l % 32, in every lane (v_permlane32_swap of the
+// register with itself; no LDS traffic).
+__device__ __forceinline__ void halves_u32(uint32_t v, uint32_t& lo, uint32_t& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  lo = r[0];
+  hi = r[1];
+}
+
 // Max over aligned segments of SEG lanes (power of two, <= 64); every lane
 // of a segment receives the segment's max.  All 64 lanes must be active.
 template <int SEG>

@@ -36,6 +36,11 @@ hipError_t launch_scores_qjl(const void* q, int q_f16, int64_t groups, int nq, c
                              int S_f16, int m, const uint32_t* bits, const uint16_t* norms,
                              int64_t T, int d, float* scores, const DeviceInfo& dev, hipStream_t s);
 
+hipError_t launch_residual_sketch(const void* k, int k_f16, int64_t rows, int d, int g,
+                                  const void* S, int S_f16, int m, uint8_t* codes, float* steps,
+                                  float* offsets, uint32_t* bits, uint16_t* norms,
+                                  const DeviceInfo& dev, hipStream_t s);
+
 // Token split of the decode kernel: tokens per split and number of splits.
 struct DecodeSplit {
   int64_t splits = 1;

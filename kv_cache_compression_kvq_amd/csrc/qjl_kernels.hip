@@ -54,15 +54,6 @@ template <int NT> constexpr int sketch_ring() { return NT == 1 ? 4 : 2; }
 // projection is +0 here (the accumulation starts from +0), so it gives bit 1.
 // Both halves of the wave return the token's full 32-bit word (the halves'
 // 16-bit parts are exchanged with v_permlane32_swap).
-// Both halves' values of a 64-lane register: lo = the value of lane l % 32,
-// hi = that of lane 32 + l % 32, in every lane (v_permlane32_swap of the
-// register with itself; no LDS traffic).
-__device__ __forceinline__ void halves_u32(uint32_t v, uint32_t& lo, uint32_t& hi) {
-  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  lo = r[0];
-  hi = r[1];
-}
-
 template <int KS, int NT>
 __device__ __forceinline__ void sketch_tile_words(const f16x8* sfrag, int mt, int lane,
                                                   const f16x8 (&b)[NT][KS], uint32_t (&full)[NT]) {

@@ -1,0 +1,361 @@
+// QJL on the residual of the INT4 quantizer: two-stage key compression and
+// its score, for gfx950.
+//
+// Method: the TurboQuant news item (after ArsTechnica) compresses in two
+// stages, a scalar first stage whose residual error a 1-bit QJL layer then
+// corrects, for a more accurate attention-score estimate; QJL (arXiv
+// 2406.03482, abstract) gives the sign sketch and the asymmetric estimator;
+// the first stage here is the asymmetric group-wise INT4 formula of the
+// Q-TensorFormer model card (section 6).  Per key row k:
+//   codes, step s, offset z per group      (as kvq_quantize_int4)
+//   k_hat = RN32(RN32(c * s) + z),  r = RN32(k - k_hat)
+//   bits = [S r >= 0] (LSB-first words),  n = RN16(||r||)
+// and per query q (y = S q):
+//   sigma = q . k_hat + sqrt(pi/2) / m * n * sum_i (2 b_i - 1) y_i.
+//
+// Sketch, fp16 keys and S, d = 128, m = 256: one fused pass.  A wave holds
+// 32 tokens as the B operand of v_mfma_f32_32x32x16_f16 (lane = token j,
+// half h: channels 16 ks + 8 h .. + 8), so a token's groups are reduced with
+// one v_permlane32_swap per min and max; the residual (binary32) is scaled
+// per token by a power of two (max |r| into [2^14, 2^15)) and split into two
+// binary16 parts hi + lo, which carry it to within 2^-24 relative; S r is
+// accumulated from both parts on the matrix cores (S fragments resident in
+// LDS, as in the plain sketch).  Other shapes: the INT4 quantizer, then one
+// thread per (row, sign word) with binary32 dot products.
+#include "kvq_device.h"
+#include "kvq_int4_device.h"
+#include "kvq_launch.h"
+#include "kvq_qjl_device.h"
+
+#include <algorithm>
+
+namespace kvq {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kResThreads = 512;
+constexpr int kResWaves = kResThreads / 64;
+constexpr int kResKS = 8;   // d = 128: 8 K-steps of 16 channels
+constexpr int kResMT = 8;   // m = 256: 8 projection tiles of 32
+constexpr int kResRing = 2; // token tiles in flight per wave
+
+// Sign word of projection tile mt for the wave's 32 tokens: P = S_tile
+// (hi + lo)^T on fp16 MFMA (both parts into one binary32 accumulator), then
+// bit = [P >= 0], assembled as in the plain sketch (accumulator r of lane
+// (j, h) holds projection 32 mt + 16 h + r; the halves' 16 bits are
+// exchanged).
+__device__ __forceinline__ uint32_t res_tile_word(const f16x8* sfrag, int mt, int lane,
+                                                  const f16x8 (&bh)[kResKS],
+                                                  const f16x8 (&bl)[kResKS]) {
+  f32x16 acc = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < kResKS; ++ks) {
+    const f16x8 a = sfrag[(mt * kResKS + ks) * 64 + lane];
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bh[ks], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bl[ks], acc, 0, 0, 0);
+  }
+  uint32_t sb = 0;
+#pragma unroll
+  for (int r = 15; r >= 0; --r) {
+    const float pr = acc[r];
+    sb = __builtin_amdgcn_alignbit(sb, __builtin_bit_cast(uint32_t, pr), 31);
+  }
+  uint32_t lo, hi;
+  halves_u32(~sb & 0xFFFFu, lo, hi);
+  return lo | (hi << 16);
+}
+
+__device__ __forceinline__ float other_half_f32(float v, bool take_hi) {
+  uint32_t lo, hi;
+  halves_u32(__builtin_bit_cast(uint32_t, v), lo, hi);
+  return __builtin_bit_cast(float, take_hi ? hi : lo);
+}
+
+// Fused INT4 + residual sketch for fp16 keys, fp16 S, d = 128, m = 256 and
+// group size G in {16, 32, 64, 128}.  Persistent grid; each wave strides
+// over 32-token tiles with a ring of kResRing tiles in flight (loads
+// unconditional, clamped to the last row past the end; nothing of those
+// tokens is stored).
+template <int G>
+__global__ __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void residual_sketch_kernel(const _Float16* __restrict__ k, int64_t rows,
+                            const _Float16* __restrict__ S, uint8_t* __restrict__ codes,
+                            float* __restrict__ steps, float* __restrict__ offsets,
+                            uint32_t* __restrict__ bits, uint16_t* __restrict__ norms) {
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  f16x8* sfrag = reinterpret_cast<f16x8*>(lds_raw);
+  constexpr int D = kResKS * 16;
+  constexpr int NG = D / G;          // groups per row
+  constexpr int KPG = G / 16;        // K-steps per group (G >= 16)
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const int col = lane & 31;
+
+  // S -> LDS in fragment order (as the plain sketch): fragment (mt, ks),
+  // lane l holds S[32 mt + perm(l % 32)][16 ks + 8 (l / 32) .. + 8].
+  for (int idx = tid; idx < kResMT * kResKS * 64; idx += kResThreads) {
+    const int l = idx & 63;
+    const int frag = idx >> 6;
+    const int mt = frag / kResKS, ks = frag % kResKS;
+    const int srow = 32 * mt + sketch_row_perm(l & 31);
+    sfrag[idx] = *reinterpret_cast<const f16x8*>(S + (int64_t)srow * D + 16 * ks + 8 * (l >> 5));
+  }
+  __syncthreads();
+
+  const int64_t tiles = (rows + 31) / 32;
+  auto load = [&](f16x8 (&b)[kResKS], int64_t tile) {
+    const int64_t tok = std::min<int64_t>(tile * 32 + col, rows - 1);
+    const _Float16* kr = k + tok * D + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < kResKS; ++ks) b[ks] = ld_stream(reinterpret_cast<const f16x8*>(kr + 16 * ks));
+  };
+
+  auto process = [&](const f16x8 (&b)[kResKS], int64_t tile) {
+    const int64_t tok = tile * 32 + col;
+    int off = 0;
+    asm volatile("" : "+v"(off));
+    const f16x8* sf = sfrag + off;
+
+    // 1) group min / max: this lane's 8 channels per K-step, then the other
+    //    half's
+    float mn[NG], mx[NG];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      mn[j] = (float)b[j * KPG][0];
+      mx[j] = mn[j];
+#pragma unroll
+      for (int kk = 0; kk < KPG; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = (float)b[j * KPG + kk][e];
+          mn[j] = __builtin_fminf(mn[j], v);
+          mx[j] = __builtin_fmaxf(mx[j], v);
+        }
+      mn[j] = __builtin_fminf(mn[j], other_half_f32(mn[j], h == 0));
+      mx[j] = __builtin_fmaxf(mx[j], other_half_f32(mx[j], h == 0));
+    }
+    float st[NG], sdiv[NG], rc[NG];
+    bool dv[NG];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      st[j] = group_step(mn[j], mx[j]);
+      sdiv[j] = step_divisor(st[j]);
+      rc[j] = __builtin_amdgcn_rcpf(sdiv[j]);
+      dv[j] = !rcp_ok(sdiv[j]);
+    }
+
+    // 2) codes, reconstruction and residual
+    uint32_t cw[kResKS];
+    float rr[kResKS][8];
+    float ss = 0.0f, am = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < kResKS; ++ks) {
+      const int j = ks / KPG;
+      float xv[8], c[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xv[e] = (float)b[ks][e];
+      codes_rcp<8>(xv, mn[j], sdiv[j], rc[j], dv[j], c);
+      cw[ks] = pack_nibbles<8>(c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        rr[ks][e] = xv[e] - recon4(c[e], st[j], mn[j]);
+        ss = __builtin_fmaf(rr[ks][e], rr[ks][e], ss);
+        am = __builtin_fmaxf(am, __builtin_fabsf(rr[ks][e]));
+      }
+    }
+    ss = ss + other_half_f32(ss, h == 0);
+    am = __builtin_fmaxf(am, other_half_f32(am, h == 0));
+
+    // 3) residual scaled by 2^(15 - e) (am = f 2^e, f in [0.5, 1)) and split
+    //    into binary16 hi + lo
+    const int sc = 15 - __builtin_amdgcn_frexp_expf(am);
+    f16x8 bh[kResKS], bl[kResKS];
+#pragma unroll
+    for (int ks = 0; ks < kResKS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = __builtin_amdgcn_ldexpf(rr[ks][e], sc);
+        const _Float16 vh = (_Float16)v;
+        bh[ks][e] = vh;
+        bl[ks][e] = (_Float16)(v - (float)vh);
+      }
+
+    // 4) sign words
+    uint32_t wbuf[kResMT];
+#pragma unroll
+    for (int mt = 0; mt < kResMT; ++mt) {
+      __builtin_amdgcn_sched_barrier(0);
+      wbuf[mt] = res_tile_word(sf, mt, lane, bh, bl);
+    }
+
+    // 5) stores: half h writes code bytes [32 h, 32 h + 32), the steps
+    //    (h = 0) or the offsets (h = 1), sign words [4 h, 4 h + 4) and, for
+    //    h = 0, the norm.  Lane-mask blends rather than selects, which the
+    //    compiler would turn into dynamically indexed (scratch) arrays.
+    uint32_t clo[kResKS], chi[kResKS];
+#pragma unroll
+    for (int ks = 0; ks < kResKS; ++ks) halves_u32(cw[ks], clo[ks], chi[ks]);
+    if (tok < rows) {
+      const uint32_t m0 = h == 0 ? 0xFFFFFFFFu : 0u;
+      u32x4 cv[2];
+#pragma unroll
+      for (int q4 = 0; q4 < 2; ++q4)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int idx = 4 * q4 + jj;       // word of this half's 8
+          const int ks0 = idx / 2, ks1 = 4 + idx / 2;
+          const uint32_t a = (idx & 1) ? chi[ks0] : clo[ks0];
+          const uint32_t bb = (idx & 1) ? chi[ks1] : clo[ks1];
+          cv[q4][jj] = (a & m0) | (bb & ~m0);
+        }
+      u32x4* cdst = reinterpret_cast<u32x4*>(codes + tok * (D / 2) + 32 * h);
+      cdst[0] = cv[0];
+      cdst[1] = cv[1];
+      float* sz = (h == 0 ? steps : offsets) + tok * NG;
+#pragma unroll
+      for (int j = 0; j < NG; ++j)
+        sz[j] = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, st[j]) & m0) |
+                                              (__builtin_bit_cast(uint32_t, mn[j]) & ~m0));
+      u32x4 wv;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) wv[jj] = (wbuf[jj] & m0) | (wbuf[4 + jj] & ~m0);
+      *reinterpret_cast<u32x4*>(bits + tok * kResMT + 4 * h) = wv;
+      if (h == 0) norms[tok] = f32_to_f16_bits(__builtin_sqrtf(ss));
+    }
+  };
+
+  const int64_t stride = (int64_t)gridDim.x * kResWaves;
+  const int64_t first = (int64_t)blockIdx.x * kResWaves + wave;
+  if (first >= tiles) return;
+  f16x8 bq[kResRing][kResKS];
+#pragma unroll
+  for (int r = 0; r < kResRing; ++r) load(bq[r], std::min(first + r * stride, tiles - 1));
+  for (int64_t t0 = first;; t0 += kResRing * stride) {
+#pragma unroll
+    for (int r = 0; r < kResRing; ++r) {
+      const int64_t t = t0 + r * stride;
+      process(bq[r], t);
+      if (t + stride >= tiles) return;
+      load(bq[r], std::min(t + kResRing * stride, tiles - 1));
+    }
+  }
+}
+
+// Residual value j of a row, from the key and its stored INT4 encoding.
+template <typename TK>
+__device__ __forceinline__ float residual_at(const TK* kr, const uint8_t* cr, const float* sr,
+                                             const float* zr, int g, int j) {
+  const uint32_t c = (cr[j >> 1] >> (4 * (j & 1))) & 0xFu;
+  const int grp = j / g;
+  return to_f32(kr[j]) - recon4((float)c, sr[grp], zr[grp]);
+}
+
+// Residual sketch, any shape: one thread per (row, sign word), binary32 dot
+// products of S rows with the residual (rebuilt from the key and the codes
+// the quantizer wrote); the word-0 thread also writes the norm.
+template <typename TK, typename TS>
+__global__ __launch_bounds__(256) void residual_sketch_generic_kernel(
+    const TK* __restrict__ k, int64_t rows, int d, int g, const TS* __restrict__ S, int m,
+    const uint8_t* __restrict__ codes, const float* __restrict__ steps,
+    const float* __restrict__ offsets, uint32_t* __restrict__ bits, uint16_t* __restrict__ norms) {
+  const int words = m / 32;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid / words;
+  const int w = (int)(gid % words);
+  if (row >= rows) return;
+  const TK* kr = k + row * d;
+  const uint8_t* cr = codes + row * (d / 2);
+  const float* sr = steps + row * (d / g);
+  const float* zr = offsets + row * (d / g);
+  uint32_t word = 0;
+  for (int i = 0; i < 32; ++i) {
+    const TS* srow = S + (int64_t)(32 * w + i) * d;
+    float p = 0.0f;
+    for (int j = 0; j < d; ++j) p = __builtin_fmaf(to_f32(srow[j]), residual_at(kr, cr, sr, zr, g, j), p);
+    word |= (p >= 0.0f ? 1u : 0u) << i;
+  }
+  bits[row * words + w] = word;
+  if (w == 0) {
+    float acc = 0.0f;
+    for (int j = 0; j < d; ++j) {
+      const float v = residual_at(kr, cr, sr, zr, g, j);
+      acc = __builtin_fmaf(v, v, acc);
+    }
+    norms[row] = f32_to_f16_bits(__builtin_sqrtf(acc));
+  }
+}
+
+template <int G>
+static hipError_t residual_sketch_launch(const _Float16* k, int64_t rows, const _Float16* S,
+                                         uint8_t* codes, float* steps, float* offsets,
+                                         uint32_t* bits, uint16_t* norms, const DeviceInfo& dev,
+                                         hipStream_t st) {
+  const size_t lds = (size_t)kResMT * 32 * kResKS * 16 * sizeof(_Float16);   // 64 KiB
+  const int64_t tiles = (rows + 31) / 32;
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, residual_sketch_kernel<G>,
+                                                              kResThreads, lds);
+  if (e != hipSuccess) return e;
+  const int64_t want = (tiles + kResWaves - 1) / kResWaves;
+  const int64_t cap = (int64_t)dev.cus * std::max(1, per_cu);
+  const int64_t blocks = std::max<int64_t>(1, std::min(want, cap));
+  hipLaunchKernelGGL(residual_sketch_kernel<G>, dim3((unsigned)blocks), dim3(kResThreads), lds, st,
+                     k, rows, S, codes, steps, offsets, bits, norms);
+  return hipGetLastError();
+}
+
+template <typename TK, typename TS>
+static hipError_t residual_sketch_generic(const TK* k, int64_t rows, int d, int g, const TS* S,
+                                          int m, const uint8_t* codes, const float* steps,
+                                          const float* offsets, uint32_t* bits, uint16_t* norms,
+                                          hipStream_t st) {
+  const int words = m / 32;
+  const int64_t rows_per = std::max<int64_t>(1, (int64_t(1) << 30) / words);
+  for (int64_t r0 = 0; r0 < rows; r0 += rows_per) {
+    const int64_t nr = std::min(rows_per, rows - r0);
+    const int64_t nb = (nr * words + 255) / 256;
+    hipLaunchKernelGGL((residual_sketch_generic_kernel<TK, TS>), dim3((unsigned)nb), dim3(256), 0,
+                       st, k + r0 * d, nr, d, g, S, m, codes + r0 * (d / 2), steps + r0 * (d / g),
+                       offsets + r0 * (d / g), bits + r0 * words, norms + r0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_residual_sketch(const void* k, int k_f16, int64_t rows, int d, int g,
+                                  const void* S, int S_f16, int m, uint8_t* codes, float* steps,
+                                  float* offsets, uint32_t* bits, uint16_t* norms,
+                                  const DeviceInfo& dev, hipStream_t st) {
+  if (k_f16 && S_f16 && d == 128 && m == 256 && dev.lds_per_block >= 64 * 1024) {
+    const _Float16* kh = static_cast<const _Float16*>(k);
+    const _Float16* Sh = static_cast<const _Float16*>(S);
+    switch (g) {
+      case 16: return residual_sketch_launch<16>(kh, rows, Sh, codes, steps, offsets, bits, norms, dev, st);
+      case 32: return residual_sketch_launch<32>(kh, rows, Sh, codes, steps, offsets, bits, norms, dev, st);
+      case 64: return residual_sketch_launch<64>(kh, rows, Sh, codes, steps, offsets, bits, norms, dev, st);
+      case 128: return residual_sketch_launch<128>(kh, rows, Sh, codes, steps, offsets, bits, norms, dev, st);
+      default: break;
+    }
+  }
+  hipError_t e = launch_quantize_int4(k, k_f16, rows, d, g, codes, steps, offsets, st);
+  if (e != hipSuccess) return e;
+  if (k_f16) {
+    const _Float16* kh = static_cast<const _Float16*>(k);
+    if (S_f16)
+      return residual_sketch_generic(kh, rows, d, g, static_cast<const _Float16*>(S), m, codes,
+                                     steps, offsets, bits, norms, st);
+    return residual_sketch_generic(kh, rows, d, g, static_cast<const float*>(S), m, codes, steps,
+                                   offsets, bits, norms, st);
+  }
+  const float* kf = static_cast<const float*>(k);
+  if (S_f16)
+    return residual_sketch_generic(kf, rows, d, g, static_cast<const _Float16*>(S), m, codes, steps,
+                                   offsets, bits, norms, st);
+  return residual_sketch_generic(kf, rows, d, g, static_cast<const float*>(S), m, codes, steps,
+                                 offsets, bits, norms, st);
+}
+
+}  // namespace kvq

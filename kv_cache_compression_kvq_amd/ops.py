@@ -130,6 +130,29 @@ def qjl_sketch(k: torch.Tensor, S: torch.Tensor) -> tuple[torch.Tensor, torch.Te
     return bits, norms
 
 
+def residual_sketch(k: torch.Tensor, S: torch.Tensor, g: int):
+    """Two-stage key compression: k [..., d] fp32/fp16, S [m, d] fp32/fp16,
+    group size g -> (codes uint8 [..., d/2], steps fp32 [..., d/g],
+    offsets fp32 [..., d/g], residual sign words int32 [..., m // 32],
+    residual norms fp16 [...])."""
+    _dev(k, "k"), _dev(S, "S")
+    m, d = S.shape
+    if k.shape[-1] != d:
+        raise ValueError(f"k has d = {k.shape[-1]}, S has d = {d}")
+    rows = k.numel() // d if d else 0
+    lead = k.shape[:-1]
+    ng = d // g if g > 0 else 0
+    codes = torch.empty((*lead, d // 2), dtype=torch.uint8, device=k.device)
+    steps = torch.empty((*lead, ng), dtype=torch.float32, device=k.device)
+    offsets = torch.empty((*lead, ng), dtype=torch.float32, device=k.device)
+    bits = torch.empty((*lead, m // 32), dtype=torch.int32, device=k.device)
+    norms = torch.empty(lead, dtype=torch.float16, device=k.device)
+    L.check(L.lib().kvq_residual_sketch(_p(k), _dtype_code(k, "k"), rows, d, g, _p(S),
+                                        _dtype_code(S, "S"), m, _p(codes), _p(steps), _p(offsets),
+                                        _p(bits), _p(norms), _stream(k)))
+    return codes, steps, offsets, bits, norms
+
+
 def scores_qjl(q: torch.Tensor, S: torch.Tensor, bits: torch.Tensor,
                norms: torch.Tensor) -> torch.Tensor:
     """q [G, nq, d]; S [m, d]; bits [G, T, m // 32]; norms [G, T] -> [G, nq, T] fp32."""

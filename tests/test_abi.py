@@ -95,6 +95,33 @@ def test_int4_validation():
     assert dq(None, None, None, 0, 128, 32, None, L.KVQ_F16, None) == L.KVQ_OK
 
 
+def test_residual_sketch_validation():
+    f = L.lib().kvq_residual_sketch
+    ok = (A, L.KVQ_F16, 4, 128, 32, A, L.KVQ_F16, 256, A, A, A, A, A, None)
+
+    def call(**kw):
+        names = ["k", "k_dt", "rows", "d", "g", "S", "S_dt", "m", "codes", "steps", "offsets",
+                 "bits", "norms", "stream"]
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return f(*[args[n] for n in names])
+
+    for name in ("k", "S", "codes", "steps", "offsets", "bits", "norms"):
+        _err(call(**{name: None}), L.KVQ_ERR_NULL)
+        _err(call(**{name: MIS}), L.KVQ_ERR_ALIGN)
+    _err(call(rows=-1), L.KVQ_ERR_SHAPE)
+    for d in (0, 8, 1040, 2048):
+        _err(call(d=d, g=16), L.KVQ_ERR_SHAPE)
+    for g in (0, 8, 48, 256):
+        _err(call(g=g), L.KVQ_ERR_SHAPE)
+    for m in (0, 16, 48, 2048):
+        _err(call(m=m), L.KVQ_ERR_SHAPE)
+    _err(call(k_dt=5), L.KVQ_ERR_DTYPE)
+    _err(call(S_dt=-1), L.KVQ_ERR_DTYPE)
+    assert f(None, L.KVQ_F16, 0, 128, 32, None, L.KVQ_F16, 256, None, None, None, None, None,
+             None) == L.KVQ_OK
+
+
 def test_scores_int8_validation():
     f = L.lib().kvq_scores_int8
     _err(f(A, L.KVQ_F16, 2, 0, A, A, 16, 128, A, None), L.KVQ_ERR_SHAPE)

@@ -1,0 +1,119 @@
+"""GPU parity of the two-stage (INT4 + QJL-on-residual) path against the
+oracle: INT4 codes, steps and offsets bit-exact (and identical to
+kvq_quantize_int4's), residual sign bits exact outside the
+1e-4 * ||S_i|| * ||r|| band, residual norms within one binary16 ulp."""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_kvq_amd as K
+import synth_inputs as si
+from oracle import int4 as O4
+from oracle import residual as OR
+from gpu_common import assert_bits_within_band, assert_norms_within_ulp, down, log, up
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_residual(k: np.ndarray, g: int, codes, steps, offsets) -> np.ndarray:
+    khat = O4.dequantize_int4(codes, steps, offsets, g)
+    return OR.residual(k, khat)
+
+
+def sketch_check(k: np.ndarray, S: np.ndarray, g: int, label: str):
+    """Residual sketch of k [R, d] on the GPU against the oracle."""
+    log(f"[res] {label}: k {k.shape} {k.dtype}, S {S.shape} {S.dtype}, g={g}")
+    kd = up(k)
+    cg, sg, zg, bg, ng = K.residual_sketch(kd, up(S), g)
+    co, so, zo, wo, no = OR.residual_compress(k, S, g)
+    assert np.array_equal(down(cg), co), f"{label}: codes differ"
+    assert np.array_equal(down(sg).view(np.uint32), so.view(np.uint32)), f"{label}: steps differ"
+    zgh = down(zg)
+    assert np.array_equal(zgh, zo), f"{label}: offsets differ"
+    # the INT4 fields are exactly the standalone quantizer's
+    c4, s4, z4 = K.quantize_int4(kd, g)
+    assert torch.equal(cg, c4) and torch.equal(sg.view(torch.int32), s4.view(torch.int32))
+    assert torch.equal(zg, z4)
+    r = oracle_residual(k, g, co, so, zo)
+    flips = assert_bits_within_band(down(bg, np.uint32), wo, r, S)
+    nd = assert_norms_within_ulp(down(ng), no)
+    log(f"[res] {label}: {flips} sign bits inside the band differ, {nd} norms one ulp apart")
+    return co, so, zo, wo, no
+
+
+@pytest.mark.parametrize("g", [16, 32, 64, 128])
+def test_fast_path_ragged_rows(g):
+    """fp16 keys and S, d = 128, m = 256 (the fused kernel): row counts
+    ragged against its 32-token tiles and its ring of tiles."""
+    rng = np.random.default_rng(g)
+    S = rng.standard_normal((256, 128)).astype(np.float16)
+    for rows in (1, 31, 33, 257, 1000, 4097):
+        k = (rng.standard_normal((rows, 128)) * rng.uniform(0.01, 30, (rows, 1))).astype(np.float16)
+        sketch_check(k, S, g, f"fast g={g} rows={rows}")
+
+
+@pytest.mark.parametrize("kdt,sdt,d,m,g", [("f32", "f32", 64, 96, 32), ("f16", "f32", 128, 256, 32),
+                                           ("f32", "f16", 128, 256, 128), ("f16", "f16", 48, 32, 48),
+                                           ("f16", "f16", 1024, 64, 128), ("f16", "f16", 128, 512, 16),
+                                           ("f32", "f32", 16, 32, 16)])
+def test_generic_shapes(kdt, sdt, d, m, g):
+    rng = np.random.default_rng(d + m + g)
+    S = rng.standard_normal((m, d)).astype(np.float16 if sdt == "f16" else np.float32)
+    for rows in (1, 63, 700):
+        k = rng.standard_normal((rows, d)).astype(np.float16 if kdt == "f16" else np.float32)
+        sketch_check(k, S, g, f"{kdt}/{sdt} d={d} m={m} g={g} rows={rows}")
+
+
+def test_keys_on_the_grid_and_special_rows():
+    """Rows on the INT4 grid have r = 0: all bits 1 and norm 0; constant and
+    zero rows too; a row with one spike."""
+    rng = np.random.default_rng(9)
+    d, m, g = 128, 256, 32
+    S = rng.standard_normal((m, d)).astype(np.float16)
+    k = rng.standard_normal((40, d)).astype(np.float16)
+    for r in range(8):
+        for j in range(d // g):
+            s = 2.0 ** rng.integers(-4, 2)
+            z = float(rng.integers(-8, 8)) * s
+            k[r, g * j:g * (j + 1)] = z + np.concatenate([np.arange(16), rng.integers(0, 16, g - 16)]) * s
+    k[8] = 0
+    k[9] = 1.5
+    k[10] = 0
+    k[10, 77] = 1000
+    co, so, zo, wo, no = sketch_check(k, S, g, "grid / special rows")
+    _, _, _, bg, ng = K.residual_sketch(up(k), up(S), g)
+    bg, ng = down(bg, np.uint32), down(ng)
+    assert np.all(bg[:10] == 0xFFFFFFFF) and np.all(ng[:10] == 0)
+
+
+def test_qjl_cache_full_size_sampled():
+    """8 x 32 x 8192 x 128 fp16 keys, S 256 x 128 fp16, g = 32: the whole
+    cache is compressed on the GPU in the bench's launch; 8192 sampled rows
+    are checked against the oracle, and every row's residual norm against
+    the INT4 error bound (|r_i| <= s/2 + rounding, so ||r|| <= sqrt(d) s_max / 2)."""
+    W = si.W_QJL_CACHE
+    B, H, T, d, m, g = 8, 32, 8192, 128, 256, 32
+    R = B * H * T
+    k = si.kv_tensor(W, si.K, B, H, T, d, "f16", outliers=True).reshape(R, d)
+    S = si.projection(W, m, d, "f16")
+    log("[res] full size: residual sketch")
+    cg, sg, zg, bg, ng = K.residual_sketch(up(k), up(S), g)
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, R - 1], rng.integers(0, R, 8192)]))
+    idx = torch.from_numpy(rows).to("cuda")
+    co, so, zo, wo, no = OR.residual_compress(k[rows], S, g)
+    assert np.array_equal(down(cg.index_select(0, idx)), co)
+    assert np.array_equal(down(sg.index_select(0, idx)).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(down(zg.index_select(0, idx)), zo)
+    r = oracle_residual(k[rows], g, co, so, zo)
+    assert_bits_within_band(down(bg.index_select(0, idx), np.uint32), wo, r, S)
+    assert_norms_within_ulp(down(ng.index_select(0, idx)), no)
+    bound = (sg.amax(dim=1) * (0.5 * d ** 0.5) * 1.001).to(torch.float32)
+    assert bool((ng.to(torch.float32) <= bound + 1e-3).all())
+
+
+def test_empty_input_is_a_noop():
+    k = torch.empty((0, 128), dtype=torch.float16, device="cuda")
+    S = torch.zeros((256, 128), dtype=torch.float16, device="cuda")
+    out = K.residual_sketch(k, S, 32)
+    assert [tuple(t.shape) for t in out] == [(0, 64), (0, 4), (0, 4), (0, 8), (0,)]
