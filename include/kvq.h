@@ -1,8 +1,9 @@
 /*
  * kvq.h - C ABI of libkvq, a KV-cache compressor for AMD Instinct MI355X
  * (gfx950): per-row symmetric INT8 quantization, asymmetric group-wise INT4
- * quantization and the QJL key sketch, with decode-time scoring and attention
- * read straight from the compressed cache.
+ * quantization, the QJL key sketch and a two-stage INT4 + residual-QJL key
+ * code, with decode-time scoring and attention read straight from the
+ * compressed cache.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -233,6 +234,33 @@ kvq_status kvq_residual_sketch(const void* k, kvq_dtype k_dt, int64_t rows, int3
                                const void* S, kvq_dtype S_dt, int32_t m, uint8_t* codes,
                                float* steps, float* offsets, uint32_t* bits, uint16_t* norms,
                                kvq_stream_t stream);
+
+/*
+ * kvq_scores_residual - decode-query scores against two-stage (INT4 +
+ * residual QJL) keys: the first stage's inner product plus the QJL estimate
+ * of the residual's.
+ *
+ * Same sources as kvq_residual_sketch.  With y = S q (binary32):
+ *   scores[g, j, t] = q . khat_{g,t} + sqrt(pi/2) / m * norm_{g,t}
+ *                     * sum_i (2 b_{g,t,i} - 1) * y_i
+ * where khat is the INT4 reconstruction (as kvq_dequantize_int4).  Agrees
+ * with the exact value within
+ *   1e-5 * sum_i |q_i| * (c_i * s + |z|) + 1e-4 * ||q|| * norm_{g,t}
+ * (s, z of the group of channel i): the INT4 part may be evaluated per group
+ * as s * sum q_i c_i + z * sum q_i.
+ *
+ * q        [groups, nq, d] (q_dt);  S [m, d] (S_dt)
+ * codes    [groups, T, d / 2];  steps, offsets [groups, T, d / g]
+ * bits     [groups, T, m / 32];  norms [groups, T] binary16 patterns
+ * scores   [groups, nq, T] binary32, written
+ * 1 <= nq <= 64; d, g, m as for kvq_residual_sketch.
+ * Errors: NULL, ALIGN, SHAPE, DTYPE.
+ */
+kvq_status kvq_scores_residual(const void* q, kvq_dtype q_dt, int64_t groups, int32_t nq,
+                               const void* S, kvq_dtype S_dt, int32_t m, int32_t g,
+                               const uint8_t* codes, const float* steps, const float* offsets,
+                               const uint32_t* bits, const uint16_t* norms, int64_t T, int32_t d,
+                               float* scores, kvq_stream_t stream);
 
 /*
  * kvq_decode_workspace_bytes - size of the scratch buffer kvq_decode_qjl_int8

@@ -20,4 +20,5 @@ from .ops import (  # noqa: F401
     quantize_int8,
     scores_int8,
     scores_qjl,
+    scores_residual,
 )

@@ -241,6 +241,35 @@ kvq_status kvq_residual_sketch(const void* k, kvq_dtype k_dt, int64_t rows, int3
                                                   reinterpret_cast<hipStream_t>(stream)));
 }
 
+kvq_status kvq_scores_residual(const void* q, kvq_dtype q_dt, int64_t groups, int32_t nq,
+                               const void* S, kvq_dtype S_dt, int32_t m, int32_t g,
+                               const uint8_t* codes, const float* steps, const float* offsets,
+                               const uint32_t* bits, const uint16_t* norms, int64_t T, int32_t d,
+                               float* scores, kvq_stream_t stream) {
+  const char* fn = "kvq_scores_residual";
+  kvq_status st;
+  if ((st = check_count(fn, "groups", groups)) || (st = check_count(fn, "T", T)) ||
+      (st = check_nq(fn, nq)) || (st = check_d(fn, d)) || (st = check_group(fn, d, g)) ||
+      (st = check_m(fn, m)) || (st = check_dtype(fn, "q_dt", q_dt)) ||
+      (st = check_dtype(fn, "S_dt", S_dt)))
+    return st;
+  if (d > kvq::kMaxDecodeD)
+    return fail(KVQ_ERR_SHAPE, "%s: d = %d exceeds %d", fn, (int)d, kvq::kMaxDecodeD);
+  if (groups == 0 || T == 0) return ok();
+  KVQ_CHECK_PTR(q);
+  KVQ_CHECK_PTR(S);
+  KVQ_CHECK_PTR(codes);
+  KVQ_CHECK_PTR(steps);
+  KVQ_CHECK_PTR(offsets);
+  KVQ_CHECK_PTR(bits);
+  KVQ_CHECK_PTR(norms);
+  KVQ_CHECK_PTR(scores);
+  return launched(fn, kvq::launch_scores_residual(q, q_dt == KVQ_F16, groups, nq, S,
+                                                  S_dt == KVQ_F16, m, g, codes, steps, offsets,
+                                                  bits, norms, T, d, scores,
+                                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
 kvq_status kvq_qjl_sketch(const void* k, kvq_dtype k_dt, int64_t rows, int32_t d, const void* S,
                           int32_t m, uint32_t* bits, uint16_t* norms, kvq_stream_t stream) {
   const char* fn = "kvq_qjl_sketch";

@@ -41,6 +41,12 @@ hipError_t launch_residual_sketch(const void* k, int k_f16, int64_t rows, int d,
                                   float* offsets, uint32_t* bits, uint16_t* norms,
                                   const DeviceInfo& dev, hipStream_t s);
 
+hipError_t launch_scores_residual(const void* q, int q_f16, int64_t groups, int nq, const void* S,
+                                  int S_f16, int m, int g, const uint8_t* codes,
+                                  const float* steps, const float* offsets, const uint32_t* bits,
+                                  const uint16_t* norms, int64_t T, int d, float* scores,
+                                  hipStream_t s);
+
 // Token split of the decode kernel: tokens per split and number of splits.
 struct DecodeSplit {
   int64_t splits = 1;

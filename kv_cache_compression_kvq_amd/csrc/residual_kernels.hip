@@ -358,4 +358,323 @@ hipError_t launch_residual_sketch(const void* k, int k_f16, int64_t rows, int d,
                                  offsets, bits, norms, st);
 }
 
+
+// ---------------------------------------------------------------------------
+// Scores.  fp16 S, d = 128, m = 256: one workgroup per (group, query, tile of
+// kRsTile tokens); 4 lanes per token, lane `sub` holding channels
+// 32 sub .. 32 sub + 31 of the query in registers (binary32) and reading the
+// token's codes for them (16 bytes), the steps and offsets of their groups,
+// and sign words 2 sub, 2 sub + 1.  The INT4 part is folded per group,
+// s * sum_i q_i c_i + z * sum_i q_i (sums over the lane's channels of the
+// group); the QJL part is 8 lookups of byte tables T_p[v] = sum_{j<8}
+// (bit j of v ? +1 : -1) y_{8p+j}, stored as 256 rows v of the 32 tables'
+// entries.  Lane (token slot tt, sub) reads table 8 sub + ((b + tt) mod 8) at
+// step b, so the 32 lanes of a half-wave read 32 different tables, i.e. 32
+// different LDS banks, whatever the bytes; the lane's 8 sign bytes are
+// rotated by tt mod 8 beforehand.  The quad's 4 partial scores are summed
+// with DPP.
+constexpr int kRsThreads = 256;
+constexpr int kRsU = 4;                          // tokens in flight per lane
+constexpr int kRsIters = 8;
+constexpr int kRsTile = 64 * kRsU * kRsIters;    // 2048 tokens per workgroup
+constexpr int kRsRowFloats = 32;
+constexpr int kRsLutFloats = 256 * kRsRowFloats; // 32 KiB, at LDS address 0
+
+// Tables of y[0..255] in rows of 32 entries: lut[32 v + p] = T_p[v] (same
+// binary32 values as the other table builders: low-nibble partial sums plus
+// a high-nibble sum).
+__device__ void build_tables32(const float* y, float* lut) {
+  for (int task = threadIdx.x; task < 32 * 16; task += blockDim.x) {
+    const int p = task & 31;
+    const int a = task >> 5;
+    const float* yp = y + 8 * p;
+    float lo[16];
+    lo[0] = -(((yp[0] + yp[1]) + yp[2]) + yp[3]);
+#pragma unroll
+    for (int b = 1; b < 16; ++b) {
+      const int low = b & (-b);
+      const int j = __builtin_ctz(low);
+      lo[b] = lo[b ^ low] + 2.0f * yp[j];
+    }
+    float hi = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hi += ((a >> j) & 1) ? yp[4 + j] : -yp[4 + j];
+#pragma unroll
+    for (int b = 0; b < 16; ++b) lut[(16 * a + b) * kRsRowFloats + p] = hi + lo[b];
+  }
+}
+
+// One lane's share of one token: code bytes of its 32 channels, its two sign
+// words, the steps and offsets of the (one or two) groups its channels touch,
+// the norm bits.
+template <int GPL>
+struct RsTok {
+  u32x4 c;
+  uint32_t w[2];
+  float s[GPL], z[GPL];
+  uint32_t n;
+};
+
+template <typename TQ, int G>
+__global__ __launch_bounds__(kRsThreads) void scores_residual_kernel(
+    const TQ* __restrict__ q, int nq, const _Float16* __restrict__ S,
+    const uint8_t* __restrict__ codes, const float* __restrict__ steps,
+    const float* __restrict__ offsets, const uint32_t* __restrict__ bits,
+    const uint16_t* __restrict__ norms, int64_t T, int64_t tiles, float* __restrict__ scores) {
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  float* lut = reinterpret_cast<float*>(lds_raw);
+  float* y = lut + kRsLutFloats;
+  float* qs = y + 256;
+  constexpr int D = 128, M = 256, NG = D / G;
+  constexpr int GPL = G >= 32 ? 1 : 2;
+  const int64_t gq = blockIdx.x / tiles;
+  const int64_t tile = blockIdx.x % tiles;
+  const int64_t grp = gq / nq;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int sub = lane & 3;
+  const int tt = lane >> 2;
+  const int j0 = (32 * sub) / G;                  // first group of the lane's channels
+  const int64_t tb = tile * kRsTile + wave * 16 + tt;
+  const uint8_t* cg = codes + grp * T * (D / 2);
+  const float* sg = steps + grp * T * NG;
+  const float* zg = offsets + grp * T * NG;
+  const uint32_t* bg = bits + grp * T * (M / 32);
+  const uint16_t* ngp = norms + grp * T;
+
+  // loads are unconditional (tokens past T re-read token T - 1; their scores
+  // are not stored)
+  auto load = [&](RsTok<GPL> (&tk)[kRsU], int it) {
+#pragma unroll
+    for (int u = 0; u < kRsU; ++u) {
+      const int64_t t = std::min<int64_t>(tb + 64 * (it * kRsU + u), T - 1);
+      tk[u].c = ld_stream(reinterpret_cast<const u32x4*>(cg + t * (D / 2) + 16 * sub));
+      const u32x2 wv = ld_stream(reinterpret_cast<const u32x2*>(bg + t * (M / 32) + 2 * sub));
+      tk[u].w[0] = wv[0];
+      tk[u].w[1] = wv[1];
+#pragma unroll
+      for (int k = 0; k < GPL; ++k) {
+        tk[u].s[k] = sg[t * NG + j0 + k];
+        tk[u].z[k] = zg[t * NG + j0 + k];
+      }
+      tk[u].n = ngp[t];
+    }
+  };
+
+  QueryProj16<TQ> pj;
+  pj.issue(S, q + gq * D, M, D);
+  RsTok<GPL> ka[kRsU];
+  load(ka, 0);
+  pj.finish(qs, y, M, D);
+  __syncthreads();
+  build_tables32(y, lut);
+  // the lane's query channels (binary32) in nibble order, and their sums per
+  // group
+  float qv[32];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const f32x4 x = reinterpret_cast<const f32x4*>(qs + 32 * sub)[v];
+    qv[4 * v] = x[0]; qv[4 * v + 1] = x[1]; qv[4 * v + 2] = x[2]; qv[4 * v + 3] = x[3];
+  }
+  float qsum[GPL];
+#pragma unroll
+  for (int k = 0; k < GPL; ++k) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32 / GPL; ++i) a += qv[(32 / GPL) * k + i];
+    qsum[k] = a;
+  }
+  // twice the table byte offset per step, 8 * (8 sub + ((b + tt) mod 8)): a
+  // byte permute puts the token's byte above it (256 v + 8 p) and one shift
+  // gives the LDS address 128 v + 4 p of entry p of row v
+  uint32_t rq[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) rq[b] = 8u * (uint32_t)(8 * sub + ((b + tt) & 7));
+  const uint32_t swap_mask = 0u - (uint32_t)((tt >> 2) & 1);
+  const uint32_t rot_sh = 8u * (uint32_t)(tt & 3);
+  __syncthreads();
+
+  auto score = [&](const RsTok<GPL>& tk) -> float {
+    // INT4 part: nibble e of word k is channel 8 k + e; the low nibbles
+    // (even e) and high nibbles (odd e) are taken a byte at a time
+    float acc[GPL];
+#pragma unroll
+    for (int k = 0; k < GPL; ++k) acc[k] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = tk.c[k] & 0x0F0F0F0Fu;
+      const uint32_t hi = (tk.c[k] >> 4) & 0x0F0F0F0Fu;
+      const int a = (GPL == 2) ? (k >> 1) : 0;
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        acc[a] = __builtin_fmaf(qv[8 * k + 2 * bb], (float)((lo >> (8 * bb)) & 0xFFu), acc[a]);
+        acc[a] = __builtin_fmaf(qv[8 * k + 2 * bb + 1], (float)((hi >> (8 * bb)) & 0xFFu), acc[a]);
+      }
+    }
+    float part = 0.0f;
+#pragma unroll
+    for (int k = 0; k < GPL; ++k) part += tk.s[k] * acc[k] + tk.z[k] * qsum[k];
+    // QJL part: the 8 sign bytes rotated by tt mod 8 (words swapped for
+    // tt mod 8 >= 4, then a byte shift), one table read per byte
+    const uint32_t a0 = tk.w[0] ^ ((tk.w[0] ^ tk.w[1]) & swap_mask);
+    const uint32_t a1 = tk.w[1] ^ ((tk.w[0] ^ tk.w[1]) & swap_mask);
+    uint32_t x[2];
+    x[0] = __builtin_amdgcn_alignbit(a1, a0, rot_sh);
+    x[1] = __builtin_amdgcn_alignbit(a0, a1, rot_sh);
+    float v[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const uint32_t off =
+          __builtin_amdgcn_perm(rq[b], x[b >> 2], 0x07060004u | ((uint32_t)(b & 3) << 8)) >> 1;
+      v[b] = *(lds_cfloat_ptr)(uintptr_t)off;
+    }
+    const float l = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    const float nrm = (float)__builtin_bit_cast(_Float16, (uint16_t)tk.n);
+    return part + (kSqrtHalfPi / (float)M) * nrm * l;
+  };
+
+  auto finish = [&](const RsTok<GPL> (&tk)[kRsU], int it) {
+#pragma unroll
+    for (int u = 0; u < kRsU; ++u) {
+      const float tot = seg_sum_f32<4>(score(tk[u]));
+      const int64_t t = tb + 64 * (it * kRsU + u);
+      if (sub == 0 && t < T) scores[gq * T + t] = tot;
+    }
+  };
+
+#pragma unroll
+  for (int it = 0; it < kRsIters; it += 2) {
+    RsTok<GPL> kb[kRsU];
+    load(kb, std::min(it + 1, kRsIters - 1));
+    finish(ka, it);
+    if (it + 2 < kRsIters) load(ka, it + 2);
+    finish(kb, it + 1);
+  }
+}
+
+// Scores, any shape: one workgroup per (group, query, 256 tokens), one token
+// per thread; q . k_hat from the reconstructed values (binary32 fused
+// multiply-adds) and the estimator over the m sign bits with y in LDS.
+constexpr int kRsGenTok = 256;
+
+template <typename TQ, typename TS>
+__global__ __launch_bounds__(256) void scores_residual_generic_kernel(
+    const TQ* __restrict__ q, int nq, const TS* __restrict__ S, int m, int d, int g,
+    const uint8_t* __restrict__ codes, const float* __restrict__ steps,
+    const float* __restrict__ offsets, const uint32_t* __restrict__ bits,
+    const uint16_t* __restrict__ norms, int64_t T, int64_t tiles, float* __restrict__ scores) {
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  float* y = reinterpret_cast<float*>(lds_raw);     // m
+  float* qf = y + kMaxM;                             // d
+  float* qs = qf + kMaxDecodeD;                      // staging
+  const int64_t gq = blockIdx.x / tiles;
+  const int64_t tile = blockIdx.x % tiles;
+  const int64_t grp = gq / nq;
+  const TQ* qg = q + gq * d;
+  project_query_block<TS, TQ>(S, qg, m, d, qs, y);
+  for (int i = threadIdx.x; i < d; i += blockDim.x) qf[i] = to_f32(qg[i]);
+  __syncthreads();
+  const int64_t t = tile * kRsGenTok + threadIdx.x;
+  if (t >= T) return;
+  const int64_t row = grp * T + t;
+  const uint8_t* cr = codes + row * (d / 2);
+  const float* sr = steps + row * (d / g);
+  const float* zr = offsets + row * (d / g);
+  float a = 0.0f;
+  for (int j = 0; j < d; ++j) {
+    const uint32_t c = (cr[j >> 1] >> (4 * (j & 1))) & 0xFu;
+    a = __builtin_fmaf(qf[j], recon4((float)c, sr[j / g], zr[j / g]), a);
+  }
+  const uint32_t* wr = bits + row * (m / 32);
+  float l = 0.0f;
+  for (int i = 0; i < m; ++i) l += ((wr[i >> 5] >> (i & 31)) & 1u) ? y[i] : -y[i];
+  const float nrm = (float)__builtin_bit_cast(_Float16, norms[row]);
+  scores[gq * T + t] = a + (kSqrtHalfPi / (float)m) * nrm * l;
+}
+
+template <typename TQ>
+static hipError_t scores_residual_fast(const TQ* q, int64_t groups, int nq, const _Float16* S,
+                                       int g, const uint8_t* codes, const float* steps,
+                                       const float* offsets, const uint32_t* bits,
+                                       const uint16_t* norms, int64_t T, float* scores,
+                                       hipStream_t st) {
+  const size_t lds = (size_t)(kRsLutFloats + 512) * sizeof(float);
+  const int64_t tiles = (T + kRsTile - 1) / kRsTile;
+  const int64_t per_group = tiles * nq;
+  const int64_t max_groups = std::max<int64_t>(1, (int64_t(1) << 22) / per_group);
+  constexpr int D = 128, M = 256;
+  for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
+    const int64_t ngr = std::min(max_groups, groups - g0);
+    const unsigned blocks = (unsigned)(ngr * per_group);
+    const TQ* qp = q + g0 * nq * D;
+    const uint8_t* cp = codes + g0 * T * (D / 2);
+    const float* sp = steps + g0 * T * (D / g);
+    const float* zp = offsets + g0 * T * (D / g);
+    const uint32_t* bp = bits + g0 * T * (M / 32);
+    const uint16_t* np = norms + g0 * T;
+    float* op = scores + g0 * nq * T;
+    switch (g) {
+      case 16: hipLaunchKernelGGL((scores_residual_kernel<TQ, 16>), dim3(blocks), dim3(kRsThreads), lds, st, qp, nq, S, cp, sp, zp, bp, np, T, tiles, op); break;
+      case 32: hipLaunchKernelGGL((scores_residual_kernel<TQ, 32>), dim3(blocks), dim3(kRsThreads), lds, st, qp, nq, S, cp, sp, zp, bp, np, T, tiles, op); break;
+      case 64: hipLaunchKernelGGL((scores_residual_kernel<TQ, 64>), dim3(blocks), dim3(kRsThreads), lds, st, qp, nq, S, cp, sp, zp, bp, np, T, tiles, op); break;
+      default: hipLaunchKernelGGL((scores_residual_kernel<TQ, 128>), dim3(blocks), dim3(kRsThreads), lds, st, qp, nq, S, cp, sp, zp, bp, np, T, tiles, op); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename TQ, typename TS>
+static hipError_t scores_residual_generic(const TQ* q, int64_t groups, int nq, const TS* S, int m,
+                                          int d, int g, const uint8_t* codes, const float* steps,
+                                          const float* offsets, const uint32_t* bits,
+                                          const uint16_t* norms, int64_t T, float* scores,
+                                          hipStream_t st) {
+  const size_t lds = (size_t)(kMaxM + kMaxDecodeD + kProjQChunk) * sizeof(float);
+  const int64_t tiles = (T + kRsGenTok - 1) / kRsGenTok;
+  const int64_t per_group = tiles * nq;
+  const int64_t max_groups = std::max<int64_t>(1, (int64_t(1) << 22) / per_group);
+  for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
+    const int64_t ngr = std::min(max_groups, groups - g0);
+    const unsigned blocks = (unsigned)(ngr * per_group);
+    hipLaunchKernelGGL((scores_residual_generic_kernel<TQ, TS>), dim3(blocks), dim3(256), lds, st,
+                       q + g0 * nq * d, nq, S, m, d, g, codes + g0 * T * (d / 2),
+                       steps + g0 * T * (d / g), offsets + g0 * T * (d / g),
+                       bits + g0 * T * (m / 32), norms + g0 * T, T, tiles, scores + g0 * nq * T);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_scores_residual(const void* q, int q_f16, int64_t groups, int nq, const void* S,
+                                  int S_f16, int m, int g, const uint8_t* codes,
+                                  const float* steps, const float* offsets, const uint32_t* bits,
+                                  const uint16_t* norms, int64_t T, int d, float* scores,
+                                  hipStream_t st) {
+  if (S_f16 && d == 128 && m == 256 && (g == 16 || g == 32 || g == 64 || g == 128)) {
+    const _Float16* Sh = static_cast<const _Float16*>(S);
+    if (q_f16)
+      return scores_residual_fast(static_cast<const _Float16*>(q), groups, nq, Sh, g, codes, steps,
+                                  offsets, bits, norms, T, scores, st);
+    return scores_residual_fast(static_cast<const float*>(q), groups, nq, Sh, g, codes, steps,
+                                offsets, bits, norms, T, scores, st);
+  }
+  if (q_f16) {
+    const _Float16* qh = static_cast<const _Float16*>(q);
+    if (S_f16)
+      return scores_residual_generic(qh, groups, nq, static_cast<const _Float16*>(S), m, d, g,
+                                     codes, steps, offsets, bits, norms, T, scores, st);
+    return scores_residual_generic(qh, groups, nq, static_cast<const float*>(S), m, d, g, codes,
+                                   steps, offsets, bits, norms, T, scores, st);
+  }
+  const float* qf = static_cast<const float*>(q);
+  if (S_f16)
+    return scores_residual_generic(qf, groups, nq, static_cast<const _Float16*>(S), m, d, g, codes,
+                                   steps, offsets, bits, norms, T, scores, st);
+  return scores_residual_generic(qf, groups, nq, static_cast<const float*>(S), m, d, g, codes,
+                                 steps, offsets, bits, norms, T, scores, st);
+}
+
 }  // namespace kvq

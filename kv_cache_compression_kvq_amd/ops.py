@@ -153,6 +153,30 @@ def residual_sketch(k: torch.Tensor, S: torch.Tensor, g: int):
     return codes, steps, offsets, bits, norms
 
 
+def scores_residual(q: torch.Tensor, S: torch.Tensor, codes: torch.Tensor, steps: torch.Tensor,
+                    offsets: torch.Tensor, bits: torch.Tensor, norms: torch.Tensor,
+                    g: int) -> torch.Tensor:
+    """q [G, nq, d]; S [m, d]; codes [G, T, d/2]; steps / offsets [G, T, d/g];
+    bits [G, T, m // 32]; norms [G, T] -> scores [G, nq, T] fp32."""
+    for t, n in ((q, "q"), (S, "S"), (codes, "codes"), (steps, "steps"), (offsets, "offsets"),
+                 (bits, "bits"), (norms, "norms")):
+        _dev(t, n)
+    G, nq, d = q.shape
+    m = S.shape[0]
+    T = codes.shape[1]
+    ng = d // g if g > 0 else 0
+    if (S.shape[1] != d or codes.shape != (G, T, d // 2) or steps.shape != (G, T, ng)
+            or offsets.shape != (G, T, ng) or bits.shape != (G, T, m // 32) or norms.shape != (G, T)):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, S {tuple(S.shape)}, codes "
+                         f"{tuple(codes.shape)}, steps {tuple(steps.shape)}, bits {tuple(bits.shape)}, "
+                         f"norms {tuple(norms.shape)}, g {g}")
+    out = torch.empty((G, nq, T), dtype=torch.float32, device=q.device)
+    L.check(L.lib().kvq_scores_residual(_p(q), _dtype_code(q, "q"), G, nq, _p(S), _dtype_code(S, "S"),
+                                        m, g, _p(codes), _p(steps), _p(offsets), _p(bits), _p(norms),
+                                        T, d, _p(out), _stream(q)))
+    return out
+
+
 def scores_qjl(q: torch.Tensor, S: torch.Tensor, bits: torch.Tensor,
                norms: torch.Tensor) -> torch.Tensor:
     """q [G, nq, d]; S [m, d]; bits [G, T, m // 32]; norms [G, T] -> [G, nq, T] fp32."""

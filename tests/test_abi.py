@@ -215,3 +215,26 @@ def test_python_binding_requires_gpu_tensors():
     from kv_cache_compression_kvq_amd import ops
     with pytest.raises(ValueError, match="GPU tensor"):
         ops.quantize_int8(torch.zeros(4, 128))
+
+
+def test_scores_residual_validation():
+    f = L.lib().kvq_scores_residual
+    names = ["q", "q_dt", "groups", "nq", "S", "S_dt", "m", "g", "codes", "steps", "offsets",
+             "bits", "norms", "T", "d", "scores", "stream"]
+    ok = (A, L.KVQ_F16, 2, 1, A, L.KVQ_F16, 256, 32, A, A, A, A, A, 16, 128, A, None)
+
+    def call(**kw):
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return f(*[args[n] for n in names])
+
+    for name in ("q", "S", "codes", "steps", "offsets", "bits", "norms", "scores"):
+        _err(call(**{name: None}), L.KVQ_ERR_NULL)
+        _err(call(**{name: MIS}), L.KVQ_ERR_ALIGN)
+    for kw in ({"groups": -1}, {"T": -1}, {"nq": 0}, {"nq": 65}, {"d": 2048, "g": 128},
+               {"g": 24}, {"m": 48}):
+        _err(call(**kw), L.KVQ_ERR_SHAPE)
+    _err(call(q_dt=3), L.KVQ_ERR_DTYPE)
+    assert call(groups=0, q=None, S=None, codes=None, steps=None, offsets=None, bits=None,
+                norms=None, scores=None) == L.KVQ_OK
+    assert call(T=0, scores=None) == L.KVQ_OK

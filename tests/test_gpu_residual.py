@@ -1,7 +1,9 @@
 """GPU parity of the two-stage (INT4 + QJL-on-residual) path against the
 oracle: INT4 codes, steps and offsets bit-exact (and identical to
 kvq_quantize_int4's), residual sign bits exact outside the
-1e-4 * ||S_i|| * ||r|| band, residual norms within one binary16 ulp."""
+1e-4 * ||S_i|| * ||r|| band, residual norms within one binary16 ulp; scores
+(given the oracle's stored codes, bits and norms) within
+1e-5 * sum_i |q_i| (c_i s + |z|) + 1e-4 * ||q|| * n."""
 import numpy as np
 import pytest
 import torch
@@ -110,6 +112,111 @@ def test_qjl_cache_full_size_sampled():
     assert_norms_within_ulp(down(ng.index_select(0, idx)), no)
     bound = (sg.amax(dim=1) * (0.5 * d ** 0.5) * 1.001).to(torch.float32)
     assert bool((ng.to(torch.float32) <= bound + 1e-3).all())
+
+
+def assert_residual_scores(gpu, q, codes, steps, offsets, norms, g, ora):
+    """|gpu - ora| <= 1e-5 sum_i |q_i| (c_i s + |z|) + 1e-4 ||q|| n + 1e-30."""
+    G, T, half = codes.shape
+    d = 2 * half
+    c = O4.unpack_nibbles(codes.reshape(G * T, half)).astype(np.float64).reshape(G, T, d // g, g)
+    terms = (c * steps.astype(np.float64)[..., None] +
+             np.abs(offsets.astype(np.float64))[..., None]).reshape(G, T, d)
+    qa = np.abs(q.astype(np.float64))
+    tol = 1e-5 * np.matmul(qa, np.swapaxes(terms, 1, 2))
+    tol += 1e-4 * np.linalg.norm(q.astype(np.float64), axis=2)[..., None] * \
+        norms.astype(np.float64)[:, None, :]
+    err = np.abs(gpu.astype(np.float64) - ora)
+    bad = err > tol + 1e-30
+    assert not bad.any(), f"{bad.sum()} scores outside the tolerance (worst {np.max(err / (tol + 1e-30)):.3g})"
+    return float(np.max(err / (tol + 1e-30)))
+
+
+def scores_check(q, S, codes, steps, offsets, words, norms, g, label):
+    sc = down(K.scores_residual(up(q), up(S), up(codes), up(steps), up(offsets), up(words),
+                                up(norms), g))
+    ora = OR.residual_scores(q, S, codes, steps, offsets, words, norms, g)
+    worst = assert_residual_scores(sc, q, codes, steps, offsets, norms, g, ora)
+    log(f"[res] {label}: worst err / tol = {worst:.3g}")
+
+
+def _stored(rng, G, T, d, m, g, sdt, kdt=np.float32):
+    S = rng.standard_normal((m, d)).astype(sdt)
+    k = (rng.standard_normal((G * T, d)) * rng.uniform(0.1, 10, (G * T, 1))).astype(kdt)
+    co, so, zo, wo, no = OR.residual_compress(k, S, g)
+    return (S, co.reshape(G, T, d // 2), so.reshape(G, T, d // g), zo.reshape(G, T, d // g),
+            wo.reshape(G, T, m // 32), no.reshape(G, T))
+
+
+@pytest.mark.parametrize("qdt", ["f16", "f32"])
+@pytest.mark.parametrize("g", [16, 32, 64, 128])
+@pytest.mark.parametrize("nq,T", [(1, 1), (1, 77), (4, 2048), (1, 2049), (2, 5000)])
+def test_scores_fast_path(qdt, g, nq, T):
+    """fp16 S, d = 128, m = 256: tiles of 2048 tokens, ragged tails."""
+    rng = np.random.default_rng(g * 100 + T + nq)
+    G, d, m = 3, 128, 256
+    S, co, so, zo, wo, no = _stored(rng, G, T, d, m, g, np.float16)
+    q = rng.standard_normal((G, nq, d)).astype(np.float16 if qdt == "f16" else np.float32)
+    scores_check(q, S, co, so, zo, wo, no, g, f"fast {qdt} g={g} nq={nq} T={T}")
+
+
+@pytest.mark.parametrize("qdt,sdt,d,m,g", [("f32", "f32", 128, 256, 32), ("f16", "f16", 64, 96, 32),
+                                           ("f32", "f16", 48, 32, 48), ("f16", "f32", 1024, 64, 128),
+                                           ("f16", "f16", 128, 512, 16), ("f32", "f32", 16, 32, 16)])
+def test_scores_generic_shapes(qdt, sdt, d, m, g):
+    rng = np.random.default_rng(d + m + g + 1)
+    G, nq, T = 2, 3, 300
+    S, co, so, zo, wo, no = _stored(rng, G, T, d, m, g, np.float16 if sdt == "f16" else np.float32)
+    q = rng.standard_normal((G, nq, d)).astype(np.float16 if qdt == "f16" else np.float32)
+    scores_check(q, S, co, so, zo, wo, no, g, f"generic {qdt}/{sdt} d={d} m={m} g={g}")
+
+
+def test_scores_full_size_and_error_correction():
+    """8 x 32 x 8192 x 128 fp16 keys, m = 256, g = 32, one fp16 query per
+    head: the cache is compressed and scored on the GPU (the bench's
+    launches); three groups get the oracle's stored values before the score
+    launch and are checked against the oracle's scores.  On them the second
+    stage corrects the first: its estimate of q . r regresses on q . r with
+    slope 1 (+-10 %, pooled), and the two-stage score is closer to the exact
+    q . k than the INT4 score alone in every group (mean squared error ratio
+    below 1; about (pi/2) d / m = 0.785 for isotropic residuals and queries,
+    higher here, where the outlier channels concentrate the residual)."""
+    W = si.W_QJL_CACHE
+    B, H, T, d, m, g = 8, 32, 8192, 128, 256, 32
+    G = B * H
+    k = si.kv_tensor(W, si.K, B, H, T, d, "f16", outliers=True).reshape(G * T, d)
+    S = si.projection(W, m, d, "f16")
+    Sd = up(S)
+    cg, sg, zg, bg, ng = K.residual_sketch(up(k), Sd, g)
+    c3, s3, z3 = cg.view(G, T, d // 2), sg.view(G, T, d // g), zg.view(G, T, d // g)
+    b3, n3 = bg.view(G, T, m // 32), ng.view(G, T)
+    groups = [0, 101, G - 1]
+    stored = {}
+    for gi in groups:
+        co, so, zo, wo, no = OR.residual_compress(k[gi * T:(gi + 1) * T], S, g)
+        stored[gi] = (co, so, zo, wo, no)
+        c3[gi].copy_(up(co)); s3[gi].copy_(up(so)); z3[gi].copy_(up(zo))
+        b3[gi].copy_(up(wo)); n3[gi].copy_(up(no))
+    q = si.queries(W, G, 1, d, "f16")
+    log("[res] full size: scores")
+    sc = down(K.scores_residual(up(q), Sd, c3, s3, z3, b3, n3, g))
+    ratios, num, den = [], 0.0, 0.0
+    for gi in groups:
+        co, so, zo, wo, no = stored[gi]
+        ora = OR.residual_scores(q[gi:gi + 1], S, co[None], so[None], zo[None], wo[None], no[None], g)
+        assert_residual_scores(sc[gi:gi + 1], q[gi:gi + 1], co[None], so[None], zo[None], no[None],
+                               g, ora)
+        kh = O4.dequantize_int4(co, so, zo, g).astype(np.float64)
+        q64 = q[gi, 0].astype(np.float64)
+        qk = k[gi * T:(gi + 1) * T].astype(np.float64) @ q64
+        first = kh @ q64
+        ratios.append(float(np.mean((sc[gi, 0] - qk) ** 2) / np.mean((first - qk) ** 2)))
+        num += float(np.sum((sc[gi, 0] - first) * (qk - first)))
+        den += float(np.sum((qk - first) ** 2))
+    slope = num / den
+    log(f"[res] full size: MSE(two-stage) / MSE(INT4 alone) per checked group = {ratios}, "
+        f"slope of the correction on q.r = {slope:.4f}")
+    assert 0.9 <= slope <= 1.1, slope
+    assert all(r < 1.0 for r in ratios), ratios
 
 
 def test_empty_input_is_a_noop():
