@@ -111,7 +111,7 @@ COLD_BYTES = 1 << 30     # rotate inputs over > 1 GiB: 4x the 256 MB last-level 
 
 
 def components(K, si, torch, np):
-    """GB/s of the INT8, INT4 and QJL kernels on their own workloads, cold: each
+    """GB/s of the INT8, INT4, QJL and two-stage kernels on their own workloads, cold: each
     timed call reads a different copy of its inputs, and the copies together
     exceed 1 GiB, so no call finds its inputs in the MALL or L2.  Calls run
     back to back in blocks timed by one pair of HIP events; the median block's
@@ -217,7 +217,24 @@ def components(K, si, torch, np):
         [lambda bn=bn: K.scores_qjl(q4, S, bn[0], bn[1]) for bn in b3])
     res["qjl_scores_gqa4_f16_m256"]["scores/s"] = round(
         4 * R / res["qjl_scores_gqa4_f16_m256"]["ms"] * 1e3, 1)
-    del kk, sk, b3
+    # two-stage keys: INT4 (groups of 32) and the QJL sketch of its residual
+    g4 = 32
+    per_tok = d // 2 + 8 * (d // g4) + m // 8 + 2
+    kks = [kk] + [kk.clone() for _ in range(ncopies(R * d * 2) - 1)]
+    first = K.residual_sketch(kk, S, g4)
+    gbs("residual_sketch_f16_m256_g32", R * d * 2 + R * per_tok + m * d * 2,
+        [lambda t=t: K.residual_sketch(t, S, g4) for t in kks], flops=2.0 * R * d * m)
+    del kks
+    c4, s4, z4, b4, n4 = first
+    st = [(c4.view(G, T, d // 2), s4.view(G, T, d // g4), z4.view(G, T, d // g4),
+           b4.view(G, T, m // 32), n4.view(G, T))]
+    while len(st) < ncopies(R * per_tok):
+        st.append(tuple(x.clone() for x in st[0]))
+    gbs("residual_scores_f16_m256_g32", R * (per_tok + 4) + G * d * 2 + m * d * 2,
+        [lambda a=a: K.scores_residual(q, S, *a, g4) for a in st])
+    res["residual_scores_f16_m256_g32"]["scores/s"] = round(
+        R / res["residual_scores_f16_m256_g32"]["ms"] * 1e3, 1)
+    del kk, sk, b3, st, first
     torch.cuda.empty_cache()
     return res
 

@@ -18,9 +18,10 @@
 // half h: channels 16 ks + 8 h .. + 8), so a token's groups are reduced with
 // one v_permlane32_swap per min and max; the residual (binary32) is scaled
 // per token by a power of two (max |r| into [2^14, 2^15)) and split into two
-// binary16 parts hi + lo, which carry it to within 2^-24 relative; S r is
-// accumulated from both parts on the matrix cores (S fragments resident in
-// LDS, as in the plain sketch).  Other shapes: the INT4 quantizer, then one
+// binary16 parts hi + lo (hi: the value's top 11 significand bits, lo: the
+// exact remainder, rounded toward zero), which carry it to within 2^-20
+// relative; S r is accumulated from both parts on the matrix cores (S
+// fragments resident in LDS, as in the plain sketch).  Other shapes: the INT4 quantizer, then one
 // thread per (row, sign word) with binary32 dot products.
 #include "kvq_device.h"
 #include "kvq_int4_device.h"
@@ -32,6 +33,7 @@
 namespace kvq {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kResThreads = 512;
 constexpr int kResWaves = kResThreads / 64;
@@ -39,21 +41,10 @@ constexpr int kResKS = 8;   // d = 128: 8 K-steps of 16 channels
 constexpr int kResMT = 8;   // m = 256: 8 projection tiles of 32
 constexpr int kResRing = 2; // token tiles in flight per wave
 
-// Sign word of projection tile mt for the wave's 32 tokens: P = S_tile
-// (hi + lo)^T on fp16 MFMA (both parts into one binary32 accumulator), then
-// bit = [P >= 0], assembled as in the plain sketch (accumulator r of lane
-// (j, h) holds projection 32 mt + 16 h + r; the halves' 16 bits are
-// exchanged).
-__device__ __forceinline__ uint32_t res_tile_word(const f16x8* sfrag, int mt, int lane,
-                                                  const f16x8 (&bh)[kResKS],
-                                                  const f16x8 (&bl)[kResKS]) {
-  f32x16 acc = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < kResKS; ++ks) {
-    const f16x8 a = sfrag[(mt * kResKS + ks) * 64 + lane];
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bh[ks], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bl[ks], acc, 0, 0, 0);
-  }
+// Sign word from a projection tile's accumulators: bit = [P >= 0], assembled
+// as in the plain sketch (accumulator r of lane (j, h) holds projection
+// 32 mt + 16 h + r; the halves' 16 bits are exchanged).
+__device__ __forceinline__ uint32_t res_acc_word(const f32x16& acc) {
   uint32_t sb = 0;
 #pragma unroll
   for (int r = 15; r >= 0; --r) {
@@ -63,6 +54,46 @@ __device__ __forceinline__ uint32_t res_tile_word(const f16x8* sfrag, int mt, in
   uint32_t lo, hi;
   halves_u32(~sb & 0xFFFFu, lo, hi);
   return lo | (hi << 16);
+}
+
+// Sign words of projection tiles mt and mt + 1 for the wave's 32 tokens:
+// P = S_tile (hi + lo)^T on fp16 MFMA, both parts into one binary32
+// accumulator per tile; the two tiles' MFMAs alternate, so two independent
+// accumulator chains are in flight.
+__device__ __forceinline__ void res_tile_words2(const f16x8* sfrag, int mt, int lane,
+                                                const f16x8 (&bh)[kResKS],
+                                                const f16x8 (&bl)[kResKS], uint32_t& w0,
+                                                uint32_t& w1) {
+  f32x16 a0c = f32x16{}, a1c = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < kResKS; ++ks) {
+    const f16x8 a0 = sfrag[(mt * kResKS + ks) * 64 + lane];
+    const f16x8 a1 = sfrag[((mt + 1) * kResKS + ks) * 64 + lane];
+    a0c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, bh[ks], a0c, 0, 0, 0);
+    a1c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, bh[ks], a1c, 0, 0, 0);
+    a0c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, bl[ks], a0c, 0, 0, 0);
+    a1c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, bl[ks], a1c, 0, 0, 0);
+  }
+  w0 = res_acc_word(a0c);
+  w1 = res_acc_word(a1c);
+}
+
+// codes_rcp for t = RN32(x - z) given, without the clamp: t >= 0 and
+// t / s <= 15 + 2^-19, so the rounded quotient is already in [0, 15].
+__device__ __forceinline__ void codes_rcp_t(const float (&t)[8], float sdiv, float r,
+                                            bool divide, float (&c)[8]) {
+  bool near = divide;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float q = t[e] * r;
+    c[e] = __builtin_rintf(q);
+    near |= __builtin_fabsf(q - c[e]) > 0.5f - 0x1p-16f;
+  }
+  if (near) {
+    __asm__ volatile("");
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = __builtin_rintf(t[e] / sdiv);
+  }
 }
 
 __device__ __forceinline__ float other_half_f32(float v, bool take_hi) {
@@ -123,16 +154,18 @@ void residual_sketch_kernel(const _Float16* __restrict__ k, int64_t rows,
     float mn[NG], mx[NG];
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
-      mn[j] = (float)b[j * KPG][0];
-      mx[j] = mn[j];
+      // packed binary16 min / max (exact), two values per instruction
+      f16x2 pmn = {b[j * KPG][0], b[j * KPG][1]}, pmx = pmn;
 #pragma unroll
       for (int kk = 0; kk < KPG; ++kk)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = (float)b[j * KPG + kk][e];
-          mn[j] = __builtin_fminf(mn[j], v);
-          mx[j] = __builtin_fmaxf(mx[j], v);
+        for (int e = 0; e < 8; e += 2) {
+          const f16x2 v2 = {b[j * KPG + kk][e], b[j * KPG + kk][e + 1]};
+          pmn = __builtin_elementwise_min(pmn, v2);
+          pmx = __builtin_elementwise_max(pmx, v2);
         }
+      mn[j] = __builtin_fminf((float)pmn[0], (float)pmn[1]);
+      mx[j] = __builtin_fmaxf((float)pmx[0], (float)pmx[1]);
       mn[j] = __builtin_fminf(mn[j], other_half_f32(mn[j], h == 0));
       mx[j] = __builtin_fmaxf(mx[j], other_half_f32(mx[j], h == 0));
     }
@@ -153,14 +186,24 @@ void residual_sketch_kernel(const _Float16* __restrict__ k, int64_t rows,
 #pragma unroll
     for (int ks = 0; ks < kResKS; ++ks) {
       const int j = ks / KPG;
-      float xv[8], c[8];
+      float tv[8], c[8];
+      // t = RN32(x - z) straight from the binary16 key (a mixed-precision
+      // fused multiply-add by 1 rounds once)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xv[e] = (float)b[ks][e];
-      codes_rcp<8>(xv, mn[j], sdiv[j], rc[j], dv[j], c);
-      cw[ks] = pack_nibbles<8>(c);
+      for (int e = 0; e < 8; ++e) tv[e] = __builtin_fmaf((float)b[ks][e], 1.0f, -mn[j]);
+      codes_rcp_t(tv, sdiv[j], rc[j], dv[j], c);
+      // codes to bytes (exact integers, so the conversion's rounding is
+      // moot), even elements in one word and odd in another, then nibbles
+      uint32_t ev = 0, od = 0;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        ev = __builtin_amdgcn_cvt_pk_u8_f32(c[2 * e2], e2, ev);
+        od = __builtin_amdgcn_cvt_pk_u8_f32(c[2 * e2 + 1], e2, od);
+      }
+      cw[ks] = ev | (od << 4);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        rr[ks][e] = xv[e] - recon4(c[e], st[j], mn[j]);
+        rr[ks][e] = __builtin_fmaf((float)b[ks][e], 1.0f, -recon4(c[e], st[j], mn[j]));
         ss = __builtin_fmaf(rr[ks][e], rr[ks][e], ss);
         am = __builtin_fmaxf(am, __builtin_fabsf(rr[ks][e]));
       }
@@ -170,24 +213,31 @@ void residual_sketch_kernel(const _Float16* __restrict__ k, int64_t rows,
 
     // 3) residual scaled by 2^(15 - e) (am = f 2^e, f in [0.5, 1)) and split
     //    into binary16 hi + lo
+    // hi = v with its 13 low significand bits cleared (binary16-representable
+    // for |v| >= 2^-14), lo = v - hi exactly; both converted toward zero
+    // two at a time (lo's truncation is below 2^-20 |v|)
     const int sc = 15 - __builtin_amdgcn_frexp_expf(am);
     f16x8 bh[kResKS], bl[kResKS];
 #pragma unroll
     for (int ks = 0; ks < kResKS; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = __builtin_amdgcn_ldexpf(rr[ks][e], sc);
-        const _Float16 vh = (_Float16)v;
-        bh[ks][e] = vh;
-        bl[ks][e] = (_Float16)(v - (float)vh);
+      for (int e = 0; e < 8; e += 2) {
+        const float v0 = __builtin_amdgcn_ldexpf(rr[ks][e], sc);
+        const float v1 = __builtin_amdgcn_ldexpf(rr[ks][e + 1], sc);
+        const float h0 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v0) & 0xFFFFE000u);
+        const float h1 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v1) & 0xFFFFE000u);
+        const auto ph = __builtin_amdgcn_cvt_pkrtz(h0, h1);
+        const auto pl = __builtin_amdgcn_cvt_pkrtz(v0 - h0, v1 - h1);
+        bh[ks][e] = ph[0]; bh[ks][e + 1] = ph[1];
+        bl[ks][e] = pl[0]; bl[ks][e + 1] = pl[1];
       }
 
     // 4) sign words
     uint32_t wbuf[kResMT];
 #pragma unroll
-    for (int mt = 0; mt < kResMT; ++mt) {
+    for (int mt = 0; mt < kResMT; mt += 2) {
       __builtin_amdgcn_sched_barrier(0);
-      wbuf[mt] = res_tile_word(sf, mt, lane, bh, bl);
+      res_tile_words2(sf, mt, lane, bh, bl, wbuf[mt], wbuf[mt + 1]);
     }
 
     // 5) stores: half h writes code bytes [32 h, 32 h + 32), the steps
