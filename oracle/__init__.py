@@ -18,10 +18,11 @@ qjl     QJL key sketch (JL projection, sign bits, key norm) and the
 decode  one decode step over a QJL-key / INT8-value cache: scores, softmax,
         weighted sum of dequantised values
 int4    asymmetric group-wise INT4 quantize / dequantize
+int8_channel  per-channel (over a head's tokens) INT8 quantize / dequantize / score
 residual  QJL sketch of the INT4 residual and the two-stage score
 
 Every function is pinned by CPU tests (``tests/test_oracle_*.py``) against
 exact rational arithmetic, brute force on tiny inputs, closed forms and
 hand-derived fixtures; none is "parity unpinned".
 """
-from . import int8, int4, qjl, decode, residual  # noqa: F401
+from . import int8, int4, int8_channel, qjl, decode, residual  # noqa: F401
