@@ -1,6 +1,7 @@
 /*
  * kvq.h - C ABI of libkvq, a KV-cache compressor for AMD Instinct MI355X
- * (gfx950): per-row symmetric INT8 quantization, asymmetric group-wise INT4
+ * (gfx950): per-row and per-channel symmetric INT8 quantization, asymmetric
+ * group-wise INT4
  * quantization, the QJL key sketch and a two-stage INT4 + residual-QJL key
  * code, with decode-time scoring and attention read straight from the
  * compressed cache.
@@ -114,6 +115,56 @@ kvq_status kvq_dequantize_int8(const int8_t* codes, const float* scales, int64_t
 kvq_status kvq_scores_int8(const void* q, kvq_dtype q_dt, int64_t groups, int32_t nq,
                            const int8_t* codes, const float* scales, int64_t T, int32_t d,
                            float* scores, kvq_stream_t stream);
+
+/*
+ * kvq_quantize_int8_channel - per-channel symmetric INT8 quantization of a
+ * key cache: one scale per channel of each group, over the group's tokens.
+ *
+ * The symmetric INT8 formula of the Q-TensorFormer model card (section 6,
+ * labelled channel-wise there) with the scale taken per channel: for group
+ * g (one (batch, head)) of x [T, d] and channel c,
+ *   s_gc = RN32(max_t |x_gtc| / 127)
+ *   c_gtc = clamp(rne(RN32(x_gtc / s_gc)), -128, 127)
+ * (IEEE binary32 divisions, ties to even; a zero scale gives codes 0).
+ * Bit-identical to this definition.  The scales cover the T tokens given.
+ *
+ * x       [groups, T, d] KVQ_F32 or KVQ_F16 (x_dt)
+ * codes   [groups, T, d] int8, written (also used as scratch by the call)
+ * scales  [groups, d] binary32, written
+ * 16 <= d <= 8192, d % 16 == 0.  groups == 0 or T == 0 is a no-op.
+ * Errors: NULL, ALIGN, SHAPE, DTYPE.
+ */
+kvq_status kvq_quantize_int8_channel(const void* x, kvq_dtype x_dt, int64_t groups, int64_t T,
+                                     int32_t d, int8_t* codes, float* scales,
+                                     kvq_stream_t stream);
+
+/*
+ * kvq_dequantize_int8_channel - reconstruction of per-channel INT8 keys:
+ * out_gtc = RN32(c_gtc * s_gc); KVQ_F16 output is RN16 of it.  Bit-exact.
+ *
+ * codes [groups, T, d] int8;  scales [groups, d] binary32
+ * out   [groups, T, d] (out_dt), written.  d as kvq_quantize_int8_channel.
+ * Errors: NULL, ALIGN, SHAPE, DTYPE.
+ */
+kvq_status kvq_dequantize_int8_channel(const int8_t* codes, const float* scales, int64_t groups,
+                                       int64_t T, int32_t d, void* out, kvq_dtype out_dt,
+                                       kvq_stream_t stream);
+
+/*
+ * kvq_scores_int8_channel - decode-query scores against per-channel INT8
+ * keys: scores[g, j, t] = sum_c q[g, j, c] * s_gc * c_gtc, with the channel
+ * scales folded into the query (one binary32 product per channel) and
+ * binary32 accumulation.  Agrees with the exact value within
+ * 1e-5 * sum_c |q_c * s_gc * c_gtc|.
+ *
+ * q       [groups, nq, d] (q_dt);  codes [groups, T, d];  scales [groups, d]
+ * scores  [groups, nq, T] binary32, written
+ * 1 <= nq <= 64; d as kvq_quantize_int8_channel.
+ * Errors: NULL, ALIGN, SHAPE, DTYPE.
+ */
+kvq_status kvq_scores_int8_channel(const void* q, kvq_dtype q_dt, int64_t groups, int32_t nq,
+                                   const int8_t* codes, const float* scales, int64_t T, int32_t d,
+                                   float* scores, kvq_stream_t stream);
 
 /*
  * kvq_quantize_int4 - asymmetric group-wise INT4 quantization.

@@ -26,6 +26,12 @@ PROTOTYPES = {
     "kvq_scores_residual": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_void_p, c_int32, c_int32,
                                       c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_int64, c_int32, c_void_p, c_void_p]),
+    "kvq_quantize_int8_channel": (c_int32, [c_void_p, c_int32, c_int64, c_int64, c_int32, c_void_p,
+                                            c_void_p, c_void_p]),
+    "kvq_dequantize_int8_channel": (c_int32, [c_void_p, c_void_p, c_int64, c_int64, c_int32, c_void_p,
+                                              c_int32, c_void_p]),
+    "kvq_scores_int8_channel": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_void_p, c_void_p,
+                                          c_int64, c_int32, c_void_p, c_void_p]),
     "kvq_quantize_int4": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_int32, c_void_p, c_void_p,
                                     c_void_p, c_void_p]),
     "kvq_dequantize_int4": (c_int32, [c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_int32, c_void_p,

@@ -377,7 +377,9 @@ __device__ __forceinline__ void query_chunk(const float* qs, const TQ* qg, int d
   }
 }
 
-template <typename TQ, bool QLDS>
+// CH: per-channel scales (scales [groups, d]): the query staged in LDS is
+// q_c * s_c (one binary32 product) and the token factor is 1.
+template <typename TQ, bool QLDS, bool CH = false>
 __global__ __launch_bounds__(256) void scores_int8_kernel(const TQ* __restrict__ q, int nq,
                                                           const int8_t* __restrict__ codes,
                                                           const float* __restrict__ scales,
@@ -404,7 +406,10 @@ __global__ __launch_bounds__(256) void scores_int8_kernel(const TQ* __restrict__
 #pragma unroll
   for (int u = 0; u < kScoreUnroll; ++u) {
     tc[u] = std::min<int64_t>(t0 + u * 8 + slot, T - 1);
-    st[u] = scales[g * T + tc[u]];
+    if constexpr (CH)
+      st[u] = 1.0f;
+    else
+      st[u] = scales[g * T + tc[u]];
   }
   const int c_first = min(sub, cpr - 1);
   u32x4 w_first[kScoreUnroll];
@@ -417,7 +422,11 @@ __global__ __launch_bounds__(256) void scores_int8_kernel(const TQ* __restrict__
     const TQ* qg = q + ((int64_t)g * nq + j0) * d;
     if constexpr (QLDS) {
       __syncthreads();
-      for (int i = threadIdx.x; i < nqc * d; i += 256) qs[i] = to_f32(qg[i]);
+      if constexpr (CH) {
+        for (int i = threadIdx.x; i < nqc * d; i += 256) qs[i] = to_f32(qg[i]) * scales[g * d + i % d];
+      } else {
+        for (int i = threadIdx.x; i < nqc * d; i += 256) qs[i] = to_f32(qg[i]);
+      }
       __syncthreads();
     }
     float acc[kScoreUnroll][kScoreNqc];
@@ -483,6 +492,33 @@ static hipError_t scores_dispatch(const TQ* q, int64_t groups, int nq, const int
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+template <typename TQ>
+static hipError_t scores_channel_dispatch(const TQ* q, int64_t groups, int nq, const int8_t* codes,
+                                          const float* scales, int64_t T, int d, float* scores,
+                                          hipStream_t s) {
+  const int64_t tiles = (T + kScoreTokensPerBlock - 1) / kScoreTokensPerBlock;
+  const int64_t max_groups = std::max<int64_t>(1, (int64_t(1) << 22) / tiles);
+  for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
+    const int64_t ng = std::min(max_groups, groups - g0);
+    hipLaunchKernelGGL((scores_int8_kernel<TQ, true, true>), dim3((unsigned)(ng * tiles)),
+                       dim3(256), 0, s, q + g0 * nq * d, nq, codes + g0 * T * d, scales + g0 * d,
+                       T, d, tiles, scores + g0 * nq * T);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_scores_int8_channel(const void* q, int q_f16, int64_t groups, int nq,
+                                      const int8_t* codes, const float* scales, int64_t T, int d,
+                                      float* scores, hipStream_t s) {
+  if (q_f16)
+    return scores_channel_dispatch(static_cast<const _Float16*>(q), groups, nq, codes, scales, T,
+                                   d, scores, s);
+  return scores_channel_dispatch(static_cast<const float*>(q), groups, nq, codes, scales, T, d,
+                                 scores, s);
 }
 
 hipError_t launch_scores_int8(const void* q, int q_f16, int64_t groups, int nq,

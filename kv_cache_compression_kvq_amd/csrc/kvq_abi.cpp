@@ -87,6 +87,13 @@ kvq_status check_group(const char* fn, int32_t d, int32_t g) {
   return KVQ_OK;
 }
 
+kvq_status check_channel_d(const char* fn, int32_t d) {
+  if (d < 16 || d > kvq::kMaxChannelD || d % 16 != 0)
+    return fail(KVQ_ERR_SHAPE, "%s: d = %d must be a multiple of 16 in [16, %d]", fn, (int)d,
+                kvq::kMaxChannelD);
+  return KVQ_OK;
+}
+
 }  // namespace
 
 namespace kvq {
@@ -178,6 +185,59 @@ kvq_status kvq_scores_int8(const void* q, kvq_dtype q_dt, int64_t groups, int32_
   KVQ_CHECK_PTR(scores);
   return launched(fn, kvq::launch_scores_int8(q, q_dt == KVQ_F16, groups, nq, codes, scales, T, d,
                                               scores, reinterpret_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_quantize_int8_channel(const void* x, kvq_dtype x_dt, int64_t groups, int64_t T,
+                                     int32_t d, int8_t* codes, float* scales,
+                                     kvq_stream_t stream) {
+  const char* fn = "kvq_quantize_int8_channel";
+  kvq_status st;
+  if ((st = check_count(fn, "groups", groups)) || (st = check_count(fn, "T", T)) ||
+      (st = check_channel_d(fn, d)) || (st = check_dtype(fn, "x_dt", x_dt)))
+    return st;
+  if (groups == 0 || T == 0) return ok();
+  KVQ_CHECK_PTR(x);
+  KVQ_CHECK_PTR(codes);
+  KVQ_CHECK_PTR(scales);
+  return launched(fn, kvq::launch_quantize_int8_channel(x, x_dt == KVQ_F16, groups, T, d, codes,
+                                                        scales,
+                                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_dequantize_int8_channel(const int8_t* codes, const float* scales, int64_t groups,
+                                       int64_t T, int32_t d, void* out, kvq_dtype out_dt,
+                                       kvq_stream_t stream) {
+  const char* fn = "kvq_dequantize_int8_channel";
+  kvq_status st;
+  if ((st = check_count(fn, "groups", groups)) || (st = check_count(fn, "T", T)) ||
+      (st = check_channel_d(fn, d)) || (st = check_dtype(fn, "out_dt", out_dt)))
+    return st;
+  if (groups == 0 || T == 0) return ok();
+  KVQ_CHECK_PTR(codes);
+  KVQ_CHECK_PTR(scales);
+  KVQ_CHECK_PTR(out);
+  return launched(fn, kvq::launch_dequantize_int8_channel(codes, scales, groups, T, d, out,
+                                                          out_dt == KVQ_F16,
+                                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_scores_int8_channel(const void* q, kvq_dtype q_dt, int64_t groups, int32_t nq,
+                                   const int8_t* codes, const float* scales, int64_t T, int32_t d,
+                                   float* scores, kvq_stream_t stream) {
+  const char* fn = "kvq_scores_int8_channel";
+  kvq_status st;
+  if ((st = check_count(fn, "groups", groups)) || (st = check_count(fn, "T", T)) ||
+      (st = check_nq(fn, nq)) || (st = check_channel_d(fn, d)) ||
+      (st = check_dtype(fn, "q_dt", q_dt)))
+    return st;
+  if (groups == 0 || T == 0) return ok();
+  KVQ_CHECK_PTR(q);
+  KVQ_CHECK_PTR(codes);
+  KVQ_CHECK_PTR(scales);
+  KVQ_CHECK_PTR(scores);
+  return launched(fn, kvq::launch_scores_int8_channel(q, q_dt == KVQ_F16, groups, nq, codes, scales,
+                                                      T, d, scores,
+                                                      reinterpret_cast<hipStream_t>(stream)));
 }
 
 kvq_status kvq_quantize_int4(const void* x, kvq_dtype x_dt, int64_t rows, int32_t d, int32_t g,

@@ -25,6 +25,13 @@ hipError_t launch_dequantize_int8(const int8_t* codes, const float* scales, int6
 hipError_t launch_scores_int8(const void* q, int q_f16, int64_t groups, int nq,
                               const int8_t* codes, const float* scales, int64_t T, int d,
                               float* scores, hipStream_t s);
+hipError_t launch_quantize_int8_channel(const void* x, int x_f16, int64_t groups, int64_t T, int d,
+                                        int8_t* codes, float* scales, hipStream_t s);
+hipError_t launch_dequantize_int8_channel(const int8_t* codes, const float* scales, int64_t groups,
+                                          int64_t T, int d, void* out, int out_f16, hipStream_t s);
+hipError_t launch_scores_int8_channel(const void* q, int q_f16, int64_t groups, int nq,
+                                      const int8_t* codes, const float* scales, int64_t T, int d,
+                                      float* scores, hipStream_t s);
 hipError_t launch_quantize_int4(const void* x, int x_f16, int64_t rows, int d, int g,
                                 uint8_t* codes, float* steps, float* offsets, hipStream_t s);
 hipError_t launch_dequantize_int4(const uint8_t* codes, const float* steps, const float* offsets,
@@ -80,5 +87,6 @@ constexpr int kMinM = 32;
 constexpr int kMaxM = 1024;
 constexpr int kMaxNq = 64;
 constexpr int kMaxDecodeD = 1024;
+constexpr int kMaxChannelD = 8192;   // per-channel INT8: scales and query in LDS
 
 }  // namespace kvq

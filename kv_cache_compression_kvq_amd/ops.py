@@ -67,6 +67,47 @@ def dequantize_int8(codes: torch.Tensor, scales: torch.Tensor,
     return out
 
 
+def quantize_int8_channel(x: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """Keys x [G, T, d] fp32/fp16 -> (codes int8 [G, T, d], per-channel
+    scales fp32 [G, d])."""
+    _dev(x, "x")
+    G, T, d = x.shape
+    codes = torch.empty((G, T, d), dtype=torch.int8, device=x.device)
+    scales = torch.empty((G, d), dtype=torch.float32, device=x.device)
+    L.check(L.lib().kvq_quantize_int8_channel(_p(x), _dtype_code(x, "x"), G, T, d, _p(codes),
+                                              _p(scales), _stream(x)))
+    return codes, scales
+
+
+def dequantize_int8_channel(codes: torch.Tensor, scales: torch.Tensor,
+                            out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """codes int8 [G, T, d], scales fp32 [G, d] -> [G, T, d] in out_dtype."""
+    _dev(codes, "codes"), _dev(scales, "scales")
+    if codes.dtype != torch.int8 or scales.dtype != torch.float32:
+        raise TypeError("codes must be int8 and scales float32")
+    G, T, d = codes.shape
+    if tuple(scales.shape) != (G, d):
+        raise ValueError(f"scales {tuple(scales.shape)} for codes {tuple(codes.shape)}")
+    out = torch.empty((G, T, d), dtype=out_dtype, device=codes.device)
+    L.check(L.lib().kvq_dequantize_int8_channel(_p(codes), _p(scales), G, T, d, _p(out),
+                                                _dtype_code(out, "out_dtype"), _stream(codes)))
+    return out
+
+
+def scores_int8_channel(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
+    """q [G, nq, d]; codes [G, T, d] int8; scales [G, d] -> scores [G, nq, T] fp32."""
+    _dev(q, "q"), _dev(codes, "codes"), _dev(scales, "scales")
+    G, nq, d = q.shape
+    if codes.shape[0] != G or codes.shape[2] != d or tuple(scales.shape) != (G, d):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, codes {tuple(codes.shape)}, "
+                         f"scales {tuple(scales.shape)}")
+    T = codes.shape[1]
+    out = torch.empty((G, nq, T), dtype=torch.float32, device=q.device)
+    L.check(L.lib().kvq_scores_int8_channel(_p(q), _dtype_code(q, "q"), G, nq, _p(codes),
+                                            _p(scales), T, d, _p(out), _stream(q)))
+    return out
+
+
 def quantize_int4(x: torch.Tensor, g: int) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """x [..., d] fp32/fp16, group size g -> (codes uint8 [..., d/2] two per
     byte, steps fp32 [..., d/g], offsets fp32 [..., d/g])."""

@@ -238,3 +238,25 @@ def test_scores_residual_validation():
     assert call(groups=0, q=None, S=None, codes=None, steps=None, offsets=None, bits=None,
                 norms=None, scores=None) == L.KVQ_OK
     assert call(T=0, scores=None) == L.KVQ_OK
+
+
+def test_int8_channel_validation():
+    qf = L.lib().kvq_quantize_int8_channel
+    _err(qf(None, L.KVQ_F16, 2, 64, 128, A, A, None), L.KVQ_ERR_NULL)
+    _err(qf(A, L.KVQ_F16, 2, 64, 128, MIS, A, None), L.KVQ_ERR_ALIGN)
+    for d in (0, 8, 8208, 100):
+        _err(qf(A, L.KVQ_F16, 2, 64, d, A, A, None), L.KVQ_ERR_SHAPE)
+    _err(qf(A, L.KVQ_F16, -1, 64, 128, A, A, None), L.KVQ_ERR_SHAPE)
+    _err(qf(A, L.KVQ_F16, 2, -64, 128, A, A, None), L.KVQ_ERR_SHAPE)
+    _err(qf(A, 9, 2, 64, 128, A, A, None), L.KVQ_ERR_DTYPE)
+    assert qf(None, L.KVQ_F16, 0, 64, 128, None, None, None) == L.KVQ_OK
+    assert qf(None, L.KVQ_F16, 2, 0, 128, None, None, None) == L.KVQ_OK
+    dq = L.lib().kvq_dequantize_int8_channel
+    _err(dq(A, None, 2, 64, 128, A, L.KVQ_F32, None), L.KVQ_ERR_NULL)
+    _err(dq(A, A, 2, 64, 120, A, L.KVQ_F32, None), L.KVQ_ERR_SHAPE)
+    _err(dq(A, A, 2, 64, 128, A, 4, None), L.KVQ_ERR_DTYPE)
+    sc = L.lib().kvq_scores_int8_channel
+    _err(sc(A, L.KVQ_F16, 2, 0, A, A, 64, 128, A, None), L.KVQ_ERR_SHAPE)
+    _err(sc(A, L.KVQ_F16, 2, 1, A, A, 64, 16384, A, None), L.KVQ_ERR_SHAPE)
+    _err(sc(A, L.KVQ_F16, 2, 1, A, MIS, 64, 128, A, None), L.KVQ_ERR_ALIGN)
+    assert sc(None, L.KVQ_F16, 2, 1, None, None, 0, 128, None, None) == L.KVQ_OK
