@@ -111,8 +111,9 @@ COLD_BYTES = 1 << 30     # rotate inputs over > 1 GiB: 4x the 256 MB last-level 
 
 
 def components(K, si, torch, np):
-    """GB/s of the INT8, INT4, QJL and two-stage kernels on their own workloads, cold: each
-    timed call reads a different copy of its inputs, and the copies together
+    """GB/s of the INT8 (per row and per channel), INT4, QJL and two-stage
+    kernels on their own workloads, cold: each timed call reads a different
+    copy of its inputs, and the copies together
     exceed 1 GiB, so no call finds its inputs in the MALL or L2.  Calls run
     back to back in blocks timed by one pair of HIP events; the median block's
     mean per call is reported."""
@@ -182,6 +183,18 @@ def components(K, si, torch, np):
         gbs(f"llama_layer_dequantize_int4_kv_f16_g{g}", R * 64 + 8 * R * (128 // g) + 2 * R * 128,
             [lambda c=c: K.dequantize_int4(c[0], c[1], c[2], g, torch.float16) for c in c4])
         del c4
+    # per-channel INT8 keys (one scale per channel over a head's 4096 tokens)
+    k3s = [t[: R // 2].view(32, 4096, 128) for t in kvs]
+    cch = [K.quantize_int8_channel(t) for t in k3s]
+    half = R // 2
+    gbs("llama_layer_quantize_int8_channel_k_f16", 2 * half * 128 + half * 128 + 4 * 32 * 128,
+        [lambda t=t: K.quantize_int8_channel(t) for t in k3s])
+    gbs("llama_layer_dequantize_int8_channel_k_f16", half * 128 + 4 * 32 * 128 + 2 * half * 128,
+        [lambda c=c: K.dequantize_int8_channel(c[0], c[1], torch.float16) for c in cch])
+    qch = torch.from_numpy(si.queries(W, 32, 1, 128, "f16")).to(dev)
+    gbs("llama_layer_scores_int8_channel", 32 * 4096 * (128 + 4) + 32 * 128 * (2 + 4),
+        [lambda c=c: K.scores_int8_channel(qch, c[0], c[1]) for c in cch])
+    del k3s, cch
     q = torch.from_numpy(si.queries(W, 32, 1, 128, "f16")).to(dev)
     halves = [(c[0][: R // 2].view(32, 4096, 128), c[1][: R // 2].view(32, 4096)) for c in cs]
     gbs("llama_layer_scores_int8", 32 * 4096 * (128 + 4 + 4) + 32 * 128 * 2,
