@@ -112,7 +112,14 @@ __global__ __launch_bounds__(kChThreads) void channel_scale_kernel(
   const int c = (int)(idx % d);
   const uint32_t* p = partials + g * nslab * d + c;
   uint32_t a = 0;
-  for (int64_t s = 0; s < nslab; ++s) a = max(a, p[s * d]);
+  // 8 slabs' loads in flight at a time (past the last slab: the last one again)
+  for (int64_t s0 = 0; s0 < nslab; s0 += 8) {
+    uint32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[std::min<int64_t>(s0 + u, nslab - 1) * d];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a = max(a, v[u]);
+  }
   scales[idx] = __builtin_bit_cast(float, a) / 127.0f;
 }
 
