@@ -203,6 +203,16 @@ def components(K, si, torch, np):
     q4 = torch.from_numpy(si.queries(W, 32, 4, 128, "f16")).to(dev)
     gbs("llama_layer_scores_int8_gqa4", 32 * 4096 * (128 + 4 + 4 * 4) + 32 * 4 * 128 * 2,
         [lambda h=h: K.scores_int8(q4, h[0], h[1]) for h in halves])
+    # INT8 scores at a cache length where HBM, not launch latency, bounds
+    # them: 32 heads x 262144 tokens x 128 (1.1 GB of codes), 1 and 4 queries
+    Tl = 262144
+    big = [(torch.randint(-127, 128, (32, Tl, 128), dtype=torch.int8, device=dev),
+            torch.rand(32, Tl, device=dev)) for _ in range(2)]
+    gbs("scores_int8_32x262144x128", 32 * Tl * (128 + 4 + 4) + 32 * 128 * 2,
+        [lambda c=c: K.scores_int8(q, c[0], c[1]) for c in big])
+    gbs("scores_int8_gqa4_32x262144x128", 32 * Tl * (128 + 4 + 4 * 4) + 32 * 4 * 128 * 2,
+        [lambda c=c: K.scores_int8(q4, c[0], c[1]) for c in big])
+    del big
     del k, v, kv, kvs, cs, halves
     torch.cuda.empty_cache()
 

@@ -469,10 +469,135 @@ __global__ __launch_bounds__(256) void scores_int8_kernel(const TQ* __restrict__
   }
 }
 
+// Scale-folded INT8 score, d = 128, up to 4 queries per group: 8 lanes per
+// token (lane `sub` owns channels 16 sub .. 16 sub + 15, its query values in
+// registers), 8 tokens per wave pass, kS128U passes in flight and the next
+// iteration's codes and scales requested before the current one is scored.
+// Each block covers ITERS * 128 tokens of one group.  Same arithmetic as
+// scores_int8_kernel (per-lane fused multiply-adds in channel order, an
+// 8-lane DPP sum, then the token scale), so the same scores bit for bit.
+constexpr int kS128U = 4;
+constexpr int kS128Step = 4 * 8 * kS128U;                 // tokens per block iteration
+
+template <typename TQ, int NQ, bool CH, int ITERS>
+__global__ __launch_bounds__(256) void scores_int8_d128_kernel(const TQ* __restrict__ q,
+                                                               const int8_t* __restrict__ codes,
+                                                               const float* __restrict__ scales,
+                                                               int64_t T, int64_t tiles,
+                                                               float* __restrict__ scores) {
+  constexpr int D = 128;
+  __shared__ __align__(16) float qs[NQ * D];
+  const int64_t g = blockIdx.x / tiles;
+  const int64_t tile = blockIdx.x % tiles;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int sub = lane & 7;
+  const int slot = lane >> 3;
+  const int8_t* cg = codes + g * T * D + sub * 16;
+  const float* sg = scales + g * T;
+  const int64_t t0 = tile * (ITERS * kS128Step) + wave * (8 * kS128U) + slot;
+  struct Batch {
+    u32x4 c[kS128U];
+    float s[kS128U];
+  };
+  // unconditional loads (tokens past T re-read token T - 1, not stored)
+  auto load = [&](Batch& B, int it) {
+#pragma unroll
+    for (int u = 0; u < kS128U; ++u) {
+      const int64_t t = std::min<int64_t>(t0 + it * (32 * kS128U) + u * 8, T - 1);
+      B.c[u] = ld_stream(reinterpret_cast<const u32x4*>(cg + t * D));
+      if constexpr (!CH) B.s[u] = sg[t];
+    }
+  };
+  Batch ba, bb;
+  load(ba, 0);
+  const TQ* qg = q + g * NQ * D;
+  for (int i = threadIdx.x; i < NQ * D; i += 256) {
+    if constexpr (CH)
+      qs[i] = to_f32(qg[i]) * scales[g * D + (i & (D - 1))];
+    else
+      qs[i] = to_f32(qg[i]);
+  }
+  __syncthreads();
+  float qv[NQ][16];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const f32x4 x = reinterpret_cast<const f32x4*>(qs + j * D + sub * 16)[v];
+      qv[j][4 * v] = x[0]; qv[j][4 * v + 1] = x[1]; qv[j][4 * v + 2] = x[2]; qv[j][4 * v + 3] = x[3];
+    }
+  auto score = [&](const Batch& B, int it) {
+#pragma unroll
+    for (int u = 0; u < kS128U; ++u) {
+      const int64_t t = t0 + it * (32 * kS128U) + u * 8;
+      float cf[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) cf[e] = i8_to_f32(B.c[u][e >> 2], e & 3);
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        float a = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) a = __builtin_fmaf(qv[j][e], cf[e], a);
+        float tot = seg_sum_f32<8>(a);
+        if constexpr (!CH) tot = tot * B.s[u];
+        if (sub == 0 && t < T) scores[(g * NQ + j) * T + t] = tot;
+      }
+    }
+  };
+#pragma unroll
+  for (int it = 0; it < ITERS; it += 2) {
+    if (it + 1 < ITERS) load(bb, it + 1);
+    score(ba, it);
+    if (it + 2 < ITERS) load(ba, it + 2);
+    if (it + 1 < ITERS) score(bb, it + 1);
+  }
+}
+
+template <typename TQ, bool CH, int ITERS>
+static hipError_t scores_d128_launch_it(const TQ* q, int64_t groups, int nq, const int8_t* codes,
+                                        const float* scales, int64_t T, float* scores,
+                                        hipStream_t s) {
+  const int64_t tiles = (T + ITERS * kS128Step - 1) / (ITERS * kS128Step);
+  const int64_t max_groups = std::max<int64_t>(1, (int64_t(1) << 22) / tiles);
+  for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
+    const int64_t ng = std::min(max_groups, groups - g0);
+    const TQ* qp = q + g0 * nq * 128;
+    const int8_t* cp = codes + g0 * T * 128;
+    const float* sp = scales + g0 * (CH ? 128 : T);
+    float* op = scores + g0 * nq * T;
+    const dim3 grid((unsigned)(ng * tiles));
+    switch (nq) {
+      case 1: hipLaunchKernelGGL((scores_int8_d128_kernel<TQ, 1, CH, ITERS>), grid, dim3(256), 0, s, qp, cp, sp, T, tiles, op); break;
+      case 2: hipLaunchKernelGGL((scores_int8_d128_kernel<TQ, 2, CH, ITERS>), grid, dim3(256), 0, s, qp, cp, sp, T, tiles, op); break;
+      case 3: hipLaunchKernelGGL((scores_int8_d128_kernel<TQ, 3, CH, ITERS>), grid, dim3(256), 0, s, qp, cp, sp, T, tiles, op); break;
+      default: hipLaunchKernelGGL((scores_int8_d128_kernel<TQ, 4, CH, ITERS>), grid, dim3(256), 0, s, qp, cp, sp, T, tiles, op); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Longer token ranges per block where the grid stays at >= 1024 blocks
+// (4 per compute unit).
+template <typename TQ, bool CH>
+static hipError_t scores_d128_launch(const TQ* q, int64_t groups, int nq, const int8_t* codes,
+                                     const float* scales, int64_t T, float* scores,
+                                     hipStream_t s) {
+  const int64_t rows = groups * T;
+  if (rows >= 1024LL * 8 * kS128Step)
+    return scores_d128_launch_it<TQ, CH, 8>(q, groups, nq, codes, scales, T, scores, s);
+  if (rows >= 1024LL * 2 * kS128Step)
+    return scores_d128_launch_it<TQ, CH, 2>(q, groups, nq, codes, scales, T, scores, s);
+  return scores_d128_launch_it<TQ, CH, 1>(q, groups, nq, codes, scales, T, scores, s);
+}
+
 template <typename TQ>
 static hipError_t scores_dispatch(const TQ* q, int64_t groups, int nq, const int8_t* codes,
                                   const float* scales, int64_t T, int d, float* scores,
                                   hipStream_t s) {
+  if (d == 128 && nq <= 4) return scores_d128_launch<TQ, false>(q, groups, nq, codes, scales, T, scores, s);
   const int64_t tiles = (T + kScoreTokensPerBlock - 1) / kScoreTokensPerBlock;
   // launch in slices of whole groups so grid.x stays far below 2^32
   const int64_t max_groups = std::max<int64_t>(1, (int64_t(1) << 22) / tiles);
@@ -498,6 +623,7 @@ template <typename TQ>
 static hipError_t scores_channel_dispatch(const TQ* q, int64_t groups, int nq, const int8_t* codes,
                                           const float* scales, int64_t T, int d, float* scores,
                                           hipStream_t s) {
+  if (d == 128 && nq <= 4) return scores_d128_launch<TQ, true>(q, groups, nq, codes, scales, T, scores, s);
   const int64_t tiles = (T + kScoreTokensPerBlock - 1) / kScoreTokensPerBlock;
   const int64_t max_groups = std::max<int64_t>(1, (int64_t(1) << 22) / tiles);
   for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
