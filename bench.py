@@ -259,6 +259,46 @@ def components(K, si, torch, np):
         R / res["residual_scores_f16_m256_g32"]["ms"] * 1e3, 1)
     del kk, sk, b3, st, first
     torch.cuda.empty_cache()
+
+    # grouped-query decode: 128 KV heads (16 x 8) x 32768 tokens, 4 query
+    # heads per KV head (m = 256, d = 128), against the same 4 queries
+    # decoded one at a time; cache from the bench's decode generator recipe
+    # (fp16 N(0,1) keys and values, QJL keys, INT8 values) on 16 x 8 heads
+    Gk, Tq, nqg = 128, 32768, 4
+    kbits_, knorm_, vcode_, vscal_ = [], [], [], []
+    Sg = torch.from_numpy(si.projection(si.W_DECODE, m, d, "f16")).to(dev)
+    for g0 in range(0, Gk, 16):
+        kk_ = torch.from_numpy(si.stream(si.W_DECODE, si.K, 16 * Tq * d, "f16",
+                                         start=g0 * Tq * d)).to(dev).view(-1, d)
+        vv_ = torch.from_numpy(si.stream(si.W_DECODE, si.V, 16 * Tq * d, "f16",
+                                         start=g0 * Tq * d)).to(dev).view(-1, d)
+        b_, n_ = K.qjl_sketch(kk_, Sg)
+        c_, s_ = K.quantize_int8(vv_)
+        kbits_.append(b_); knorm_.append(n_); vcode_.append(c_); vscal_.append(s_)
+        del kk_, vv_
+    kbg = torch.cat(kbits_).view(Gk, Tq, m // 32)
+    kng = torch.cat(knorm_).view(Gk, Tq)
+    vcg = torch.cat(vcode_).view(Gk, Tq, d)
+    vsg = torch.cat(vscal_).view(Gk, Tq)
+    del kbits_, knorm_, vcode_, vscal_
+    qg = torch.from_numpy(si.queries(si.W_DECODE, Gk, nqg, d, "f16")).to(dev)
+    wsg = torch.empty(K.decode_gqa_workspace_bytes(Gk, nqg, Tq, d, m), dtype=torch.uint8, device=dev)
+    og = torch.empty((Gk, nqg, d), dtype=torch.float32, device=dev)
+    gbs("decode_gqa4_128x32768", Gk * Tq * (m // 8 + 2 + d + 4) + Gk * nqg * d * (2 + 4),
+        [lambda: K.decode_qjl_int8_gqa(qg, Sg, kbg, kng, vcg, vsg, workspace=wsg, out=og)],
+        reps=10)
+    res["decode_gqa4_128x32768"]["scores/s"] = round(
+        Gk * nqg * Tq / res["decode_gqa4_128x32768"]["ms"] * 1e3, 1)
+    qs1 = [qg[:, j].contiguous() for j in range(nqg)]
+    ws1 = torch.empty(K.decode_workspace_bytes(Gk, Tq, d, m), dtype=torch.uint8, device=dev)
+    o1 = torch.empty((Gk, d), dtype=torch.float32, device=dev)
+    gbs("decode_4x1query_128x32768", 4 * (Gk * Tq * (m // 8 + 2 + d + 4) + Gk * d * (2 + 4)),
+        [lambda: [K.decode_qjl_int8(qq, Sg, kbg, kng, vcg, vsg, workspace=ws1, out=o1)
+                  for qq in qs1]], reps=10)
+    res["decode_4x1query_128x32768"]["scores/s"] = round(
+        Gk * nqg * Tq / res["decode_4x1query_128x32768"]["ms"] * 1e3, 1)
+    del kbg, kng, vcg, vsg, qg, wsg, og, ws1, o1
+    torch.cuda.empty_cache()
     return res
 
 

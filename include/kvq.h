@@ -356,6 +356,35 @@ kvq_status kvq_decode_qjl_int8(const void* q, kvq_dtype q_dt, int64_t groups, co
                                void* ws, size_t ws_bytes, float* out, kvq_stream_t stream);
 
 /*
+ * kvq_decode_gqa_workspace_bytes - scratch size for kvq_decode_qjl_int8_gqa
+ * (0 for invalid shapes or when the device cannot be queried).
+ */
+size_t kvq_decode_gqa_workspace_bytes(int64_t groups, int32_t nq, int64_t T, int32_t d,
+                                      int32_t m);
+
+/*
+ * kvq_decode_qjl_int8_gqa - kvq_decode_qjl_int8 for grouped-query attention:
+ * nq query heads share each group's compressed keys and values (the
+ * Q-TensorFormer card, section 4, shares one KV head among several query
+ * heads).  For every query j of group g the result is exactly what
+ * kvq_decode_qjl_int8 computes for that query alone (same tolerance).  The
+ * nq workgroups that read the same token range run on one XCD at about the
+ * same time, so the range comes from HBM about once.
+ *
+ * q    [groups, nq, d] (q_dt);  out [groups, nq, d] binary32, written
+ * ws   device scratch of ws_bytes >= kvq_decode_gqa_workspace_bytes(groups,
+ *      nq, T, d, m); other arguments as kvq_decode_qjl_int8.
+ * 1 <= nq <= 64.
+ * Errors: NULL, ALIGN, SHAPE, DTYPE, WORKSPACE.
+ */
+kvq_status kvq_decode_qjl_int8_gqa(const void* q, kvq_dtype q_dt, int64_t groups, int32_t nq,
+                                   const void* S, kvq_dtype S_dt, int32_t m,
+                                   const uint32_t* kbits, const uint16_t* knorms,
+                                   const int8_t* vcodes, const float* vscales, int64_t T,
+                                   int32_t d, float sm_scale, void* ws, size_t ws_bytes,
+                                   float* out, kvq_stream_t stream);
+
+/*
  * kvq_cache_append - compress-on-write for one decode step: the newest key
  * and value of every group are compressed and written into token position
  * `pos` of the group's compressed cache (the cache layout of

@@ -11,7 +11,9 @@ streams; every step of the computation runs in libkvq.
 from ._lib import KvqError, LIB_PATH, lib  # noqa: F401
 from .ops import (  # noqa: F401
     cache_append,
+    decode_gqa_workspace_bytes,
     decode_qjl_int8,
+    decode_qjl_int8_gqa,
     decode_workspace_bytes,
     dequantize_int4,
     dequantize_int8,

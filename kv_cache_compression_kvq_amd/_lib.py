@@ -42,6 +42,11 @@ PROTOTYPES = {
                                  c_void_p, c_void_p]),
     "kvq_scores_qjl": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_void_p, c_int32, c_int32,
                                  c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p]),
+    "kvq_decode_gqa_workspace_bytes": (c_size_t, [c_int64, c_int32, c_int64, c_int32, c_int32]),
+    "kvq_decode_qjl_int8_gqa": (c_int32, [c_void_p, c_int32, c_int64, c_int32, c_void_p, c_int32,
+                                          c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
+                                          c_int32, c_float, c_void_p, c_size_t, c_void_p,
+                                          c_void_p]),
     "kvq_decode_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int32, c_int32]),
     "kvq_decode_qjl_int8": (c_int32, [c_void_p, c_int32, c_int64, c_void_p, c_int32, c_int32,
                                       c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32,

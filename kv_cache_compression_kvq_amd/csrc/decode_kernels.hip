@@ -8,7 +8,7 @@
 //   out     = sum_t softmax_t(lam * sigma_t) * s_t * c_t
 //
 // Work split: the T tokens of a (batch, head) group are cut into `splits`
-// ranges; one workgroup per (group, range) builds the byte tables from y = S q
+// ranges; one workgroup per (group, range, query) builds the byte tables from y = S q
 // in LDS, streams its tokens once (sign words, norm, value codes, value
 // scale) and keeps a running max / sum / weighted value sum per wave
 // (online softmax).  The eight waves are merged in LDS and the workgroup
@@ -19,6 +19,11 @@
 // lanes per token row, so a wave's load covers 64 / LPV whole rows (1 KiB);
 // they are issued at the top of each 64-token chunk, before the scores that
 // weight them are known, to keep HBM busy.
+//
+// Grouped-query attention (nq query heads per KV head): the nq workgroups of
+// one (group, range) are numbered blockIdx = 8 (nq k + j) + x, so they run on
+// the same XCD (workgroups go to XCD blockIdx mod 8) at about the same time
+// and all but the first find the range's cache lines in that XCD's L2.
 #include "kvq_device.h"
 #include "kvq_launch.h"
 #include "kvq_qjl_device.h"
@@ -68,7 +73,7 @@ template <int W, int LPV>
 __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(4))) void decode_split_kernel(
     const float* __restrict__ yall, int m_rt, int d, const uint32_t* __restrict__ kbits, const uint16_t* __restrict__ knorms,
     const int8_t* __restrict__ vcodes, const float* __restrict__ vscales, int64_t T,
-    int64_t splits, int64_t tps, float lam, float* __restrict__ partials) {
+    int64_t splits, int64_t tps, float lam, int nq, int64_t pairs, float* __restrict__ partials) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   const int m = W > 0 ? 32 * W : m_rt;
   const int words = m / 32;
@@ -77,8 +82,16 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   float* y = lut + byte_table_floats(m, W == 8);
   float* wpart = y + m;                                // [kDecodeWaves][d + 2]
 
-  const int64_t g = blockIdx.x / splits;
-  const int64_t sp = blockIdx.x % splits;
+  // (group, range) pair p and query j of this workgroup; padding workgroups
+  // past the last pair exit here, before any barrier
+  const int64_t bx = blockIdx.x;
+  const int64_t rest = bx >> 3;
+  const int jq = (int)(rest % nq);
+  const int64_t p = (rest / nq) * 8 + (bx & 7);
+  if (p >= pairs) return;
+  const int64_t g = p / splits;             // KV group
+  const int64_t sp = p % splits;
+  const int64_t vg = g * nq + jq;           // query (group, head)
   const int64_t t_begin = sp * tps;
   const int64_t t_end = std::min<int64_t>(T, t_begin + tps);
   const int lane = threadIdx.x & 63;
@@ -170,7 +183,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
 
     // y first (so its wait leaves the chunk loads in flight); every thread
     // writes, past m into the merge area, which is written again later
-    const float yv = yall[g * m + min((int)threadIdx.x, m - 1)];
+    const float yv = yall[vg * m + min((int)threadIdx.x, m - 1)];
     const int first = wave * kDecodeChunk;
     Keys ka, kb;
     Vals va, vb;
@@ -198,7 +211,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
       }
     }
   } else {
-    for (int i = threadIdx.x; i < m; i += kDecodeThreads) y[i] = yall[g * m + i];
+    for (int i = threadIdx.x; i < m; i += kDecodeThreads) y[i] = yall[vg * m + i];
     __syncthreads();
     build_byte_tables(y, m / 8, lut);
     __syncthreads();
@@ -276,7 +289,7 @@ __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(
   float sc[kDecodeWaves];
 #pragma unroll
   for (int w = 0; w < kDecodeWaves; ++w) sc[w] = (Mw[w] == -INFINITY) ? 0.0f : __expf(Mw[w] - Ms);
-  float* out = partials + (g * splits + sp) * (int64_t)(d + 2);
+  float* out = partials + (vg * splits + sp) * (int64_t)(d + 2);
   if (threadIdx.x == 0) {
     float Ls = 0.0f;
 #pragma unroll
@@ -334,9 +347,11 @@ static size_t decode_y_bytes(int64_t groups, int m) {
   return ((size_t)groups * (size_t)m * sizeof(float) + 255) / 256 * 256;
 }
 
-size_t decode_workspace_bytes(int64_t groups, int64_t T, int d, int m, const DeviceInfo& dev) {
-  const DecodeSplit s = decode_split(groups, T, dev);
-  return decode_y_bytes(groups, m) + (size_t)groups * (size_t)s.splits * (size_t)(d + 2) * sizeof(float);
+size_t decode_workspace_bytes(int64_t groups, int nq, int64_t T, int d, int m,
+                              const DeviceInfo& dev) {
+  const DecodeSplit s = decode_split(groups * nq, T, dev);
+  return decode_y_bytes(groups * nq, m) +
+         (size_t)groups * (size_t)nq * (size_t)s.splits * (size_t)(d + 2) * sizeof(float);
 }
 
 // The specialised kernel (m = 256, d = 128) reads the rotated byte tables.
@@ -348,20 +363,24 @@ size_t decode_lds_bytes(int m, int d) {
 }
 
 template <int W, int LPV>
-static hipError_t decode_launch(const float* y, int64_t groups, int m, const uint32_t* kbits,
-                                const uint16_t* knorms, const int8_t* vcodes,
-                                const float* vscales, int64_t T, int d, float lam, float* partials,
-                                const DecodeSplit& sp, hipStream_t st) {
+static hipError_t decode_launch(const float* y, int64_t groups, int nq, int m,
+                                const uint32_t* kbits, const uint16_t* knorms,
+                                const int8_t* vcodes, const float* vscales, int64_t T, int d,
+                                float lam, float* partials, const DecodeSplit& sp,
+                                hipStream_t st) {
   const size_t lds = decode_lds_bytes(m, d);
   hipError_t e0 = allow_dynamic_lds(decode_split_kernel<W, LPV>, lds);
   if (e0 != hipSuccess) return e0;
-  const int64_t max_groups = std::max<int64_t>(1, (int64_t(1) << 22) / sp.splits);
+  const int64_t max_groups = std::max<int64_t>(1, (int64_t(1) << 21) / (sp.splits * nq));
   for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
     const int64_t ng = std::min(max_groups, groups - g0);
-    hipLaunchKernelGGL((decode_split_kernel<W, LPV>), dim3((unsigned)(ng * sp.splits)),
-                       dim3(kDecodeThreads), lds, st, y + g0 * m, m, d, kbits + g0 * T * (m / 32),
-                       knorms + g0 * T, vcodes + g0 * T * d, vscales + g0 * T, T, sp.splits,
-                       sp.tokens_per_split, lam, partials + g0 * sp.splits * (d + 2));
+    const int64_t pairs = ng * sp.splits;
+    const int64_t blocks = (pairs + 7) / 8 * 8 * nq;
+    hipLaunchKernelGGL((decode_split_kernel<W, LPV>), dim3((unsigned)blocks),
+                       dim3(kDecodeThreads), lds, st, y + g0 * nq * m, m, d,
+                       kbits + g0 * T * (m / 32), knorms + g0 * T, vcodes + g0 * T * d,
+                       vscales + g0 * T, T, sp.splits, sp.tokens_per_split, lam, nq, pairs,
+                       partials + g0 * nq * sp.splits * (d + 2));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -369,16 +388,18 @@ static hipError_t decode_launch(const float* y, int64_t groups, int m, const uin
 }
 
 template <typename TS, typename TQ>
-static hipError_t decode_typed(const TQ* q, int64_t groups, const TS* S, int m,
+static hipError_t decode_typed(const TQ* q, int64_t groups, int nq, const TS* S, int m,
                                const uint32_t* kbits, const uint16_t* knorms, const int8_t* vcodes,
                                const float* vscales, int64_t T, int d, float lam, void* ws,
                                float* out, const DeviceInfo& dev, hipStream_t st) {
-  const DecodeSplit sp = decode_split(groups, T, dev);
+  // queries are numbered (group, head) = g nq + j throughout: y, partials, out
+  const int64_t nqg = groups * nq;
+  const DecodeSplit sp = decode_split(nqg, T, dev);
   float* y = static_cast<float*>(ws);
-  float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + decode_y_bytes(groups, m));
+  float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + decode_y_bytes(nqg, m));
   const int64_t max_groups = int64_t(1) << 22;
-  for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
-    const int64_t ng = std::min(max_groups, groups - g0);
+  for (int64_t g0 = 0; g0 < nqg; g0 += max_groups) {
+    const int64_t ng = std::min(max_groups, nqg - g0);
     hipLaunchKernelGGL((qjl_project_kernel<TS, TQ>), dim3((unsigned)ng), dim3(256), 0, st,
                        q + g0 * d, S, m, d, y + g0 * m);
     hipError_t e1 = hipGetLastError();
@@ -386,23 +407,23 @@ static hipError_t decode_typed(const TQ* q, int64_t groups, const TS* S, int m,
   }
   hipError_t e;
   if (decode_rotated(m, d))
-    e = decode_launch<8, 8>(y, groups, m, kbits, knorms, vcodes, vscales, T, d, lam, partials, sp, st);
+    e = decode_launch<8, 8>(y, groups, nq, m, kbits, knorms, vcodes, vscales, T, d, lam, partials, sp, st);
   else if (d == 64)
-    e = decode_launch<0, 4>(y, groups, m, kbits, knorms, vcodes, vscales, T, d, lam, partials, sp, st);
+    e = decode_launch<0, 4>(y, groups, nq, m, kbits, knorms, vcodes, vscales, T, d, lam, partials, sp, st);
   else if (d == 128)
-    e = decode_launch<0, 8>(y, groups, m, kbits, knorms, vcodes, vscales, T, d, lam, partials, sp, st);
+    e = decode_launch<0, 8>(y, groups, nq, m, kbits, knorms, vcodes, vscales, T, d, lam, partials, sp, st);
   else if (d == 256)
-    e = decode_launch<0, 16>(y, groups, m, kbits, knorms, vcodes, vscales, T, d, lam, partials, sp, st);
+    e = decode_launch<0, 16>(y, groups, nq, m, kbits, knorms, vcodes, vscales, T, d, lam, partials, sp, st);
   else
-    e = decode_launch<0, 64>(y, groups, m, kbits, knorms, vcodes, vscales, T, d, lam, partials, sp, st);
+    e = decode_launch<0, 64>(y, groups, nq, m, kbits, knorms, vcodes, vscales, T, d, lam, partials, sp, st);
   if (e != hipSuccess) return e;
-  const int64_t n = groups * d;
+  const int64_t n = nqg * d;
   hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                     partials, groups, sp.splits, d, out);
+                     partials, nqg, sp.splits, d, out);
   return hipGetLastError();
 }
 
-hipError_t launch_decode_qjl_int8(const void* q, int q_f16, int64_t groups, const void* S,
+hipError_t launch_decode_qjl_int8(const void* q, int q_f16, int64_t groups, int nq, const void* S,
                                   int S_f16, int m, const uint32_t* kbits, const uint16_t* knorms,
                                   const int8_t* vcodes, const float* vscales, int64_t T, int d,
                                   float sm_scale, void* ws, float* out, const DeviceInfo& dev,
@@ -410,16 +431,16 @@ hipError_t launch_decode_qjl_int8(const void* q, int q_f16, int64_t groups, cons
   if (S_f16) {
     const _Float16* Sp = static_cast<const _Float16*>(S);
     if (q_f16)
-      return decode_typed(static_cast<const _Float16*>(q), groups, Sp, m, kbits, knorms, vcodes,
+      return decode_typed(static_cast<const _Float16*>(q), groups, nq, Sp, m, kbits, knorms, vcodes,
                           vscales, T, d, sm_scale, ws, out, dev, st);
-    return decode_typed(static_cast<const float*>(q), groups, Sp, m, kbits, knorms, vcodes,
+    return decode_typed(static_cast<const float*>(q), groups, nq, Sp, m, kbits, knorms, vcodes,
                         vscales, T, d, sm_scale, ws, out, dev, st);
   }
   const float* Sp = static_cast<const float*>(S);
   if (q_f16)
-    return decode_typed(static_cast<const _Float16*>(q), groups, Sp, m, kbits, knorms, vcodes,
+    return decode_typed(static_cast<const _Float16*>(q), groups, nq, Sp, m, kbits, knorms, vcodes,
                         vscales, T, d, sm_scale, ws, out, dev, st);
-  return decode_typed(static_cast<const float*>(q), groups, Sp, m, kbits, knorms, vcodes, vscales,
+  return decode_typed(static_cast<const float*>(q), groups, nq, Sp, m, kbits, knorms, vcodes, vscales,
                       T, d, sm_scale, ws, out, dev, st);
 }
 

@@ -94,6 +94,43 @@ kvq_status check_channel_d(const char* fn, int32_t d) {
   return KVQ_OK;
 }
 
+kvq_status decode_impl(const char* fn, const void* q, kvq_dtype q_dt, int64_t groups, int32_t nq,
+                       const void* S, kvq_dtype S_dt, int32_t m, const uint32_t* kbits,
+                       const uint16_t* knorms, const int8_t* vcodes, const float* vscales,
+                       int64_t T, int32_t d, float sm_scale, void* ws, size_t ws_bytes,
+                       float* out, kvq_stream_t stream) {
+  kvq_status st;
+  if ((st = check_count(fn, "groups", groups)) || (st = check_count(fn, "T", T)) ||
+      (st = check_nq(fn, nq)) || (st = check_d(fn, d)) || (st = check_m(fn, m)) ||
+      (st = check_dtype(fn, "q_dt", q_dt)) || (st = check_dtype(fn, "S_dt", S_dt)))
+    return st;
+  if (d > kvq::kMaxDecodeD)
+    return fail(KVQ_ERR_SHAPE, "%s: d = %d exceeds %d", fn, (int)d, kvq::kMaxDecodeD);
+  if (groups == 0) return ok();
+  if (T == 0) return fail(KVQ_ERR_SHAPE, "%s: T = 0 (attention over no tokens)", fn);
+  KVQ_CHECK_PTR(q);
+  KVQ_CHECK_PTR(S);
+  KVQ_CHECK_PTR(kbits);
+  KVQ_CHECK_PTR(knorms);
+  KVQ_CHECK_PTR(vcodes);
+  KVQ_CHECK_PTR(vscales);
+  KVQ_CHECK_PTR(out);
+  kvq::DeviceInfo dev;
+  if ((st = device_info(fn, &dev))) return st;
+  const size_t need = kvq::decode_workspace_bytes(groups, nq, T, d, m, dev);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(KVQ_ERR_WORKSPACE, "%s: workspace of %zu bytes at %p, need %zu", fn, ws_bytes, ws,
+                need);
+  if (!aligned16(ws)) return fail(KVQ_ERR_ALIGN, "%s: ws is not 16-byte aligned", fn);
+  if (kvq::decode_lds_bytes(m, d) > dev.lds_per_block)
+    return fail(KVQ_ERR_SHAPE, "%s: m = %d, d = %d need %zu bytes of LDS, the device has %zu", fn,
+                (int)m, (int)d, kvq::decode_lds_bytes(m, d), dev.lds_per_block);
+  return launched(fn, kvq::launch_decode_qjl_int8(q, q_dt == KVQ_F16, groups, nq, S,
+                                                  S_dt == KVQ_F16, m, kbits, knorms, vcodes,
+                                                  vscales, T, d, sm_scale, ws, out, dev,
+                                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 namespace kvq {
@@ -372,12 +409,17 @@ kvq_status kvq_scores_qjl(const void* q, kvq_dtype q_dt, int64_t groups, int32_t
 }
 
 size_t kvq_decode_workspace_bytes(int64_t groups, int64_t T, int32_t d, int32_t m) {
-  if (groups <= 0 || T <= 0 || d < 16 || d > kvq::kMaxDecodeD || d % 16 != 0 || m < kvq::kMinM ||
-      m > kvq::kMaxM || m % 32 != 0)
+  return kvq_decode_gqa_workspace_bytes(groups, 1, T, d, m);
+}
+
+size_t kvq_decode_gqa_workspace_bytes(int64_t groups, int32_t nq, int64_t T, int32_t d,
+                                      int32_t m) {
+  if (groups <= 0 || nq < 1 || nq > kvq::kMaxNq || T <= 0 || d < 16 || d > kvq::kMaxDecodeD ||
+      d % 16 != 0 || m < kvq::kMinM || m > kvq::kMaxM || m % 32 != 0)
     return 0;
   kvq::DeviceInfo dev;
   if (kvq::current_device_info(&dev) != hipSuccess) return 0;
-  return kvq::decode_workspace_bytes(groups, T, d, m, dev);
+  return kvq::decode_workspace_bytes(groups, nq, T, d, m, dev);
 }
 
 kvq_status kvq_decode_qjl_int8(const void* q, kvq_dtype q_dt, int64_t groups, const void* S,
@@ -385,37 +427,18 @@ kvq_status kvq_decode_qjl_int8(const void* q, kvq_dtype q_dt, int64_t groups, co
                                const uint16_t* knorms, const int8_t* vcodes,
                                const float* vscales, int64_t T, int32_t d, float sm_scale,
                                void* ws, size_t ws_bytes, float* out, kvq_stream_t stream) {
-  const char* fn = "kvq_decode_qjl_int8";
-  kvq_status st;
-  if ((st = check_count(fn, "groups", groups)) || (st = check_count(fn, "T", T)) ||
-      (st = check_d(fn, d)) || (st = check_m(fn, m)) || (st = check_dtype(fn, "q_dt", q_dt)) ||
-      (st = check_dtype(fn, "S_dt", S_dt)))
-    return st;
-  if (d > kvq::kMaxDecodeD)
-    return fail(KVQ_ERR_SHAPE, "%s: d = %d exceeds %d", fn, (int)d, kvq::kMaxDecodeD);
-  if (groups == 0) return ok();
-  if (T == 0) return fail(KVQ_ERR_SHAPE, "%s: T = 0 (attention over no tokens)", fn);
-  KVQ_CHECK_PTR(q);
-  KVQ_CHECK_PTR(S);
-  KVQ_CHECK_PTR(kbits);
-  KVQ_CHECK_PTR(knorms);
-  KVQ_CHECK_PTR(vcodes);
-  KVQ_CHECK_PTR(vscales);
-  KVQ_CHECK_PTR(out);
-  kvq::DeviceInfo dev;
-  if ((st = device_info(fn, &dev))) return st;
-  const size_t need = kvq::decode_workspace_bytes(groups, T, d, m, dev);
-  if (ws == nullptr || ws_bytes < need)
-    return fail(KVQ_ERR_WORKSPACE, "%s: workspace of %zu bytes at %p, need %zu", fn, ws_bytes, ws,
-                need);
-  if (!aligned16(ws)) return fail(KVQ_ERR_ALIGN, "%s: ws is not 16-byte aligned", fn);
-  if (kvq::decode_lds_bytes(m, d) > dev.lds_per_block)
-    return fail(KVQ_ERR_SHAPE, "%s: m = %d, d = %d need %zu bytes of LDS, the device has %zu", fn,
-                (int)m, (int)d, kvq::decode_lds_bytes(m, d), dev.lds_per_block);
-  return launched(fn, kvq::launch_decode_qjl_int8(q, q_dt == KVQ_F16, groups, S, S_dt == KVQ_F16,
-                                                  m, kbits, knorms, vcodes, vscales, T, d,
-                                                  sm_scale, ws, out, dev,
-                                                  reinterpret_cast<hipStream_t>(stream)));
+  return decode_impl("kvq_decode_qjl_int8", q, q_dt, groups, 1, S, S_dt, m, kbits, knorms, vcodes,
+                     vscales, T, d, sm_scale, ws, ws_bytes, out, stream);
+}
+
+kvq_status kvq_decode_qjl_int8_gqa(const void* q, kvq_dtype q_dt, int64_t groups, int32_t nq,
+                                   const void* S, kvq_dtype S_dt, int32_t m,
+                                   const uint32_t* kbits, const uint16_t* knorms,
+                                   const int8_t* vcodes, const float* vscales, int64_t T,
+                                   int32_t d, float sm_scale, void* ws, size_t ws_bytes,
+                                   float* out, kvq_stream_t stream) {
+  return decode_impl("kvq_decode_qjl_int8_gqa", q, q_dt, groups, nq, S, S_dt, m, kbits, knorms,
+                     vcodes, vscales, T, d, sm_scale, ws, ws_bytes, out, stream);
 }
 
 kvq_status kvq_cache_append(const void* k, const void* v, kvq_dtype kv_dt, int64_t groups,

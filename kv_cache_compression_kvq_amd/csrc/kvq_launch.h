@@ -60,9 +60,10 @@ struct DecodeSplit {
   int64_t tokens_per_split = 0;
 };
 DecodeSplit decode_split(int64_t groups, int64_t T, const DeviceInfo& dev);
-size_t decode_workspace_bytes(int64_t groups, int64_t T, int d, int m, const DeviceInfo& dev);
+size_t decode_workspace_bytes(int64_t groups, int nq, int64_t T, int d, int m,
+                              const DeviceInfo& dev);
 size_t decode_lds_bytes(int m, int d);
-hipError_t launch_decode_qjl_int8(const void* q, int q_f16, int64_t groups, const void* S,
+hipError_t launch_decode_qjl_int8(const void* q, int q_f16, int64_t groups, int nq, const void* S,
                                   int S_f16, int m, const uint32_t* kbits, const uint16_t* knorms,
                                   const int8_t* vcodes, const float* vscales, int64_t T, int d,
                                   float sm_scale, void* ws, float* out, const DeviceInfo& dev,

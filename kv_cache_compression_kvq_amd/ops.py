@@ -238,6 +238,40 @@ def decode_workspace_bytes(groups: int, T: int, d: int, m: int) -> int:
     return int(L.lib().kvq_decode_workspace_bytes(groups, T, d, m))
 
 
+def decode_gqa_workspace_bytes(groups: int, nq: int, T: int, d: int, m: int) -> int:
+    return int(L.lib().kvq_decode_gqa_workspace_bytes(groups, nq, T, d, m))
+
+
+def decode_qjl_int8_gqa(q: torch.Tensor, S: torch.Tensor, kbits: torch.Tensor,
+                        knorms: torch.Tensor, vcodes: torch.Tensor, vscales: torch.Tensor,
+                        sm_scale: float | None = None, workspace: torch.Tensor | None = None,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """One decode step for grouped-query attention: q [G, nq, d] (nq query
+    heads per KV head) against the group's QJL keys and INT8 values.
+    Returns out [G, nq, d] fp32."""
+    for t, n in ((q, "q"), (S, "S"), (kbits, "kbits"), (knorms, "knorms"), (vcodes, "vcodes"),
+                 (vscales, "vscales")):
+        _dev(t, n)
+    G, nq, d = q.shape
+    m = S.shape[0]
+    T = kbits.shape[1]
+    if (kbits.shape != (G, T, m // 32) or knorms.shape != (G, T) or vcodes.shape != (G, T, d)
+            or vscales.shape != (G, T) or S.shape[1] != d):
+        raise ValueError("shape mismatch between q, S and the cache tensors")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    need = decode_gqa_workspace_bytes(G, nq, T, d, m)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((G, nq, d), dtype=torch.float32, device=q.device)
+    L.check(L.lib().kvq_decode_qjl_int8_gqa(
+        _p(q), _dtype_code(q, "q"), G, nq, _p(S), _dtype_code(S, "S"), m, _p(kbits), _p(knorms),
+        _p(vcodes), _p(vscales), T, d, float(sm_scale), _p(workspace), workspace.numel(), _p(out),
+        _stream(q)))
+    return out
+
+
 def decode_qjl_int8(q: torch.Tensor, S: torch.Tensor, kbits: torch.Tensor, knorms: torch.Tensor,
                     vcodes: torch.Tensor, vscales: torch.Tensor, sm_scale: float | None = None,
                     workspace: torch.Tensor | None = None,

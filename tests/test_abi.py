@@ -260,3 +260,27 @@ def test_int8_channel_validation():
     _err(sc(A, L.KVQ_F16, 2, 1, A, A, 64, 16384, A, None), L.KVQ_ERR_SHAPE)
     _err(sc(A, L.KVQ_F16, 2, 1, A, MIS, 64, 128, A, None), L.KVQ_ERR_ALIGN)
     assert sc(None, L.KVQ_F16, 2, 1, None, None, 0, 128, None, None) == L.KVQ_OK
+
+
+def test_decode_gqa_validation():
+    f = L.lib().kvq_decode_qjl_int8_gqa
+    args = [A, L.KVQ_F16, 2, 4, A, L.KVQ_F16, 256, A, A, A, A, 16, 128, 0.1, A, 1 << 20, A, None]
+    names = ["q", "q_dt", "groups", "nq", "S", "S_dt", "m", "kbits", "knorms", "vcodes", "vscales",
+             "T", "d", "sm", "ws", "ws_bytes", "out", "stream"]
+
+    def call(**kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    _err(call(nq=0), L.KVQ_ERR_SHAPE)
+    _err(call(nq=65), L.KVQ_ERR_SHAPE)
+    _err(call(T=0), L.KVQ_ERR_SHAPE)
+    _err(call(out=None), L.KVQ_ERR_NULL)
+    _err(call(q=MIS), L.KVQ_ERR_ALIGN)
+    _err(call(S_dt=7), L.KVQ_ERR_DTYPE)
+    assert call(groups=0, q=None, S=None, kbits=None, knorms=None, vcodes=None, vscales=None,
+                ws=None, out=None) == L.KVQ_OK
+    assert L.lib().kvq_decode_gqa_workspace_bytes(2, 0, 16, 128, 256) == 0
+    assert L.lib().kvq_decode_gqa_workspace_bytes(2, 4, 16, 120, 256) == 0

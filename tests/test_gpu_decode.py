@@ -139,3 +139,42 @@ def test_decode_full_size_sampled():
         kw, kn, vc, vs = cache[g]
         ora = OD.decode_qjl_int8(q[g:g + 1], S, kw, kn, vc, vs, 1 / math.sqrt(d))
         decode_tolerance_check(out[g:g + 1], q[g:g + 1], S, kw, kn, vc, vs, 1 / math.sqrt(d), ora)
+
+
+# --- grouped-query attention: nq query heads per KV head -------------------------
+
+@pytest.mark.parametrize("G,nq,T,d,m", [(2, 4, 3000, 128, 256), (3, 2, 257, 128, 256), (1, 8, 5000, 128, 256),
+                                        (4, 3, 700, 64, 128), (2, 5, 63, 256, 256), (8, 4, 1, 128, 256)])
+def test_decode_grouped_queries(G, nq, T, d, m):
+    """Each of a group's nq queries gets what the oracle's decode gives for it
+    alone (every query checked against the one-query definition)."""
+    rng = np.random.default_rng(G * 100 + nq * 10 + T)
+    k = rng.standard_normal((G, T, d)).astype(np.float16)
+    v = rng.standard_normal((G, T, d)).astype(np.float16)
+    S = rng.standard_normal((m, d)).astype(np.float16)
+    kw, kn, vc, vs = make_cache(k, v, S)
+    q = rng.standard_normal((G, nq, d)).astype(np.float16)
+    lam = 1 / math.sqrt(d)
+    log(f"[decode-gqa] G={G} nq={nq} T={T} d={d} m={m}")
+    out = down(K.decode_qjl_int8_gqa(up(q), up(S), up(kw), up(kn), up(vc), up(vs), lam))
+    assert out.shape == (G, nq, d)
+    worst = 0.0
+    for j in range(nq):
+        qj = np.ascontiguousarray(q[:, j])
+        ora = OD.decode_qjl_int8(qj, S, kw, kn, vc, vs, lam)
+        worst = max(worst, decode_tolerance_check(out[:, j], qj, S, kw, kn, vc, vs, lam, ora))
+    log(f"[decode-gqa] worst err / tol = {worst:.3g}")
+
+
+def test_decode_grouped_single_query_equals_plain_decode():
+    """nq = 1 through the grouped entry point is the plain decode, bit for bit."""
+    rng = np.random.default_rng(77)
+    G, T, d, m = 5, 3000, 128, 256
+    k = rng.standard_normal((G, T, d)).astype(np.float16)
+    v = rng.standard_normal((G, T, d)).astype(np.float16)
+    S = rng.standard_normal((m, d)).astype(np.float16)
+    kw, kn, vc, vs = (up(a) for a in make_cache(k, v, S))
+    q = rng.standard_normal((G, 1, d)).astype(np.float16)
+    a = down(K.decode_qjl_int8_gqa(up(q), up(S), kw, kn, vc, vs))
+    b = down(K.decode_qjl_int8(up(np.ascontiguousarray(q[:, 0])), up(S), kw, kn, vc, vs))
+    assert np.array_equal(a[:, 0].view(np.uint32), b.view(np.uint32))
