@@ -331,6 +331,7 @@ hipError_t launch_qjl_sketch(const void* k, int k_f16, int64_t rows, int d, cons
 // kQjlBatch (sign words and norm) before any of them is scored.
 constexpr int kQjlBatch = 8;
 constexpr int kQjlThreads = 256;
+constexpr int kQjlWideThreads = 512;
 constexpr int kQjlTokPerThread = 16;
 constexpr int kQjlTok = kQjlThreads * kQjlTokPerThread;
 
@@ -344,9 +345,11 @@ __host__ __device__ inline size_t qjl_table_lds_floats(int m) {
 
 // NB: batches of kQjlBatch tokens per thread in the m = 256 kernel (2 for a
 // single query per group; 1 when the group's queries share the pass, whose
-// tokens stay in registers across the queries).
-template <typename TS, typename TQ, int W, int NB>
-__global__ __launch_bounds__(kQjlThreads) __attribute__((amdgpu_waves_per_eu(2))) void scores_qjl_kernel(const TQ* __restrict__ q, int nq,
+// tokens stay in registers across the queries).  TH: threads per workgroup
+// (512 for long caches: one workgroup then covers twice the tokens per query
+// projection and table build).
+template <typename TS, typename TQ, int W, int NB, int TH = kQjlThreads>
+__global__ __launch_bounds__(TH) __attribute__((amdgpu_waves_per_eu(2))) void scores_qjl_kernel(const TQ* __restrict__ q, int nq,
                                                          const TS* __restrict__ S, int m_rt, int d,
                                                          const uint32_t* __restrict__ bits,
                                                          const uint16_t* __restrict__ norms,
@@ -363,7 +366,7 @@ __global__ __launch_bounds__(kQjlThreads) __attribute__((amdgpu_waves_per_eu(2))
   const float c = kSqrtHalfPi / (float)m;
   if constexpr (W == 8) {
     static_assert(NB == 1 || NB == 2, "one or two batches per thread");
-    constexpr int kTile = kQjlThreads * kQjlBatch * NB;
+    constexpr int kTile = TH * kQjlBatch * NB;
     // One workgroup per (group, tile) scores all nq queries of the group
     // (grouped-query attention: the queries of a KV head share one pass over
     // its sign words and norms, which stay in registers).  Per query: y = S q
@@ -384,7 +387,7 @@ __global__ __launch_bounds__(kQjlThreads) __attribute__((amdgpu_waves_per_eu(2))
     auto load_batch = [&](int bi) {
 #pragma unroll
       for (int u = 0; u < kQjlBatch; ++u) {
-        const int64_t t = std::min(t0 + (int64_t)(bi * kQjlBatch + u) * kQjlThreads, T - 1);
+        const int64_t t = std::min(t0 + (int64_t)(bi * kQjlBatch + u) * TH, T - 1);
         load_rot_words(bg + t * 8, r, wv[bi][u]);
         nv[bi][u] = (float)__builtin_bit_cast(_Float16, ld_stream(ng + t));
       }
@@ -411,7 +414,7 @@ __global__ __launch_bounds__(kQjlThreads) __attribute__((amdgpu_waves_per_eu(2))
       for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
         for (int u = 0; u < kQjlBatch; ++u) {
-          const int64_t t = t0 + (int64_t)(bi * kQjlBatch + u) * kQjlThreads;
+          const int64_t t = t0 + (int64_t)(bi * kQjlBatch + u) * TH;
           const float acc = rot_lut_sum_rotated(wv[bi][u], rq);
           if (t < T) sg[t] = c * nv[bi][u] * acc;
         }
@@ -477,8 +480,11 @@ static hipError_t scores_qjl_typed(const TQ* q, int64_t groups, int nq, const TS
   // m = 256 with fp16 S and d <= 128: one workgroup per (group, tile) scores
   // all nq queries; else one per (group, query, tile)
   const bool grouped = m == 256 && sizeof(TS) == 2 && d <= 128;
-  const int64_t tile_tokens = grouped ? (int64_t)kQjlThreads * kQjlBatch * (nq == 1 ? 2 : 1)
-                                      : (int64_t)kQjlTok;
+  const int nb = nq == 1 ? 2 : 1;
+  // 512-thread workgroups once a cache fills one of their tiles
+  const bool wide = grouped && T >= (int64_t)kQjlWideThreads * kQjlBatch * nb;
+  const int th = wide ? kQjlWideThreads : kQjlThreads;
+  const int64_t tile_tokens = grouped ? (int64_t)th * kQjlBatch * nb : (int64_t)kQjlTok;
   const int64_t tiles = (T + tile_tokens - 1) / tile_tokens;
   const int64_t per_group = grouped ? tiles : tiles * nq;
   // launch in slices of whole groups so grid.x stays far below 2^32
@@ -490,24 +496,22 @@ static hipError_t scores_qjl_typed(const TQ* q, int64_t groups, int nq, const TS
     const uint16_t* np = norms + g0 * T;
     float* sp = scores + g0 * nq * T;
     const unsigned blocks = (unsigned)(ng * per_group);
+    auto launch = [&](auto kernel, int threads) {
+      hipError_t e = allow_dynamic_lds(kernel, lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kernel, dim3(blocks), dim3(threads), lds, st, qp, nq, S, m, d, bp, np, T,
+                         tiles, sp);
+      return hipGetLastError();
+    };
     hipError_t e;
-    if (grouped && nq == 1) {
-      e = allow_dynamic_lds(scores_qjl_kernel<TS, TQ, 8, 2>, lds);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((scores_qjl_kernel<TS, TQ, 8, 2>), dim3(blocks), dim3(kQjlThreads), lds,
-                         st, qp, nq, S, m, d, bp, np, T, tiles, sp);
-    } else if (grouped) {
-      e = allow_dynamic_lds(scores_qjl_kernel<TS, TQ, 8, 1>, lds);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((scores_qjl_kernel<TS, TQ, 8, 1>), dim3(blocks), dim3(kQjlThreads), lds,
-                         st, qp, nq, S, m, d, bp, np, T, tiles, sp);
-    } else {
-      e = allow_dynamic_lds(scores_qjl_kernel<TS, TQ, 0, 2>, lds);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((scores_qjl_kernel<TS, TQ, 0, 2>), dim3(blocks), dim3(kQjlThreads), lds,
-                         st, qp, nq, S, m, d, bp, np, T, tiles, sp);
-    }
-    e = hipGetLastError();
+    if (grouped && nq == 1)
+      e = wide ? launch(scores_qjl_kernel<TS, TQ, 8, 2, kQjlWideThreads>, kQjlWideThreads)
+               : launch(scores_qjl_kernel<TS, TQ, 8, 2>, kQjlThreads);
+    else if (grouped)
+      e = wide ? launch(scores_qjl_kernel<TS, TQ, 8, 1, kQjlWideThreads>, kQjlWideThreads)
+               : launch(scores_qjl_kernel<TS, TQ, 8, 1>, kQjlThreads);
+    else
+      e = launch(scores_qjl_kernel<TS, TQ, 0, 2>, kQjlThreads);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -118,7 +118,8 @@ def test_sketch_zero_and_scaled_keys():
 @pytest.mark.parametrize("qdt,sdt", [("f16", "f16"), ("f32", "f32"), ("f16", "f32"), ("f32", "f16")])
 @pytest.mark.parametrize("nq,T,m,d", [(1, 1, 256, 128), (3, 2049, 256, 128), (8, 300, 64, 64),
                                       (2, 513, 512, 128), (1, 100, 1024, 256), (4, 77, 96, 48),
-                                      (4, 4100, 256, 128), (8, 1000, 256, 64), (2, 5, 256, 16)])
+                                      (4, 4100, 256, 128), (8, 1000, 256, 64), (2, 5, 256, 16),
+                                      (1, 8193, 256, 128), (2, 4096, 256, 128), (1, 12000, 256, 96)])
 def test_scores_shapes(qdt, sdt, nq, T, m, d):
     rng = np.random.default_rng(nq + T + m)
     G = 3
@@ -146,7 +147,7 @@ def test_bit_order_matches_fixture_on_gpu():
         assert down(bits, np.uint32).tolist() == want
 
 
-@pytest.mark.parametrize("nq,T,d", [(4, 4100, 128), (8, 999, 64)])
+@pytest.mark.parametrize("nq,T,d", [(4, 4100, 128), (8, 999, 64), (2, 9000, 128)])
 def test_grouped_queries_equal_single_query_runs(nq, T, d):
     """Grouped-query scoring (one pass over a KV head's sign words for all of
     its queries) gives, bit for bit, what scoring each query alone gives."""
