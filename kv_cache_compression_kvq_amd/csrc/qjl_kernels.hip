@@ -54,10 +54,12 @@ template <int NT> constexpr int sketch_ring() { return NT == 1 ? 4 : 2; }
 // projection is +0 here (the accumulation starts from +0), so it gives bit 1.
 // Both halves of the wave return the token's full 32-bit word (the halves'
 // 16-bit parts are exchanged with v_permlane32_swap).
+
+// Multiplies of projection tile mt for the NT x 32 tokens of a wave:
+// P = S_tile K^T on fp16 MFMA into acc.
 template <int KS, int NT>
-__device__ __forceinline__ void sketch_tile_words(const f16x8* sfrag, int mt, int lane,
-                                                  const f16x8 (&b)[NT][KS], uint32_t (&full)[NT]) {
-  f32x16 acc[NT];
+__device__ __forceinline__ void sketch_tile_mfma(const f16x8* sfrag, int mt, int lane,
+                                                 const f16x8 (&b)[NT][KS], f32x16 (&acc)[NT]) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16{};
 #pragma unroll
@@ -67,6 +69,11 @@ __device__ __forceinline__ void sketch_tile_words(const f16x8* sfrag, int mt, in
     for (int nt = 0; nt < NT; ++nt)
       acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[nt][ks], acc[nt], 0, 0, 0);
   }
+}
+
+// Sign word of each token from the accumulators of one projection tile.
+template <int NT>
+__device__ __forceinline__ void sketch_tile_signs(const f32x16 (&acc)[NT], uint32_t (&full)[NT]) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     uint32_t sb = 0;
@@ -79,6 +86,14 @@ __device__ __forceinline__ void sketch_tile_words(const f16x8* sfrag, int mt, in
     halves_u32(~sb & 0xFFFFu, lo, hi);
     full[nt] = lo | (hi << 16);
   }
+}
+
+template <int KS, int NT>
+__device__ __forceinline__ void sketch_tile_words(const f16x8* sfrag, int mt, int lane,
+                                                  const f16x8 (&b)[NT][KS], uint32_t (&full)[NT]) {
+  f32x16 acc[NT];
+  sketch_tile_mfma<KS, NT>(sfrag, mt, lane, b, acc);
+  sketch_tile_signs<NT>(acc, full);
 }
 
 constexpr int kSketchThreads = 512;
@@ -167,13 +182,35 @@ void sketch_mfma_kernel(const _Float16* __restrict__ k,
       // unrolled so the words stay in registers; the scheduling barrier
       // keeps each tile's S-fragment reads inside its own iteration
       uint32_t wbuf[kSketchNT][MT];
+      // two accumulator sets: the sign words of tile mt - 1 are taken while
+      // the multiplies of tile mt run, interleaved per k-step (an S fragment
+      // read two k-steps ahead, the step's multiplies, five sign-extraction
+      // instructions), so the matrix cores do not wait for the extraction
+      f32x16 acc0[kSketchNT], acc1[kSketchNT];
+      __builtin_amdgcn_sched_barrier(0);
+      sketch_tile_mfma<KS, kSketchNT>(sf, 0, lane, b, acc0);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+      for (int mt = 1; mt <= MT; ++mt) {
         __builtin_amdgcn_sched_barrier(0);
         uint32_t f[kSketchNT];
-        sketch_tile_words<KS, kSketchNT>(sf, mt, lane, b, f);
+        if (mt & 1) {
+          if (mt < MT) sketch_tile_mfma<KS, kSketchNT>(sf, mt, lane, b, acc1);
+          sketch_tile_signs<kSketchNT>(acc0, f);
+        } else {
+          if (mt < MT) sketch_tile_mfma<KS, kSketchNT>(sf, mt, lane, b, acc0);
+          sketch_tile_signs<kSketchNT>(acc1, f);
+        }
+        if (mt < MT) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);        // LDS reads
 #pragma unroll
-        for (int nt = 0; nt < kSketchNT; ++nt) wbuf[nt][mt] = f[nt];
+          for (int ks = 0; ks < KS; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, kSketchNT, 0);   // MFMA
+            if (ks + 2 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);      // VALU
+          }
+        }
+#pragma unroll
+        for (int nt = 0; nt < kSketchNT; ++nt) wbuf[nt][mt - 1] = f[nt];
       }
       // half h stores words [h * MT/2, (h + 1) * MT/2) of its token
       constexpr int HALF = MT / 2;
