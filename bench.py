@@ -20,7 +20,11 @@ the QJL-cache sketch and score, each timed with HIP events on the stream the
 kernels run on.  ``cpu_baseline`` times the fp64 oracle on a bounded sample
 of the same decode workload.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-components]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 1000] [--no-components]
+
+The default warm-up (1000 steps, ~0.45 s) brings the GPU's clocks up after
+the seconds of host-side input generation before the timed region: with 3
+warm-up steps the same 20 timed steps measured ~4 % slower.
 """
 from __future__ import annotations
 
@@ -44,8 +48,8 @@ DECODE_SOURCES = ["decode_kernels.hip", "kvq_qjl_device.h", "kvq_device.h"]
 def parse_args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=1000)
     p.add_argument("--no-components", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
