@@ -141,6 +141,25 @@ def components(K, si, torch, np):
     def ncopies(bytes_per_call):
         return max(1, -(-COLD_BYTES // int(bytes_per_call)) + 1)
 
+    # INT8 round-trip error on the sweep (fp32 rows, N(0, 1)) and the
+    # U(-1, 1) context row: max and mean |dequantize(quantize(x)) - x|
+    acc = {}
+
+    def round_trip_error(name, xv):
+        codes, scales = K.quantize_int8(xv)
+        err = (K.dequantize_int8(codes, scales) - xv).abs_()
+        acc[name] = {"max_abs": float(err.max()),
+                     "mean_abs": float(err.sum(dtype=torch.float64)) / err.numel()}
+        del codes, scales, err
+
+    for nlog in (20, 24):
+        x = torch.from_numpy(si.flat_rows(si.W_SWEEP, 1 << nlog, 128).reshape(-1)).to(dev)
+        for d in (128, 1024, 8192):
+            round_trip_error(f"f32_2^{nlog}_d{d}", x.view(-1, d))
+    x = torch.from_numpy(si.flat_rows(si.W_SWEEP, 1 << 24, 128, dist="uniform").reshape(-1)).to(dev)
+    round_trip_error("uniform_f32_2^24_d128", x.view(-1, 128))
+    del x
+
     # element-count sweep, fp32 rows of d in {128, 1024, 8192}
     for nlog in (28, 30):
         n = 1 << nlog
@@ -149,6 +168,7 @@ def components(K, si, torch, np):
         for d in (128, 1024, 8192):
             rows = n // d
             views = [t.view(rows, d) for t in xs]
+            round_trip_error(f"f32_2^{nlog}_d{d}", views[0])
             cs = [K.quantize_int8(v) for v in views]
             gbs(f"quantize_f32_2^{nlog}_d{d}", 4 * n + n + 4 * rows,
                 [lambda v=v: K.quantize_int8(v) for v in views])
@@ -303,6 +323,8 @@ def components(K, si, torch, np):
         Gk * nqg * Tq / res["decode_4x1query_128x32768"]["ms"] * 1e3, 1)
     del kbg, kng, vcg, vsg, qg, wsg, og, ws1, o1
     torch.cuda.empty_cache()
+    res["int8_round_trip_error"] = acc
+    log(f"  int8_round_trip_error: {acc}")
     return res
 
 
