@@ -362,10 +362,11 @@ hipError_t launch_qjl_sketch(const void* k, int k_f16, int64_t rows, int d, cons
 }
 
 // ---------------------------------------------------------------------------
-// QJL scores: one workgroup per (group, tile of kQjlTok tokens) for m = 256
-// (all of the group's queries), else per (group, query, tile).  Each thread
-// owns kQjlTokPerThread tokens, kQjlThreads apart, loaded in batches of
-// kQjlBatch (sign words and norm) before any of them is scored.
+// QJL scores.  m = 256 (fp16 S, d <= 128): one workgroup per (group, tile of
+// TH * kQjlBatch tokens) scores all of the group's queries, each thread
+// holding kQjlBatch tokens TH apart in registers.  Other shapes: one
+// workgroup per (group, query, tile of kQjlTok tokens), kQjlTokPerThread
+// tokens per thread.
 constexpr int kQjlBatch = 8;
 constexpr int kQjlThreads = 256;
 constexpr int kQjlWideThreads = 512;
@@ -380,13 +381,12 @@ __host__ __device__ inline size_t qjl_table_lds_floats(int m) {
   return (size_t)m + (tables > (size_t)kProjQChunk ? tables : (size_t)kProjQChunk);
 }
 
-// NB: batches of kQjlBatch tokens per thread in the m = 256 kernel (2 for a
-// single query per group; 1 when the group's queries share the pass, whose
-// tokens stay in registers across the queries).  TH: threads per workgroup
-// (512 for long caches: one workgroup then covers twice the tokens per query
-// projection and table build).
-template <typename TS, typename TQ, int W, int NB, int TH = kQjlThreads>
-__global__ __launch_bounds__(TH) __attribute__((amdgpu_waves_per_eu(2))) void scores_qjl_kernel(const TQ* __restrict__ q, int nq,
+// TH: threads per workgroup.  ONEQ: one query per group; the kernel then
+// keeps under 128 registers so that two workgroups (64 KiB of tables each)
+// share a CU at four waves per SIMD, which hides more of the lookups' LDS
+// latency, and its projection holds no S rows across the token loads.
+template <typename TS, typename TQ, int W, int TH = kQjlThreads, bool ONEQ = false>
+__global__ __launch_bounds__(TH) __attribute__((amdgpu_waves_per_eu(ONEQ ? 4 : 2))) void scores_qjl_kernel(const TQ* __restrict__ q, int nq,
                                                          const TS* __restrict__ S, int m_rt, int d,
                                                          const uint32_t* __restrict__ bits,
                                                          const uint16_t* __restrict__ norms,
@@ -402,44 +402,41 @@ __global__ __launch_bounds__(TH) __attribute__((amdgpu_waves_per_eu(2))) void sc
   float* y = lut + (tfl > (size_t)kProjQChunk ? tfl : (size_t)kProjQChunk);
   const float c = kSqrtHalfPi / (float)m;
   if constexpr (W == 8) {
-    static_assert(NB == 1 || NB == 2, "one or two batches per thread");
-    constexpr int kTile = TH * kQjlBatch * NB;
+    constexpr int kTile = TH * kQjlBatch;
     // One workgroup per (group, tile) scores all nq queries of the group
     // (grouped-query attention: the queries of a KV head share one pass over
     // its sign words and norms, which stay in registers).  Per query: y = S q
     // and the byte tables are rebuilt in LDS, then the tokens are scored.
-    // The first batch of tokens is requested right after the first
-    // projection's own loads (so those can be waited for alone), the second
-    // before the first batch is scored.  The loads are unconditional (tokens
-    // past T re-read token T - 1 and are not stored): loads under a branch
-    // make the compiler wait for each one.
+    // The tokens are requested before the first projection is finished (for
+    // several queries, right after that projection's own loads, so those can
+    // be waited for alone).  The loads are unconditional (tokens past T
+    // re-read token T - 1 and are not stored): loads under a branch make the
+    // compiler wait for each one.
     const int64_t g = blockIdx.x / tiles;
     const int64_t tile = blockIdx.x % tiles;
     const uint32_t* bg = bits + g * T * words;
     const uint16_t* ng = norms + g * T;
     const int64_t t0 = tile * kTile + threadIdx.x;
     const int r = threadIdx.x & 31;
-    uint32_t wv[NB][kQjlBatch][8];
-    float nv[NB][kQjlBatch];
-    auto load_batch = [&](int bi) {
+    uint32_t wv[kQjlBatch][8];
+    float nv[kQjlBatch];
+    auto load_tokens = [&]() {
 #pragma unroll
       for (int u = 0; u < kQjlBatch; ++u) {
-        const int64_t t = std::min(t0 + (int64_t)(bi * kQjlBatch + u) * TH, T - 1);
-        load_rot_words(bg + t * 8, r, wv[bi][u]);
-        nv[bi][u] = (float)__builtin_bit_cast(_Float16, ld_stream(ng + t));
+        const int64_t t = std::min(t0 + (int64_t)u * TH, T - 1);
+        load_rot_words(bg + t * 8, r, wv[u]);
+        nv[u] = (float)__builtin_bit_cast(_Float16, ld_stream(ng + t));
       }
     };
     // the words are rotated in place once (rot_words) and serve every query
     auto rotate_all = [&]() {
 #pragma unroll
-      for (int bi = 0; bi < NB; ++bi)
+      for (int u = 0; u < kQjlBatch; ++u) {
+        uint32_t xr[8];
+        rot_words(wv[u], r, xr);
 #pragma unroll
-        for (int u = 0; u < kQjlBatch; ++u) {
-          uint32_t xr[8];
-          rot_words(wv[bi][u], r, xr);
-#pragma unroll
-          for (int k = 0; k < 8; ++k) wv[bi][u][k] = xr[k];
-        }
+        for (int k = 0; k < 8; ++k) wv[u][k] = xr[k];
+      }
     };
     auto score_all = [&](float* sg) {
       // opaque per call: the lookup addresses depend only on the words and
@@ -448,40 +445,42 @@ __global__ __launch_bounds__(TH) __attribute__((amdgpu_waves_per_eu(2))) void sc
       uint32_t rq = rot_lane_base(lut, r);
       asm volatile("" : "+v"(rq));
 #pragma unroll
-      for (int bi = 0; bi < NB; ++bi)
-#pragma unroll
-        for (int u = 0; u < kQjlBatch; ++u) {
-          const int64_t t = t0 + (int64_t)(bi * kQjlBatch + u) * TH;
-          const float acc = rot_lut_sum_rotated(wv[bi][u], rq);
-          if (t < T) sg[t] = c * nv[bi][u] * acc;
-        }
+      for (int u = 0; u < kQjlBatch; ++u) {
+        const int64_t t = t0 + (int64_t)u * TH;
+        const float acc = rot_lut_sum_rotated(wv[u], rq);
+        if (t < T) sg[t] = c * nv[u] * acc;
+      }
     };
     // query 0 (this kernel is launched for fp16 S with d <= 128 only)
     const TQ* q0 = q + g * nq * d;
     if constexpr (sizeof(TS) == 2) {
-      QueryProj16<TQ> pj;
-      pj.issue(S, q0, m, d);
-      __builtin_amdgcn_sched_barrier(0);   // keep the projection's loads first
-      load_batch(0);
-      __builtin_amdgcn_sched_barrier(0);
-      pj.finish(lut, y, m, d);
+      if constexpr (ONEQ) {
+        load_tokens();
+        __builtin_amdgcn_sched_barrier(0);
+        project16_lite(S, q0, m, d, lut, y);
+      } else {
+        QueryProj16<TQ> pj;
+        pj.issue(S, q0, m, d);
+        __builtin_amdgcn_sched_barrier(0);   // keep the projection's loads first
+        load_tokens();
+        __builtin_amdgcn_sched_barrier(0);
+        pj.finish(lut, y, m, d);
+      }
       __syncthreads();
       build_rot_tables(y, lut);
       __syncthreads();
-      if constexpr (NB == 2) load_batch(1);
       rotate_all();
       score_all(scores + g * nq * T);
-      // queries 1 .. nq - 1: the tokens are already in registers (the
-      // two-batch kernel is launched for one query per group only)
-      if constexpr (NB == 1)
-      for (int j = 1; j < nq; ++j) {
-        __syncthreads();                       // every lookup of query j - 1 is done
-        project16_lite(S, q0 + (int64_t)j * d, m, d, lut, y);
-        __syncthreads();
-        build_rot_tables(y, lut);
-        __syncthreads();
-        score_all(scores + (g * nq + j) * T);
-      }
+      // queries 1 .. nq - 1: the tokens are already in registers
+      if constexpr (!ONEQ)
+        for (int j = 1; j < nq; ++j) {
+          __syncthreads();                     // every lookup of query j - 1 is done
+          project16_lite(S, q0 + (int64_t)j * d, m, d, lut, y);
+          __syncthreads();
+          build_rot_tables(y, lut);
+          __syncthreads();
+          score_all(scores + (g * nq + j) * T);
+        }
     }
     return;
   }
@@ -517,11 +516,13 @@ static hipError_t scores_qjl_typed(const TQ* q, int64_t groups, int nq, const TS
   // m = 256 with fp16 S and d <= 128: one workgroup per (group, tile) scores
   // all nq queries; else one per (group, query, tile)
   const bool grouped = m == 256 && sizeof(TS) == 2 && d <= 128;
-  const int nb = nq == 1 ? 2 : 1;
-  // 512-thread workgroups once a cache fills one of their tiles
-  const bool wide = grouped && T >= (int64_t)kQjlWideThreads * kQjlBatch * nb;
-  const int th = wide ? kQjlWideThreads : kQjlThreads;
-  const int64_t tile_tokens = grouped ? (int64_t)th * kQjlBatch * nb : (int64_t)kQjlTok;
+  // one query: 512-thread workgroups, two per CU; several: 512 threads once
+  // the cache fills their tile (the queries' projections and table builds
+  // are then paid once per 4096 tokens), else 256
+  const int th = !grouped ? kQjlThreads
+                 : (nq == 1 || T >= (int64_t)kQjlWideThreads * kQjlBatch) ? kQjlWideThreads
+                                                                        : kQjlThreads;
+  const int64_t tile_tokens = grouped ? (int64_t)th * kQjlBatch : (int64_t)kQjlTok;
   const int64_t tiles = (T + tile_tokens - 1) / tile_tokens;
   const int64_t per_group = grouped ? tiles : tiles * nq;
   // launch in slices of whole groups so grid.x stays far below 2^32
@@ -542,13 +543,12 @@ static hipError_t scores_qjl_typed(const TQ* q, int64_t groups, int nq, const TS
     };
     hipError_t e;
     if (grouped && nq == 1)
-      e = wide ? launch(scores_qjl_kernel<TS, TQ, 8, 2, kQjlWideThreads>, kQjlWideThreads)
-               : launch(scores_qjl_kernel<TS, TQ, 8, 2>, kQjlThreads);
+      e = launch(scores_qjl_kernel<TS, TQ, 8, kQjlWideThreads, true>, kQjlWideThreads);
     else if (grouped)
-      e = wide ? launch(scores_qjl_kernel<TS, TQ, 8, 1, kQjlWideThreads>, kQjlWideThreads)
-               : launch(scores_qjl_kernel<TS, TQ, 8, 1>, kQjlThreads);
+      e = th == kQjlWideThreads ? launch(scores_qjl_kernel<TS, TQ, 8, kQjlWideThreads>, th)
+                                : launch(scores_qjl_kernel<TS, TQ, 8>, th);
     else
-      e = launch(scores_qjl_kernel<TS, TQ, 0, 2>, kQjlThreads);
+      e = launch(scores_qjl_kernel<TS, TQ, 0>, kQjlThreads);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
