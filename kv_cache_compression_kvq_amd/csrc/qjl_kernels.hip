@@ -381,12 +381,14 @@ __host__ __device__ inline size_t qjl_table_lds_floats(int m) {
   return (size_t)m + (tables > (size_t)kProjQChunk ? tables : (size_t)kProjQChunk);
 }
 
-// TH: threads per workgroup.  ONEQ: one query per group; the kernel then
-// keeps under 128 registers so that two workgroups (64 KiB of tables each)
-// share a CU at four waves per SIMD, which hides more of the lookups' LDS
-// latency, and its projection holds no S rows across the token loads.
+// TH: threads per workgroup.  ONEQ: one query per group (the query loop is
+// compiled out).  The m = 256 kernels stay under 128 registers so that two
+// workgroups (64 KiB of tables each) share a CU at four waves per SIMD,
+// which hides more of the lookups' LDS latency: the projection holds only
+// four S rows at a time across the token loads, and per-lane token offsets
+// are 32-bit from workgroup-uniform bases.
 template <typename TS, typename TQ, int W, int TH = kQjlThreads, bool ONEQ = false>
-__global__ __launch_bounds__(TH) __attribute__((amdgpu_waves_per_eu(ONEQ ? 4 : 2))) void scores_qjl_kernel(const TQ* __restrict__ q, int nq,
+__global__ __launch_bounds__(TH) __attribute__((amdgpu_waves_per_eu(W == 8 ? 4 : 2))) void scores_qjl_kernel(const TQ* __restrict__ q, int nq,
                                                          const TS* __restrict__ S, int m_rt, int d,
                                                          const uint32_t* __restrict__ bits,
                                                          const uint16_t* __restrict__ norms,
@@ -407,23 +409,22 @@ __global__ __launch_bounds__(TH) __attribute__((amdgpu_waves_per_eu(ONEQ ? 4 : 2
     // (grouped-query attention: the queries of a KV head share one pass over
     // its sign words and norms, which stay in registers).  Per query: y = S q
     // and the byte tables are rebuilt in LDS, then the tokens are scored.
-    // The tokens are requested before the first projection is finished (for
-    // several queries, right after that projection's own loads, so those can
-    // be waited for alone).  The loads are unconditional (tokens past T
-    // re-read token T - 1 and are not stored): loads under a branch make the
-    // compiler wait for each one.
+    // The tokens are requested before the first projection.  The loads are
+    // unconditional (tokens past T re-read the tile's last token and are not
+    // stored): loads under a branch make the compiler wait for each one.
     const int64_t g = blockIdx.x / tiles;
     const int64_t tile = blockIdx.x % tiles;
-    const uint32_t* bg = bits + g * T * words;
-    const uint16_t* ng = norms + g * T;
-    const int64_t t0 = tile * kTile + threadIdx.x;
+    const int64_t tbase = tile * kTile;
+    const int nlive = (int)std::min<int64_t>(kTile, T - tbase);   // tokens of this tile
+    const uint32_t* bg = bits + (g * T + tbase) * words;
+    const uint16_t* ng = norms + g * T + tbase;
     const int r = threadIdx.x & 31;
     uint32_t wv[kQjlBatch][8];
     float nv[kQjlBatch];
     auto load_tokens = [&]() {
 #pragma unroll
       for (int u = 0; u < kQjlBatch; ++u) {
-        const int64_t t = std::min(t0 + (int64_t)u * TH, T - 1);
+        const int t = min((int)threadIdx.x + u * TH, nlive - 1);
         load_rot_words(bg + t * 8, r, wv[u]);
         nv[u] = (float)__builtin_bit_cast(_Float16, ld_stream(ng + t));
       }
@@ -444,28 +445,20 @@ __global__ __launch_bounds__(TH) __attribute__((amdgpu_waves_per_eu(ONEQ ? 4 : 2
       // registers
       uint32_t rq = rot_lane_base(lut, r);
       asm volatile("" : "+v"(rq));
+      float* st = sg + tbase;
 #pragma unroll
       for (int u = 0; u < kQjlBatch; ++u) {
-        const int64_t t = t0 + (int64_t)u * TH;
+        const int t = (int)threadIdx.x + u * TH;
         const float acc = rot_lut_sum_rotated(wv[u], rq);
-        if (t < T) sg[t] = c * nv[u] * acc;
+        if (t < nlive) st[t] = c * nv[u] * acc;
       }
     };
     // query 0 (this kernel is launched for fp16 S with d <= 128 only)
     const TQ* q0 = q + g * nq * d;
     if constexpr (sizeof(TS) == 2) {
-      if constexpr (ONEQ) {
-        load_tokens();
-        __builtin_amdgcn_sched_barrier(0);
-        project16_lite(S, q0, m, d, lut, y);
-      } else {
-        QueryProj16<TQ> pj;
-        pj.issue(S, q0, m, d);
-        __builtin_amdgcn_sched_barrier(0);   // keep the projection's loads first
-        load_tokens();
-        __builtin_amdgcn_sched_barrier(0);
-        pj.finish(lut, y, m, d);
-      }
+      load_tokens();
+      __builtin_amdgcn_sched_barrier(0);
+      project16_lite(S, q0, m, d, lut, y);
       __syncthreads();
       build_rot_tables(y, lut);
       __syncthreads();
