@@ -25,7 +25,7 @@
 
 namespace kvq {
 
-constexpr int kAppendTok = 4;
+constexpr int kAppendTok = 2;   // 512 groups: 6.3 us against 7.7 us with 4
 constexpr int kAppendThreads = 256;
 constexpr int kAppendWaves = kAppendThreads / 64;
 constexpr int kAppendVals = kMaxDecodeD / 64;   // value elements per lane
