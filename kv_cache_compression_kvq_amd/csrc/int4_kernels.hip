@@ -273,7 +273,9 @@ static hipError_t dequantize_int4_dispatch(const uint8_t* codes, const float* st
                                            const float* offsets, int64_t ngroups, int g, TO* out,
                                            hipStream_t st) {
   constexpr int N = Out4<TO>::N;
-  constexpr int UNROLL = 4;
+  // two output chunks per thread: against four, 2-5 % faster with fp16
+  // output, the same with fp32 output
+  constexpr int UNROLL = 2;
   const int cpg = g / N;
   const int64_t nchunks = ngroups * cpg;
   const int64_t blocks = (nchunks + 256 * UNROLL - 1) / (256 * UNROLL);

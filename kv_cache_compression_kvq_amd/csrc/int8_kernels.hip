@@ -319,7 +319,9 @@ template <typename TO>
 static hipError_t dequantize_dispatch(const int8_t* codes, const float* scales, int64_t rows, int d,
                                       TO* out, hipStream_t st) {
   constexpr int N = OutChunk<TO>::N;
-  constexpr int UNROLL = 4;
+  // two output chunks per thread: against four, 6-9 % faster with fp32
+  // output at 2^28 / 2^30 elements and 5-9 % with fp16 output
+  constexpr int UNROLL = 2;
   const int cpr = d / N;
   const int64_t nchunks = rows * cpr;
   const int64_t blocks = (nchunks + 256 * UNROLL - 1) / (256 * UNROLL);
