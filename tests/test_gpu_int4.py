@@ -41,6 +41,35 @@ def roundtrip_check(x: np.ndarray, g: int, label: str):
     return co, so, zo
 
 
+# --- element-count sweep sizes (the bench's fp32 workloads) --------------------
+
+@pytest.mark.parametrize("n_log2", [28, 30])
+def test_sweep_large_sizes_sampled(n_log2):
+    """2^28 and 2^30 fp32 elements as rows of 128 with groups of 32 and 128
+    (the bench's launches; 2^30 with g = 32 takes the two-pass-per-wave
+    kernel): 2048 sampled rows plus the first and last compared bit-exactly
+    with the oracle (codes, steps, offsets, fp32 reconstruction)."""
+    n = 1 << n_log2
+    x_host = si.flat_rows(si.W_SWEEP, n, 128)
+    x = up(x_host)
+    rows = x_host.shape[0]
+    rng = np.random.default_rng(n_log2 + 4)
+    sample = np.unique(np.concatenate([[0, rows - 1], rng.integers(0, rows, 2048)]))
+    idx = torch.from_numpy(sample).to(x.device)
+    xs = x_host[sample]
+    for g in (32, 128):
+        log(f"[int4] sweep 2^{n_log2} g={g}: quantize {rows} rows")
+        c_t, s_t, z_t = K.quantize_int4(x, g)
+        d_t = K.dequantize_int4(c_t, s_t, z_t, g)
+        co, so, zo = O.quantize_int4(xs, g)
+        assert np.array_equal(down(c_t.index_select(0, idx)), co), f"2^{n_log2} g={g}: codes differ"
+        assert np.array_equal(down(s_t.index_select(0, idx)).view(np.uint32), so.view(np.uint32))
+        _cmp_offsets(down(z_t.index_select(0, idx)), zo, f"2^{n_log2} g={g}")
+        do = O.dequantize_int4(co, so, zo, g, "f32")
+        assert np.array_equal(down(d_t.index_select(0, idx)).view(np.uint32), do.view(np.uint32))
+        del c_t, s_t, z_t, d_t
+
+
 # --- Llama-7B-shaped layer: 32 heads x 4096 tokens x 128, fp16, outliers --------
 
 @pytest.mark.parametrize("g", [32, 128])
