@@ -56,7 +56,7 @@ def test_llama_layer_keys_full_size():
 @pytest.mark.parametrize("d", [16, 48, 128, 1024, 2048, 8192])
 def test_shapes_and_ragged_token_counts(dtype, d):
     rng = np.random.default_rng(d)
-    for T in (1, 3, 255, 256, 257, 1000) if d <= 1024 else (1, 300):
+    for T in (1, 3, 127, 128, 129, 255, 256, 257, 1000) if d <= 1024 else (1, 129, 300):
         G = 3
         x = rng.standard_normal((G, T, d)).astype(np.float32)
         x *= np.exp(rng.uniform(-6, 6, (G, 1, d))).astype(np.float32)
@@ -66,7 +66,7 @@ def test_shapes_and_ragged_token_counts(dtype, d):
 
 
 def test_many_slabs():
-    """T = 5000 (20 slabs of 256 tokens) for 5 groups, fp32 and fp16."""
+    """T = 5000 (40 slabs of 128 tokens) for 5 groups, fp32 and fp16."""
     rng = np.random.default_rng(50)
     x = (rng.standard_normal((5, 5000, 64)) * rng.uniform(0.1, 50, (5, 1, 64))).astype(np.float32)
     roundtrip_check(x, "fp32 T=5000")
