@@ -160,8 +160,11 @@ __global__ __launch_bounds__(256) void quantize_int4_generic_kernel(const T* __r
 }
 
 template <typename T>
-static hipError_t quantize_int4_dispatch(const T* x, int64_t ngroups, int g, uint8_t* codes,
-                                         float* steps, float* offsets, hipStream_t st) {
+// ngroups: groups of this launch; total: groups of the whole call (it picks
+// the passes per wave; calls are launched in slices of kGroupsPerLaunch)
+static hipError_t quantize_int4_dispatch(const T* x, int64_t ngroups, int64_t total, int g,
+                                         uint8_t* codes, float* steps, float* offsets,
+                                         hipStream_t st) {
   constexpr int N = In4<T>::N;
   const int cpg = g / N;
   auto lanes = [&](auto kernel, int lpg, int unroll) {
@@ -178,12 +181,12 @@ static hipError_t quantize_int4_dispatch(const T* x, int64_t ngroups, int g, uin
       // wave up to 2^24 groups (6 % faster on the 2^20 groups of one
       // Llama-7B layer's keys and values), eight above (3 % faster at 2^25)
       case 4:
-        return ngroups <= (int64_t(1) << 24) ? lanes(quantize_int4_kernel<T, 4, 1, 2>, 4, 2)
-                                             : lanes(quantize_int4_kernel<T, 4, 1, 8>, 4, 8);
+        return total <= (int64_t(1) << 24) ? lanes(quantize_int4_kernel<T, 4, 1, 2>, 4, 2)
+                                           : lanes(quantize_int4_kernel<T, 4, 1, 8>, 4, 8);
       // fp32 g = 32 above 2^24 groups: two group passes per wave (938 ->
       // 849 us at 2^25 groups; at 2^23 eight stay 3 % faster)
       case 8:
-        return sizeof(T) == 4 && ngroups > (int64_t(1) << 24)
+        return sizeof(T) == 4 && total > (int64_t(1) << 24)
                    ? lanes(quantize_int4_kernel<T, 8, 1, 2>, 8, 2)
                    : lanes(quantize_int4_kernel<T, 8, 1, 8>, 8, 8);
       case 16: return lanes(quantize_int4_kernel<T, 16, 1, 8>, 16, 8);
@@ -208,8 +211,8 @@ static hipError_t quantize_int4_sliced(const T* x, int64_t ngroups, int g, uint8
                                        float* steps, float* offsets, hipStream_t s) {
   for (int64_t g0 = 0; g0 < ngroups; g0 += kGroupsPerLaunch) {
     const int64_t n = std::min(kGroupsPerLaunch, ngroups - g0);
-    hipError_t e = quantize_int4_dispatch(x + g0 * g, n, g, codes + g0 * (g / 2), steps + g0,
-                                          offsets + g0, s);
+    hipError_t e = quantize_int4_dispatch(x + g0 * g, n, ngroups, g, codes + g0 * (g / 2),
+                                          steps + g0, offsets + g0, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
