@@ -56,28 +56,6 @@ __device__ __forceinline__ uint32_t res_acc_word(const f32x16& acc) {
   return lo | (hi << 16);
 }
 
-// Sign words of projection tiles mt and mt + 1 for the wave's 32 tokens:
-// P = S_tile (hi + lo)^T on fp16 MFMA, both parts into one binary32
-// accumulator per tile; the two tiles' MFMAs alternate, so two independent
-// accumulator chains are in flight.
-__device__ __forceinline__ void res_tile_words2(const f16x8* sfrag, int mt, int lane,
-                                                const f16x8 (&bh)[kResKS],
-                                                const f16x8 (&bl)[kResKS], uint32_t& w0,
-                                                uint32_t& w1) {
-  f32x16 a0c = f32x16{}, a1c = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < kResKS; ++ks) {
-    const f16x8 a0 = sfrag[(mt * kResKS + ks) * 64 + lane];
-    const f16x8 a1 = sfrag[((mt + 1) * kResKS + ks) * 64 + lane];
-    a0c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, bh[ks], a0c, 0, 0, 0);
-    a1c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, bh[ks], a1c, 0, 0, 0);
-    a0c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, bl[ks], a0c, 0, 0, 0);
-    a1c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, bl[ks], a1c, 0, 0, 0);
-  }
-  w0 = res_acc_word(a0c);
-  w1 = res_acc_word(a1c);
-}
-
 // codes_rcp for t = RN32(x - z) given, without the clamp: t >= 0 and
 // t / s <= 15 + 2^-19, so the rounded quotient is already in [0, 15].
 __device__ __forceinline__ void codes_rcp_t(const float (&t)[8], float sdiv, float r,
@@ -234,10 +212,41 @@ void residual_sketch_kernel(const _Float16* __restrict__ k, int64_t rows,
 
     // 4) sign words
     uint32_t wbuf[kResMT];
+    // one accumulator chain per projection tile (hi and lo parts in turn);
+    // the sign word of tile mt - 1 is taken between the MFMAs of tile mt
+    f32x16 accA, accB;
+    auto chain = [&](int mt, f32x16& acc) {
+      acc = f32x16{};
 #pragma unroll
-    for (int mt = 0; mt < kResMT; mt += 2) {
+      for (int ks = 0; ks < kResKS; ++ks) {
+        const f16x8 a = sf[(mt * kResKS + ks) * 64 + lane];
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bh[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bl[ks], acc, 0, 0, 0);
+      }
+    };
+    __builtin_amdgcn_sched_barrier(0);
+    chain(0, accA);
+#pragma unroll
+    for (int mt = 1; mt <= kResMT; ++mt) {
       __builtin_amdgcn_sched_barrier(0);
-      res_tile_words2(sf, mt, lane, bh, bl, wbuf[mt], wbuf[mt + 1]);
+      uint32_t w;
+      if (mt & 1) {
+        if (mt < kResMT) chain(mt, accB);
+        w = res_acc_word(accA);
+      } else {
+        if (mt < kResMT) chain(mt, accA);
+        w = res_acc_word(accB);
+      }
+      if (mt < kResMT) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);        // LDS reads
+#pragma unroll
+        for (int ks = 0; ks < kResKS; ++ks) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);      // MFMA
+          if (ks + 2 < kResKS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);      // VALU
+        }
+      }
+      wbuf[mt - 1] = w;
     }
 
     // 5) stores: half h writes code bytes [32 h, 32 h + 32), the steps
