@@ -18,11 +18,13 @@
 // 0..15; its sign word is then built with shift-and-insert steps and one
 // exchange with the other half.
 //
-// Score: per (group, query) workgroup y = S q goes to LDS and is expanded
-// into one 256-entry table per byte of the sign words:
+// Score: per query, y = S q goes to LDS and is expanded into one 256-entry
+// table per byte of the sign words:
 //   T_p[v] = sum_{j<8} (bit j of v ? +1 : -1) * y_{8p+j},
 // so a token costs one table lookup per 8 bits (for m = 256 in a layout
-// whose lookups never share an LDS bank within a half-wave).
+// whose lookups never share an LDS bank within a half-wave).  For m = 256 a
+// workgroup takes one tile of a group's tokens and scores all of the group's
+// queries against it; other shapes take one (group, query, tile).
 #include "kvq_device.h"
 #include "kvq_launch.h"
 #include "kvq_qjl_device.h"
