@@ -188,6 +188,40 @@ def test_scores_shapes(qdt, nq, T, d):
     assert_int8_scores(sc, q, codes, scales, O.scores_int8(q, codes, scales))
 
 
+@pytest.mark.parametrize("nq", [1, 4])
+def test_scores_long_cache_sampled(nq):
+    """32 heads x 262144 tokens x 128 (the bench's long-cache launch: 2 or 8
+    token iterations per block): 4096 sampled (head, token) scores plus each
+    head's first and last compared with the oracle."""
+    G, T, d = 32, 262144, 128
+    rng = np.random.default_rng(40 + nq)
+    codes = rng.integers(-127, 128, size=(G, T, d), dtype=np.int8)
+    scales = rng.uniform(1e-3, 5e-2, size=(G, T)).astype(np.float32)
+    q = rng.standard_normal((G, nq, d)).astype(np.float16)
+    log(f"[int8] long-cache scores nq={nq}")
+    sc = K.scores_int8(up(q), up(codes), up(scales))
+    gs = np.concatenate([np.arange(G), np.arange(G), rng.integers(0, G, 4096)])
+    ts = np.concatenate([np.zeros(G, np.int64), np.full(G, T - 1), rng.integers(0, T, 4096)])
+    gpu = down(sc[torch.from_numpy(gs).cuda(), :, torch.from_numpy(ts).cuda()])   # [S, nq]
+    cs = codes[gs, ts][:, None, :]                                 # [S, 1, d]
+    ss = scales[gs, ts][:, None]                                   # [S, 1]
+    ora = O.scores_int8(q[gs], cs, ss)                             # [S, nq, 1]
+    assert_int8_scores(gpu[:, :, None], q[gs], cs, ss, ora)
+
+
+@pytest.mark.parametrize("nq,G,T", [(1, 5, 60001), (4, 5, 60001), (4, 9, 131073)])
+def test_scores_iteration_paths_ragged(nq, G, T):
+    """Caches large enough for the 2- and 8-iteration blocks, with ragged
+    last tiles: every score compared with the oracle."""
+    rng = np.random.default_rng(nq * 7 + G)
+    d = 128
+    codes = rng.integers(-127, 128, size=(G, T, d), dtype=np.int8)
+    scales = rng.uniform(1e-3, 5e-2, size=(G, T)).astype(np.float32)
+    q = rng.standard_normal((G, nq, d)).astype(np.float32)
+    sc = down(K.scores_int8(up(q), up(codes), up(scales)))
+    assert_int8_scores(sc, q, codes, scales, O.scores_int8(q, codes, scales))
+
+
 def test_empty_inputs_are_noops():
     x = torch.empty((0, 128), dtype=torch.float32, device="cuda")
     c, s = K.quantize_int8(x)
