@@ -70,6 +70,26 @@ def test_sweep_large_sizes_sampled(n_log2):
         del c_t, s_t, z_t, d_t
 
 
+def test_fp16_above_2e24_groups_sampled():
+    """fp16 rows of 128 with g = 32 and 2^24 + 12 groups (the launch with
+    eight group passes per wave, in two slices): 2048 sampled rows plus the
+    first and last compared bit-exactly with the oracle."""
+    rows = (1 << 22) + 3
+    x_host = si.flat_rows(si.W_SWEEP, rows * 128, 128, dtype="f16")
+    x = up(x_host)
+    rng = np.random.default_rng(77)
+    sample = np.unique(np.concatenate([[0, rows - 1], rng.integers(0, rows, 2048)]))
+    idx = torch.from_numpy(sample).to(x.device)
+    c_t, s_t, z_t = K.quantize_int4(x, 32)
+    d_t = K.dequantize_int4(c_t, s_t, z_t, 32, torch.float16)
+    co, so, zo = O.quantize_int4(x_host[sample], 32)
+    assert np.array_equal(down(c_t.index_select(0, idx)), co), "codes differ"
+    assert np.array_equal(down(s_t.index_select(0, idx)).view(np.uint32), so.view(np.uint32))
+    _cmp_offsets(down(z_t.index_select(0, idx)), zo, "fp16 2^24+ groups")
+    do = O.dequantize_int4(co, so, zo, 32, "f16")
+    assert np.array_equal(down(d_t.index_select(0, idx)).view(np.uint16), do.view(np.uint16))
+
+
 # --- Llama-7B-shaped layer: 32 heads x 4096 tokens x 128, fp16, outliers --------
 
 @pytest.mark.parametrize("g", [32, 128])
