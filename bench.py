@@ -441,6 +441,25 @@ def main():
     torch.cuda.synchronize()
     dec_ms = d0.elapsed_time(d1) / args.steps
     ms_step = elapsed * 1e3 / args.steps
+
+    # The same step captured 20 times in one HIP graph and replayed: the
+    # per-step time with host launch overhead taken out (reported beside the
+    # eager figure, which is `value`).
+    graph = torch.cuda.CUDAGraph()
+    graph_steps = 20
+    with torch.cuda.graph(graph):
+        for _ in range(graph_steps):
+            step()
+    torch.cuda.synchronize()
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    t_g = time.perf_counter()
+    for _ in range(5):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_ms_step = (time.perf_counter() - t_g) * 1e3 / (5 * graph_steps)
+    del graph
     scores = G * T
     value = scores / (ms_step / 1e3)
 
@@ -453,6 +472,7 @@ def main():
                 "kernel": "kvq_decode_qjl_int8 (qjl_project_kernel + decode_split_kernel + decode_merge_kernel)",
                 "alg_bytes_per_launch": alg_bytes, "avg_launch_ms": round(dec_ms, 4),
                 "launch_timing": f"{args.steps} back-to-back launches between HIP events"}
+    log(f"bench: graph replay {graph_ms_step:.3f} ms/step")
     log(f"bench: {args.steps} steps, {ms_step:.3f} ms/step (events {step_ev_ms:.3f}), "
         f"decode {dec_ms:.3f} ms "
         f"({achieved:.0f} GB/s)")
@@ -477,6 +497,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "graph_ms_per_step": round(graph_ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
