@@ -143,6 +143,15 @@ def components(K, si, torch, np):
     def ncopies(bytes_per_call):
         return max(1, -(-COLD_BYTES // int(bytes_per_call)) + 1)
 
+    # context: a plain device copy of 1 GiB (1 GiB read + 1 GiB written), the
+    # practical rate of a stream that mixes reads and writes equally
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dsts = [torch.empty_like(src) for _ in range(2)]
+    it_c = iter(range(10 ** 9))
+    gbs("device_copy_1GiB", 2 * src.numel() * 4,
+        [lambda: dsts[next(it_c) % 2].copy_(src)], reps=10)
+    del src, dsts
+
     # INT8 round-trip error on the sweep (fp32 rows, N(0, 1)) and the
     # U(-1, 1) context row: max and mean |dequantize(quantize(x)) - x|
     acc = {}
