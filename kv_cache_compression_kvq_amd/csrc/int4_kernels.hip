@@ -174,22 +174,25 @@ static hipError_t quantize_int4_dispatch(const T* x, int64_t ngroups, int64_t to
                        offsets);
     return hipGetLastError();
   };
+  const int64_t elems = total * g;
+  const bool few_passes = sizeof(T) == 2 ? elems <= (int64_t(1) << 27) : elems > (int64_t(1) << 28);
   if ((cpg & (cpg - 1)) == 0) {
     switch (cpg) {
       case 2: return lanes(quantize_int4_kernel<T, 2, 1, 8>, 2, 8);
-      // groups of 4 chunks (fp16 g = 32, fp32 g = 16): two group passes per
-      // wave up to 2^24 groups (6 % faster on the 2^20 groups of one
-      // Llama-7B layer's keys and values), eight above (3 % faster at 2^25)
+      // Groups of 4, 8 or 16 chunks: two group passes per wave for fp16 calls
+      // of up to 2^27 elements and fp32 calls of more than 2^28, else eight
+      // (measured: fp16 g = 32 / 128 on a Llama-7B layer, 2^25 elements, 6-7 %
+      // faster with two, at 2^30 2-3 % slower; fp32 g = 32 / 64 at 2^30 7-9 %
+      // faster with two, g = 32 at 2^28 3 % slower)
       case 4:
-        return total <= (int64_t(1) << 24) ? lanes(quantize_int4_kernel<T, 4, 1, 2>, 4, 2)
-                                           : lanes(quantize_int4_kernel<T, 4, 1, 8>, 4, 8);
-      // fp32 g = 32 above 2^24 groups: two group passes per wave (938 ->
-      // 849 us at 2^25 groups; at 2^23 eight stay 3 % faster)
+        return few_passes ? lanes(quantize_int4_kernel<T, 4, 1, 2>, 4, 2)
+                          : lanes(quantize_int4_kernel<T, 4, 1, 8>, 4, 8);
       case 8:
-        return sizeof(T) == 4 && total > (int64_t(1) << 24)
-                   ? lanes(quantize_int4_kernel<T, 8, 1, 2>, 8, 2)
-                   : lanes(quantize_int4_kernel<T, 8, 1, 8>, 8, 8);
-      case 16: return lanes(quantize_int4_kernel<T, 16, 1, 8>, 16, 8);
+        return few_passes ? lanes(quantize_int4_kernel<T, 8, 1, 2>, 8, 2)
+                          : lanes(quantize_int4_kernel<T, 8, 1, 8>, 8, 8);
+      case 16:
+        return few_passes ? lanes(quantize_int4_kernel<T, 16, 1, 2>, 16, 2)
+                          : lanes(quantize_int4_kernel<T, 16, 1, 8>, 16, 8);
       case 32: return lanes(quantize_int4_kernel<T, 16, 2, 4>, 16, 4);
       case 64: return lanes(quantize_int4_kernel<T, 64, 1, 4>, 64, 4);
       case 128: return lanes(quantize_int4_kernel<T, 64, 2, 4>, 64, 4);

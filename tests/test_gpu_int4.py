@@ -45,10 +45,11 @@ def roundtrip_check(x: np.ndarray, g: int, label: str):
 
 @pytest.mark.parametrize("n_log2", [28, 30])
 def test_sweep_large_sizes_sampled(n_log2):
-    """2^28 and 2^30 fp32 elements as rows of 128 with groups of 32 and 128
-    (the bench's launches; 2^30 with g = 32 takes the two-pass-per-wave
-    kernel): 2048 sampled rows plus the first and last compared bit-exactly
-    with the oracle (codes, steps, offsets, fp32 reconstruction)."""
+    """2^28 and 2^30 fp32 elements as rows of 128 with groups of 32, 64 and
+    128 (the bench's launches; at 2^30 groups of 32 and 64 take the
+    two-pass-per-wave kernel): 2048 sampled rows plus the first and last
+    compared bit-exactly with the oracle (codes, steps, offsets, fp32
+    reconstruction)."""
     n = 1 << n_log2
     x_host = si.flat_rows(si.W_SWEEP, n, 128)
     x = up(x_host)
@@ -57,7 +58,7 @@ def test_sweep_large_sizes_sampled(n_log2):
     sample = np.unique(np.concatenate([[0, rows - 1], rng.integers(0, rows, 2048)]))
     idx = torch.from_numpy(sample).to(x.device)
     xs = x_host[sample]
-    for g in (32, 128):
+    for g in (32, 64, 128):
         log(f"[int4] sweep 2^{n_log2} g={g}: quantize {rows} rows")
         c_t, s_t, z_t = K.quantize_int4(x, g)
         d_t = K.dequantize_int4(c_t, s_t, z_t, g)
@@ -70,23 +71,25 @@ def test_sweep_large_sizes_sampled(n_log2):
         del c_t, s_t, z_t, d_t
 
 
-def test_fp16_above_2e24_groups_sampled():
-    """fp16 rows of 128 with g = 32 and 2^24 + 12 groups (the launch with
-    eight group passes per wave, in two slices): 2048 sampled rows plus the
-    first and last compared bit-exactly with the oracle."""
+@pytest.mark.parametrize("g", [32, 64, 128])
+def test_fp16_above_2e24_groups_sampled(g):
+    """fp16 rows of 128 with more than 2^24 groups for g = 32 (the launch
+    with eight group passes per wave, in slices) and the same rows with
+    g = 64, 128: 2048 sampled rows plus the first and last compared
+    bit-exactly with the oracle."""
     rows = (1 << 22) + 3
     x_host = si.flat_rows(si.W_SWEEP, rows * 128, 128, dtype="f16")
     x = up(x_host)
     rng = np.random.default_rng(77)
     sample = np.unique(np.concatenate([[0, rows - 1], rng.integers(0, rows, 2048)]))
     idx = torch.from_numpy(sample).to(x.device)
-    c_t, s_t, z_t = K.quantize_int4(x, 32)
-    d_t = K.dequantize_int4(c_t, s_t, z_t, 32, torch.float16)
-    co, so, zo = O.quantize_int4(x_host[sample], 32)
+    c_t, s_t, z_t = K.quantize_int4(x, g)
+    d_t = K.dequantize_int4(c_t, s_t, z_t, g, torch.float16)
+    co, so, zo = O.quantize_int4(x_host[sample], g)
     assert np.array_equal(down(c_t.index_select(0, idx)), co), "codes differ"
     assert np.array_equal(down(s_t.index_select(0, idx)).view(np.uint32), so.view(np.uint32))
-    _cmp_offsets(down(z_t.index_select(0, idx)), zo, "fp16 2^24+ groups")
-    do = O.dequantize_int4(co, so, zo, 32, "f16")
+    _cmp_offsets(down(z_t.index_select(0, idx)), zo, f"fp16 g={g}")
+    do = O.dequantize_int4(co, so, zo, g, "f16")
     assert np.array_equal(down(d_t.index_select(0, idx)).view(np.uint16), do.view(np.uint16))
 
 
