@@ -57,6 +57,9 @@ enum {
 typedef int32_t kvq_dtype;
 enum { KVQ_F32 = 0, KVQ_F16 = 1 };
 
+/* Size of the per-device scratch array used by kvq_decode_qjl_int8_noalloc. */
+#define KVQ_STATIC_SCRATCH_BYTES ((size_t)8 << 20)
+
 /*
  * kvq_quantize_int8 - per-row symmetric INT8 quantization.
  *
@@ -383,6 +386,42 @@ kvq_status kvq_decode_qjl_int8_gqa(const void* q, kvq_dtype q_dt, int64_t groups
                                    const int8_t* vcodes, const float* vscales, int64_t T,
                                    int32_t d, float sm_scale, void* ws, size_t ws_bytes,
                                    float* out, kvq_stream_t stream);
+
+/*
+ * kvq_decode_qjl_int8_noalloc - kvq_decode_qjl_int8 without a caller
+ * workspace and without any allocation, for callers that cannot allocate
+ * device memory (code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc).
+ *
+ * Runs the same kernels as kvq_decode_qjl_int8 with the same token split,
+ * so its output is bit-identical to that call's for the same arguments.  The
+ * scratch it needs (kvq_decode_workspace_bytes(groups, T, d, m) bytes: the
+ * projected queries and the softmax partials) lives in a device array of
+ * KVQ_STATIC_SCRATCH_BYTES bytes inside the library, one per GPU, held from
+ * the library's load until the process ends.  Its contents need no
+ * initialisation: every call writes each scratch value before reading it.
+ * The array's device address is looked up once per device, on the first
+ * call with that device current.  The call never calls hipMalloc, hipFree
+ * or any allocating routine.
+ *
+ * All calls on one GPU share that GPU's array: two calls whose executions
+ * overlap on the device (different streams, or host threads without
+ * ordering between their streams) race on it and give undefined results.
+ * Calls on one stream are ordered and safe.
+ *
+ * Arguments as kvq_decode_qjl_int8 without ws / ws_bytes.
+ * Errors: NULL, ALIGN, SHAPE, DTYPE as kvq_decode_qjl_int8; WORKSPACE when
+ * the call would need more than KVQ_STATIC_SCRATCH_BYTES of scratch (at
+ * d = 128, m = 256 and T <= 2^20: up to about 5000 groups fit; the need is
+ * 4 * groups * (m + splits * (d + 2)) bytes for the call's token split);
+ * LAUNCH when the device query, the address lookup or a launch fails.
+ */
+kvq_status kvq_decode_qjl_int8_noalloc(const void* q, kvq_dtype q_dt, int64_t groups,
+                                       const void* S, kvq_dtype S_dt, int32_t m,
+                                       const uint32_t* kbits, const uint16_t* knorms,
+                                       const int8_t* vcodes, const float* vscales, int64_t T,
+                                       int32_t d, float sm_scale, float* out,
+                                       kvq_stream_t stream);
 
 /*
  * kvq_cache_append - compress-on-write for one decode step: the newest key

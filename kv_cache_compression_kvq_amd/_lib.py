@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(HERE, "libkvq.so")
 KVQ_OK, KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_ALIGN = 0, 1, 2, 3
 KVQ_ERR_DTYPE, KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH = 4, 5, 6
 KVQ_F32, KVQ_F16 = 0, 1
+KVQ_STATIC_SCRATCH_BYTES = 8 << 20   # include/kvq.h
 
 # name -> (restype, argtypes), mirroring include/kvq.h
 PROTOTYPES = {
@@ -51,6 +52,9 @@ PROTOTYPES = {
     "kvq_decode_qjl_int8": (c_int32, [c_void_p, c_int32, c_int64, c_void_p, c_int32, c_int32,
                                       c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32,
                                       c_float, c_void_p, c_size_t, c_void_p, c_void_p]),
+    "kvq_decode_qjl_int8_noalloc": (c_int32, [c_void_p, c_int32, c_int64, c_void_p, c_int32, c_int32,
+                                              c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
+                                              c_int32, c_float, c_void_p, c_void_p]),
     "kvq_cache_append": (c_int32, [c_void_p, c_void_p, c_int32, c_int64, c_int32, c_void_p, c_int32,
                                    c_int64, c_int64, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_void_p]),

@@ -98,7 +98,7 @@ kvq_status decode_impl(const char* fn, const void* q, kvq_dtype q_dt, int64_t gr
                        const void* S, kvq_dtype S_dt, int32_t m, const uint32_t* kbits,
                        const uint16_t* knorms, const int8_t* vcodes, const float* vscales,
                        int64_t T, int32_t d, float sm_scale, void* ws, size_t ws_bytes,
-                       float* out, kvq_stream_t stream) {
+                       float* out, kvq_stream_t stream, bool static_ws = false) {
   kvq_status st;
   if ((st = check_count(fn, "groups", groups)) || (st = check_count(fn, "T", T)) ||
       (st = check_nq(fn, nq)) || (st = check_d(fn, d)) || (st = check_m(fn, m)) ||
@@ -118,6 +118,19 @@ kvq_status decode_impl(const char* fn, const void* q, kvq_dtype q_dt, int64_t gr
   kvq::DeviceInfo dev;
   if ((st = device_info(fn, &dev))) return st;
   const size_t need = kvq::decode_workspace_bytes(groups, nq, T, d, m, dev);
+  if (static_ws) {
+    if (need > kvq::kStaticScratchBytes)
+      return fail(KVQ_ERR_WORKSPACE,
+                  "%s: groups = %lld, T = %lld, d = %d, m = %d need %zu bytes of scratch; the "
+                  "static scratch array holds %zu",
+                  fn, (long long)groups, (long long)T, (int)d, (int)m, need,
+                  kvq::kStaticScratchBytes);
+    hipError_t e = kvq::static_scratch(&ws);
+    if (e != hipSuccess)
+      return fail(KVQ_ERR_LAUNCH, "%s: scratch address lookup failed: %s", fn,
+                  hipGetErrorString(e));
+    ws_bytes = kvq::kStaticScratchBytes;
+  }
   if (ws == nullptr || ws_bytes < need)
     return fail(KVQ_ERR_WORKSPACE, "%s: workspace of %zu bytes at %p, need %zu", fn, ws_bytes, ws,
                 need);
@@ -439,6 +452,16 @@ kvq_status kvq_decode_qjl_int8_gqa(const void* q, kvq_dtype q_dt, int64_t groups
                                    float* out, kvq_stream_t stream) {
   return decode_impl("kvq_decode_qjl_int8_gqa", q, q_dt, groups, nq, S, S_dt, m, kbits, knorms,
                      vcodes, vscales, T, d, sm_scale, ws, ws_bytes, out, stream);
+}
+
+kvq_status kvq_decode_qjl_int8_noalloc(const void* q, kvq_dtype q_dt, int64_t groups,
+                                       const void* S, kvq_dtype S_dt, int32_t m,
+                                       const uint32_t* kbits, const uint16_t* knorms,
+                                       const int8_t* vcodes, const float* vscales, int64_t T,
+                                       int32_t d, float sm_scale, float* out,
+                                       kvq_stream_t stream) {
+  return decode_impl("kvq_decode_qjl_int8_noalloc", q, q_dt, groups, 1, S, S_dt, m, kbits, knorms,
+                     vcodes, vscales, T, d, sm_scale, nullptr, 0, out, stream, true);
 }
 
 kvq_status kvq_cache_append(const void* k, const void* v, kvq_dtype kv_dt, int64_t groups,

@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "kvq.h"
+
 namespace kvq {
 
 struct DeviceInfo {
@@ -69,6 +71,11 @@ hipError_t launch_decode_qjl_int8(const void* q, int q_f16, int64_t groups, int 
                                   float sm_scale, void* ws, float* out, const DeviceInfo& dev,
                                   hipStream_t s);
 
+// Device address of the allocation-free decode's scratch array on the
+// current device (kStaticScratchBytes bytes, 256-byte aligned; looked up
+// with hipGetSymbolAddress on the first call per device).
+hipError_t static_scratch(void** out);
+
 hipError_t launch_cache_append(const void* k, const void* v, int kv_f16, int64_t groups, int d,
                                const void* S, int m, int64_t T, int64_t pos, uint32_t* kbits,
                                uint16_t* knorms, int8_t* vcodes, float* vscales, hipStream_t s);
@@ -89,5 +96,6 @@ constexpr int kMaxM = 1024;
 constexpr int kMaxNq = 64;
 constexpr int kMaxDecodeD = 1024;
 constexpr int kMaxChannelD = 8192;   // per-channel INT8: scales and query in LDS
+constexpr size_t kStaticScratchBytes = KVQ_STATIC_SCRATCH_BYTES;
 
 }  // namespace kvq

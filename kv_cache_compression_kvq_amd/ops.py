@@ -303,6 +303,35 @@ def decode_qjl_int8(q: torch.Tensor, S: torch.Tensor, kbits: torch.Tensor, knorm
     return out
 
 
+def decode_qjl_int8_noalloc(q: torch.Tensor, S: torch.Tensor, kbits: torch.Tensor,
+                            knorms: torch.Tensor, vcodes: torch.Tensor, vscales: torch.Tensor,
+                            sm_scale: float | None = None,
+                            out: torch.Tensor | None = None) -> torch.Tensor:
+    """decode_qjl_int8 through the entry point that takes no workspace and
+    allocates nothing (its scratch is a fixed per-device array inside the
+    library).  Pass ``out`` [G, d] fp32 to make the whole call allocation-free."""
+    for t, n in ((q, "q"), (S, "S"), (kbits, "kbits"), (knorms, "knorms"), (vcodes, "vcodes"),
+                 (vscales, "vscales")):
+        _dev(t, n)
+    G, d = q.shape
+    m = S.shape[0]
+    T = kbits.shape[1]
+    if (kbits.shape != (G, T, m // 32) or knorms.shape != (G, T) or vcodes.shape != (G, T, d)
+            or vscales.shape != (G, T) or S.shape[1] != d):
+        raise ValueError("shape mismatch between q, S and the cache tensors")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((G, d), dtype=torch.float32, device=q.device)
+    elif out.shape != (G, d) or out.dtype != torch.float32:
+        raise ValueError("out must be float32 [G, d]")
+    _dev(out, "out")
+    L.check(L.lib().kvq_decode_qjl_int8_noalloc(
+        _p(q), _dtype_code(q, "q"), G, _p(S), _dtype_code(S, "S"), m, _p(kbits), _p(knorms),
+        _p(vcodes), _p(vscales), T, d, float(sm_scale), _p(out), _stream(q)))
+    return out
+
+
 def cache_append(k: torch.Tensor, v: torch.Tensor, S: torch.Tensor, kbits: torch.Tensor,
                  knorms: torch.Tensor, vcodes: torch.Tensor, vscales: torch.Tensor,
                  pos: int) -> None:

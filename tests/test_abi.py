@@ -174,6 +174,33 @@ def test_decode_validation():
                 ws=None, out=None) == L.KVQ_OK
 
 
+def test_decode_noalloc_validation():
+    """The allocation-free decode validates like the workspace form (before any
+    HIP call), and has no workspace argument to get wrong."""
+    f = L.lib().kvq_decode_qjl_int8_noalloc
+    args = [A, L.KVQ_F16, 2, A, L.KVQ_F16, 256, A, A, A, A, 16, 128, 0.1, A, None]
+    names = ["q", "q_dt", "groups", "S", "S_dt", "m", "kbits", "knorms", "vcodes", "vscales",
+             "T", "d", "sm", "out", "stream"]
+
+    def call(**kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    _err(call(T=0), L.KVQ_ERR_SHAPE)
+    _err(call(m=33), L.KVQ_ERR_SHAPE)
+    _err(call(d=24), L.KVQ_ERR_SHAPE)
+    _err(call(d=2048), L.KVQ_ERR_SHAPE)
+    _err(call(groups=-3), L.KVQ_ERR_SHAPE)
+    _err(call(kbits=None), L.KVQ_ERR_NULL)
+    _err(call(out=None), L.KVQ_ERR_NULL)
+    _err(call(vscales=MIS), L.KVQ_ERR_ALIGN)
+    _err(call(S_dt=3), L.KVQ_ERR_DTYPE)
+    assert call(groups=0, q=None, S=None, kbits=None, knorms=None, vcodes=None, vscales=None,
+                out=None) == L.KVQ_OK
+
+
 def test_cache_append_validation():
     f = L.lib().kvq_cache_append
     args = [A, A, L.KVQ_F16, 4, 128, A, 256, 16, 15, A, A, A, A, None]
