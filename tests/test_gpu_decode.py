@@ -10,6 +10,7 @@ import torch
 import kv_cache_compression_kvq_amd as K
 import synth_inputs as si
 from oracle import decode as OD, int8 as OI, qjl as OQ
+import full_size as FS
 from gpu_common import (assert_bits_within_band, assert_norms_within_ulp, decode_tolerance_check,
                         down, log, up)
 
@@ -98,47 +99,48 @@ def test_split_invariance():
     assert np.allclose(many, alone[0][None, :], rtol=2e-5, atol=1e-6)
 
 
-def test_decode_full_size_sampled():
+def test_decode_full_size_every_group():
     """16 x 32 x 32768 x 128: K sketched and V quantized on the GPU from the
-    generator's fp16 tensors (sampled groups compared with the oracle's
-    cache), then three groups get the oracle's compressed rows and the
-    full-size decode (the bench's launch) is checked on them."""
+    generator's fp16 tensors; every row of that cache is checked against the
+    oracle (sign bits within the band, norms within one ulp, value codes and
+    scales bit-exact).  The full-size decode (the bench's launch) then runs
+    on the GPU-built cache, and the oracle, fed the same cache, checks the
+    output of every one of the 512 groups."""
     W = si.W_DECODE
     B, H, T, d, m = 16, 32, 32768, 128, 256
     G = B * H
+    lam = 1 / math.sqrt(d)
     log("[decode] full size: generate K")
-    k = si.kv_tensor(W, si.K, B, H, T, d, "f16").reshape(G, T, d)
+    k = si.kv_tensor(W, si.K, B, H, T, d, "f16").reshape(G * T, d)
     S = si.projection(W, m, d, "f16")
     Sd = up(S)
     kd = up(k)
     kbits, knorms = K.qjl_sketch(kd, Sd)
     del kd
+    kw, kn = down(kbits, np.uint32), down(knorms)
+    log("[decode] full size: check every key row")
+    flips, ulps = FS.sketch_every_row(k, S, kw, kn)
+    log(f"[decode] full size: {flips} key bits inside the band differ, {ulps} norms one ulp apart")
+    del k
     log("[decode] full size: generate V")
-    v = si.kv_tensor(W, si.V, B, H, T, d, "f16").reshape(G, T, d)
+    v = si.kv_tensor(W, si.V, B, H, T, d, "f16").reshape(G * T, d)
     vd = up(v)
     vcodes, vscales = K.quantize_int8(vd)
     del vd
-    torch.cuda.synchronize()
-    groups = [0, 301, G - 1]
+    vc, vs = down(vcodes), down(vscales)
+    log("[decode] full size: check every value row")
+    FS.int8_every_row(v, vc, vs, K.dequantize_int8(vcodes, vscales, torch.float16).cpu().numpy(),
+                      "decode V", out_dtype="f16")
+    del v
     q = si.queries(W, G, 1, d, "f16")[:, 0]
-    cache = {}
-    for g in groups:
-        kw, kn, vc, vs = make_cache(k[g:g + 1], v[g:g + 1], S)
-        assert_bits_within_band(down(kbits[g], np.uint32), kw[0], k[g], S)
-        assert_norms_within_ulp(down(knorms[g]), kn[0])
-        assert np.array_equal(down(vcodes[g]), vc[0])
-        assert np.array_equal(down(vscales[g]).view(np.uint32), vs[0].view(np.uint32))
-        kbits[g].copy_(up(kw[0]))
-        knorms[g].copy_(up(kn[0]))
-        cache[g] = (kw, kn, vc, vs)
-    del k, v
     log("[decode] full size: decode")
-    out = down(K.decode_qjl_int8(up(q), Sd, kbits, knorms, vcodes, vscales, 1 / math.sqrt(d)))
+    out = down(K.decode_qjl_int8(up(q), Sd, kbits.view(G, T, m // 32), knorms.view(G, T),
+                                 vcodes.view(G, T, d), vscales.view(G, T), lam))
     assert np.all(np.isfinite(out))
-    for g in groups:
-        kw, kn, vc, vs = cache[g]
-        ora = OD.decode_qjl_int8(q[g:g + 1], S, kw, kn, vc, vs, 1 / math.sqrt(d))
-        decode_tolerance_check(out[g:g + 1], q[g:g + 1], S, kw, kn, vc, vs, 1 / math.sqrt(d), ora)
+    log("[decode] full size: oracle on every group")
+    worst = FS.decode_every_group(q, S, kw.reshape(G, T, m // 32), kn.reshape(G, T),
+                                  vc.reshape(G, T, d), vs.reshape(G, T), lam, out)
+    log(f"[decode] full size: all {G} groups within tolerance; worst err / tol = {worst:.3g}")
 
 
 # --- grouped-query attention: nq query heads per KV head -------------------------

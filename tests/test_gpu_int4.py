@@ -9,6 +9,7 @@ import torch
 import kv_cache_compression_kvq_amd as K
 import synth_inputs as si
 from oracle import int4 as O
+import full_size as FS
 from gpu_common import down, log, up
 
 pytestmark = pytest.mark.gpu
@@ -44,53 +45,39 @@ def roundtrip_check(x: np.ndarray, g: int, label: str):
 # --- element-count sweep sizes (the bench's fp32 workloads) --------------------
 
 @pytest.mark.parametrize("n_log2", [28, 30])
-def test_sweep_large_sizes_sampled(n_log2):
+def test_sweep_large_sizes_every_row(n_log2):
     """2^28 and 2^30 fp32 elements as rows of 128 with groups of 32, 64 and
     128 (the bench's launches; at 2^30 groups of 32 and 64 take the
-    two-pass-per-wave kernel): 2048 sampled rows plus the first and last
-    compared bit-exactly with the oracle (codes, steps, offsets, fp32
-    reconstruction)."""
+    two-pass-per-wave kernel): every row compared bit-exactly with the oracle
+    (codes, steps, offsets, fp32 reconstruction)."""
     n = 1 << n_log2
     x_host = si.flat_rows(si.W_SWEEP, n, 128)
     x = up(x_host)
     rows = x_host.shape[0]
-    rng = np.random.default_rng(n_log2 + 4)
-    sample = np.unique(np.concatenate([[0, rows - 1], rng.integers(0, rows, 2048)]))
-    idx = torch.from_numpy(sample).to(x.device)
-    xs = x_host[sample]
     for g in (32, 64, 128):
         log(f"[int4] sweep 2^{n_log2} g={g}: quantize {rows} rows")
         c_t, s_t, z_t = K.quantize_int4(x, g)
         d_t = K.dequantize_int4(c_t, s_t, z_t, g)
-        co, so, zo = O.quantize_int4(xs, g)
-        assert np.array_equal(down(c_t.index_select(0, idx)), co), f"2^{n_log2} g={g}: codes differ"
-        assert np.array_equal(down(s_t.index_select(0, idx)).view(np.uint32), so.view(np.uint32))
-        _cmp_offsets(down(z_t.index_select(0, idx)), zo, f"2^{n_log2} g={g}")
-        do = O.dequantize_int4(co, so, zo, g, "f32")
-        assert np.array_equal(down(d_t.index_select(0, idx)).view(np.uint32), do.view(np.uint32))
+        c, s_, z, dq = down(c_t), down(s_t), down(z_t), down(d_t)
         del c_t, s_t, z_t, d_t
+        FS.int4_every_row(x_host, g, c, s_, z, dq, f"2^{n_log2} g={g}")
+        log(f"[int4] sweep 2^{n_log2} g={g}: every row bit-exact")
+        del c, s_, z, dq
 
 
 @pytest.mark.parametrize("g", [32, 64, 128])
-def test_fp16_above_2e24_groups_sampled(g):
+def test_fp16_above_2e24_groups_every_row(g):
     """fp16 rows of 128 with more than 2^24 groups for g = 32 (the launch
     with eight group passes per wave, in slices) and the same rows with
-    g = 64, 128: 2048 sampled rows plus the first and last compared
-    bit-exactly with the oracle."""
+    g = 64, 128: every row compared bit-exactly with the oracle (fp16
+    reconstruction)."""
     rows = (1 << 22) + 3
     x_host = si.flat_rows(si.W_SWEEP, rows * 128, 128, dtype="f16")
     x = up(x_host)
-    rng = np.random.default_rng(77)
-    sample = np.unique(np.concatenate([[0, rows - 1], rng.integers(0, rows, 2048)]))
-    idx = torch.from_numpy(sample).to(x.device)
     c_t, s_t, z_t = K.quantize_int4(x, g)
     d_t = K.dequantize_int4(c_t, s_t, z_t, g, torch.float16)
-    co, so, zo = O.quantize_int4(x_host[sample], g)
-    assert np.array_equal(down(c_t.index_select(0, idx)), co), "codes differ"
-    assert np.array_equal(down(s_t.index_select(0, idx)).view(np.uint32), so.view(np.uint32))
-    _cmp_offsets(down(z_t.index_select(0, idx)), zo, f"fp16 g={g}")
-    do = O.dequantize_int4(co, so, zo, g, "f16")
-    assert np.array_equal(down(d_t.index_select(0, idx)).view(np.uint16), do.view(np.uint16))
+    FS.int4_every_row(x_host, g, down(c_t), down(s_t), down(z_t), down(d_t), f"fp16 g={g}",
+                      out_dtype="f16")
 
 
 # --- Llama-7B-shaped layer: 32 heads x 4096 tokens x 128, fp16, outliers --------
@@ -111,36 +98,6 @@ def test_llama_layer_full_size(g):
 def test_sweep_2p24_full_compare(d, g):
     x = si.flat_rows(si.W_SWEEP, 1 << 24, d)
     roundtrip_check(x, g, f"sweep 2^24 d={d}")
-
-
-def test_sweep_2p28_sampled():
-    """2^28 fp32 elements, d = 128, g = 32: every group is quantized on the
-    GPU; 4096 sampled rows plus the first and last are compared bit-exactly
-    with the oracle; on every group the minimum code is 0 and the maximum 15
-    (or the step is 0), checked on the device."""
-    n, d, g = 1 << 28, 128, 32
-    x_host = si.flat_rows(si.W_SWEEP, n, d)
-    x = up(x_host)
-    rows = n // d
-    codes, steps, offsets = K.quantize_int4(x, g)
-    deq = K.dequantize_int4(codes, steps, offsets, g)
-    rng = np.random.default_rng(28)
-    sample = np.unique(np.concatenate([[0, rows - 1], rng.integers(0, rows, 4096)]))
-    idx = torch.from_numpy(sample).to(x.device)
-    co, so, zo = O.quantize_int4(x_host[sample], g)
-    assert np.array_equal(down(codes.index_select(0, idx)), co)
-    assert np.array_equal(down(steps.index_select(0, idx)).view(np.uint32), so.view(np.uint32))
-    _cmp_offsets(down(offsets.index_select(0, idx)), zo, "2^28 sample")
-    do = O.dequantize_int4(co, so, zo, g)
-    assert np.array_equal(down(deq.index_select(0, idx)).view(np.uint32), do.view(np.uint32))
-    lo = (codes & 0xF).to(torch.int32)
-    hi = (codes >> 4).to(torch.int32)
-    both = torch.stack([lo, hi], dim=-1).reshape(rows, d // g, g)
-    live = steps != 0
-    assert bool((both.amin(dim=2)[live] == 0).all()) and bool((both.amax(dim=2)[live] == 15).all())
-    err = (x - deq).abs().reshape(rows, d // g, g).amax(dim=2)
-    assert bool((err <= steps * 0.50001 + 1e-6 * x.abs().reshape(rows, d // g, g).amax(dim=2)).all())
-    log(f"[int4] 2^28: max|x-x_hat| {float(err.max()):.4g}")
 
 
 # --- edge cases -------------------------------------------------------------------

@@ -12,6 +12,7 @@ import kv_cache_compression_kvq_amd as K
 import synth_inputs as si
 from oracle import int4 as O4
 from oracle import residual as OR
+import full_size as FS
 from gpu_common import assert_bits_within_band, assert_norms_within_ulp, down, log, up
 
 pytestmark = pytest.mark.gpu
@@ -88,11 +89,13 @@ def test_keys_on_the_grid_and_special_rows():
     assert np.all(bg[:10] == 0xFFFFFFFF) and np.all(ng[:10] == 0)
 
 
-def test_qjl_cache_full_size_sampled():
+def test_qjl_cache_full_size_every_row():
     """8 x 32 x 8192 x 128 fp16 keys, S 256 x 128 fp16, g = 32: the whole
-    cache is compressed on the GPU in the bench's launch; 8192 sampled rows
-    are checked against the oracle, and every row's residual norm against
-    the INT4 error bound (|r_i| <= s/2 + rounding, so ||r|| <= sqrt(d) s_max / 2)."""
+    cache is compressed on the GPU in the bench's launch and every row is
+    checked against the oracle (INT4 part bit-exact, residual sign bits within
+    the band, residual norm within one ulp), and every row's residual norm
+    against the INT4 error bound (|r_i| <= s/2 + rounding, so
+    ||r|| <= sqrt(d) s_max / 2)."""
     W = si.W_QJL_CACHE
     B, H, T, d, m, g = 8, 32, 8192, 128, 256, 32
     R = B * H * T
@@ -100,18 +103,12 @@ def test_qjl_cache_full_size_sampled():
     S = si.projection(W, m, d, "f16")
     log("[res] full size: residual sketch")
     cg, sg, zg, bg, ng = K.residual_sketch(up(k), up(S), g)
-    rng = np.random.default_rng(6)
-    rows = np.unique(np.concatenate([[0, R - 1], rng.integers(0, R, 8192)]))
-    idx = torch.from_numpy(rows).to("cuda")
-    co, so, zo, wo, no = OR.residual_compress(k[rows], S, g)
-    assert np.array_equal(down(cg.index_select(0, idx)), co)
-    assert np.array_equal(down(sg.index_select(0, idx)).view(np.uint32), so.view(np.uint32))
-    assert np.array_equal(down(zg.index_select(0, idx)), zo)
-    r = oracle_residual(k[rows], g, co, so, zo)
-    assert_bits_within_band(down(bg.index_select(0, idx), np.uint32), wo, r, S)
-    assert_norms_within_ulp(down(ng.index_select(0, idx)), no)
     bound = (sg.amax(dim=1) * (0.5 * d ** 0.5) * 1.001).to(torch.float32)
     assert bool((ng.to(torch.float32) <= bound + 1e-3).all())
+    flips, ulps = FS.residual_every_row(k, S, g, down(cg), down(sg), down(zg), down(bg, np.uint32),
+                                        down(ng))
+    log(f"[res] full size: every row checked; {flips} residual bits inside the band differ, "
+        f"{ulps} norms one ulp apart")
 
 
 def assert_residual_scores(gpu, q, codes, steps, offsets, norms, g, ora):
@@ -173,13 +170,17 @@ def test_scores_generic_shapes(qdt, sdt, d, m, g):
 def test_scores_full_size_and_error_correction():
     """8 x 32 x 8192 x 128 fp16 keys, m = 256, g = 32, one fp16 query per
     head: the cache is compressed and scored on the GPU (the bench's
-    launches); three groups get the oracle's stored values before the score
-    launch and are checked against the oracle's scores.  On them the second
-    stage corrects the first: its estimate of q . r regresses on q . r with
-    slope 1 (+-10 %, pooled), and the two-stage score is closer to the exact
-    q . k than the INT4 score alone in every group (mean squared error ratio
-    below 1; about (pi/2) d / m = 0.785 for isotropic residuals and queries,
-    higher here, where the outlier channels concentrate the residual)."""
+    launches); the oracle scores every group against the GPU-built stored
+    values (identical inputs) and every score is checked.  Over the whole
+    cache the second stage corrects the first: its estimate of q . r
+    regresses on q . r with slope 1 (+-10 %, pooled), and the two-stage
+    score is closer to the exact q . k than the INT4 score alone (pooled mean
+    squared error ratio below 1; about (pi/2) d / m = 0.785 for isotropic
+    residuals and queries).  Not in every group: the estimate's variance is
+    ((pi/2) ||q||^2 ||r||^2 - <q, r>^2) / m per token, so a query nearly
+    orthogonal to the directions the outlier channels give the residual has
+    <q, r>^2 below it and its group gets a larger error; most groups
+    improve."""
     W = si.W_QJL_CACHE
     B, H, T, d, m, g = 8, 32, 8192, 128, 256, 32
     G = B * H
@@ -189,34 +190,41 @@ def test_scores_full_size_and_error_correction():
     cg, sg, zg, bg, ng = K.residual_sketch(up(k), Sd, g)
     c3, s3, z3 = cg.view(G, T, d // 2), sg.view(G, T, d // g), zg.view(G, T, d // g)
     b3, n3 = bg.view(G, T, m // 32), ng.view(G, T)
-    groups = [0, 101, G - 1]
-    stored = {}
-    for gi in groups:
-        co, so, zo, wo, no = OR.residual_compress(k[gi * T:(gi + 1) * T], S, g)
-        stored[gi] = (co, so, zo, wo, no)
-        c3[gi].copy_(up(co)); s3[gi].copy_(up(so)); z3[gi].copy_(up(zo))
-        b3[gi].copy_(up(wo)); n3[gi].copy_(up(no))
     q = si.queries(W, G, 1, d, "f16")
     log("[res] full size: scores")
     sc = down(K.scores_residual(up(q), Sd, c3, s3, z3, b3, n3, g))
-    ratios, num, den = [], 0.0, 0.0
-    for gi in groups:
-        co, so, zo, wo, no = stored[gi]
-        ora = OR.residual_scores(q[gi:gi + 1], S, co[None], so[None], zo[None], wo[None], no[None], g)
-        assert_residual_scores(sc[gi:gi + 1], q[gi:gi + 1], co[None], so[None], zo[None], no[None],
-                               g, ora)
-        kh = O4.dequantize_int4(co, so, zo, g).astype(np.float64)
-        q64 = q[gi, 0].astype(np.float64)
-        qk = k[gi * T:(gi + 1) * T].astype(np.float64) @ q64
-        first = kh @ q64
-        ratios.append(float(np.mean((sc[gi, 0] - qk) ** 2) / np.mean((first - qk) ** 2)))
-        num += float(np.sum((sc[gi, 0] - first) * (qk - first)))
-        den += float(np.sum((qk - first) ** 2))
-    slope = num / den
-    log(f"[res] full size: MSE(two-stage) / MSE(INT4 alone) per checked group = {ratios}, "
-        f"slope of the correction on q.r = {slope:.4f}")
+    co, so, zo, wo, no = down(c3), down(s3), down(z3), down(b3, np.uint32), down(n3)
+
+    def one(span):
+        a, b = span
+        ora = OR.residual_scores(q[a:b], S, co[a:b], so[a:b], zo[a:b], wo[a:b], no[a:b], g)
+        worst = assert_residual_scores(sc[a:b], q[a:b], co[a:b], so[a:b], zo[a:b], no[a:b], g,
+                                       ora)
+        stats = []
+        for gi in range(a, b):
+            kh = O4.dequantize_int4(co[gi], so[gi], zo[gi], g).astype(np.float64)
+            q64 = q[gi, 0].astype(np.float64)
+            qk = k[gi * T:(gi + 1) * T].astype(np.float64) @ q64
+            first = kh @ q64
+            stats.append((float(np.sum((sc[gi, 0] - qk) ** 2)),
+                          float(np.sum((sc[gi, 0] - first) * (qk - first))),
+                          float(np.sum((qk - first) ** 2))))
+        return worst, stats
+
+    res = FS._pool_map(one, FS._chunks(G, 4))
+    worst = max(w for w, _ in res)
+    stats = [t for _, st in res for t in st]
+    ratios = [e2 / e1 for e2, _, e1 in stats]
+    pooled = sum(e2 for e2, _, _ in stats) / sum(e1 for _, _, e1 in stats)
+    slope = sum(n for _, n, _ in stats) / sum(e1 for _, _, e1 in stats)
+    improved = sum(r < 1.0 for r in ratios)
+    log(f"[res] full size: every score checked (worst err / tol = {worst:.3g}); MSE(two-stage) / "
+        f"MSE(INT4 alone): pooled {pooled:.3f}, per group median {float(np.median(ratios)):.3f}, "
+        f"max {max(ratios):.3f}, {improved} of {G} groups improved; slope of the correction on "
+        f"q.r = {slope:.4f}")
     assert 0.9 <= slope <= 1.1, slope
-    assert all(r < 1.0 for r in ratios), ratios
+    assert pooled < 1.0, pooled
+    assert improved > G // 2, improved
 
 
 def test_empty_input_is_a_noop():
