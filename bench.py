@@ -51,8 +51,15 @@ def parse_args():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=1000)
     p.add_argument("--no-components", action="store_true")
+    p.add_argument("--only", default=",".join(SECTIONS),
+                   help="comma-separated component sections to run (" + ", ".join(SECTIONS) + ")")
+    p.add_argument("--no-graph", action="store_true",
+                   help="skip the HIP-graph replay timings (profiling aid)")
+    p.add_argument("--no-decode", action="store_true",
+                   help="skip the decode step (profiling aid: the line then has no value)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--cpu-seconds", type=float, default=6.0,
+                   help="oracle compute time per CPU-baseline measurement (four of them)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a 1 GiB device-to-device copy 3 times (the known-size "
                         "kernel used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -106,26 +113,69 @@ def block_times(fn, calls_per_block, blocks, warmup, stream=None):
     return out
 
 
+def graph_times(calls, reps, blocks=5):
+    """Mean duration (ms) of one call when `reps` back-to-back calls (cycling
+    through `calls`) are captured in one HIP graph and replayed, for each of
+    `blocks` replays timed by a pair of HIP events: no host launch work sits
+    between the kernels.  The calls write preallocated outputs."""
+    import torch
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            calls[i % len(calls)]()
+    g.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(blocks):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) / reps)
+    del g
+    return out
+
+
+def stream_probe():
+    """ctypes handle of the HBM stream reference (libkvq_probe.so)."""
+    import ctypes
+    from ctypes import c_int, c_int64, c_void_p
+    lib = ctypes.CDLL(os.path.join(ROOT, "kv_cache_compression_kvq_amd", "libkvq_probe.so"))
+    lib.kvqprobe_stream_rw.restype = c_int
+    lib.kvqprobe_stream_rw.argtypes = [c_void_p, c_int64, c_int, c_void_p, c_int, c_void_p, c_int,
+                                       c_void_p]
+    return lib
+
+
 def med(xs):
     s = sorted(xs)
     return s[len(s) // 2]
 
 
 COLD_BYTES = 1 << 30     # rotate inputs over > 1 GiB: 4x the 256 MB last-level cache (MALL)
+SECTIONS = ("copy", "sweep", "llama", "qjl", "residual", "gqa")
 
 
-def components(K, si, torch, np):
+def components(K, si, torch, np, only=SECTIONS, use_graph=True):
     """GB/s of the INT8 (per row and per channel), INT4, QJL and two-stage
     kernels on their own workloads, cold: each timed call reads a different
-    copy of its inputs, and the copies together
-    exceed 1 GiB, so no call finds its inputs in the MALL or L2.  Calls run
-    back to back in blocks timed by one pair of HIP events; the median block's
-    mean per call is reported ("ms", and the rates from it) with the fastest
-    block's ("ms_min")."""
+    copy of its inputs, and the copies together exceed 1 GiB, so no call
+    finds its inputs in the MALL or L2.  Outputs are preallocated (one set
+    per component), so a call is the ctypes call and its launches only.
+    Calls run back to back in blocks timed by one pair of HIP events; the
+    median block's mean per call is reported ("ms", and the rates from it)
+    with the fastest block's ("ms_min").  Kernels of a few microseconds (the
+    Llama-7B layer, the QJL-cache scores) are also replayed from a HIP graph
+    of back-to-back launches ("graph_ms"), which leaves the host's per-call
+    launch work out."""
     res = {}
     dev = "cuda"
 
-    def gbs(name, nbytes, calls, reps=20, flops=None):
+    def gbs(name, nbytes, calls, reps=20, flops=None, graph=False):
         """calls: list of zero-argument launches, one per input copy."""
         it = iter(range(10 ** 9))
         fn = lambda: calls[next(it) % len(calls)]()
@@ -134,6 +184,12 @@ def components(K, si, torch, np):
         r = {"ms": round(ms, 4), "ms_min": round(min(times), 4), "GB/s": round(nbytes / ms / 1e6, 1),
              "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 3), "bytes": int(nbytes),
              "copies": len(calls)}
+        if graph and use_graph:
+            gt = graph_times(calls, len(calls) * max(1, 100 // len(calls)))
+            gms = med(gt)
+            r["graph_ms"] = round(gms, 4)
+            r["graph_GB/s"] = round(nbytes / gms / 1e6, 1)
+            r["graph_frac_hbm"] = round(nbytes / gms / 1e6 / HBM_PEAK_GBS, 3)
         if flops:
             r["TFLOP/s"] = round(flops / ms / 1e9, 1)
             r["frac_mfma_f16"] = round(flops / ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 3)
@@ -143,14 +199,21 @@ def components(K, si, torch, np):
     def ncopies(bytes_per_call):
         return max(1, -(-COLD_BYTES // int(bytes_per_call)) + 1)
 
-    # context: a plain device copy of 1 GiB (1 GiB read + 1 GiB written), the
-    # practical rate of a stream that mixes reads and writes equally
-    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    dsts = [torch.empty_like(src) for _ in range(2)]
-    it_c = iter(range(10 ** 9))
-    gbs("device_copy_1GiB", 2 * src.numel() * 4,
-        [lambda: dsts[next(it_c) % 2].copy_(src)], reps=10)
-    del src, dsts
+    def like(outs):
+        """A second set of outputs shaped like `outs` (a tensor or a tuple)."""
+        if isinstance(outs, tuple):
+            return tuple(torch.empty_like(t) for t in outs)
+        return torch.empty_like(outs)
+
+    if "copy" in only:
+        # context: a plain device copy of 1 GiB (1 GiB read + 1 GiB written),
+        # the practical rate of a stream that mixes reads and writes equally
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dsts = [torch.empty_like(src) for _ in range(2)]
+        it_c = iter(range(10 ** 9))
+        gbs("device_copy_1GiB", 2 * src.numel() * 4,
+            [lambda: dsts[next(it_c) % 2].copy_(src)], reps=10)
+        del src, dsts
 
     # INT8 round-trip error on the sweep (fp32 rows, N(0, 1)) and the
     # U(-1, 1) context row: max and mean |dequantize(quantize(x)) - x|
@@ -163,206 +226,368 @@ def components(K, si, torch, np):
                      "mean_abs": float(err.sum(dtype=torch.float64)) / err.numel()}
         del codes, scales, err
 
-    for nlog in (20, 24):
-        x = torch.from_numpy(si.flat_rows(si.W_SWEEP, 1 << nlog, 128).reshape(-1)).to(dev)
-        for d in (128, 1024, 8192):
-            round_trip_error(f"f32_2^{nlog}_d{d}", x.view(-1, d))
-    x = torch.from_numpy(si.flat_rows(si.W_SWEEP, 1 << 24, 128, dist="uniform").reshape(-1)).to(dev)
-    round_trip_error("uniform_f32_2^24_d128", x.view(-1, 128))
-    del x
+    if "sweep" in only:
+        for nlog in (20, 24):
+            x = torch.from_numpy(si.flat_rows(si.W_SWEEP, 1 << nlog, 128).reshape(-1)).to(dev)
+            for d in (128, 1024, 8192):
+                round_trip_error(f"f32_2^{nlog}_d{d}", x.view(-1, d))
+        x = torch.from_numpy(si.flat_rows(si.W_SWEEP, 1 << 24, 128, dist="uniform").reshape(-1)).to(dev)
+        round_trip_error("uniform_f32_2^24_d128", x.view(-1, 128))
+        del x
 
-    # element-count sweep, fp32 rows of d in {128, 1024, 8192}
-    for nlog in (28, 30):
-        n = 1 << nlog
-        x = torch.from_numpy(si.flat_rows(si.W_SWEEP, n, 128).reshape(-1)).to(dev)
-        xs = [x] + [x.clone() for _ in range(ncopies(4 * n) - 1)] if nlog < 30 else [x]
-        for d in (128, 1024, 8192):
-            rows = n // d
-            views = [t.view(rows, d) for t in xs]
-            round_trip_error(f"f32_2^{nlog}_d{d}", views[0])
-            cs = [K.quantize_int8(v) for v in views]
-            gbs(f"quantize_f32_2^{nlog}_d{d}", 4 * n + n + 4 * rows,
-                [lambda v=v: K.quantize_int8(v) for v in views])
-            gbs(f"dequantize_f32_2^{nlog}_d{d}", n + 4 * rows + 4 * n,
-                [lambda c=c: K.dequantize_int8(c[0], c[1]) for c in cs])
-            del cs
-            if d == 128:
-                # asymmetric group-wise INT4, groups of 32 and 128
-                for g in (32, 128):
-                    c4 = [K.quantize_int4(v, g) for v in views]
-                    gbs(f"quantize_int4_f32_2^{nlog}_d{d}_g{g}", 4 * n + n // 2 + 8 * (n // g),
-                        [lambda v=v: K.quantize_int4(v, g) for v in views])
-                    gbs(f"dequantize_int4_f32_2^{nlog}_d{d}_g{g}", n // 2 + 8 * (n // g) + 4 * n,
-                        [lambda c=c: K.dequantize_int4(c[0], c[1], c[2], g) for c in c4])
-                    del c4
-        del x, xs
+        # element-count sweep, fp32 rows of d in {128, 1024, 8192}
+        for nlog in (28, 30):
+            n = 1 << nlog
+            x = torch.from_numpy(si.flat_rows(si.W_SWEEP, n, 128).reshape(-1)).to(dev)
+            xs = [x] + [x.clone() for _ in range(ncopies(4 * n) - 1)] if nlog < 30 else [x]
+            for d in (128, 1024, 8192):
+                rows = n // d
+                views = [t.view(rows, d) for t in xs]
+                round_trip_error(f"f32_2^{nlog}_d{d}", views[0])
+                cs = [K.quantize_int8(v) for v in views]
+                oq = like(cs[0])
+                gbs(f"quantize_f32_2^{nlog}_d{d}", 4 * n + n + 4 * rows,
+                    [lambda v=v: K.quantize_int8(v, out=oq) for v in views])
+                del oq
+                od = torch.empty((rows, d), dtype=torch.float32, device=dev)
+                gbs(f"dequantize_f32_2^{nlog}_d{d}", n + 4 * rows + 4 * n,
+                    [lambda c=c: K.dequantize_int8(c[0], c[1], out=od) for c in cs])
+                del cs, od
+                if d == 128:
+                    # asymmetric group-wise INT4, groups of 32 and 128
+                    for g in (32, 128):
+                        c4 = [K.quantize_int4(v, g) for v in views]
+                        o4 = like(c4[0])
+                        gbs(f"quantize_int4_f32_2^{nlog}_d{d}_g{g}", 4 * n + n // 2 + 8 * (n // g),
+                            [lambda v=v: K.quantize_int4(v, g, out=o4) for v in views])
+                        del o4
+                        od = torch.empty((rows, d), dtype=torch.float32, device=dev)
+                        gbs(f"dequantize_int4_f32_2^{nlog}_d{d}_g{g}", n // 2 + 8 * (n // g) + 4 * n,
+                            [lambda c=c: K.dequantize_int4(c[0], c[1], c[2], g, out=od) for c in c4])
+                        del c4, od
+            del x, xs
+            torch.cuda.empty_cache()
+
+    if "llama" in only:
+        # Llama-7B-shaped layer, fp16: K and V quantized, dequantized, scored
+        W = si.W_LLAMA_LAYER
+        k = torch.from_numpy(si.kv_tensor(W, si.K, 1, 32, 4096, 128, "f16", outliers=True)).to(dev)
+        v = torch.from_numpy(si.kv_tensor(W, si.V, 1, 32, 4096, 128, "f16")).to(dev)
+        kv = torch.stack([k, v]).view(-1, 128)
+        R = kv.shape[0]
+        nc = ncopies(2 * R * 128)
+        kvs = [kv] + [kv.clone() for _ in range(nc - 1)]
+        cs = [K.quantize_int8(t) for t in kvs]
+        oq = like(cs[0])
+        gbs("llama_layer_quantize_kv_f16", 2 * R * 128 + R * 128 + 4 * R,
+            [lambda t=t: K.quantize_int8(t, out=oq) for t in kvs], graph=True)
+        od = torch.empty((R, 128), dtype=torch.float16, device=dev)
+        gbs("llama_layer_dequantize_kv_f16", R * 128 + 4 * R + 2 * R * 128,
+            [lambda c=c: K.dequantize_int8(c[0], c[1], torch.float16, out=od) for c in cs],
+            graph=True)
+        for g in (32, 128):
+            c4 = [K.quantize_int4(t, g) for t in kvs]
+            o4 = like(c4[0])
+            gbs(f"llama_layer_quantize_int4_kv_f16_g{g}", 2 * R * 128 + R * 64 + 8 * R * (128 // g),
+                [lambda t=t: K.quantize_int4(t, g, out=o4) for t in kvs], graph=True)
+            gbs(f"llama_layer_dequantize_int4_kv_f16_g{g}", R * 64 + 8 * R * (128 // g) + 2 * R * 128,
+                [lambda c=c: K.dequantize_int4(c[0], c[1], c[2], g, torch.float16, out=od)
+                 for c in c4], graph=True)
+            del c4, o4
+        # per-channel INT8 keys (one scale per channel over a head's 4096 tokens)
+        k3s = [t[: R // 2].view(32, 4096, 128) for t in kvs]
+        cch = [K.quantize_int8_channel(t) for t in k3s]
+        och = like(cch[0])
+        half = R // 2
+        gbs("llama_layer_quantize_int8_channel_k_f16", 2 * half * 128 + half * 128 + 4 * 32 * 128,
+            [lambda t=t: K.quantize_int8_channel(t, out=och) for t in k3s], graph=True)
+        odh = torch.empty((32, 4096, 128), dtype=torch.float16, device=dev)
+        gbs("llama_layer_dequantize_int8_channel_k_f16", half * 128 + 4 * 32 * 128 + 2 * half * 128,
+            [lambda c=c: K.dequantize_int8_channel(c[0], c[1], torch.float16, out=odh) for c in cch],
+            graph=True)
+        q = torch.from_numpy(si.queries(W, 32, 1, 128, "f16")).to(dev)
+        osc = torch.empty((32, 1, 4096), dtype=torch.float32, device=dev)
+        gbs("llama_layer_scores_int8_channel", 32 * 4096 * (128 + 4) + 32 * 128 * (2 + 4),
+            [lambda c=c: K.scores_int8_channel(q, c[0], c[1], out=osc) for c in cch], graph=True)
+        del k3s, cch, och, odh
+        halves = [(c[0][: R // 2].view(32, 4096, 128), c[1][: R // 2].view(32, 4096)) for c in cs]
+        gbs("llama_layer_scores_int8", 32 * 4096 * (128 + 4 + 4) + 32 * 128 * 2,
+            [lambda h=h: K.scores_int8(q, h[0], h[1], out=osc) for h in halves], graph=True)
+        # grouped-query attention, 4 query heads per KV head: one pass over the codes
+        q4 = torch.from_numpy(si.queries(W, 32, 4, 128, "f16")).to(dev)
+        osc4 = torch.empty((32, 4, 4096), dtype=torch.float32, device=dev)
+        gbs("llama_layer_scores_int8_gqa4", 32 * 4096 * (128 + 4 + 4 * 4) + 32 * 4 * 128 * 2,
+            [lambda h=h: K.scores_int8(q4, h[0], h[1], out=osc4) for h in halves], graph=True)
+        # INT8 scores at a cache length where HBM, not launch latency, bounds
+        # them: 32 heads x 262144 tokens x 128 (1.1 GB of codes), 1 and 4 queries
+        Tl = 262144
+        big = [(torch.randint(-127, 128, (32, Tl, 128), dtype=torch.int8, device=dev),
+                torch.rand(32, Tl, device=dev)) for _ in range(2)]
+        osl = torch.empty((32, 1, Tl), dtype=torch.float32, device=dev)
+        gbs("scores_int8_32x262144x128", 32 * Tl * (128 + 4 + 4) + 32 * 128 * 2,
+            [lambda c=c: K.scores_int8(q, c[0], c[1], out=osl) for c in big])
+        osl4 = torch.empty((32, 4, Tl), dtype=torch.float32, device=dev)
+        gbs("scores_int8_gqa4_32x262144x128", 32 * Tl * (128 + 4 + 4 * 4) + 32 * 4 * 128 * 2,
+            [lambda c=c: K.scores_int8(q4, c[0], c[1], out=osl4) for c in big])
+        del big, osl, osl4
+        del k, v, kv, kvs, cs, halves, oq, od, osc, osc4
         torch.cuda.empty_cache()
-
-    # Llama-7B-shaped layer, fp16: K and V quantized, dequantized, scored
-    W = si.W_LLAMA_LAYER
-    k = torch.from_numpy(si.kv_tensor(W, si.K, 1, 32, 4096, 128, "f16", outliers=True)).to(dev)
-    v = torch.from_numpy(si.kv_tensor(W, si.V, 1, 32, 4096, 128, "f16")).to(dev)
-    kv = torch.stack([k, v]).view(-1, 128)
-    R = kv.shape[0]
-    nc = ncopies(2 * R * 128)
-    kvs = [kv] + [kv.clone() for _ in range(nc - 1)]
-    cs = [K.quantize_int8(t) for t in kvs]
-    gbs("llama_layer_quantize_kv_f16", 2 * R * 128 + R * 128 + 4 * R,
-        [lambda t=t: K.quantize_int8(t) for t in kvs])
-    gbs("llama_layer_dequantize_kv_f16", R * 128 + 4 * R + 2 * R * 128,
-        [lambda c=c: K.dequantize_int8(c[0], c[1], torch.float16) for c in cs])
-    for g in (32, 128):
-        c4 = [K.quantize_int4(t, g) for t in kvs]
-        gbs(f"llama_layer_quantize_int4_kv_f16_g{g}", 2 * R * 128 + R * 64 + 8 * R * (128 // g),
-            [lambda t=t: K.quantize_int4(t, g) for t in kvs])
-        gbs(f"llama_layer_dequantize_int4_kv_f16_g{g}", R * 64 + 8 * R * (128 // g) + 2 * R * 128,
-            [lambda c=c: K.dequantize_int4(c[0], c[1], c[2], g, torch.float16) for c in c4])
-        del c4
-    # per-channel INT8 keys (one scale per channel over a head's 4096 tokens)
-    k3s = [t[: R // 2].view(32, 4096, 128) for t in kvs]
-    cch = [K.quantize_int8_channel(t) for t in k3s]
-    half = R // 2
-    gbs("llama_layer_quantize_int8_channel_k_f16", 2 * half * 128 + half * 128 + 4 * 32 * 128,
-        [lambda t=t: K.quantize_int8_channel(t) for t in k3s])
-    gbs("llama_layer_dequantize_int8_channel_k_f16", half * 128 + 4 * 32 * 128 + 2 * half * 128,
-        [lambda c=c: K.dequantize_int8_channel(c[0], c[1], torch.float16) for c in cch])
-    qch = torch.from_numpy(si.queries(W, 32, 1, 128, "f16")).to(dev)
-    gbs("llama_layer_scores_int8_channel", 32 * 4096 * (128 + 4) + 32 * 128 * (2 + 4),
-        [lambda c=c: K.scores_int8_channel(qch, c[0], c[1]) for c in cch])
-    del k3s, cch
-    q = torch.from_numpy(si.queries(W, 32, 1, 128, "f16")).to(dev)
-    halves = [(c[0][: R // 2].view(32, 4096, 128), c[1][: R // 2].view(32, 4096)) for c in cs]
-    gbs("llama_layer_scores_int8", 32 * 4096 * (128 + 4 + 4) + 32 * 128 * 2,
-        [lambda h=h: K.scores_int8(q, h[0], h[1]) for h in halves])
-    # grouped-query attention, 4 query heads per KV head: one pass over the codes
-    q4 = torch.from_numpy(si.queries(W, 32, 4, 128, "f16")).to(dev)
-    gbs("llama_layer_scores_int8_gqa4", 32 * 4096 * (128 + 4 + 4 * 4) + 32 * 4 * 128 * 2,
-        [lambda h=h: K.scores_int8(q4, h[0], h[1]) for h in halves])
-    # INT8 scores at a cache length where HBM, not launch latency, bounds
-    # them: 32 heads x 262144 tokens x 128 (1.1 GB of codes), 1 and 4 queries
-    Tl = 262144
-    big = [(torch.randint(-127, 128, (32, Tl, 128), dtype=torch.int8, device=dev),
-            torch.rand(32, Tl, device=dev)) for _ in range(2)]
-    gbs("scores_int8_32x262144x128", 32 * Tl * (128 + 4 + 4) + 32 * 128 * 2,
-        [lambda c=c: K.scores_int8(q, c[0], c[1]) for c in big])
-    gbs("scores_int8_gqa4_32x262144x128", 32 * Tl * (128 + 4 + 4 * 4) + 32 * 4 * 128 * 2,
-        [lambda c=c: K.scores_int8(q4, c[0], c[1]) for c in big])
-    del big
-    del k, v, kv, kvs, cs, halves
-    torch.cuda.empty_cache()
 
     # QJL key cache: 8 x 32 x 8192 x 128 fp16, m = 256
     W = si.W_QJL_CACHE
     G, T, d, m = 256, 8192, 128, 256
-    kk = torch.from_numpy(si.kv_tensor(W, si.K, 8, 32, T, d, "f16", outliers=True)).to(dev).view(-1, d)
-    S = torch.from_numpy(si.projection(W, m, d, "f16")).to(dev)
-    R = kk.shape[0]
-    kks = [kk] + [kk.clone() for _ in range(ncopies(R * d * 2) - 1)]
-    sk = [K.qjl_sketch(t, S) for t in kks]
-    gbs("qjl_sketch_f16_m256", R * d * 2 + R * (m // 8) + 2 * R + m * d * 2,
-        [lambda t=t: K.qjl_sketch(t, S) for t in kks], flops=2.0 * R * d * m)
-    del kks
-    q = torch.from_numpy(si.queries(W, G, 1, d, "f16")).to(dev)
-    b3 = [(b.view(G, T, m // 32), n.view(G, T)) for b, n in sk]
-    while len(b3) < ncopies(R * (m // 8 + 2)):
-        b3.append((b3[0][0].clone(), b3[0][1].clone()))
-    gbs("qjl_scores_f16_m256", R * (m // 8 + 2 + 4) + G * d * 2 + m * d * 2,
-        [lambda bn=bn: K.scores_qjl(q, S, bn[0], bn[1]) for bn in b3])
-    res["qjl_scores_f16_m256"]["scores/s"] = round(R / res["qjl_scores_f16_m256"]["ms"] * 1e3, 1)
-    # grouped-query attention, 4 query heads per KV head: one pass over the sign words
-    q4 = torch.from_numpy(si.queries(W, G, 4, d, "f16")).to(dev)
-    gbs("qjl_scores_gqa4_f16_m256", R * (m // 8 + 2 + 4 * 4) + G * 4 * d * 2 + m * d * 2,
-        [lambda bn=bn: K.scores_qjl(q4, S, bn[0], bn[1]) for bn in b3])
-    res["qjl_scores_gqa4_f16_m256"]["scores/s"] = round(
-        4 * R / res["qjl_scores_gqa4_f16_m256"]["ms"] * 1e3, 1)
-    # two-stage keys: INT4 (groups of 32) and the QJL sketch of its residual
-    g4 = 32
-    per_tok = d // 2 + 8 * (d // g4) + m // 8 + 2
-    kks = [kk] + [kk.clone() for _ in range(ncopies(R * d * 2) - 1)]
-    first = K.residual_sketch(kk, S, g4)
-    gbs("residual_sketch_f16_m256_g32", R * d * 2 + R * per_tok + m * d * 2,
-        [lambda t=t: K.residual_sketch(t, S, g4) for t in kks], flops=2.0 * R * d * m)
-    del kks
-    c4, s4, z4, b4, n4 = first
-    st = [(c4.view(G, T, d // 2), s4.view(G, T, d // g4), z4.view(G, T, d // g4),
-           b4.view(G, T, m // 32), n4.view(G, T))]
-    while len(st) < ncopies(R * per_tok):
-        st.append(tuple(x.clone() for x in st[0]))
-    gbs("residual_scores_f16_m256_g32", R * (per_tok + 4) + G * d * 2 + m * d * 2,
-        [lambda a=a: K.scores_residual(q, S, *a, g4) for a in st])
-    res["residual_scores_f16_m256_g32"]["scores/s"] = round(
-        R / res["residual_scores_f16_m256_g32"]["ms"] * 1e3, 1)
-    del kk, sk, b3, st, first
-    torch.cuda.empty_cache()
+    if "qjl" in only or "residual" in only:
+        kk = torch.from_numpy(si.kv_tensor(W, si.K, 8, 32, T, d, "f16", outliers=True)).to(dev).view(-1, d)
+        S = torch.from_numpy(si.projection(W, m, d, "f16")).to(dev)
+        R = kk.shape[0]
+        q = torch.from_numpy(si.queries(W, G, 1, d, "f16")).to(dev)
+    if "qjl" in only:
+        # practical HBM ceilings for the sketch's and the score's traffic
+        # (a plain stream, no compression work): rows of 256 B read and 32 B
+        # written, and rows of 32 B read only, over the same row count
+        probe = stream_probe()
+        sink = torch.zeros(4096, dtype=torch.uint8, device=dev)
+        src = [torch.empty(R * 256, dtype=torch.uint8, device=dev).fill_(i + 1)
+               for i in range(ncopies(R * 256))]
+        dst = torch.empty(R * 32, dtype=torch.uint8, device=dev)
+        nblk = 16 * torch.cuda.get_device_properties(0).multi_processor_count
 
-    # grouped-query decode: 128 KV heads (16 x 8) x 32768 tokens, 4 query
-    # heads per KV head (m = 256, d = 128), against the same 4 queries
-    # decoded one at a time; cache from the bench's decode generator recipe
-    # (fp16 N(0,1) keys and values, QJL keys, INT8 values) on 16 x 8 heads
-    Gk, Tq, nqg = 128, 32768, 4
-    kbits_, knorm_, vcode_, vscal_ = [], [], [], []
-    Sg = torch.from_numpy(si.projection(si.W_DECODE, m, d, "f16")).to(dev)
-    for g0 in range(0, Gk, 16):
-        kk_ = torch.from_numpy(si.stream(si.W_DECODE, si.K, 16 * Tq * d, "f16",
-                                         start=g0 * Tq * d)).to(dev).view(-1, d)
-        vv_ = torch.from_numpy(si.stream(si.W_DECODE, si.V, 16 * Tq * d, "f16",
-                                         start=g0 * Tq * d)).to(dev).view(-1, d)
-        b_, n_ = K.qjl_sketch(kk_, Sg)
-        c_, s_ = K.quantize_int8(vv_)
-        kbits_.append(b_); knorm_.append(n_); vcode_.append(c_); vscal_.append(s_)
-        del kk_, vv_
-    kbg = torch.cat(kbits_).view(Gk, Tq, m // 32)
-    kng = torch.cat(knorm_).view(Gk, Tq)
-    vcg = torch.cat(vcode_).view(Gk, Tq, d)
-    vsg = torch.cat(vscal_).view(Gk, Tq)
-    del kbits_, knorm_, vcode_, vscal_
-    qg = torch.from_numpy(si.queries(si.W_DECODE, Gk, nqg, d, "f16")).to(dev)
-    wsg = torch.empty(K.decode_gqa_workspace_bytes(Gk, nqg, Tq, d, m), dtype=torch.uint8, device=dev)
-    og = torch.empty((Gk, nqg, d), dtype=torch.float32, device=dev)
-    gbs("decode_gqa4_128x32768", Gk * Tq * (m // 8 + 2 + d + 4) + Gk * nqg * d * (2 + 4),
-        [lambda: K.decode_qjl_int8_gqa(qg, Sg, kbg, kng, vcg, vsg, workspace=wsg, out=og)],
-        reps=10)
-    res["decode_gqa4_128x32768"]["scores/s"] = round(
-        Gk * nqg * Tq / res["decode_gqa4_128x32768"]["ms"] * 1e3, 1)
-    qs1 = [qg[:, j].contiguous() for j in range(nqg)]
-    ws1 = torch.empty(K.decode_workspace_bytes(Gk, Tq, d, m), dtype=torch.uint8, device=dev)
-    o1 = torch.empty((Gk, d), dtype=torch.float32, device=dev)
-    gbs("decode_4x1query_128x32768", 4 * (Gk * Tq * (m // 8 + 2 + d + 4) + Gk * d * (2 + 4)),
-        [lambda: [K.decode_qjl_int8(qq, Sg, kbg, kng, vcg, vsg, workspace=ws1, out=o1)
-                  for qq in qs1]], reps=10)
-    res["decode_4x1query_128x32768"]["scores/s"] = round(
-        Gk * nqg * Tq / res["decode_4x1query_128x32768"]["ms"] * 1e3, 1)
-    del kbg, kng, vcg, vsg, qg, wsg, og, ws1, o1
-    torch.cuda.empty_cache()
-    res["int8_round_trip_error"] = acc
-    log(f"  int8_round_trip_error: {acc}")
+        def run_probe(a, rd_log2, b, wr16):
+            rc = probe.kvqprobe_stream_rw(a.data_ptr(), R, rd_log2, b.data_ptr() if b is not None
+                                          else None, wr16, sink.data_ptr(), nblk,
+                                          torch.cuda.current_stream().cuda_stream)
+            assert rc == 0, rc
+
+        gbs("stream_ref_read256_write32_B_per_row", R * (256 + 32),
+            [lambda a=a: run_probe(a, 4, dst, 2) for a in src])
+        src32 = [a[: R * 32] for a in src]
+        gbs("stream_ref_read32_B_per_row", R * 32,
+            [lambda a=a: run_probe(a, 1, None, 0) for a in src32], graph=True)
+        del src, src32, dst, sink
+        kks = [kk] + [kk.clone() for _ in range(ncopies(R * d * 2) - 1)]
+        sk = [K.qjl_sketch(t, S) for t in kks]
+        osk = like(sk[0])
+        gbs("qjl_sketch_f16_m256", R * d * 2 + R * (m // 8) + 2 * R + m * d * 2,
+            [lambda t=t: K.qjl_sketch(t, S, out=osk) for t in kks], flops=2.0 * R * d * m)
+        del kks, osk
+        b3 = [(b.view(G, T, m // 32), n.view(G, T)) for b, n in sk]
+        while len(b3) < ncopies(R * (m // 8 + 2)):
+            b3.append((b3[0][0].clone(), b3[0][1].clone()))
+        oqs = torch.empty((G, 1, T), dtype=torch.float32, device=dev)
+        gbs("qjl_scores_f16_m256", R * (m // 8 + 2 + 4) + G * d * 2 + m * d * 2,
+            [lambda bn=bn: K.scores_qjl(q, S, bn[0], bn[1], out=oqs) for bn in b3], graph=True)
+        res["qjl_scores_f16_m256"]["scores/s"] = round(R / res["qjl_scores_f16_m256"]["ms"] * 1e3, 1)
+        # grouped-query attention, 4 query heads per KV head: one pass over the sign words
+        q4 = torch.from_numpy(si.queries(W, G, 4, d, "f16")).to(dev)
+        oqs4 = torch.empty((G, 4, T), dtype=torch.float32, device=dev)
+        gbs("qjl_scores_gqa4_f16_m256", R * (m // 8 + 2 + 4 * 4) + G * 4 * d * 2 + m * d * 2,
+            [lambda bn=bn: K.scores_qjl(q4, S, bn[0], bn[1], out=oqs4) for bn in b3], graph=True)
+        res["qjl_scores_gqa4_f16_m256"]["scores/s"] = round(
+            4 * R / res["qjl_scores_gqa4_f16_m256"]["ms"] * 1e3, 1)
+        del sk, b3, oqs, oqs4
+    if "residual" in only:
+        # two-stage keys: INT4 (groups of 32) and the QJL sketch of its residual
+        g4 = 32
+        per_tok = d // 2 + 8 * (d // g4) + m // 8 + 2
+        kks = [kk] + [kk.clone() for _ in range(ncopies(R * d * 2) - 1)]
+        first = K.residual_sketch(kk, S, g4)
+        ors = like(first)
+        gbs("residual_sketch_f16_m256_g32", R * d * 2 + R * per_tok + m * d * 2,
+            [lambda t=t: K.residual_sketch(t, S, g4, out=ors) for t in kks], flops=2.0 * R * d * m)
+        del kks, ors
+        c4, s4, z4, b4, n4 = first
+        st = [(c4.view(G, T, d // 2), s4.view(G, T, d // g4), z4.view(G, T, d // g4),
+               b4.view(G, T, m // 32), n4.view(G, T))]
+        while len(st) < ncopies(R * per_tok):
+            st.append(tuple(x.clone() for x in st[0]))
+        ors = torch.empty((G, 1, T), dtype=torch.float32, device=dev)
+        gbs("residual_scores_f16_m256_g32", R * (per_tok + 4) + G * d * 2 + m * d * 2,
+            [lambda a=a: K.scores_residual(q, S, *a, g4, out=ors) for a in st])
+        res["residual_scores_f16_m256_g32"]["scores/s"] = round(
+            R / res["residual_scores_f16_m256_g32"]["ms"] * 1e3, 1)
+        del st, first, ors
+    if "qjl" in only or "residual" in only:
+        del kk, S, q
+        torch.cuda.empty_cache()
+
+    if "gqa" in only:
+        # grouped-query decode: 128 KV heads (16 x 8) x 32768 tokens, 4 query
+        # heads per KV head (m = 256, d = 128), against the same 4 queries
+        # decoded one at a time; cache from the bench's decode generator recipe
+        # (fp16 N(0,1) keys and values, QJL keys, INT8 values) on 16 x 8 heads
+        Gk, Tq, nqg = 128, 32768, 4
+        kbits_, knorm_, vcode_, vscal_ = [], [], [], []
+        Sg = torch.from_numpy(si.projection(si.W_DECODE, m, d, "f16")).to(dev)
+        for g0 in range(0, Gk, 16):
+            kk_ = torch.from_numpy(si.stream(si.W_DECODE, si.K, 16 * Tq * d, "f16",
+                                             start=g0 * Tq * d)).to(dev).view(-1, d)
+            vv_ = torch.from_numpy(si.stream(si.W_DECODE, si.V, 16 * Tq * d, "f16",
+                                             start=g0 * Tq * d)).to(dev).view(-1, d)
+            b_, n_ = K.qjl_sketch(kk_, Sg)
+            c_, s_ = K.quantize_int8(vv_)
+            kbits_.append(b_); knorm_.append(n_); vcode_.append(c_); vscal_.append(s_)
+            del kk_, vv_
+        kbg = torch.cat(kbits_).view(Gk, Tq, m // 32)
+        kng = torch.cat(knorm_).view(Gk, Tq)
+        vcg = torch.cat(vcode_).view(Gk, Tq, d)
+        vsg = torch.cat(vscal_).view(Gk, Tq)
+        del kbits_, knorm_, vcode_, vscal_
+        qg = torch.from_numpy(si.queries(si.W_DECODE, Gk, nqg, d, "f16")).to(dev)
+        wsg = torch.empty(K.decode_gqa_workspace_bytes(Gk, nqg, Tq, d, m), dtype=torch.uint8, device=dev)
+        og = torch.empty((Gk, nqg, d), dtype=torch.float32, device=dev)
+        gbs("decode_gqa4_128x32768", Gk * Tq * (m // 8 + 2 + d + 4) + Gk * nqg * d * (2 + 4),
+            [lambda: K.decode_qjl_int8_gqa(qg, Sg, kbg, kng, vcg, vsg, workspace=wsg, out=og)],
+            reps=10)
+        res["decode_gqa4_128x32768"]["scores/s"] = round(
+            Gk * nqg * Tq / res["decode_gqa4_128x32768"]["ms"] * 1e3, 1)
+        qs1 = [qg[:, j].contiguous() for j in range(nqg)]
+        ws1 = torch.empty(K.decode_workspace_bytes(Gk, Tq, d, m), dtype=torch.uint8, device=dev)
+        o1 = torch.empty((Gk, d), dtype=torch.float32, device=dev)
+        gbs("decode_4x1query_128x32768", 4 * (Gk * Tq * (m // 8 + 2 + d + 4) + Gk * d * (2 + 4)),
+            [lambda: [K.decode_qjl_int8(qq, Sg, kbg, kng, vcg, vsg, workspace=ws1, out=o1)
+                      for qq in qs1]], reps=10)
+        res["decode_4x1query_128x32768"]["scores/s"] = round(
+            Gk * nqg * Tq / res["decode_4x1query_128x32768"]["ms"] * 1e3, 1)
+        del kbg, kng, vcg, vsg, qg, wsg, og, ws1, o1
+        torch.cuda.empty_cache()
+    if acc:
+        res["int8_round_trip_error"] = acc
+        log(f"  int8_round_trip_error: {acc}")
     return res
 
 
-def cpu_baseline(si, np, seconds):
-    """The fp64 oracle's decode on one thread over whole groups of the same
-    workload, until `seconds` of compute have been timed (at least 2)."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_threads() -> int:
+    """Host threads the oracle may use: the process's CPU affinity, capped at
+    16 (the host share of one GPU on a GPU machine)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _timed_pool(fn, items, threads):
+    """Wall time of fn over items on a pool of `threads` threads (numpy
+    releases the GIL inside its array operations; BLAS is held to one thread
+    per call by the caller)."""
+    from concurrent.futures import ThreadPoolExecutor
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(fn, items))
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(si, np, seconds, gpu_quantize_ms=None):
+    """The fp64 oracle, timed on the host's cores on bounded samples of two
+    workloads (the oracle as it stands: a correctness reference, not a tuned
+    CPU kernel):
+      * the decode step (16 x 32 x 32768 x 128, m = 256): whole (batch, head)
+        groups, on one thread, then on every thread of the process's CPU
+        affinity (one group per task);
+      * INT8 quantize of the 2^28-element fp32 sweep at d = 128: 2^22-element
+        row blocks, one thread and every thread; with the GPU kernel's time
+        for the whole 2^28 elements, the GPU/CPU ratio is printed beside the
+        INT8 page's "up to 1,694x" (context only).
+    Input generation and cache building are outside the timed regions."""
     from threadpoolctl import threadpool_limits
     from oracle import decode as OD, int8 as OI, qjl as OQ
+    nth = cpu_threads()
     W, B, H, T, d, m = si.W_DECODE, 16, 32, 32768, 128, 256
     S = si.projection(W, m, d, "f16")
     q = si.queries(W, B * H, 1, d, "f16")[:, 0]
     lam = 1.0 / math.sqrt(d)
-    done, spent = 0, 0.0
-    while done < B * H and (spent < seconds or done < 2):
-        # group `done` is rows [done * T, (done + 1) * T) of the [B*H*T, d] tensors
-        k = si.stream(W, si.K, T * d, "f16", start=done * T * d).reshape(T, d)
-        v = si.stream(W, si.V, T * d, "f16", start=done * T * d).reshape(T, d)
-        kw, kn = OQ.qjl_sketch(k, S)                  # cache build (untimed)
+
+    def group(g):
+        # group g is rows [g * T, (g + 1) * T) of the [B*H*T, d] tensors
+        k = si.stream(W, si.K, T * d, "f16", start=g * T * d, workers=1).reshape(T, d)
+        v = si.stream(W, si.V, T * d, "f16", start=g * T * d, workers=1).reshape(T, d)
+        kw, kn = OQ.qjl_sketch(k, S)
         vc, vs = OI.quantize_int8(v)
-        with threadpool_limits(1):
+        return kw[None], kn[None], vc[None], vs[None]
+
+    def decode(args):
+        g, (kw, kn, vc, vs) = args
+        OD.decode_qjl_int8(q[g:g + 1], S, kw, kn, vc, vs, lam)
+
+    with threadpool_limits(1):
+        # one thread: groups until `seconds` of compute (at least 2 groups)
+        done, spent = 0, 0.0
+        while done < B * H and (spent < seconds or done < 2):
+            c = group(done)
             t0 = time.perf_counter()
-            OD.decode_qjl_int8(q[done:done + 1], S, kw[None], kn[None], vc[None], vs[None], lam)
+            decode((done, c))
             spent += time.perf_counter() - t0
-        done += 1
-    return {"value": round(done * T / spent, 1), "unit": "scores/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {B * H} (batch, head) groups x {T} tokens, one decode query each; "
-                      f"fp64 numpy oracle on one thread, {spent:.1f} s of compute timed"}
+            done += 1
+        one = {"value": round(done * T / spent, 1), "unit": "scores/s", "cores": 1,
+               "seconds": round(spent, 2),
+               "sample": f"{done} of {B * H} (batch, head) groups x {T} tokens, one decode query each"}
+        # every thread: enough groups for about `seconds` of wall time
+        n = min(B * H, max(nth, int(nth * seconds * one["value"] / T)))
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=nth) as ex:     # cache build, untimed
+            caches = list(zip(range(n), ex.map(group, range(n))))
+        wall = _timed_pool(decode, caches, nth)
+        del caches
+        allc = {"value": round(n * T / wall, 1), "unit": "scores/s", "cores": nth,
+                "seconds": round(wall, 2),
+                "sample": f"{n} of {B * H} (batch, head) groups x {T} tokens, one decode query each, "
+                          f"one group per task on {nth} threads"}
+
+        # INT8 quantize, fp32 sweep 2^28 elements as rows of 128
+        n_el, dq = 1 << 28, 128
+        blk = 1 << 22
+        nblk_total = n_el // blk
+        x0 = si.flat_rows(si.W_SWEEP, blk, dq, rows=range(0, blk // dq))
+        t0 = time.perf_counter()
+        nb = 0
+        while nb < nblk_total and (time.perf_counter() - t0 < seconds / 2 or nb < 1):
+            OI.quantize_int8(x0)
+            nb += 1
+        t1 = time.perf_counter() - t0
+        bytes_per_el = 4 + 1 + 4 / dq
+        q1 = {"value": round(nb * blk * bytes_per_el / t1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+              "seconds": round(t1, 2),
+              "sample": f"{nb} of the {nblk_total} 2^22-element blocks of the 2^28 sweep (d = 128)"}
+        nb_all = min(nblk_total, max(nth, int(nth * seconds / 2 / (t1 / nb))))
+        blocks = [si.flat_rows(si.W_SWEEP, n_el, dq, rows=range(i * (blk // dq), (i + 1) * (blk // dq)))
+                  for i in range(min(nb_all, nth))]
+        wall = _timed_pool(lambda i: OI.quantize_int8(blocks[i % len(blocks)]), range(nb_all), nth)
+        qa = {"value": round(nb_all * blk * bytes_per_el / wall / 1e9, 3), "unit": "GB/s",
+              "cores": nth, "seconds": round(wall, 2),
+              "sample": f"{nb_all} 2^22-element blocks of the 2^28 sweep (d = 128), one per task "
+                        f"on {nth} threads"}
+        del blocks
+    quant = {"one_core": q1, "all_cores": qa}
+    if gpu_quantize_ms:
+        gpu_gbs = n_el * bytes_per_el / (gpu_quantize_ms / 1e3) / 1e9
+        quant["gpu_GB/s"] = round(gpu_gbs, 1)
+        quant["gpu_over_cpu"] = {"one_core": round(gpu_gbs / q1["value"], 1),
+                                 "all_cores": round(gpu_gbs / qa["value"], 1),
+                                 "context": "the INT8 page (arXiv 2601.04719, Abstract) reports up "
+                                            "to 1,694x over its CPU baselines, hardware not stated"}
+    return {"value": allc["value"], "unit": "scores/s", "cores": nth, "kind": "oracle",
+            "sample": allc["sample"] + "; fp64 numpy oracle (decode of the long-context workload)",
+            "cpu_model": cpu_model(), "one_core": one, "all_cores": allc,
+            "int8_quantize_2^28_d128": quant}
+
+
+PROVENANCE = {
+    "measured": ["ms_per_step (wall clock around the timed steps)", "graph_ms_per_step",
+                 "roofline.avg_launch_ms (HIP events)", "roofline.traffic (rocprofv3 FETCH_SIZE "
+                 "and WRITE_SIZE, scaled by a known copy)", "components.*.ms, ms_min, graph_ms "
+                 "(HIP events)", "cpu_baseline.*.seconds"],
+    "derived": ["value = scores per step / ms_per_step", "roofline.achieved, frac = algorithmic "
+                "bytes / avg_launch_ms", "components.*.GB/s, frac_hbm, TFLOP/s, frac_mfma_f16, "
+                "scores/s = algorithmic bytes, flops or scores / ms", "cpu_baseline.*.value = work "
+                "/ seconds", "cpu_baseline.int8_quantize_2^28_d128.gpu_over_cpu"],
+}
 
 
 def main():
@@ -389,6 +614,60 @@ def main():
     import synth_inputs as si
 
     torch.cuda.set_device(0)
+
+    only = tuple(x for x in args.only.split(",") if x)
+    bad = [x for x in only if x not in SECTIONS]
+    if bad:
+        print(f"unknown section(s) {bad}; sections: {', '.join(SECTIONS)}", file=sys.stderr)
+        sys.exit(2)
+
+    value = ms_step = graph_ms_step = roofline = None
+    if not args.no_decode:
+        value, ms_step, graph_ms_step, roofline = decode_step(K, si, torch, args)
+
+    comp = None
+    if not args.no_components:
+        torch.cuda.empty_cache()
+        log("bench: components")
+        comp = components(K, si, torch, np, only, not args.no_graph)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        gq = (comp or {}).get("quantize_f32_2^28_d128", {}).get("ms")
+        cpu = cpu_baseline(si, np, args.cpu_seconds, gq)
+
+    line = {
+        "metric": "KV quantize/dequant HBM GB/s (% of peak); QJL+INT8 decode scores/sec",
+        "value": None if value is None else round(value, 1),
+        "unit": "scores/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": None if ms_step is None else round(ms_step, 4),
+        "graph_ms_per_step": None if graph_ms_step is None else round(graph_ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode step over a QJL-key / INT8-value cache: batch 16 x 32 heads "
+                               "x 32768 tokens x d 128, m 256, 1 fp16 query per head, newest token "
+                               "compressed in-step",
+                   "global_batch": 16, "seq_len": 32768, "heads": 32, "head_dim": 128, "qjl_m": 256,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "components": comp,
+        "provenance": PROVENANCE,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def decode_step(K, si, torch, args):
+    """The headline: K decode steps timed back to back (see the module
+    docstring).  Returns (scores/s, ms per step, ms per step from a HIP graph
+    replay, roofline of the decode launch)."""
     dev = "cuda"
     W, B, H, T, d, m = si.W_DECODE, 16, 32, 32768, 128, 256
     G = B * H
@@ -485,43 +764,8 @@ def main():
     log(f"bench: {args.steps} steps, {ms_step:.3f} ms/step (events {step_ev_ms:.3f}), "
         f"decode {dec_ms:.3f} ms "
         f"({achieved:.0f} GB/s)")
-
-    comp = None
-    if not args.no_components:
-        del kbits, knorms, vcodes, vscales
-        torch.cuda.empty_cache()
-        log("bench: components")
-        comp = components(K, si, torch, np)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("bench: cpu baseline (oracle)")
-        cpu = cpu_baseline(si, np, args.cpu_seconds)
-
-    line = {
-        "metric": "KV quantize/dequant HBM GB/s (% of peak); QJL+INT8 decode scores/sec",
-        "value": round(value, 1),
-        "unit": "scores/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "graph_ms_per_step": round(graph_ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": "decode step over a QJL-key / INT8-value cache: batch 16 x 32 heads "
-                               "x 32768 tokens x d 128, m 256, 1 fp16 query per head, newest token "
-                               "compressed in-step",
-                   "global_batch": 16, "seq_len": T, "heads": H, "head_dim": d, "qjl_m": m,
-                   "parallelism": "single GPU"},
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "components": comp,
-    }
-    print(json.dumps(line), flush=True)
+    del kbits, knorms, vcodes, vscales, k_new, v_new, ws, out, q, S
+    return value, ms_step, graph_ms_step, roofline
 
 
 if __name__ == "__main__":

@@ -45,8 +45,9 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // Token tiles of 32 per wave iteration: two, or one when d = 256 would
 // otherwise spill.
 template <int KS> constexpr int sketch_nt() { return KS <= 8 ? 2 : 1; }
-// Key tiles in flight per wave (a ring of register buffers).
-template <int NT> constexpr int sketch_ring() { return NT == 1 ? 4 : 2; }
+// Key tiles in flight per wave (a ring of register buffers): four single
+// tiles up to d = 192, two above (four would spill registers).
+template <int KS> constexpr int sketch_ring() { return sketch_nt<KS>() == 1 && KS <= 12 ? 4 : 2; }
 
 // Sign words of projection tile mt (32 projections) for the NT x 32 tokens
 // of a wave: P = S_tile K^T on fp16 MFMA, then bit = [P >= 0].  Accumulator
@@ -101,18 +102,22 @@ __device__ __forceinline__ void sketch_tile_words(const f16x8* sfrag, int mt, in
 constexpr int kSketchThreads = 512;
 constexpr int kSketchWaves = kSketchThreads / 64;
 
+// A launch computes projection tiles [mt0, mt0 + m_rt / 32) of every row
+// (sign words mt0 .. of words_total per row); S larger than a workgroup's
+// LDS takes several launches, and the one with mt0 == 0 writes the norms.
 template <int KS, int MT>
 __global__ __launch_bounds__(kSketchThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void sketch_mfma_kernel(const _Float16* __restrict__ k,
                                                           int64_t rows,
                                                           const _Float16* __restrict__ S,
                                                           int m_rt, uint32_t* __restrict__ bits,
-                                                          uint16_t* __restrict__ norms) {
+                                                          uint16_t* __restrict__ norms,
+                                                          int mt0, int words_total) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   f16x8* sfrag = reinterpret_cast<f16x8*>(lds_raw);
   constexpr int D = KS * 16;
   const int mt_count = MT > 0 ? MT : m_rt / 32;
-  const int words = mt_count;  // sign words per token
+  const int words = MT > 0 ? MT : words_total;  // sign words per token
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -126,7 +131,7 @@ void sketch_mfma_kernel(const _Float16* __restrict__ k,
     const int l = idx & 63;
     const int frag = idx >> 6;
     const int mt = frag / KS, ks = frag % KS;
-    const int srow = 32 * mt + sketch_row_perm(l & 31);
+    const int srow = 32 * (mt0 + mt) + sketch_row_perm(l & 31);
     sfrag[idx] = *reinterpret_cast<const f16x8*>(S + (int64_t)srow * D + 16 * ks + 8 * (l >> 5));
   }
   __syncthreads();
@@ -178,7 +183,7 @@ void sketch_mfma_kernel(const _Float16* __restrict__ k,
       halves_u32(__builtin_bit_cast(uint32_t, ss[nt]), slo, shi);
       const float tot = __builtin_bit_cast(float, slo) + __builtin_bit_cast(float, shi);
       const int64_t tok = tok0 + 32 * nt + col;
-      if (h == 0 && tok < rows) norms[tok] = f32_to_f16_bits(__builtin_sqrtf(tot));
+      if (h == 0 && tok < rows && mt0 == 0) norms[tok] = f32_to_f16_bits(__builtin_sqrtf(tot));
     }
     if constexpr (MT > 0) {
       // unrolled so the words stay in registers; the scheduling barrier
@@ -242,7 +247,7 @@ void sketch_mfma_kernel(const _Float16* __restrict__ k,
 #pragma unroll
         for (int nt = 0; nt < kSketchNT; ++nt) {
           const int64_t tok = tok0 + 32 * nt + col;
-          if (h == 0 && tok < rows) bits[tok * words + mt] = f[nt];
+          if (h == 0 && tok < rows) bits[tok * words + mt0 + mt] = f[nt];
         }
       }
     }
@@ -251,7 +256,7 @@ void sketch_mfma_kernel(const _Float16* __restrict__ k,
   // RING token tiles in flight per wave: a ring of register buffers, each
   // refilled (unconditionally, clamped past the end) right after its tile's
   // multiplies are issued.
-  constexpr int RING = sketch_ring<kSketchNT>();
+  constexpr int RING = sketch_ring<KS>();
   const int64_t stride = (int64_t)gridDim.x * kSketchWaves;
   const int64_t first = (int64_t)blockIdx.x * kSketchWaves + wave;
   if (first >= tiles) return;
@@ -270,8 +275,182 @@ void sketch_mfma_kernel(const _Float16* __restrict__ k,
 }
 
 // ---------------------------------------------------------------------------
-// Sketch, any shape (and fp32 keys): one thread per (row, sign word), 32
-// binary32 dot products each; the word-0 thread also writes the norm.
+// Sketch, fp32 keys and S, on fp16 matrix cores.  Each row of S and each key
+// is scaled by a power of two (exact; it does not change a projection's
+// sign) so that its largest magnitude lies in [2^14, 2^15), then split into
+// two binary16 parts: hi = the value with its 13 low significand bits
+// cleared, lo = the exact remainder rounded toward zero, so hi + lo is within
+// 2^-20 relative (2^-24 absolute below the binary16 normal range) of the
+// scaled value.  P = S_hi k_hi + S_hi k_lo + S_lo k_hi (three MFMAs per
+// K-step, fp32 accumulation) then differs from the exact projection by a few
+// 2^-20 sum_j |S_ij k_j| <= 2^-18 ||S_i|| ||k||, well inside the 1e-4 sign
+// band.  The norm is accumulated from the binary32 key values.  One 32-token
+// tile per wave iteration; S's hi and lo fragments (projection tiles
+// [mt0, mt0 + mt_pass)) are resident in LDS.
+template <int KS>
+constexpr int split_ring() { return KS <= 8 ? 2 : 1; }
+
+// hi / lo binary16 parts of two scaled binary32 values.
+__device__ __forceinline__ void split2(float v0, float v1, _Float16& h0, _Float16& h1,
+                                       _Float16& l0, _Float16& l1) {
+  const float a0 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v0) & 0xFFFFE000u);
+  const float a1 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v1) & 0xFFFFE000u);
+  const auto ph = __builtin_amdgcn_cvt_pkrtz(a0, a1);
+  const auto pl = __builtin_amdgcn_cvt_pkrtz(v0 - a0, v1 - a1);
+  h0 = ph[0];
+  h1 = ph[1];
+  l0 = pl[0];
+  l1 = pl[1];
+}
+
+// The same lane value of the other half of the wave (lane l <-> l ^ 32).
+__device__ __forceinline__ float other_half(float v, int h) {
+  uint32_t lo, hi;
+  halves_u32(__builtin_bit_cast(uint32_t, v), lo, hi);
+  return __builtin_bit_cast(float, h == 0 ? hi : lo);
+}
+
+template <int KS>
+__global__ __launch_bounds__(kSketchThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void sketch_split_kernel(const float* __restrict__ k, int64_t rows, const float* __restrict__ S,
+                         int mt_pass, uint32_t* __restrict__ bits, uint16_t* __restrict__ norms,
+                         int mt0, int words_total) {
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  constexpr int D = KS * 16;
+  const int nfrag_lanes = mt_pass * KS * 64;
+  f16x8* shi = reinterpret_cast<f16x8*>(lds_raw);
+  f16x8* slo = shi + nfrag_lanes;
+  int* rsc = reinterpret_cast<int*>(slo + nfrag_lanes);     // [32 mt_pass] row exponents
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const int col = lane & 31;
+
+  // scale exponent of every S row of this pass
+  for (int r = tid; r < 32 * mt_pass; r += kSketchThreads) {
+    const float* sr = S + (int64_t)(32 * mt0 + r) * D;
+    float a = 0.0f;
+    for (int j = 0; j < D; j += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(sr + j);
+      a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
+                                             __builtin_fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3]))));
+    }
+    rsc[r] = 15 - __builtin_amdgcn_frexp_expf(a);
+  }
+  __syncthreads();
+  // S -> LDS in fragment order (as the fp16 sketch), hi and lo parts
+  for (int idx = tid; idx < nfrag_lanes; idx += kSketchThreads) {
+    const int l = idx & 63;
+    const int frag = idx >> 6;
+    const int mt = frag / KS, ks = frag % KS;
+    const int rloc = 32 * mt + sketch_row_perm(l & 31);
+    const float* sp = S + (int64_t)(32 * mt0 + rloc) * D + 16 * ks + 8 * (l >> 5);
+    const f32x4 u = *reinterpret_cast<const f32x4*>(sp);
+    const f32x4 w = *reinterpret_cast<const f32x4*>(sp + 4);
+    const int e = rsc[rloc];
+    const float v[8] = {u[0], u[1], u[2], u[3], w[0], w[1], w[2], w[3]};
+    f16x8 hv, lv;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      _Float16 h0, h1, l0, l1;
+      split2(__builtin_amdgcn_ldexpf(v[i], e), __builtin_amdgcn_ldexpf(v[i + 1], e), h0, h1, l0, l1);
+      hv[i] = h0;
+      hv[i + 1] = h1;
+      lv[i] = l0;
+      lv[i + 1] = l1;
+    }
+    shi[idx] = hv;
+    slo[idx] = lv;
+  }
+  __syncthreads();
+
+  const int64_t tiles = (rows + 31) / 32;
+  // lane (token j, half h) holds channels 16 ks + 8 h .. + 8 of token j;
+  // loads unconditional (clamped to the last row past the end)
+  auto load = [&](f32x4 (&b)[KS][2], int64_t tile) {
+    const int64_t tok = std::min<int64_t>(tile * 32 + col, rows - 1);
+    const float* kr = k + tok * D + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      b[ks][0] = *reinterpret_cast<const f32x4*>(kr + 16 * ks);
+      b[ks][1] = *reinterpret_cast<const f32x4*>(kr + 16 * ks + 4);
+    }
+  };
+
+  auto process = [&](const f32x4 (&b)[KS][2], int64_t tile) {
+    const int64_t tok = tile * 32 + col;
+    int off = 0;
+    asm volatile("" : "+v"(off));
+    const f16x8* sh = shi + off;
+    const f16x8* sl = slo + off;
+    float ss = 0.0f, am = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ss = __builtin_fmaf(b[ks][p][e], b[ks][p][e], ss);
+          am = __builtin_fmaxf(am, __builtin_fabsf(b[ks][p][e]));
+        }
+    ss += other_half(ss, h);
+    am = __builtin_fmaxf(am, other_half(am, h));
+    if (h == 0 && tok < rows && mt0 == 0) norms[tok] = f32_to_f16_bits(__builtin_sqrtf(ss));
+    const int sc = 15 - __builtin_amdgcn_frexp_expf(am);
+    f16x8 bh[KS], bl[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        _Float16 h0, h1, l0, l1;
+        split2(__builtin_amdgcn_ldexpf(b[ks][i >> 2][i & 3], sc),
+               __builtin_amdgcn_ldexpf(b[ks][(i + 1) >> 2][(i + 1) & 3], sc), h0, h1, l0, l1);
+        bh[ks][i] = h0;
+        bh[ks][i + 1] = h1;
+        bl[ks][i] = l0;
+        bl[ks][i + 1] = l1;
+      }
+#pragma unroll 1
+    for (int mt = 0; mt < mt_pass; ++mt) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const f16x8 ah = sh[(mt * KS + ks) * 64 + lane];
+        const f16x8 al = sl[(mt * KS + ks) * 64 + lane];
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh[ks], acc, 0, 0, 0);
+      }
+      const f32x16 a1[1] = {acc};
+      uint32_t f[1];
+      sketch_tile_signs<1>(a1, f);
+      if (h == 0 && tok < rows) bits[tok * words_total + mt0 + mt] = f[0];
+    }
+  };
+
+  constexpr int RING = split_ring<KS>();
+  const int64_t stride = (int64_t)gridDim.x * kSketchWaves;
+  const int64_t first = (int64_t)blockIdx.x * kSketchWaves + wave;
+  if (first >= tiles) return;
+  f32x4 bq[RING][KS][2];
+#pragma unroll
+  for (int r = 0; r < RING; ++r) load(bq[r], std::min(first + r * stride, tiles - 1));
+  for (int64_t t0 = first;; t0 += RING * stride) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) {
+      const int64_t t = t0 + r * stride;
+      process(bq[r], t);
+      if (t + stride >= tiles) return;
+      load(bq[r], std::min(t + RING * stride, tiles - 1));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Sketch, d > 256 (beyond the MFMA kernels' register-resident K-steps): one
+// thread per (row, sign word), 32 binary32 dot products each; the word-0
+// thread also writes the norm.
 template <typename T>
 __global__ __launch_bounds__(256) void sketch_generic_kernel(const T* __restrict__ k, int64_t rows,
                                                              int d, const T* __restrict__ S, int m,
@@ -301,49 +480,117 @@ __global__ __launch_bounds__(256) void sketch_generic_kernel(const T* __restrict
   }
 }
 
+// Persistent grid: exactly the workgroups that fit on the device at once
+// (registers and LDS both limit it), each striding over the token tiles.
+template <typename Kernel>
+static hipError_t persistent_blocks(Kernel kernel, size_t lds, int64_t tiles,
+                                    const DeviceInfo& dev, int64_t* blocks) {
+  hipError_t e = allow_dynamic_lds(kernel, lds);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kSketchThreads, lds);
+  if (e != hipSuccess) return e;
+  const int64_t want = (tiles + kSketchWaves - 1) / kSketchWaves;
+  const int64_t cap = (int64_t)dev.cus * std::max(1, per_cu);
+  *blocks = std::max<int64_t>(1, std::min(want, cap));
+  return hipSuccess;
+}
+
+// Projection tiles per launch when S's fragments (bytes_per_tile each) must
+// fit in `lds` bytes: the m / 32 tiles in as few, equal launches as fit.
+static int tiles_per_pass(int mt_total, size_t bytes_per_tile, size_t lds) {
+  const int fit = std::max<int>(1, (int)(lds / bytes_per_tile));
+  const int passes = (mt_total + fit - 1) / fit;
+  return (mt_total + passes - 1) / passes;
+}
+
 template <int KS, int MT>
 static hipError_t sketch_mfma_launch(const _Float16* k, int64_t rows, const _Float16* S, int m,
                                      uint32_t* bits, uint16_t* norms, const DeviceInfo& dev,
                                      hipStream_t st) {
-  const size_t lds = (size_t)m * KS * 16 * sizeof(_Float16);
   constexpr int kSketchNT = sketch_nt<KS>();
   const int64_t tiles = (rows + 32 * kSketchNT - 1) / (32 * kSketchNT);
-  // persistent grid: exactly the workgroups that fit on the device at once
-  // (registers and LDS both limit it), each striding over the token tiles
-  int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sketch_mfma_kernel<KS, MT>,
-                                                              kSketchThreads, lds);
-  if (e != hipSuccess) return e;
-  const int64_t want = (tiles + kSketchWaves - 1) / kSketchWaves;
-  const int64_t cap = (int64_t)dev.cus * std::max(1, per_cu);
-  const int64_t blocks = std::max<int64_t>(1, std::min(want, cap));
-  hipLaunchKernelGGL((sketch_mfma_kernel<KS, MT>), dim3((unsigned)blocks), dim3(kSketchThreads), lds, st, k,
-                     rows, S, m, bits, norms);
-  return hipGetLastError();
+  const int mt_total = m / 32;
+  const size_t tile_bytes = (size_t)32 * KS * 16 * sizeof(_Float16);
+  const int per = MT > 0 ? MT : tiles_per_pass(mt_total, tile_bytes, dev.lds_per_block);
+  for (int mt0 = 0; mt0 < mt_total; mt0 += per) {
+    const int mtp = std::min(per, mt_total - mt0);
+    const size_t lds = (size_t)mtp * tile_bytes;
+    int64_t blocks = 0;
+    hipError_t e = persistent_blocks(sketch_mfma_kernel<KS, MT>, lds, tiles, dev, &blocks);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((sketch_mfma_kernel<KS, MT>), dim3((unsigned)blocks), dim3(kSketchThreads),
+                       lds, st, k, rows, S, 32 * mtp, bits, norms, mt0, mt_total);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
+
+template <int KS>
+static hipError_t sketch_split_launch(const float* k, int64_t rows, const float* S, int m,
+                                      uint32_t* bits, uint16_t* norms, const DeviceInfo& dev,
+                                      hipStream_t st) {
+  const int64_t tiles = (rows + 31) / 32;
+  const int mt_total = m / 32;
+  // hi and lo fragments plus one exponent per S row, per projection tile
+  const size_t tile_bytes = (size_t)2 * 32 * KS * 16 * sizeof(_Float16) + 32 * sizeof(int);
+  const int per = tiles_per_pass(mt_total, tile_bytes, dev.lds_per_block);
+  for (int mt0 = 0; mt0 < mt_total; mt0 += per) {
+    const int mtp = std::min(per, mt_total - mt0);
+    const size_t lds = (size_t)mtp * tile_bytes;
+    int64_t blocks = 0;
+    hipError_t e = persistent_blocks(sketch_split_kernel<KS>, lds, tiles, dev, &blocks);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((sketch_split_kernel<KS>), dim3((unsigned)blocks), dim3(kSketchThreads), lds,
+                       st, k, rows, S, mtp, bits, norms, mt0, mt_total);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int KS>
+static hipError_t sketch_by_ks(const void* k, int k_f16, int64_t rows, const void* S, int m,
+                               uint32_t* bits, uint16_t* norms, const DeviceInfo& dev,
+                               hipStream_t st) {
+  if (k_f16)
+    return sketch_mfma_launch<KS, 0>(static_cast<const _Float16*>(k), rows,
+                                     static_cast<const _Float16*>(S), m, bits, norms, dev, st);
+  return sketch_split_launch<KS>(static_cast<const float*>(k), rows, static_cast<const float*>(S),
+                                 m, bits, norms, dev, st);
+}
+
+// Largest head dimension whose K-steps the MFMA sketches hold in registers.
+constexpr int kSketchMfmaMaxD = 256;
 
 hipError_t launch_qjl_sketch(const void* k, int k_f16, int64_t rows, int d, const void* S, int m,
                              uint32_t* bits, uint16_t* norms, const DeviceInfo& dev,
                              hipStream_t st) {
-  if (k_f16) {
-    const size_t lds = (size_t)m * d * sizeof(_Float16);
-    const _Float16* kh = static_cast<const _Float16*>(k);
-    const _Float16* Sh = static_cast<const _Float16*>(S);
-    if (lds <= std::min<size_t>(dev.lds_per_block, 64 * 1024)) {
-      if (d == 128 && m == 256) return sketch_mfma_launch<8, 8>(kh, rows, Sh, m, bits, norms, dev, st);
-      switch (d) {
-        case 16: return sketch_mfma_launch<1, 0>(kh, rows, Sh, m, bits, norms, dev, st);
-        case 32: return sketch_mfma_launch<2, 0>(kh, rows, Sh, m, bits, norms, dev, st);
-        case 64: return sketch_mfma_launch<4, 0>(kh, rows, Sh, m, bits, norms, dev, st);
-        case 128: return sketch_mfma_launch<8, 0>(kh, rows, Sh, m, bits, norms, dev, st);
-        case 256: return sketch_mfma_launch<16, 0>(kh, rows, Sh, m, bits, norms, dev, st);
-        default: break;
-      }
-    }
+  if (k_f16 && d == 128 && m == 256 && dev.lds_per_block >= (size_t)m * d * sizeof(_Float16))
+    return sketch_mfma_launch<8, 8>(static_cast<const _Float16*>(k), rows,
+                                    static_cast<const _Float16*>(S), m, bits, norms, dev, st);
+  switch (d) {
+    case 16: return sketch_by_ks<1>(k, k_f16, rows, S, m, bits, norms, dev, st);
+    case 32: return sketch_by_ks<2>(k, k_f16, rows, S, m, bits, norms, dev, st);
+    case 48: return sketch_by_ks<3>(k, k_f16, rows, S, m, bits, norms, dev, st);
+    case 64: return sketch_by_ks<4>(k, k_f16, rows, S, m, bits, norms, dev, st);
+    case 80: return sketch_by_ks<5>(k, k_f16, rows, S, m, bits, norms, dev, st);
+    case 96: return sketch_by_ks<6>(k, k_f16, rows, S, m, bits, norms, dev, st);
+    case 112: return sketch_by_ks<7>(k, k_f16, rows, S, m, bits, norms, dev, st);
+    case 128: return sketch_by_ks<8>(k, k_f16, rows, S, m, bits, norms, dev, st);
+    case 144: return sketch_by_ks<9>(k, k_f16, rows, S, m, bits, norms, dev, st);
+    case 160: return sketch_by_ks<10>(k, k_f16, rows, S, m, bits, norms, dev, st);
+    case 176: return sketch_by_ks<11>(k, k_f16, rows, S, m, bits, norms, dev, st);
+    case 192: return sketch_by_ks<12>(k, k_f16, rows, S, m, bits, norms, dev, st);
+    case 208: return sketch_by_ks<13>(k, k_f16, rows, S, m, bits, norms, dev, st);
+    case 224: return sketch_by_ks<14>(k, k_f16, rows, S, m, bits, norms, dev, st);
+    case 240: return sketch_by_ks<15>(k, k_f16, rows, S, m, bits, norms, dev, st);
+    case 256: return sketch_by_ks<16>(k, k_f16, rows, S, m, bits, norms, dev, st);
+    default: break;
   }
-  const int64_t threads = rows * (m / 32);
-  const int64_t blocks = (threads + 255) / 256;
-  // the generic path is launched in row slices to bound the grid
+  static_assert(kSketchMfmaMaxD == 256, "the switch above covers d = 16 .. 256");
+  // d > 256: the generic kernel, launched in row slices to bound the grid
   const int64_t rows_per = std::max<int64_t>(1, (int64_t(1) << 30) / (m / 32));
   for (int64_t r0 = 0; r0 < rows; r0 += rows_per) {
     const int64_t nr = std::min(rows_per, rows - r0);
@@ -359,7 +606,6 @@ hipError_t launch_qjl_sketch(const void* k, int k_f16, int64_t rows, int d, cons
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  (void)blocks;
   return hipSuccess;
 }
 
@@ -400,7 +646,9 @@ __global__ __launch_bounds__(TH) __attribute__((amdgpu_waves_per_eu(W == 8 ? 4 :
   const int m = W > 0 ? 32 * W : m_rt;
   const int words = m / 32;
   // tables first: at LDS address 0 a lookup's address is the byte permute's
-  // result plus the instruction offset, with no base to add
+  // result plus the instruction offset, with no base to add.  The rotated
+  // lookups require it (see rot_lane_base): this kernel declares no static
+  // __shared__ data, so its dynamic LDS starts at address 0.
   float* lut = reinterpret_cast<float*>(lds_raw);
   const size_t tfl = byte_table_floats(m, m == 256);
   float* y = lut + (tfl > (size_t)kProjQChunk ? tfl : (size_t)kProjQChunk);

@@ -437,7 +437,10 @@ constexpr int kRsU = 4;                          // tokens in flight per lane
 constexpr int kRsIters = 8;
 constexpr int kRsTile = 64 * kRsU * kRsIters;    // 2048 tokens per workgroup
 constexpr int kRsRowFloats = 32;
-constexpr int kRsLutFloats = 256 * kRsRowFloats; // 32 KiB, at LDS address 0
+// 32 KiB, at LDS address 0: the lookups use the byte permute's result as the
+// address itself, so the scores kernel declares no static __shared__ data
+// (its dynamic LDS then starts at address 0)
+constexpr int kRsLutFloats = 256 * kRsRowFloats;
 
 // Tables of y[0..255] in rows of 32 entries: lut[32 v + p] = T_p[v] (same
 // binary32 values as the other table builders: low-nibble partial sums plus

@@ -39,20 +39,33 @@ def _stream(t: torch.Tensor):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def quantize_int8(x: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
-    """x [..., d] fp32/fp16 -> (codes int8 [..., d], scales fp32 [...])."""
+def _out(given, shape, dtype, like: torch.Tensor, what: str) -> torch.Tensor:
+    """The caller's output tensor (checked: shape, dtype, device, contiguous)
+    or a new one; passing outputs makes a call allocation-free."""
+    shape = tuple(shape)
+    if given is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    if tuple(given.shape) != shape or given.dtype != dtype or given.device != like.device:
+        raise ValueError(f"{what}: expected {dtype} {shape} on {like.device}, got "
+                         f"{given.dtype} {tuple(given.shape)} on {given.device}")
+    return _dev(given, what)
+
+
+def quantize_int8(x: torch.Tensor, out=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """x [..., d] fp32/fp16 -> (codes int8 [..., d], scales fp32 [...]).
+    ``out``: optional (codes, scales) to write into."""
     _dev(x, "x")
     d = x.shape[-1]
     rows = x.numel() // d if d else 0
-    codes = torch.empty(x.shape, dtype=torch.int8, device=x.device)
-    scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    codes = _out(out and out[0], x.shape, torch.int8, x, "codes")
+    scales = _out(out and out[1], x.shape[:-1], torch.float32, x, "scales")
     L.check(L.lib().kvq_quantize_int8(_p(x), _dtype_code(x, "x"), rows, d, _p(codes),
                                       _p(scales), _stream(x)))
     return codes, scales
 
 
 def dequantize_int8(codes: torch.Tensor, scales: torch.Tensor,
-                    out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+                    out_dtype: torch.dtype = torch.float32, out=None) -> torch.Tensor:
     """codes int8 [..., d], scales fp32 [...] -> [..., d] in out_dtype."""
     _dev(codes, "codes"), _dev(scales, "scales")
     if codes.dtype != torch.int8 or scales.dtype != torch.float32:
@@ -61,26 +74,26 @@ def dequantize_int8(codes: torch.Tensor, scales: torch.Tensor,
     rows = codes.numel() // d if d else 0
     if scales.numel() != rows:
         raise ValueError(f"scales has {scales.numel()} entries for {rows} rows")
-    out = torch.empty(codes.shape, dtype=out_dtype, device=codes.device)
+    out = _out(out, codes.shape, out_dtype, codes, "out")
     L.check(L.lib().kvq_dequantize_int8(_p(codes), _p(scales), rows, d, _p(out),
                                         _dtype_code(out, "out_dtype"), _stream(codes)))
     return out
 
 
-def quantize_int8_channel(x: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+def quantize_int8_channel(x: torch.Tensor, out=None) -> tuple[torch.Tensor, torch.Tensor]:
     """Keys x [G, T, d] fp32/fp16 -> (codes int8 [G, T, d], per-channel
-    scales fp32 [G, d])."""
+    scales fp32 [G, d]).  ``out``: optional (codes, scales)."""
     _dev(x, "x")
     G, T, d = x.shape
-    codes = torch.empty((G, T, d), dtype=torch.int8, device=x.device)
-    scales = torch.empty((G, d), dtype=torch.float32, device=x.device)
+    codes = _out(out and out[0], (G, T, d), torch.int8, x, "codes")
+    scales = _out(out and out[1], (G, d), torch.float32, x, "scales")
     L.check(L.lib().kvq_quantize_int8_channel(_p(x), _dtype_code(x, "x"), G, T, d, _p(codes),
                                               _p(scales), _stream(x)))
     return codes, scales
 
 
 def dequantize_int8_channel(codes: torch.Tensor, scales: torch.Tensor,
-                            out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+                            out_dtype: torch.dtype = torch.float32, out=None) -> torch.Tensor:
     """codes int8 [G, T, d], scales fp32 [G, d] -> [G, T, d] in out_dtype."""
     _dev(codes, "codes"), _dev(scales, "scales")
     if codes.dtype != torch.int8 or scales.dtype != torch.float32:
@@ -88,13 +101,14 @@ def dequantize_int8_channel(codes: torch.Tensor, scales: torch.Tensor,
     G, T, d = codes.shape
     if tuple(scales.shape) != (G, d):
         raise ValueError(f"scales {tuple(scales.shape)} for codes {tuple(codes.shape)}")
-    out = torch.empty((G, T, d), dtype=out_dtype, device=codes.device)
+    out = _out(out, (G, T, d), out_dtype, codes, "out")
     L.check(L.lib().kvq_dequantize_int8_channel(_p(codes), _p(scales), G, T, d, _p(out),
                                                 _dtype_code(out, "out_dtype"), _stream(codes)))
     return out
 
 
-def scores_int8_channel(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
+def scores_int8_channel(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                        out=None) -> torch.Tensor:
     """q [G, nq, d]; codes [G, T, d] int8; scales [G, d] -> scores [G, nq, T] fp32."""
     _dev(q, "q"), _dev(codes, "codes"), _dev(scales, "scales")
     G, nq, d = q.shape
@@ -102,29 +116,31 @@ def scores_int8_channel(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tens
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, codes {tuple(codes.shape)}, "
                          f"scales {tuple(scales.shape)}")
     T = codes.shape[1]
-    out = torch.empty((G, nq, T), dtype=torch.float32, device=q.device)
+    out = _out(out, (G, nq, T), torch.float32, q, "out")
     L.check(L.lib().kvq_scores_int8_channel(_p(q), _dtype_code(q, "q"), G, nq, _p(codes),
                                             _p(scales), T, d, _p(out), _stream(q)))
     return out
 
 
-def quantize_int4(x: torch.Tensor, g: int) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+def quantize_int4(x: torch.Tensor, g: int,
+                  out=None) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """x [..., d] fp32/fp16, group size g -> (codes uint8 [..., d/2] two per
-    byte, steps fp32 [..., d/g], offsets fp32 [..., d/g])."""
+    byte, steps fp32 [..., d/g], offsets fp32 [..., d/g]).  ``out``: optional
+    (codes, steps, offsets)."""
     _dev(x, "x")
     d = x.shape[-1]
     rows = x.numel() // d if d else 0
     ng = d // g if g > 0 else 0
-    codes = torch.empty((*x.shape[:-1], d // 2), dtype=torch.uint8, device=x.device)
-    steps = torch.empty((*x.shape[:-1], ng), dtype=torch.float32, device=x.device)
-    offsets = torch.empty((*x.shape[:-1], ng), dtype=torch.float32, device=x.device)
+    codes = _out(out and out[0], (*x.shape[:-1], d // 2), torch.uint8, x, "codes")
+    steps = _out(out and out[1], (*x.shape[:-1], ng), torch.float32, x, "steps")
+    offsets = _out(out and out[2], (*x.shape[:-1], ng), torch.float32, x, "offsets")
     L.check(L.lib().kvq_quantize_int4(_p(x), _dtype_code(x, "x"), rows, d, g, _p(codes), _p(steps),
                                       _p(offsets), _stream(x)))
     return codes, steps, offsets
 
 
 def dequantize_int4(codes: torch.Tensor, steps: torch.Tensor, offsets: torch.Tensor, g: int,
-                    out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+                    out_dtype: torch.dtype = torch.float32, out=None) -> torch.Tensor:
     """codes uint8 [..., d/2], steps / offsets fp32 [..., d/g] -> [..., d]."""
     _dev(codes, "codes"), _dev(steps, "steps"), _dev(offsets, "offsets")
     if codes.dtype != torch.uint8 or steps.dtype != torch.float32 or offsets.dtype != torch.float32:
@@ -134,13 +150,14 @@ def dequantize_int4(codes: torch.Tensor, steps: torch.Tensor, offsets: torch.Ten
     if g <= 0 or d % g != 0 or steps.shape != offsets.shape or steps.numel() != rows * (d // g):
         raise ValueError(f"shape mismatch: codes {tuple(codes.shape)}, g {g}, "
                          f"steps {tuple(steps.shape)}, offsets {tuple(offsets.shape)}")
-    out = torch.empty((*codes.shape[:-1], d), dtype=out_dtype, device=codes.device)
+    out = _out(out, (*codes.shape[:-1], d), out_dtype, codes, "out")
     L.check(L.lib().kvq_dequantize_int4(_p(codes), _p(steps), _p(offsets), rows, d, g, _p(out),
                                         _dtype_code(out, "out_dtype"), _stream(codes)))
     return out
 
 
-def scores_int8(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
+def scores_int8(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                out=None) -> torch.Tensor:
     """q [G, nq, d]; codes [G, T, d] int8; scales [G, T] -> scores [G, nq, T] fp32."""
     _dev(q, "q"), _dev(codes, "codes"), _dev(scales, "scales")
     G, nq, d = q.shape
@@ -148,15 +165,15 @@ def scores_int8(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor) -> t
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, codes {tuple(codes.shape)}, "
                          f"scales {tuple(scales.shape)}")
     T = codes.shape[1]
-    out = torch.empty((G, nq, T), dtype=torch.float32, device=q.device)
+    out = _out(out, (G, nq, T), torch.float32, q, "out")
     L.check(L.lib().kvq_scores_int8(_p(q), _dtype_code(q, "q"), G, nq, _p(codes), _p(scales), T, d,
                                     _p(out), _stream(q)))
     return out
 
 
-def qjl_sketch(k: torch.Tensor, S: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+def qjl_sketch(k: torch.Tensor, S: torch.Tensor, out=None) -> tuple[torch.Tensor, torch.Tensor]:
     """k [..., d] and S [m, d] of the same dtype -> (sign words int32 [..., m // 32],
-    norms fp16 [...])."""
+    norms fp16 [...]).  ``out``: optional (bits, norms)."""
     _dev(k, "k"), _dev(S, "S")
     if S.dtype != k.dtype:
         raise TypeError("S must have the keys' dtype")
@@ -164,18 +181,18 @@ def qjl_sketch(k: torch.Tensor, S: torch.Tensor) -> tuple[torch.Tensor, torch.Te
     if k.shape[-1] != d:
         raise ValueError(f"k has d = {k.shape[-1]}, S has d = {d}")
     rows = k.numel() // d if d else 0
-    bits = torch.empty((*k.shape[:-1], m // 32), dtype=torch.int32, device=k.device)
-    norms = torch.empty(k.shape[:-1], dtype=torch.float16, device=k.device)
+    bits = _out(out and out[0], (*k.shape[:-1], m // 32), torch.int32, k, "bits")
+    norms = _out(out and out[1], k.shape[:-1], torch.float16, k, "norms")
     L.check(L.lib().kvq_qjl_sketch(_p(k), _dtype_code(k, "k"), rows, d, _p(S), m, _p(bits),
                                    _p(norms), _stream(k)))
     return bits, norms
 
 
-def residual_sketch(k: torch.Tensor, S: torch.Tensor, g: int):
+def residual_sketch(k: torch.Tensor, S: torch.Tensor, g: int, out=None):
     """Two-stage key compression: k [..., d] fp32/fp16, S [m, d] fp32/fp16,
     group size g -> (codes uint8 [..., d/2], steps fp32 [..., d/g],
     offsets fp32 [..., d/g], residual sign words int32 [..., m // 32],
-    residual norms fp16 [...])."""
+    residual norms fp16 [...]).  ``out``: optional tuple of the five outputs."""
     _dev(k, "k"), _dev(S, "S")
     m, d = S.shape
     if k.shape[-1] != d:
@@ -183,11 +200,12 @@ def residual_sketch(k: torch.Tensor, S: torch.Tensor, g: int):
     rows = k.numel() // d if d else 0
     lead = k.shape[:-1]
     ng = d // g if g > 0 else 0
-    codes = torch.empty((*lead, d // 2), dtype=torch.uint8, device=k.device)
-    steps = torch.empty((*lead, ng), dtype=torch.float32, device=k.device)
-    offsets = torch.empty((*lead, ng), dtype=torch.float32, device=k.device)
-    bits = torch.empty((*lead, m // 32), dtype=torch.int32, device=k.device)
-    norms = torch.empty(lead, dtype=torch.float16, device=k.device)
+    o = out or (None,) * 5
+    codes = _out(o[0], (*lead, d // 2), torch.uint8, k, "codes")
+    steps = _out(o[1], (*lead, ng), torch.float32, k, "steps")
+    offsets = _out(o[2], (*lead, ng), torch.float32, k, "offsets")
+    bits = _out(o[3], (*lead, m // 32), torch.int32, k, "bits")
+    norms = _out(o[4], lead, torch.float16, k, "norms")
     L.check(L.lib().kvq_residual_sketch(_p(k), _dtype_code(k, "k"), rows, d, g, _p(S),
                                         _dtype_code(S, "S"), m, _p(codes), _p(steps), _p(offsets),
                                         _p(bits), _p(norms), _stream(k)))
@@ -196,7 +214,7 @@ def residual_sketch(k: torch.Tensor, S: torch.Tensor, g: int):
 
 def scores_residual(q: torch.Tensor, S: torch.Tensor, codes: torch.Tensor, steps: torch.Tensor,
                     offsets: torch.Tensor, bits: torch.Tensor, norms: torch.Tensor,
-                    g: int) -> torch.Tensor:
+                    g: int, out=None) -> torch.Tensor:
     """q [G, nq, d]; S [m, d]; codes [G, T, d/2]; steps / offsets [G, T, d/g];
     bits [G, T, m // 32]; norms [G, T] -> scores [G, nq, T] fp32."""
     for t, n in ((q, "q"), (S, "S"), (codes, "codes"), (steps, "steps"), (offsets, "offsets"),
@@ -211,7 +229,7 @@ def scores_residual(q: torch.Tensor, S: torch.Tensor, codes: torch.Tensor, steps
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, S {tuple(S.shape)}, codes "
                          f"{tuple(codes.shape)}, steps {tuple(steps.shape)}, bits {tuple(bits.shape)}, "
                          f"norms {tuple(norms.shape)}, g {g}")
-    out = torch.empty((G, nq, T), dtype=torch.float32, device=q.device)
+    out = _out(out, (G, nq, T), torch.float32, q, "out")
     L.check(L.lib().kvq_scores_residual(_p(q), _dtype_code(q, "q"), G, nq, _p(S), _dtype_code(S, "S"),
                                         m, g, _p(codes), _p(steps), _p(offsets), _p(bits), _p(norms),
                                         T, d, _p(out), _stream(q)))
@@ -219,7 +237,7 @@ def scores_residual(q: torch.Tensor, S: torch.Tensor, codes: torch.Tensor, steps
 
 
 def scores_qjl(q: torch.Tensor, S: torch.Tensor, bits: torch.Tensor,
-               norms: torch.Tensor) -> torch.Tensor:
+               norms: torch.Tensor, out=None) -> torch.Tensor:
     """q [G, nq, d]; S [m, d]; bits [G, T, m // 32]; norms [G, T] -> [G, nq, T] fp32."""
     for t, n in ((q, "q"), (S, "S"), (bits, "bits"), (norms, "norms")):
         _dev(t, n)
@@ -228,7 +246,7 @@ def scores_qjl(q: torch.Tensor, S: torch.Tensor, bits: torch.Tensor,
     T = bits.shape[1]
     if bits.shape != (G, T, m // 32) or norms.shape != (G, T) or S.shape[1] != d:
         raise ValueError("shape mismatch between q, S, bits and norms")
-    out = torch.empty((G, nq, T), dtype=torch.float32, device=q.device)
+    out = _out(out, (G, nq, T), torch.float32, q, "out")
     L.check(L.lib().kvq_scores_qjl(_p(q), _dtype_code(q, "q"), G, nq, _p(S), _dtype_code(S, "S"), m,
                                    _p(bits), _p(norms), T, d, _p(out), _stream(q)))
     return out
@@ -263,8 +281,7 @@ def decode_qjl_int8_gqa(q: torch.Tensor, S: torch.Tensor, kbits: torch.Tensor,
     need = decode_gqa_workspace_bytes(G, nq, T, d, m)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty((G, nq, d), dtype=torch.float32, device=q.device)
+    out = _out(out, (G, nq, d), torch.float32, q, "out")
     L.check(L.lib().kvq_decode_qjl_int8_gqa(
         _p(q), _dtype_code(q, "q"), G, nq, _p(S), _dtype_code(S, "S"), m, _p(kbits), _p(knorms),
         _p(vcodes), _p(vscales), T, d, float(sm_scale), _p(workspace), workspace.numel(), _p(out),
@@ -294,8 +311,7 @@ def decode_qjl_int8(q: torch.Tensor, S: torch.Tensor, kbits: torch.Tensor, knorm
     need = decode_workspace_bytes(G, T, d, m)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty((G, d), dtype=torch.float32, device=q.device)
+    out = _out(out, (G, d), torch.float32, q, "out")
     L.check(L.lib().kvq_decode_qjl_int8(
         _p(q), _dtype_code(q, "q"), G, _p(S), _dtype_code(S, "S"), m, _p(kbits), _p(knorms),
         _p(vcodes), _p(vscales), T, d, float(sm_scale), _p(workspace), workspace.numel(), _p(out),
@@ -321,11 +337,7 @@ def decode_qjl_int8_noalloc(q: torch.Tensor, S: torch.Tensor, kbits: torch.Tenso
         raise ValueError("shape mismatch between q, S and the cache tensors")
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((G, d), dtype=torch.float32, device=q.device)
-    elif out.shape != (G, d) or out.dtype != torch.float32:
-        raise ValueError("out must be float32 [G, d]")
-    _dev(out, "out")
+    out = _out(out, (G, d), torch.float32, q, "out")
     L.check(L.lib().kvq_decode_qjl_int8_noalloc(
         _p(q), _dtype_code(q, "q"), G, _p(S), _dtype_code(S, "S"), m, _p(kbits), _p(knorms),
         _p(vcodes), _p(vscales), T, d, float(sm_scale), _p(out), _stream(q)))

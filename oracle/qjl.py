@@ -71,7 +71,8 @@ def unpack_signs(words: np.ndarray, m: int) -> np.ndarray:
 def key_norms(k: np.ndarray) -> np.ndarray:
     """n_r = RN16(||k_r||_2); float64 -> float16 is a single rounding."""
     kw = _widen(k)
-    return np.sqrt(np.sum(kw * kw, axis=1)).astype(np.float16)
+    with np.errstate(over="ignore"):      # beyond binary16 range -> +inf (RN16)
+        return np.sqrt(np.sum(kw * kw, axis=1)).astype(np.float16)
 
 
 def qjl_sketch(k: np.ndarray, S: np.ndarray) -> tuple[np.ndarray, np.ndarray]:

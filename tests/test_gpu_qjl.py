@@ -81,8 +81,13 @@ def test_qjl_cache_full_size_every_row_and_group():
 
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 @pytest.mark.parametrize("d,m", [(16, 32), (64, 64), (128, 256), (128, 512), (256, 256), (96, 128),
-                                 (128, 96), (256, 1024), (48, 64)])
+                                 (128, 96), (256, 1024), (48, 64), (208, 96), (240, 64), (160, 320),
+                                 (128, 1024), (272, 64), (512, 32)])
 def test_sketch_shapes(dtype, d, m):
+    """Every head dimension up to 256 runs on the matrix cores (fp16 keys
+    directly, fp32 keys through the hi/lo split), with S in one or several
+    launches when its fragments exceed a workgroup's LDS (fp16: m d > 80 K
+    entries, fp32: m d > ~40 K); d > 256 takes the generic kernel."""
     rng = np.random.default_rng(d * 7 + m)
     npdt = np.float16 if dtype == "f16" else np.float32
     for rows in (1, 31, 65, 1000):
@@ -153,3 +158,35 @@ def test_grouped_queries_equal_single_query_runs(nq, T, d):
     for j in range(nq):
         alone = down(K.scores_qjl(up(np.ascontiguousarray(q[:, j:j + 1])), Sd, w, n))
         assert np.array_equal(grouped[:, j:j + 1].view(np.uint32), alone.view(np.uint32)), j
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("d,m", [(128, 256), (128, 512), (64, 1024)])
+def test_sketch_many_ragged_rows(dtype, d, m):
+    """100003 rows (ragged against every tile and the persistent grid's
+    stride); fp32 m = 512 and m = 1024 at d = 64 take two launches over S."""
+    rng = np.random.default_rng(d + m + (dtype == "f16"))
+    npdt = np.float16 if dtype == "f16" else np.float32
+    k = rng.standard_normal((100003, d)).astype(npdt)
+    S = rng.standard_normal((m, d)).astype(npdt)
+    sketch_check(k, S, f"{dtype} d={d} m={m} rows=100003")
+
+
+def test_sketch_fp32_dynamic_range():
+    """fp32 keys and S rows scaled by powers of two from 2^-126 to 2^120 (the
+    split scales each S row and each key into binary16 range), rows with one
+    huge and many tiny entries, subnormal keys, a zero S row and a zero key."""
+    rng = np.random.default_rng(5)
+    d, m, R = 128, 256, 3000
+    k = rng.standard_normal((R, d)).astype(np.float64)
+    k *= np.exp2(rng.integers(-126, 121, (R, 1)))
+    k[10] = 0.0
+    k[11] = rng.standard_normal(d) * 2.0 ** -140          # subnormal keys
+    k[12] = rng.standard_normal(d) * 1e-30
+    k[12, 5] = 1e30                                       # one huge entry among tiny ones
+    k[13] = np.where(rng.random(d) < 0.5, 3.0e38, -3.0e38) * rng.random(d)
+    S = rng.standard_normal((m, d)) * np.exp2(rng.integers(-100, 101, (m, 1)))
+    S[7] = 0.0
+    S[8, :] = 0.0
+    S[8, 3] = 2.0 ** -149
+    sketch_check(k.astype(np.float32), S.astype(np.float32), "fp32 dynamic range")
