@@ -91,16 +91,24 @@ def measured_traffic(bytes_per_launch_alg: float):
     return t.get("hbm_bytes_per_launch")
 
 
-def block_times(fn, calls_per_block, blocks, warmup, stream=None):
+def block_times(fn, calls_per_block, blocks, warmup, stream=None, warm_s=0.0):
     """Mean duration (ms) of one call of fn, for each of `blocks` blocks of
     `calls_per_block` back-to-back calls bracketed by one pair of HIP events
     on the stream fn launches on.  (A timing event recorded between two
     launches idles the GPU for ~10-15 us on this stack, so events never sit
-    between the calls being timed.)"""
+    between the calls being timed.)  Before timing, fn runs `warmup` times
+    and then until `warm_s` seconds have passed, so the blocks are timed at
+    the clocks the GPU reaches under this load (after seconds of host-side
+    input generation it starts from idle clocks)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        for _ in range(calls_per_block):
+            fn()
+        torch.cuda.synchronize()
     out = []
     for _ in range(blocks):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -119,9 +127,11 @@ def graph_times(calls, reps, blocks=5):
     `blocks` replays timed by a pair of HIP events: no host launch work sits
     between the kernels.  The calls write preallocated outputs."""
     import torch
-    for c in calls:
-        c()
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.1:
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(reps):
@@ -162,7 +172,8 @@ SECTIONS = ("copy", "sweep", "llama", "qjl", "residual", "gqa")
 
 def components(K, si, torch, np, only=SECTIONS, use_graph=True):
     """GB/s of the INT8 (per row and per channel), INT4, QJL and two-stage
-    kernels on their own workloads, cold: each timed call reads a different
+    kernels on their own workloads, cold (warmed-up clocks, cold caches): each
+    timed call reads a different
     copy of its inputs, and the copies together exceed 1 GiB, so no call
     finds its inputs in the MALL or L2.  Outputs are preallocated (one set
     per component), so a call is the ctypes call and its launches only.
@@ -179,7 +190,7 @@ def components(K, si, torch, np, only=SECTIONS, use_graph=True):
         """calls: list of zero-argument launches, one per input copy."""
         it = iter(range(10 ** 9))
         fn = lambda: calls[next(it) % len(calls)]()
-        times = block_times(fn, max(reps, len(calls)), 5, 3)
+        times = block_times(fn, max(reps, len(calls)), 5, 3, warm_s=0.25)
         ms = med(times)
         r = {"ms": round(ms, 4), "ms_min": round(min(times), 4), "GB/s": round(nbytes / ms / 1e6, 1),
              "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 3), "bytes": int(nbytes),

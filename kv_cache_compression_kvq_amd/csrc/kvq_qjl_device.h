@@ -90,16 +90,17 @@ __device__ __forceinline__ float row_dot(const TS* __restrict__ sr, const float*
 // the thread's element of q (all unconditionally, so the compiler's wait
 // counts stay exact), finish() stages q in LDS and writes y (callers
 // synchronise before reading y).
-template <typename TQ>
+// RG: row groups (4 rows each) held per wave, 16 covers m <= 64 * waves.
+template <typename TQ, int RG = 16>
 struct QueryProj16 {
-  f16x8 raw[16];
+  f16x8 raw[RG];
   TQ qreg;                          // converted in finish(), not here: a use
                                     // would make the compiler wait for the load
   int rpw;                          // rows per wave, a multiple of 4
 
   __device__ __forceinline__ static bool fits(int m, int d) {
     const int nw = (int)blockDim.x / 64;
-    return d <= 128 && (int)blockDim.x >= d && ((m + nw - 1) / nw + 3) / 4 * 4 <= 64;
+    return d <= 128 && (int)blockDim.x >= d && ((m + nw - 1) / nw + 3) / 4 * 4 <= 4 * RG;
   }
 
   __device__ __forceinline__ void issue(const _Float16* __restrict__ S, const TQ* __restrict__ q,
@@ -112,7 +113,7 @@ struct QueryProj16 {
     const int r4 = lane >> 4;
     const int cc = min(c, d / 8 - 1);          // chunks past the row: reloaded, unused
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
+    for (int it = 0; it < RG; ++it) {
       const int row = min(wave * rpw + 4 * min(it, rpw / 4 - 1) + r4, m - 1);
       raw[it] = *reinterpret_cast<const f16x8*>(S + (int64_t)row * d + 8 * cc);
     }
@@ -136,11 +137,11 @@ struct QueryProj16 {
     const f32x4 q0 = p4[0], q1 = p4[1];
     qv[0] = q0[0]; qv[1] = q0[1]; qv[2] = q0[2]; qv[3] = q0[3];
     qv[4] = q1[0]; qv[5] = q1[1]; qv[6] = q1[2]; qv[7] = q1[3];
-    // all 16 row groups are formed (past rpw they repeat the last one and are
+    // all RG row groups are formed (past rpw they repeat the last one and are
     // not stored): a use under a branch would let the compiler sink the S
     // loads of issue() next to it
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
+    for (int it = 0; it < RG; ++it) {
       float part = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)raw[it][e], qv[e], part);

@@ -703,12 +703,23 @@ __global__ __launch_bounds__(TH) __attribute__((amdgpu_waves_per_eu(W == 8 ? 4 :
         if (t < nlive) st[t] = c * nv[u] * acc;
       }
     };
-    // query 0 (this kernel is launched for fp16 S with d <= 128 only)
+    // query 0 (this kernel is launched for fp16 S with d <= 128 only): its
+    // projection's S rows and query are requested before the tokens, so
+    // that the projection waits for its own loads only (wait counts are in
+    // issue order) while the tokens stream in behind it
     const TQ* q0 = q + g * nq * d;
     if constexpr (sizeof(TS) == 2) {
-      load_tokens();
-      __builtin_amdgcn_sched_barrier(0);
-      project16_lite(S, q0, m, d, lut, y);
+      if (TH == kQjlWideThreads) {
+        QueryProj16<TQ, 8> pj;                 // m = 256 over 8 waves: 8 row groups
+        pj.issue(S, q0, m, d);
+        load_tokens();
+        __builtin_amdgcn_sched_barrier(0);
+        pj.finish(lut, y, m, d);
+      } else {
+        load_tokens();
+        __builtin_amdgcn_sched_barrier(0);
+        project16_lite(S, q0, m, d, lut, y);
+      }
       __syncthreads();
       build_rot_tables(y, lut);
       __syncthreads();
