@@ -60,6 +60,12 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=6.0,
                    help="oracle compute time per CPU-baseline measurement (four of them)")
+    p.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV",
+                                                          "CAL_WRITE_CSV"),
+                   help="CPU only: write the decode's HBM traffic per launch (profiles/"
+                        "decode_split_hbm_traffic.json) from rocprofv3 --pmc FETCH_SIZE and "
+                        "WRITE_SIZE counter_collection.csv files of a decode run and of a "
+                        "--copy-calibration run")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a 1 GiB device-to-device copy 3 times (the known-size "
                         "kernel used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -601,8 +607,61 @@ PROVENANCE = {
 }
 
 
+DECODE_KERNELS = ("qjl_project_kernel", "decode_split_kernel", "decode_merge_kernel")
+
+
+def traffic_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
+    """HBM bytes per kvq_decode_qjl_int8 launch from rocprofv3 counters:
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch, mean over the run's
+    dispatches of each decode kernel) summed over the launch's three kernels,
+    each scaled by known bytes / counter bytes of a 1 GiB device copy."""
+    import csv
+    from collections import defaultdict
+
+    def per_kernel(path, counter):
+        acc = defaultdict(list)
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+    def copy_scale(path, counter):
+        vals, _ = per_kernel(path, counter)
+        kib = [v for k, v in vals.items() if "copyBuffer" in k]
+        return (1 << 30) / 1024 / kib[0]
+
+    f, nf = per_kernel(fetch_csv, "FETCH_SIZE")
+    w, _ = per_kernel(write_csv, "WRITE_SIZE")
+    fs, ws = copy_scale(cal_fetch_csv, "FETCH_SIZE"), copy_scale(cal_write_csv, "WRITE_SIZE")
+    kernels = {}
+    for k in f:
+        if any(n in k for n in DECODE_KERNELS):
+            kernels[k] = {"fetch_kib": round(f[k], 1), "write_kib": round(w.get(k, 0.0), 1),
+                          "dispatches": nf[k]}
+    fk = sum(v["fetch_kib"] for v in kernels.values())
+    wk = sum(v["write_kib"] for v in kernels.values())
+    hbm = int(round(fk * 1024 * fs + wk * 1024 * ws))
+    G, T, d, m = 512, 32768, 128, 256
+    alg = G * T * (m // 8 + 2 + d + 4) + G * d * 2 + m * d * 2 + G * d * 4
+    out = {"source_sha": decode_source_hash(), "hbm_bytes_per_launch": hbm,
+           "alg_bytes_per_launch": alg, "traffic_over_alg": round(hbm / alg, 3),
+           "fetch_kib_per_launch": round(fk, 1), "write_kib_per_launch": round(wk, 1),
+           "fetch_scale": round(fs, 3), "write_scale": round(ws, 3), "kernels": kernels,
+           "how": "rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE (KiB per dispatch, mean over the "
+                  "bench's decode dispatches), each scaled by the ratio of a 1 GiB device copy's "
+                  "known bytes to the same counter (bench.py --traffic-summary)"}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out, indent=1))
+
+
 def main():
     args = parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
