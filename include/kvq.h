@@ -369,10 +369,13 @@ size_t kvq_decode_gqa_workspace_bytes(int64_t groups, int32_t nq, int64_t T, int
  * kvq_decode_qjl_int8_gqa - kvq_decode_qjl_int8 for grouped-query attention:
  * nq query heads share each group's compressed keys and values (the
  * Q-TensorFormer card, section 4, shares one KV head among several query
- * heads).  For every query j of group g the result is exactly what
- * kvq_decode_qjl_int8 computes for that query alone (same tolerance).  The
- * nq workgroups that read the same token range run on one XCD at about the
- * same time, so the range comes from HBM about once.
+ * heads).  Every query j of group g gets the decode of that query alone,
+ * within kvq_decode_qjl_int8's tolerance (nq = 1 is that call, bit for bit).
+ * For m = 256, d = 128 and nq >= 2 one workgroup per (group, token range)
+ * carries up to four of the group's queries through one pass over the range
+ * (byte tables of all four in LDS), so the cache is read once per four query
+ * heads; other shapes run one workgroup per query and range, numbered so
+ * that those sharing a range run on one XCD at about the same time.
  *
  * q    [groups, nq, d] (q_dt);  out [groups, nq, d] binary32, written
  * ws   device scratch of ws_bytes >= kvq_decode_gqa_workspace_bytes(groups,

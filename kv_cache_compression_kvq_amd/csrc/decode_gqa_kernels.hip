@@ -1,0 +1,392 @@
+// Grouped-query decode in one pass over the cache, for gfx950: nq query heads
+// share each KV head's compressed keys and values (the Q-TensorFormer model
+// card, section 4, shares a KV head among several query heads).  Per query
+// the step is the decode of one query over QJL-sketched keys (arXiv
+// 2406.03482, abstract: sign bits of a JL projection, scored against the
+// query's unquantized projection) and per-row INT8 values (symmetric INT8
+// formula of the same card, section 6):
+//   sigma_t = sqrt(pi/2)/m * n_t * sum_i (2 b_ti - 1) (S q)_i
+//   out     = sum_t softmax_t(lam * sigma_t) * s_t * c_t
+// Here one workgroup per (KV head, token range) reads the range once and
+// carries up to four of the head's queries through it: byte tables of all
+// four in LDS, four online softmaxes, four weighted value sums from each
+// value load.  Heads with more queries take one launch per four.
+//
+// Tables (m = 256: 32 tables of 256 binary32 entries per query): a 64 KiB
+// block holds two queries, row v (256 bytes) = entries T_p[v] of query a
+// (p = 0..31) then of query b.  Two lanes share a token: lane (r, h) =
+// (lane % 32, lane / 32) scores token r of the wave's 32 for query h of each
+// block.  Lane r visits the token's sign bytes in the order p = (r + i) mod
+// 32 (its words rotated once by r), so at step i the 32 lanes of a half read
+// 32 different entries of their rows: columns 32 h + p, one per LDS bank.  The
+// byte address 256 v + 128 h + 4 p is one byte permute of the token's byte v
+// and a per-lane constant byte (4 ((r + i) mod 32) + 128 h, eight registers
+// of them); the second block is the same address plus 64 KiB.
+//
+// Values: 32 rows of 128 codes per wave step, 16 codes per lane (lane = slot
+// 8 + sub: row 8 k + slot, codes 16 sub .. + 15 at load k); the softmax
+// weight times the value scale of each row comes from the scoring lanes by
+// ds_bpermute, once per query.  Partials (max, sum, o[d]) per (query, token
+// range) go to the same workspace layout as the one-query decode, whose
+// merge kernel finishes the step.
+#include "kvq_device.h"
+#include "kvq_launch.h"
+#include "kvq_qjl_device.h"
+
+#include <algorithm>
+#include <cmath>
+
+namespace kvq {
+
+constexpr int kGqaWaves = 8;
+constexpr int kGqaThreads = 64 * kGqaWaves;
+constexpr int kGqaChunk = 32;                            // tokens per wave step
+constexpr int kGqaBlockTokens = kGqaWaves * kGqaChunk;   // tokens per workgroup step
+constexpr int kGqaD = 128, kGqaM = 256;
+constexpr uint32_t kGqaBlockBytes = 65536;               // one table block (two queries)
+
+// Table block of queries a and b (y vectors of 256 values): row v, entry
+// 32 hq + p = T_p[v] of query hq, built from nibble partial sums like the
+// one-query tables (same additions, so the same binary32 entries).
+__device__ void build_pair_tables(const float* ya, const float* yb, float* blk) {
+  for (int task = threadIdx.x; task < 2 * 32 * 16; task += blockDim.x) {
+    const int hq = task >> 9;                  // query of the pair
+    const int p = task & 31;                   // table
+    const int a = (task >> 5) & 15;            // high nibble of v
+    const float* yp = (hq ? yb : ya) + 8 * p;
+    float lo[16];
+    lo[0] = -(((yp[0] + yp[1]) + yp[2]) + yp[3]);
+#pragma unroll
+    for (int b = 1; b < 16; ++b) {
+      const int low = b & (-b);
+      const int j = __builtin_ctz(low);
+      lo[b] = lo[b ^ low] + 2.0f * yp[j];
+    }
+    float hi = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hi += ((a >> j) & 1) ? yp[4 + j] : -yp[4 + j];
+#pragma unroll
+    for (int b = 0; b < 16; ++b) blk[(16 * a + b) * 64 + 32 * hq + p] = hi + lo[b];
+  }
+}
+
+// NB table blocks (2 NB query slots per launch).  yall: projected queries
+// [groups * nq_total][m]; this launch takes queries q_off .. q_off + nq_pass
+// - 1 of every group (nq_pass <= 2 NB; the other slots score zero tables and
+// are not written).
+template <int NB>
+__global__ __launch_bounds__(kGqaThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, int nq_pass,
+                       const uint32_t* __restrict__ kbits, const uint16_t* __restrict__ knorms,
+                       const int8_t* __restrict__ vcodes, const float* __restrict__ vscales,
+                       int64_t T, int64_t splits, int64_t tps, float lam, int64_t pairs,
+                       float* __restrict__ partials) {
+  constexpr int NQ = 2 * NB;
+  constexpr int D = kGqaD, M = kGqaM;
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  // tables first, at LDS address 0: the byte permute's result is the
+  // address itself (this kernel declares no static __shared__ data)
+  float* lut = reinterpret_cast<float*>(lds_raw);
+  float* y = reinterpret_cast<float*>(lds_raw + NB * kGqaBlockBytes);   // [NQ][M]
+  float* wpart = lut;                        // [waves][NQ][D + 2], after the last lookup
+
+  const int64_t p = blockIdx.x;
+  if (p >= pairs) return;
+  const int64_t g = p / splits;
+  const int64_t sp = p % splits;
+  const int64_t t_begin = sp * tps;
+  const int ntok = (int)(std::min<int64_t>(T, t_begin + tps) - t_begin);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 31;                   // token of the wave step (scoring)
+  const int h = lane >> 5;                   // query slot within each block
+  const int slot = lane >> 3;                // value row within each group of 8
+  const int sub = lane & 7;                  // 16-code chunk of the value row
+  const float c = kSqrtHalfPi / (float)M;
+  const int64_t row0 = g * T + t_begin;
+  const uint32_t* bblk = kbits + row0 * (M / 32);
+  const uint16_t* nblk = knorms + row0;
+  const int8_t* vblk = vcodes + row0 * D + sub * 16;
+  const float* sblk = vscales + row0;
+
+  struct Keys {
+    uint32_t wv[8];
+    uint16_t nb;
+    float vs;
+  };
+  struct Vals {
+    u32x4 vc[4];
+  };
+  auto load_keys = [&](Keys& kk, int base) {
+    const int tc = min(base + r, ntok - 1);
+    load_rot_words(bblk + tc * 8, r, kk.wv);
+    kk.nb = ld_stream(nblk + tc);
+    kk.vs = ld_stream(sblk + tc);
+  };
+  auto load_vals = [&](Vals& vv, int base) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int tv = min(base + 8 * k + slot, ntok - 1);
+      vv.vc[k] = ld_stream(reinterpret_cast<const u32x4*>(vblk + tv * D));
+    }
+  };
+
+  // per-lane address bytes: byte i of cs = 4 ((r + i) mod 32) + 128 h
+  uint32_t cs[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      v |= (uint32_t)(4 * ((r + 4 * w + b) & 31) + 128 * h) << (8 * b);
+    cs[w] = v;
+  }
+
+  float Mq[NQ], Lq[NQ], o[NQ][16];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    Mq[q] = -INFINITY;
+    Lq[q] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[q][e] = 0.0f;
+  }
+
+  // z of this lane's token for query h of each block (-inf past the range)
+  auto scores = [&](const Keys& kk, int base, float (&z)[NB]) {
+    uint32_t x[8];
+    rot_words(kk.wv, r, x);
+    float acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = 0.0f;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      float v[NB][16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int i = 16 * hf + k;
+        // byte 0: the lane's address byte of step i; byte 1: the token's
+        // byte; bytes 2, 3: zero
+        const uint32_t a = __builtin_amdgcn_perm(x[i >> 2], cs[i >> 2],
+                                                 0x0C0C0400u | (uint32_t)(i & 3) | ((uint32_t)(i & 3) << 8));
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          v[b][k] = *(lds_cfloat_ptr)(uintptr_t)(a + (uint32_t)b * kGqaBlockBytes);
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          s0 += v[b][k];
+          s1 += v[b][8 + k];
+        }
+        acc[b] += s0 + s1;
+      }
+    }
+    const bool valid = base + r < ntok;
+    const float n = (float)__builtin_bit_cast(_Float16, kk.nb);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) z[b] = valid ? lam * (c * n * acc[b]) : -INFINITY;
+  };
+
+  // online softmax of the wave step for every query, then the value sums;
+  // ws[b] = softmax weight x value scale of this lane's token, query 2 b + h
+  auto step = [&](const Keys& kk, const Vals& vv, int base) {
+    float z[NB];
+    scores(kk, base, z);
+    float ws[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      // max over the 32 tokens of each half (query 2 b + half)
+      uint32_t mlo, mhi;
+      halves_u32(__builtin_bit_cast(uint32_t, seg_max_f32<32>(z[b])), mlo, mhi);
+      const float mx0 = __builtin_bit_cast(float, mlo), mx1 = __builtin_bit_cast(float, mhi);
+      const float Mn0 = __builtin_fmaxf(Mq[2 * b], mx0), Mn1 = __builtin_fmaxf(Mq[2 * b + 1], mx1);
+      const float al0 = __expf(Mq[2 * b] - Mn0), al1 = __expf(Mq[2 * b + 1] - Mn1);
+      const float pz = __expf(z[b] - (h ? Mn1 : Mn0));
+      uint32_t slo, shi;
+      halves_u32(__builtin_bit_cast(uint32_t, seg_sum_f32<32>(pz)), slo, shi);
+      Lq[2 * b] = Lq[2 * b] * al0 + __builtin_bit_cast(float, slo);
+      Lq[2 * b + 1] = Lq[2 * b + 1] * al1 + __builtin_bit_cast(float, shi);
+      Mq[2 * b] = Mn0;
+      Mq[2 * b + 1] = Mn1;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        o[2 * b][e] *= al0;
+        o[2 * b + 1][e] *= al1;
+      }
+      ws[b] = pz * kk.vs;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int t = 8 * k + slot;             // value row of this load
+      float cv[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) cv[e] = i8_to_f32(vv.vc[k][e >> 2], e & 3);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int hq = 0; hq < 2; ++hq) {
+          const float w = __builtin_bit_cast(
+              float, __builtin_amdgcn_ds_bpermute((t + 32 * hq) << 2, __builtin_bit_cast(int, ws[b])));
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[2 * b + hq][e] = __builtin_fmaf(w, cv[e], o[2 * b + hq][e]);
+        }
+    }
+  };
+
+  // y of the launch's queries first (its wait leaves the first step's loads
+  // in flight); dummy query slots get zero tables
+  float yv[NQ / 2];
+#pragma unroll
+  for (int k = 0; k < NQ / 2; ++k) {
+    const int idx = (int)threadIdx.x + k * kGqaThreads;      // < NQ * M
+    const int q = idx / M;
+    const int qc = min(q, nq_pass - 1);
+    yv[k] = yall[(g * nq_total + q_off + qc) * M + (idx % M)];
+    if (q >= nq_pass) yv[k] = 0.0f;
+  }
+  const int first = wave * kGqaChunk;
+  Keys ka, kb;
+  Vals va, vb;
+  __builtin_amdgcn_sched_barrier(0);
+  load_keys(ka, first);
+  load_vals(va, first);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < NQ / 2; ++k) y[threadIdx.x + k * kGqaThreads] = yv[k];
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    build_pair_tables(y + 2 * b * M, y + (2 * b + 1) * M,
+                      reinterpret_cast<float*>(lds_raw + b * kGqaBlockBytes));
+  __syncthreads();
+  if (first < ntok) {
+    for (int base = first;; base += 2 * kGqaBlockTokens) {
+      const int nb1 = base + kGqaBlockTokens, nb2 = base + 2 * kGqaBlockTokens;
+      load_keys(kb, nb1);
+      step(ka, va, base);
+      load_vals(vb, nb1);
+      if (nb1 >= ntok) break;
+      load_keys(ka, nb2);
+      step(kb, vb, nb1);
+      load_vals(va, nb2);
+      if (nb2 >= ntok) break;
+    }
+  }
+
+  // merge the 8 value slots of the wave, then the waves of the workgroup
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float v = o[q][e];
+      v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x201F));  // lane ^ 8
+      v += swz_xor16_f32(v);
+      v += xor32_f32(v);
+      o[q][e] = v;
+    }
+  __syncthreads();                           // every lookup of the workgroup is done
+  float* wp = wpart + wave * NQ * (D + 2);
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    if (lane == 0) {
+      wp[q * (D + 2)] = Mq[q];
+      wp[q * (D + 2) + 1] = Lq[q];
+    }
+    if (slot == 0) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) wp[q * (D + 2) + 2 + sub * 16 + e] = o[q][e];
+    }
+  }
+  __syncthreads();
+  for (int q = 0; q < nq_pass; ++q) {
+    float Mw[kGqaWaves], Ms = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kGqaWaves; ++w) {
+      Mw[w] = wpart[(w * NQ + q) * (D + 2)];
+      Ms = __builtin_fmaxf(Ms, Mw[w]);
+    }
+    float sc[kGqaWaves];
+#pragma unroll
+    for (int w = 0; w < kGqaWaves; ++w) sc[w] = (Mw[w] == -INFINITY) ? 0.0f : __expf(Mw[w] - Ms);
+    float* out = partials + ((g * nq_total + q_off + q) * splits + sp) * (int64_t)(D + 2);
+    if (threadIdx.x == 0) {
+      float Ls = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kGqaWaves; ++w) Ls += sc[w] * wpart[(w * NQ + q) * (D + 2) + 1];
+      out[0] = Ms;
+      out[1] = Ls;
+    }
+    for (int j = threadIdx.x; j < D; j += kGqaThreads) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kGqaWaves; ++w)
+        if (sc[w] != 0.0f) acc += sc[w] * wpart[(w * NQ + q) * (D + 2) + 2 + j];
+      out[2 + j] = acc;
+    }
+  }
+}
+
+bool decode_gqa_supported(int m, int d, int nq) { return m == kGqaM && d == kGqaD && nq >= 2; }
+
+// Token split of the one-pass kernel: one workgroup per CU at a time (its
+// tables take 128 KiB of LDS), about two rounds of them, ranges a multiple
+// of the workgroup step.
+DecodeSplit decode_gqa_split(int64_t groups, int64_t T, const DeviceInfo& dev) {
+  DecodeSplit s;
+  const int64_t target_blocks = 2LL * std::max(1, dev.cus);
+  const int64_t max_splits = std::max<int64_t>(1, (T + kGqaBlockTokens - 1) / kGqaBlockTokens);
+  int64_t splits = std::min(max_splits, std::max<int64_t>(1, (target_blocks + groups - 1) / groups));
+  splits = std::max<int64_t>(splits, (T + (int64_t(1) << 20) - 1) >> 20);
+  int64_t tps = (T + splits - 1) / splits;
+  tps = (tps + kGqaBlockTokens - 1) / kGqaBlockTokens * kGqaBlockTokens;
+  s.tokens_per_split = tps;
+  s.splits = (T + tps - 1) / tps;
+  return s;
+}
+
+size_t decode_gqa_lds_bytes(int nb) {
+  const size_t tables = (size_t)nb * kGqaBlockBytes;
+  const size_t part = (size_t)kGqaWaves * 2 * nb * (kGqaD + 2) * sizeof(float);
+  return std::max(tables, part) + (size_t)2 * nb * kGqaM * sizeof(float);
+}
+
+hipError_t launch_decode_gqa_pass(const float* y, int64_t groups, int nq_total, int q_off,
+                                  int nq_pass, const uint32_t* kbits, const uint16_t* knorms,
+                                  const int8_t* vcodes, const float* vscales, int64_t T,
+                                  float lam, float* partials, const DecodeSplit& sp,
+                                  hipStream_t st) {
+  const int nb = nq_pass <= 2 ? 1 : 2;
+  const size_t lds = decode_gqa_lds_bytes(nb);
+  const int64_t max_groups = std::max<int64_t>(1, (int64_t(1) << 24) / sp.splits);
+  for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
+    const int64_t ng = std::min(max_groups, groups - g0);
+    const int64_t pairs = ng * sp.splits;
+    const float* yp = y + g0 * nq_total * kGqaM;
+    float* pp = partials + g0 * nq_total * sp.splits * (int64_t)(kGqaD + 2);
+    const uint32_t* kb = kbits + g0 * T * (kGqaM / 32);
+    const uint16_t* kn = knorms + g0 * T;
+    const int8_t* vc = vcodes + g0 * T * kGqaD;
+    const float* vs = vscales + g0 * T;
+    hipError_t e;
+    if (nb == 1) {
+      e = allow_dynamic_lds(decode_gqa_kernel<1>, lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(decode_gqa_kernel<1>, dim3((unsigned)pairs), dim3(kGqaThreads), lds, st,
+                         yp, nq_total, q_off, nq_pass, kb, kn, vc, vs, T, sp.splits,
+                         sp.tokens_per_split, lam, pairs, pp);
+    } else {
+      e = allow_dynamic_lds(decode_gqa_kernel<2>, lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(decode_gqa_kernel<2>, dim3((unsigned)pairs), dim3(kGqaThreads), lds, st,
+                         yp, nq_total, q_off, nq_pass, kb, kn, vc, vs, T, sp.splits,
+                         sp.tokens_per_split, lam, pairs, pp);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace kvq

@@ -351,9 +351,17 @@ static size_t decode_y_bytes(int64_t groups, int m) {
   return ((size_t)groups * (size_t)m * sizeof(float) + 255) / 256 * 256;
 }
 
+// Token split of a call: the one-pass grouped kernel's for several queries
+// per KV head where it applies, else the one-query kernel's over all queries.
+static DecodeSplit call_split(int64_t groups, int nq, int64_t T, int d, int m,
+                              const DeviceInfo& dev) {
+  return decode_gqa_supported(m, d, nq) ? decode_gqa_split(groups, T, dev)
+                                        : decode_split(groups * nq, T, dev);
+}
+
 size_t decode_workspace_bytes(int64_t groups, int nq, int64_t T, int d, int m,
                               const DeviceInfo& dev) {
-  const DecodeSplit s = decode_split(groups * nq, T, dev);
+  const DecodeSplit s = call_split(groups, nq, T, d, m, dev);
   return decode_y_bytes(groups * nq, m) +
          (size_t)groups * (size_t)nq * (size_t)s.splits * (size_t)(d + 2) * sizeof(float);
 }
@@ -398,7 +406,7 @@ static hipError_t decode_typed(const TQ* q, int64_t groups, int nq, const TS* S,
                                float* out, const DeviceInfo& dev, hipStream_t st) {
   // queries are numbered (group, head) = g nq + j throughout: y, partials, out
   const int64_t nqg = groups * nq;
-  const DecodeSplit sp = decode_split(nqg, T, dev);
+  const DecodeSplit sp = call_split(groups, nq, T, d, m, dev);
   float* y = static_cast<float*>(ws);
   float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + decode_y_bytes(nqg, m));
   const int64_t max_groups = int64_t(1) << 22;
@@ -409,8 +417,13 @@ static hipError_t decode_typed(const TQ* q, int64_t groups, int nq, const TS* S,
     hipError_t e1 = hipGetLastError();
     if (e1 != hipSuccess) return e1;
   }
-  hipError_t e;
-  if (decode_rotated(m, d))
+  hipError_t e = hipSuccess;
+  if (decode_gqa_supported(m, d, nq)) {
+    // one pass over each token range per four query heads
+    for (int q0 = 0; q0 < nq && e == hipSuccess; q0 += 4)
+      e = launch_decode_gqa_pass(y, groups, nq, q0, std::min(4, nq - q0), kbits, knorms, vcodes,
+                                 vscales, T, lam, partials, sp, st);
+  } else if (decode_rotated(m, d))
     e = decode_launch<8, 8>(y, groups, nq, m, kbits, knorms, vcodes, vscales, T, d, lam, partials, sp, st);
   else if (d == 64)
     e = decode_launch<0, 4>(y, groups, nq, m, kbits, knorms, vcodes, vscales, T, d, lam, partials, sp, st);

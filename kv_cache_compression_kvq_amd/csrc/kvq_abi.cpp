@@ -135,6 +135,9 @@ kvq_status decode_impl(const char* fn, const void* q, kvq_dtype q_dt, int64_t gr
     return fail(KVQ_ERR_WORKSPACE, "%s: workspace of %zu bytes at %p, need %zu", fn, ws_bytes, ws,
                 need);
   if (!aligned16(ws)) return fail(KVQ_ERR_ALIGN, "%s: ws is not 16-byte aligned", fn);
+  if (kvq::decode_gqa_supported(m, d, nq) && kvq::decode_gqa_lds_bytes(2) > dev.lds_per_block)
+    return fail(KVQ_ERR_SHAPE, "%s: the grouped decode needs %zu bytes of LDS, the device has %zu",
+                fn, kvq::decode_gqa_lds_bytes(2), dev.lds_per_block);
   if (kvq::decode_lds_bytes(m, d) > dev.lds_per_block)
     return fail(KVQ_ERR_SHAPE, "%s: m = %d, d = %d need %zu bytes of LDS, the device has %zu", fn,
                 (int)m, (int)d, kvq::decode_lds_bytes(m, d), dev.lds_per_block);

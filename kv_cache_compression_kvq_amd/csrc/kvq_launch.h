@@ -71,6 +71,17 @@ hipError_t launch_decode_qjl_int8(const void* q, int q_f16, int64_t groups, int 
                                   float sm_scale, void* ws, float* out, const DeviceInfo& dev,
                                   hipStream_t s);
 
+// One-pass grouped-query decode (decode_gqa_kernels.hip): m = 256, d = 128,
+// nq >= 2 query heads per KV head, up to four per launch.
+bool decode_gqa_supported(int m, int d, int nq);
+DecodeSplit decode_gqa_split(int64_t groups, int64_t T, const DeviceInfo& dev);
+size_t decode_gqa_lds_bytes(int nb);
+hipError_t launch_decode_gqa_pass(const float* y, int64_t groups, int nq_total, int q_off,
+                                  int nq_pass, const uint32_t* kbits, const uint16_t* knorms,
+                                  const int8_t* vcodes, const float* vscales, int64_t T,
+                                  float lam, float* partials, const DecodeSplit& sp,
+                                  hipStream_t st);
+
 // Device address of the allocation-free decode's scratch array on the
 // current device (kStaticScratchBytes bytes, 256-byte aligned; looked up
 // with hipGetSymbolAddress on the first call per device).

@@ -168,6 +168,32 @@ def test_decode_grouped_queries(G, nq, T, d, m):
     log(f"[decode-gqa] worst err / tol = {worst:.3g}")
 
 
+@pytest.mark.parametrize("G,nq,T,qscale", [(3, 2, 1000, 1.0), (2, 3, 2049, 1.0), (2, 4, 8191, 1.0),
+                                           (1, 5, 3000, 1.0), (2, 6, 700, 1.0), (300, 4, 513, 1.0),
+                                           (1, 4, 70001, 1.0), (4, 4, 4096, 8.0), (5, 7, 1, 1.0)])
+def test_decode_grouped_one_pass(G, nq, T, qscale):
+    """d = 128, m = 256: one pass over each token range carries up to four
+    query heads (three: one zero-table slot; five to seven: a pass of four and
+    one of the rest); every query is checked against the oracle's one-query
+    decode.  qscale > 1 makes the softmax peaky (a few tokens carry it)."""
+    rng = np.random.default_rng(G * 1000 + nq * 100 + T % 97)
+    d, m = 128, 256
+    k = rng.standard_normal((G, T, d)).astype(np.float16)
+    v = rng.standard_normal((G, T, d)).astype(np.float16)
+    S = rng.standard_normal((m, d)).astype(np.float16)
+    kw, kn, vc, vs = make_cache(k, v, S)
+    q = (rng.standard_normal((G, nq, d)) * qscale).astype(np.float16)
+    lam = 1 / math.sqrt(d)
+    log(f"[decode-gqa1] G={G} nq={nq} T={T} qscale={qscale}")
+    out = down(K.decode_qjl_int8_gqa(up(q), up(S), up(kw), up(kn), up(vc), up(vs), lam))
+    worst = 0.0
+    for j in range(nq):
+        qj = np.ascontiguousarray(q[:, j])
+        ora = OD.decode_qjl_int8(qj, S, kw, kn, vc, vs, lam)
+        worst = max(worst, decode_tolerance_check(out[:, j], qj, S, kw, kn, vc, vs, lam, ora))
+    log(f"[decode-gqa1] worst err / tol = {worst:.3g}")
+
+
 def test_decode_grouped_single_query_equals_plain_decode():
     """nq = 1 through the grouped entry point is the plain decode, bit for bit."""
     rng = np.random.default_rng(77)

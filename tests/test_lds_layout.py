@@ -16,7 +16,8 @@ import pytest
 from kv_cache_compression_kvq_amd import _lib as L
 
 LLVM = "/opt/rocm/llvm/bin"
-ADDRESS_ZERO_KERNELS = ("decode_split_kernel", "scores_qjl_kernel", "scores_residual_kernel")
+ADDRESS_ZERO_KERNELS = ("decode_split_kernel", "scores_qjl_kernel", "scores_residual_kernel",
+                        "decode_gqa_kernel")
 
 
 def _tool(name):
