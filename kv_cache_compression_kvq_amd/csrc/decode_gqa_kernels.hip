@@ -357,12 +357,13 @@ hipError_t launch_decode_gqa_pass(const float* y, int64_t groups, int nq_total, 
                                   const int8_t* vcodes, const float* vscales, int64_t T,
                                   float lam, float* partials, const DecodeSplit& sp,
                                   hipStream_t st) {
-  const int nb = nq_pass <= 2 ? 1 : 2;
+  if (nq_pass < 1 || nq_pass > 4 || q_off + nq_pass > nq_total) return hipErrorInvalidValue;
+  const int nb = nq_pass <= 2 ? 1 : 2;   // table blocks of the launch
   const size_t lds = decode_gqa_lds_bytes(nb);
   const int64_t max_groups = std::max<int64_t>(1, (int64_t(1) << 24) / sp.splits);
   for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
-    const int64_t ng = std::min(max_groups, groups - g0);
-    const int64_t pairs = ng * sp.splits;
+    const int64_t gn = std::min(max_groups, groups - g0);
+    const int64_t pairs = gn * sp.splits;
     const float* yp = y + g0 * nq_total * kGqaM;
     float* pp = partials + g0 * nq_total * sp.splits * (int64_t)(kGqaD + 2);
     const uint32_t* kb = kbits + g0 * T * (kGqaM / 32);
