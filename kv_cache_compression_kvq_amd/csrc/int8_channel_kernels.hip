@@ -17,6 +17,9 @@
 //      writes the scales directly and pass 2 is skipped);
 //   2. per (group, channel): the max over the slabs' partials, the scale;
 //   3. per (group, slab): the codes (the keys are read a second time).
+// Heads of at most kChResMaxT tokens take one launch instead: a workgroup
+// per (group, 32-byte column of the rows) holds its column of every token
+// in registers, so the keys are read once (channel_quantize_resident_kernel).
 // Dequantize is a flat stream; the score folds the channel scales into the
 // query (q_c s_c, one binary32 product) inside the INT8 score kernel.
 #include "kvq_device.h"
@@ -138,6 +141,44 @@ __device__ __forceinline__ uint32_t channel_code(float x, float sdiv, float r, b
   return (uint32_t)(int)__builtin_amdgcn_fmed3f(c, -128.0f, 127.0f) & 0xFFu;
 }
 
+// Codes of one 16-byte chunk of a row (N channels).
+template <typename T, int N = ChChunk<T>::N>
+__device__ __forceinline__ typename ChChunk<T>::Codes channel_codes(const typename ChChunk<T>::V& v,
+                                                                   const float (&sd)[N],
+                                                                   const float (&rc)[N],
+                                                                   const bool (&dv)[N]) {
+  typename ChChunk<T>::Codes out;
+  if constexpr (N == 4) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w |= channel_code(v[e], sd[e], rc[e], dv[e]) << (8 * e);
+    out = w;
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w |= channel_code((float)v[4 * h + e], sd[4 * h + e], rc[4 * h + e], dv[4 * h + e]) << (8 * e);
+      out[h] = w;
+    }
+  }
+  return out;
+}
+
+// Divisors of N consecutive channels from their scales: a zero scale
+// divides by 1; reciprocals outside [2^-120, 2^120] are not trusted.
+template <int N>
+__device__ __forceinline__ void channel_divisors(const float* s, float (&sd)[N], float (&rc)[N],
+                                                 bool (&dv)[N]) {
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    sd[e] = (s[e] == 0.0f) ? 1.0f : s[e];
+    rc[e] = __builtin_amdgcn_rcpf(sd[e]);
+    dv[e] = !(sd[e] >= 0x1p-120f && sd[e] <= 0x1p120f);
+  }
+}
+
 // Pass 3: codes of one slab.
 template <typename T>
 __global__ __launch_bounds__(kChThreads) void channel_quantize_kernel(
@@ -154,33 +195,9 @@ __global__ __launch_bounds__(kChThreads) void channel_quantize_kernel(
   int8_t* cg = codes + (g * Ttok + t0) * d;
   const float* sg = scales + g * d;
   auto encode = [&](const typename C::V& v, const float (&sd)[N], const float (&rc)[N],
-                    const bool (&dv)[N]) {
-    typename C::Codes out;
-    if constexpr (N == 4) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w |= channel_code(v[e], sd[e], rc[e], dv[e]) << (8 * e);
-      out = w;
-    } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w |= channel_code((float)v[4 * h + e], sd[4 * h + e], rc[4 * h + e], dv[4 * h + e]) << (8 * e);
-        out[h] = w;
-      }
-    }
-    return out;
-  };
+                    const bool (&dv)[N]) { return channel_codes<T>(v, sd, rc, dv); };
   auto divisors = [&](int chunk, float (&sd)[N], float (&rc)[N], bool (&dv)[N]) {
-#pragma unroll
-    for (int e = 0; e < N; ++e) {
-      const float s = sg[chunk * N + e];
-      sd[e] = (s == 0.0f) ? 1.0f : s;
-      rc[e] = __builtin_amdgcn_rcpf(sd[e]);
-      dv[e] = !(sd[e] >= 0x1p-120f && sd[e] <= 0x1p120f);
-    }
+    channel_divisors<N>(sg + chunk * N, sd, rc, dv);
   };
   if (kChThreads % cpr == 0) {
     const int chunk = threadIdx.x % cpr;
@@ -214,9 +231,118 @@ __global__ __launch_bounds__(kChThreads) void channel_quantize_kernel(
   }
 }
 
+// One launch for heads of at most kChResMaxT tokens.  Workgroup (g, col)
+// owns 16-byte chunks 2 col and 2 col + 1 of every row of group g: lane l of
+// wave w takes chunk 2 col + l / 32 of rows 256 u + 32 w + l % 32, R rows
+// per lane, all in registers.  The column maxima (a 32-lane max per chunk,
+// then over the 8 waves in LDS) give the scales, and the codes are encoded
+// from the same registers.  Rows past the head's end re-read its last row
+// (the max is unchanged) and are not stored.  When the group count is a
+// multiple of 8 the workgroups of one group are placed on one XCD
+// (workgroups go to XCDs round-robin), so a key line shared by several of
+// them is fetched into that XCD's L2 once.
+constexpr int kChResThreads = 512;
+constexpr int kChResRows = kChResThreads / 2;    // rows per load step
+constexpr int kChResMaxT = 16 * kChResRows;
+
+template <typename T, int R>
+__global__ __launch_bounds__(kChResThreads) void channel_quantize_resident_kernel(
+    const T* __restrict__ x, int64_t groups, int64_t Ttok, int d, int8_t* __restrict__ codes,
+    float* __restrict__ scales) {
+  using C = ChChunk<T>;
+  constexpr int N = C::N;
+  __shared__ uint32_t wmax[kChResThreads / 64][2][N];
+  __shared__ float wsc[2][N];
+  const int nc = d / (2 * N);                      // workgroups per group
+  const int64_t b = blockIdx.x;
+  int64_t g;
+  int col;
+  if ((groups & 7) == 0) {
+    const int64_t j = b >> 3;
+    col = (int)(j % nc);
+    g = (j / nc) * 8 + (b & 7);
+  } else {
+    col = (int)(b % nc);
+    g = b / nc;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5;
+  const int chunk = 2 * col + h;
+  const int row0 = wave * 32 + (lane & 31);
+  const int last = (int)Ttok - 1;
+  const T* xg = x + g * Ttok * d + chunk * N;
+  typename C::V v[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int r = min(u * kChResRows + row0, last);
+    v[u] = *reinterpret_cast<const typename C::V*>(xg + (int64_t)r * d);
+  }
+  uint32_t mx[N];
+#pragma unroll
+  for (int e = 0; e < N; ++e) mx[e] = 0;
+#pragma unroll
+  for (int u = 0; u < R; ++u)
+#pragma unroll
+    for (int e = 0; e < N; ++e) mx[e] = max(mx[e], abs_bits((float)v[u][e]));
+#pragma unroll
+  for (int e = 0; e < N; ++e) mx[e] = seg_max_u32<32>(mx[e]);
+  if ((lane & 31) == 0) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) wmax[wave][h][e] = mx[e];
+  }
+  __syncthreads();
+  if (threadIdx.x < 2 * N) {
+    const int hh = threadIdx.x / N, e = threadIdx.x % N;
+    uint32_t a = 0;
+#pragma unroll
+    for (int w = 0; w < kChResThreads / 64; ++w) a = max(a, wmax[w][hh][e]);
+    const float sc = __builtin_bit_cast(float, a) / 127.0f;
+    wsc[hh][e] = sc;
+    scales[g * d + (2 * col + hh) * N + e] = sc;
+  }
+  __syncthreads();
+  float sd[N], rc[N];
+  bool dv[N];
+  channel_divisors<N>(wsc[h], sd, rc, dv);
+  int8_t* cg = codes + g * Ttok * d + chunk * N;
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int r = u * kChResRows + row0;
+    const typename C::Codes cw = channel_codes<T>(v[u], sd, rc, dv);
+    if (r <= last) *reinterpret_cast<typename C::Codes*>(cg + (int64_t)r * d) = cw;
+  }
+}
+
+template <typename T, int R>
+static hipError_t quantize_channel_resident(const T* x, int64_t groups, int64_t Ttok, int d,
+                                            int8_t* codes, float* scales, hipStream_t st) {
+  const int nc = d / (2 * ChChunk<T>::N);
+  // slices of whole groups, a multiple of 8 of them, so grid.x stays far
+  // below 2^32 and the XCD placement holds within each slice
+  const int64_t max_groups = std::max<int64_t>(8, ((int64_t(1) << 22) / nc) & ~int64_t(7));
+  for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
+    const int64_t ng = std::min(max_groups, groups - g0);
+    hipLaunchKernelGGL((channel_quantize_resident_kernel<T, R>), dim3((unsigned)(ng * nc)),
+                       dim3(kChResThreads), 0, st, x + g0 * Ttok * d, ng, Ttok, d,
+                       codes + g0 * Ttok * d, scales + g0 * d);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <typename T>
 static hipError_t quantize_channel_typed(const T* x, int64_t groups, int64_t Ttok, int d,
                                          int8_t* codes, float* scales, hipStream_t st) {
+  static_assert(kChResThreads / 64 == 8 && kChResRows == 256, "row schedule of the resident kernel");
+  if (Ttok <= kChResRows * 2)
+    return quantize_channel_resident<T, 2>(x, groups, Ttok, d, codes, scales, st);
+  if (Ttok <= kChResRows * 4)
+    return quantize_channel_resident<T, 4>(x, groups, Ttok, d, codes, scales, st);
+  if (Ttok <= kChResRows * 8)
+    return quantize_channel_resident<T, 8>(x, groups, Ttok, d, codes, scales, st);
+  if (Ttok <= kChResMaxT)
+    return quantize_channel_resident<T, 16>(x, groups, Ttok, d, codes, scales, st);
   const int64_t nslab = (Ttok + kChSlab - 1) / kChSlab;
   const size_t lds = (size_t)d * sizeof(uint32_t);
   // launch in slices of whole groups so grid.x stays far below 2^32

@@ -65,6 +65,24 @@ def test_shapes_and_ragged_token_counts(dtype, d):
         roundtrip_check(x, f"{dtype} d={d} T={T}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("G", [8, 9])
+def test_one_launch_token_limits(dtype, G):
+    """Token counts around the one-launch kernel's register schedule (256
+    tokens per load step, 2 to 16 steps, at most 4096 tokens) and just past
+    it, where the slab passes take over; G = 8 places a group's workgroups
+    on one XCD, G = 9 does not."""
+    rng = np.random.default_rng(G * 7 + len(dtype))
+    for T in (2, 512, 513, 1024, 1025, 2048, 2049, 4095, 4096, 4097):
+        d = 128 if T > 1024 else 48
+        x = rng.standard_normal((G, T, d)).astype(np.float32)
+        x *= np.exp(rng.uniform(-4, 4, (G, 1, d))).astype(np.float32)
+        x[:, rng.integers(0, T), :] *= 50.0            # one loud token per group
+        if dtype == "f16":
+            x = np.clip(x, -6e4, 6e4).astype(np.float16)
+        roundtrip_check(x, f"{dtype} G={G} T={T} d={d}")
+
+
 def test_many_slabs():
     """T = 5000 (40 slabs of 128 tokens) for 5 groups, fp32 and fp16."""
     rng = np.random.default_rng(50)
