@@ -561,6 +561,244 @@ __global__ __launch_bounds__(256) void scores_int8_d128_kernel(const TQ* __restr
   }
 }
 
+// Scale-folded INT8 score on the matrix cores, d = 128, several queries per
+// group (grouped-query attention shares a head's codes among its queries):
+// v_mfma_f32_16x16x32_f16 with 16 tokens' codes as the A operand (int8 ->
+// binary16 is exact: bytes b ^ 0x80 placed under the exponent of 1024 by a
+// byte permute, minus 1152 in one packed fp16 add) and the queries as the B
+// operand's columns.  fp16 x int8 products are exact in binary32; the
+// accumulation is binary32 (in the matrix core's order).  fp32 queries, and
+// per-channel queries q_c s_c, are scaled per query by a power of two (max
+// |v| into [2^14, 2^15)) and split into binary16 hi + lo (hi: the value with
+// its 13 low significand bits cleared; lo: the remainder rounded toward
+// zero, within 2^-20 relative of the scaled value): columns j and j + 8 of
+// the same multiply, summed afterwards, then unscaled exactly.  A wave loads
+// a 16-token tile as whole rows (each instruction reads 8 rows, 1 KiB
+// contiguous: loading the A fragments directly would read 16 half-rows per
+// instruction, measured 18 % slower) and reshapes it through its own 2 KiB
+// of LDS; lane (n, kq) = (lane % 16, lane / 16) then holds channels
+// 32 ks + 8 kq .. + 7 of token n at K-step ks, and the queries' fragments use
+// the same channel order.  The result of token 4 kq + i, query column n is in
+// accumulator i of lane (n, kq).
+constexpr int kMfmaTiles = 4;                                   // 16-token tiles per wave pass
+constexpr int kMfmaStep = 4 * 16 * kMfmaTiles;                  // tokens per block pass (4 waves)
+constexpr int kMfmaMaxNq = 8;                                   // split query columns: 8 + 8
+constexpr int64_t kMfmaMaxT = int64_t(1) << 23;                 // 32-bit token offsets
+
+template <typename TQ, bool CH, int ITERS>
+__global__ __launch_bounds__(256) void scores_int8_mfma_kernel(const TQ* __restrict__ q, int nq,
+                                                               const int8_t* __restrict__ codes,
+                                                               const float* __restrict__ scales,
+                                                               int T, int64_t tiles,
+                                                               float* __restrict__ scores) {
+  constexpr int D = 128;
+  constexpr bool SPLIT = CH || sizeof(TQ) == 4;
+  __shared__ __align__(16) float qs[16 * D];
+  __shared__ float qexp[16];
+  // per wave: one 16-token tile of codes (2 KiB), row r at 128 r, its
+  // 16-byte chunk c at 16 (c ^ ((r / 2) mod 8)): the row writes and the
+  // fragment reads below each touch 64 different banks per 32 lanes
+  __shared__ __align__(16) uint32_t tileb[4][16 * D / 4];
+  const int64_t g = blockIdx.x / tiles;
+  const int tile = (int)(blockIdx.x % tiles);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n = lane & 15;
+  const int kq = lane >> 4;
+  // per-group bases; token offsets inside a group are 32-bit (T * 128 < 2^31)
+  const int8_t* cg = codes + g * (int64_t)T * D + 16 * (lane & 7);
+  const float* sg = scales + g * (int64_t)T;
+  const int tw = tile * (ITERS * kMfmaStep) + wave * (16 * kMfmaTiles);
+  struct Batch {
+    u32x4 c[kMfmaTiles][2];
+    float s;                                   // scale of token `lane` of the pass
+  };
+  // unconditional loads (tokens past T re-read token T - 1, not stored)
+  auto load = [&](Batch& B, int it) {
+    const int tb = tw + it * kMfmaStep;
+#pragma unroll
+    for (int u = 0; u < kMfmaTiles; ++u)
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        // whole rows: 8 tokens x 128 B (1 KiB contiguous) per instruction
+        const int tr = min(tb + 16 * u + 8 * a + (lane >> 3), T - 1);
+        B.c[u][a] = ld_stream(reinterpret_cast<const u32x4*>(cg + tr * D));
+      }
+    if constexpr (!CH) B.s = sg[min(tb + lane, T - 1)];
+  };
+  Batch ba, bb;
+  load(ba, 0);
+
+  // queries (times the channel scales) in LDS as binary32, then each split
+  // query's power-of-two exponent
+  const TQ* qg = q + g * nq * D;
+  for (int i = threadIdx.x; i < 16 * D; i += 256) {
+    const int j = i / D, c = i % D;
+    float v = 0.0f;
+    if (j < nq) {
+      v = to_f32(qg[j * D + c]);
+      if constexpr (CH) v = v * scales[g * D + c];
+    }
+    qs[i] = v;
+  }
+  __syncthreads();
+  if constexpr (SPLIT) {
+    if (threadIdx.x < kMfmaMaxNq) {
+      uint32_t mx = 0;
+      for (int c = 0; c < D; ++c) mx = max(mx, abs_bits(qs[threadIdx.x * D + c]));
+      // scale 2^(14 - e) with e the exponent of the largest magnitude
+      const int e = mx == 0 ? 0 : (int)((mx >> 23) & 0xFF) - 127;
+      qexp[threadIdx.x] = __builtin_ldexpf(1.0f, min(14 - e, 126));
+    }
+    __syncthreads();
+  }
+  // B fragments: column n, K-step ks, element e = channel 32 ks + 8 kq + e
+  f16x8 bq[4];
+  {
+    const int j = SPLIT ? (n & 7) : n;
+    const bool lo = SPLIT && n >= 8;
+    const float sc = SPLIT ? qexp[j] : 1.0f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = qs[j * D + 32 * ks + 8 * kq + e] * sc;
+        if constexpr (SPLIT) {
+          const float hi = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & 0xFFFFE000u);
+          const auto pk = __builtin_amdgcn_cvt_pkrtz(lo ? v - hi : hi, 0.0f);
+          bq[ks][e] = pk[0];
+        } else {
+          bq[ks][e] = (_Float16)v;
+        }
+      }
+  }
+  float unscale = 1.0f;
+  if constexpr (SPLIT) unscale = 1.0f / qexp[n & 7];      // exact: a power of two
+  const int jq = SPLIT ? (n & 7) : n;                     // query of this lane's column
+  const bool writer = SPLIT ? (n < 8 && n < nq) : (n < nq);
+  float* og = scores + (g * nq + (writer ? jq : 0)) * (int64_t)T;
+  // whole 16-byte runs of 4 tokens when every query row starts 16-byte aligned
+  const bool vec_out = (T & 3) == 0;
+
+  // 8 codes (two words) -> 8 binary16 values
+  auto codes_f16 = [](uint32_t w0, uint32_t w1) {
+    const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
+    f16x8 r;
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    uint32_t p[4];
+    p[0] = __builtin_amdgcn_perm(0x64646464u, x0, 0x07010700u);   // bytes: b0, 0x64, b1, 0x64
+    p[1] = __builtin_amdgcn_perm(0x64646464u, x0, 0x07030702u);
+    p[2] = __builtin_amdgcn_perm(0x64646464u, x1, 0x07010700u);
+    p[3] = __builtin_amdgcn_perm(0x64646464u, x1, 0x07030702u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const h2 v = __builtin_bit_cast(h2, p[i]) + bias;
+      r[2 * i] = v[0];
+      r[2 * i + 1] = v[1];
+    }
+    return r;
+  };
+  uint32_t* tl = tileb[wave];
+  // this lane's row writes (row 8 a + lane / 8, chunk lane % 8) and fragment
+  // reads (row n, bytes [32 ks + 8 kq, + 8)), as dword offsets
+  uint32_t woff[2], roff[4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int r = 8 * a + (lane >> 3);
+    woff[a] = 32 * r + 4 * ((lane & 7) ^ ((r >> 1) & 7));
+  }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int c = 2 * ks + (kq >> 1);
+    roff[ks] = 32 * n + 4 * (c ^ ((n >> 1) & 7)) + 2 * (kq & 1);
+  }
+  auto score = [&](const Batch& B, int it) {
+    const int tb = tw + it * kMfmaStep;
+#pragma unroll
+    for (int u = 0; u < kMfmaTiles; ++u) {
+      // rows -> LDS -> A fragments (the wave's own tile; LDS operations of
+      // one wave complete in order, the asm statements keep the compiler
+      // from moving the reads above the writes or the next writes above
+      // the reads)
+      __asm__ volatile("" ::: "memory");
+#pragma unroll
+      for (int a = 0; a < 2; ++a) *reinterpret_cast<u32x4*>(tl + woff[a]) = B.c[u][a];
+      __asm__ volatile("" ::: "memory");
+      u32x2 cw[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) cw[ks] = *reinterpret_cast<const u32x2*>(tl + roff[ks]);
+      __asm__ volatile("" ::: "memory");
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const f16x8 a = codes_f16(cw[ks][0], cw[ks][1]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[ks], acc, 0, 0, 0);
+      }
+      const int t0 = tb + 16 * u + 4 * kq;
+      f32x4 out;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = acc[i];
+        if constexpr (SPLIT) {
+          // the lo column's partial sum (lane n + 8) added to the hi one
+          v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x201F));
+          v *= unscale;
+        }
+        if constexpr (!CH) {
+          // token 16 u + 4 kq + i's scale from the lane that loaded it
+          v *= __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((16 * u + 4 * kq + i) << 2,
+                                                                      __builtin_bit_cast(int, B.s)));
+        }
+        out[i] = v;
+      }
+      if (writer) {
+        if (vec_out && t0 + 3 < T) {
+          *reinterpret_cast<f32x4*>(og + t0) = out;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (t0 + i < T) og[t0 + i] = out[i];
+        }
+      }
+    }
+  };
+#pragma unroll
+  for (int it = 0; it < ITERS; it += 2) {
+    if (it + 1 < ITERS) load(bb, it + 1);
+    score(ba, it);
+    if (it + 2 < ITERS) load(ba, it + 2);
+    if (it + 1 < ITERS) score(bb, it + 1);
+  }
+}
+
+template <typename TQ, bool CH, int ITERS>
+static hipError_t scores_mfma_launch_it(const TQ* q, int64_t groups, int nq, const int8_t* codes,
+                                        const float* scales, int64_t T, float* scores,
+                                        hipStream_t s) {
+  const int64_t tiles = (T + ITERS * kMfmaStep - 1) / (ITERS * kMfmaStep);
+  const int64_t max_groups = std::max<int64_t>(1, (int64_t(1) << 22) / tiles);
+  for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
+    const int64_t ng = std::min(max_groups, groups - g0);
+    hipLaunchKernelGGL((scores_int8_mfma_kernel<TQ, CH, ITERS>), dim3((unsigned)(ng * tiles)),
+                       dim3(256), 0, s, q + g0 * nq * 128, nq, codes + g0 * T * 128,
+                       scales + g0 * (CH ? 128 : T), (int)T, tiles, scores + g0 * nq * T);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename TQ, bool CH>
+static hipError_t scores_mfma_launch(const TQ* q, int64_t groups, int nq, const int8_t* codes,
+                                     const float* scales, int64_t T, float* scores,
+                                     hipStream_t s) {
+  const int64_t rows = groups * T;
+  if (rows >= 1024LL * 4 * kMfmaStep)
+    return scores_mfma_launch_it<TQ, CH, 4>(q, groups, nq, codes, scales, T, scores, s);
+  return scores_mfma_launch_it<TQ, CH, 1>(q, groups, nq, codes, scales, T, scores, s);
+}
+
 template <typename TQ, bool CH, int ITERS>
 static hipError_t scores_d128_launch_it(const TQ* q, int64_t groups, int nq, const int8_t* codes,
                                         const float* scales, int64_t T, float* scores,
@@ -607,6 +845,8 @@ template <typename TQ>
 static hipError_t scores_dispatch(const TQ* q, int64_t groups, int nq, const int8_t* codes,
                                   const float* scales, int64_t T, int d, float* scores,
                                   hipStream_t s) {
+  if (d == 128 && nq >= 2 && nq <= (sizeof(TQ) == 2 ? 16 : kMfmaMaxNq) && T <= kMfmaMaxT)
+    return scores_mfma_launch<TQ, false>(q, groups, nq, codes, scales, T, scores, s);
   if (d == 128 && nq <= 4) return scores_d128_launch<TQ, false>(q, groups, nq, codes, scales, T, scores, s);
   const int64_t tiles = (T + kScoreTokensPerBlock - 1) / kScoreTokensPerBlock;
   // launch in slices of whole groups so grid.x stays far below 2^32
@@ -633,6 +873,8 @@ template <typename TQ>
 static hipError_t scores_channel_dispatch(const TQ* q, int64_t groups, int nq, const int8_t* codes,
                                           const float* scales, int64_t T, int d, float* scores,
                                           hipStream_t s) {
+  if (d == 128 && nq >= 2 && nq <= kMfmaMaxNq && T <= kMfmaMaxT)
+    return scores_mfma_launch<TQ, true>(q, groups, nq, codes, scales, T, scores, s);
   if (d == 128 && nq <= 4) return scores_d128_launch<TQ, true>(q, groups, nq, codes, scales, T, scores, s);
   const int64_t tiles = (T + kScoreTokensPerBlock - 1) / kScoreTokensPerBlock;
   const int64_t max_groups = std::max<int64_t>(1, (int64_t(1) << 22) / tiles);

@@ -177,6 +177,25 @@ def test_scores_shapes(qdt, nq, T, d):
     assert_int8_scores(sc, q, codes, scales, O.scores_int8(q, codes, scales))
 
 
+@pytest.mark.parametrize("qdt", ["f32", "f16"])
+@pytest.mark.parametrize("nq", [2, 3, 5, 8, 9, 16])
+def test_scores_grouped_queries_matrix_cores(qdt, nq):
+    """d = 128 with 2 .. 16 queries per group (the matrix-core score: fp16
+    queries as 16 columns, fp32 queries split hi / lo into 8 + 8 columns,
+    so fp32 with 9 and 16 queries takes the vector-ALU kernel), ragged
+    token counts on both sides of the 256- and 1024-token block steps."""
+    rng = np.random.default_rng(nq * 17 + len(qdt))
+    for G, T in ((3, 1), (2, 17), (3, 255), (2, 1025), (5, 4099)):
+        x = rng.standard_normal((G * T, 128)).astype(np.float32)
+        x *= np.exp(rng.uniform(-3, 3, (G * T, 1))).astype(np.float32)
+        codes, scales = O.quantize_int8(x)
+        codes, scales = codes.reshape(G, T, 128), scales.reshape(G, T)
+        q = rng.standard_normal((G, nq, 128)) * np.exp(rng.uniform(-4, 4, (G, nq, 1)))
+        q = q.astype(np.float16 if qdt == "f16" else np.float32)
+        sc = down(K.scores_int8(up(q), up(codes), up(scales)))
+        assert_int8_scores(sc, q, codes, scales, O.scores_int8(q, codes, scales))
+
+
 @pytest.mark.parametrize("nq", [1, 4])
 def test_scores_long_cache_every_score(nq):
     """32 heads x 262144 tokens x 128 (the bench's long-cache launch: 2 or 8

@@ -122,6 +122,20 @@ def test_scores_shapes(qdt, nq, T, d):
     scores_check(q, codes, scales, f"{qdt} nq={nq} T={T} d={d}")
 
 
+@pytest.mark.parametrize("qdt", ["f16", "f32"])
+@pytest.mark.parametrize("nq", [2, 4, 8])
+def test_scores_grouped_queries_matrix_cores(qdt, nq):
+    """d = 128, 2 .. 8 queries per group: the matrix-core score with the
+    per-channel products q_c s_c split hi / lo, channel scales spanning
+    many binades."""
+    rng = np.random.default_rng(nq * 5 + len(qdt))
+    for G, T in ((2, 3), (3, 300), (2, 5000)):
+        x = (rng.standard_normal((G, T, 128)) * np.exp(rng.uniform(-8, 8, (G, 1, 128)))).astype(np.float32)
+        codes, scales = OC.quantize_int8_channel(x)
+        q = rng.standard_normal((G, nq, 128)).astype(np.float16 if qdt == "f16" else np.float32)
+        scores_check(q, codes, scales, f"{qdt} nq={nq} T={T} d=128")
+
+
 def test_empty_inputs_are_noops():
     x = torch.empty((2, 0, 128), dtype=torch.float16, device="cuda")
     codes, scales = K.quantize_int8_channel(x)
