@@ -486,7 +486,7 @@ def cpu_model() -> str:
 
 def cpu_threads() -> int:
     """Host threads the oracle may use: the process's CPU affinity, capped at
-    16 (the host share of one GPU on a GPU machine)."""
+    16 (the host cores set aside per GPU on a one-GPU MI355X host)."""
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
