@@ -14,13 +14,18 @@ Steps are launched back to back and timed as a block (wall clock, with HIP
 events at its two ends only).  Throughput is scores per second (query-token
 pairs scored per step / time).
 
-Also reported (``components``): HBM GB/s of quantize / dequantize on the
-element-count sweep (2^28 and 2^30 fp32), the Llama-7B-layer INT8 path, and
-the QJL-cache sketch and score, each timed with HIP events on the stream the
-kernels run on.  ``cpu_baseline`` times the fp64 oracle on a bounded sample
-of the same decode workload.
+Also reported (``components``, sections copy / sweep / llama / qjl /
+residual / gqa): HBM GB/s and roofline fractions of INT8 and INT4 quantize /
+dequantize on the element-count sweep (2^28 and 2^30 fp32), the Llama-7B
+layer (INT8, INT4, per-channel INT8, scores; also as HIP-graph replays), the
+QJL-cache sketch and scores with their HBM stream references, the two-stage
+compress and scores, and the grouped-query decode, each timed with HIP
+events on the stream the kernels run on.  ``cpu_baseline`` times the fp64
+oracle on bounded samples (the decode on one thread and on every thread,
+the INT8 quantizer on the 2^28 sweep).
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 1000] [--no-components]
+                    [--only SECTIONS] [--no-cpu-baseline]
 
 The default warm-up (1000 steps, ~0.45 s) brings the GPU's clocks up after
 the seconds of host-side input generation before the timed region: with 3
