@@ -9,8 +9,9 @@
 //   out     = sum_t softmax_t(lam * sigma_t) * s_t * c_t
 // Here one workgroup per (KV head, token range) reads the range once and
 // carries up to four of the head's queries through it: byte tables of all
-// four in LDS, four online softmaxes, four weighted value sums from each
-// value load.  Heads with more queries take one launch per four.
+// four in LDS, four online softmaxes, the four weighted value sums on the
+// matrix cores from each value load.  Heads with more queries take one
+// launch per four.
 //
 // Tables (m = 256: 32 tables of 256 binary32 entries per query): a 64 KiB
 // block holds two queries, row v (256 bytes) = entries T_p[v] of query a
@@ -23,12 +24,20 @@
 // and a per-lane constant byte (4 ((r + i) mod 32) + 128 h, eight registers
 // of them); the second block is the same address plus 64 KiB.
 //
-// Values: 32 rows of 128 codes per wave step, 16 codes per lane (lane = slot
-// 8 + sub: row 8 k + slot, codes 16 sub .. + 15 at load k); the softmax
-// weight times the value scale of each row comes from the scoring lanes by
-// ds_bpermute, once per query.  Partials (max, sum, o[d]) per (query, token
-// range) go to the same workspace layout as the one-query decode, whose
-// merge kernel finishes the step.
+// Values, on the matrix cores: per wave step, o[q][ch] += sum over the 32
+// tokens of w[q][t] c[t][ch] is eight v_mfma_f32_16x16x32_f16 (one per group
+// of 16 channels), the weights w = softmax weight x value scale as the A
+// operand (rows: the queries' binary16 hi halves, then their lo halves) and
+// the codes as the B operand (int8 -> binary16 exactly).  The contraction
+// runs over tokens, so lane (nl, kq) = (lane % 16, lane / 16) loads 8 bytes
+// (channels 8 nl .. 8 nl + 7) of each of the tokens 8 kq .. 8 kq + 7 (whole
+// rows per load instruction) and column nl of group j is channel 8 nl + j.
+// The weights reach the A fragments through 512 B of LDS per wave; they are
+// scaled by 2^(14 - R), R the exponent of the largest value scale the wave
+// has seen, so they stay within binary16's range (the sums are rescaled
+// with the softmax's own factor when R grows).  Partials (max, sum, o[d]) per
+// (query, token range) go to the same workspace layout as the one-query
+// decode, whose merge kernel finishes the step.
 #include "kvq_device.h"
 #include "kvq_launch.h"
 #include "kvq_qjl_device.h"
@@ -100,14 +109,17 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
   const int wave = threadIdx.x >> 6;
   const int r = lane & 31;                   // token of the wave step (scoring)
   const int h = lane >> 5;                   // query slot within each block
-  const int slot = lane >> 3;                // value row within each group of 8
-  const int sub = lane & 7;                  // 16-code chunk of the value row
+  const int nl = lane & 15;                  // matrix-core row / column of the lane
+  const int kq = lane >> 4;                  // its 8-token group of the step
   const float c = kSqrtHalfPi / (float)M;
   const int64_t row0 = g * T + t_begin;
   const uint32_t* bblk = kbits + row0 * (M / 32);
   const uint16_t* nblk = knorms + row0;
-  const int8_t* vblk = vcodes + row0 * D + sub * 16;
+  const int8_t* vblk = vcodes + row0 * D + 8 * nl;
   const float* sblk = vscales + row0;
+  // per wave: the step's softmax weights [NQ][32], staged for the matrix cores
+  float* wst = reinterpret_cast<float*>(lds_raw + NB * kGqaBlockBytes + NQ * M * sizeof(float)) +
+               wave * NQ * kGqaChunk;
 
   struct Keys {
     uint32_t wv[8];
@@ -115,7 +127,7 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
     float vs;
   };
   struct Vals {
-    u32x4 vc[4];
+    u32x2 vc[8];                             // channels 8 nl .. + 7 of tokens 8 kq + e
   };
   auto load_keys = [&](Keys& kk, int base) {
     const int tc = min(base + r, ntok - 1);
@@ -123,11 +135,12 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
     kk.nb = ld_stream(nblk + tc);
     kk.vs = ld_stream(sblk + tc);
   };
+  // whole rows per instruction: 4 tokens x 16 lanes x 8 B
   auto load_vals = [&](Vals& vv, int base) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int tv = min(base + 8 * k + slot, ntok - 1);
-      vv.vc[k] = ld_stream(reinterpret_cast<const u32x4*>(vblk + tv * D));
+    for (int e = 0; e < 8; ++e) {
+      const int tv = min(base + 8 * kq + e, ntok - 1);
+      vv.vc[e] = ld_stream(reinterpret_cast<const u32x2*>(vblk + tv * D));
     }
   };
 
@@ -142,14 +155,24 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
     cs[w] = v;
   }
 
-  float Mq[NQ], Lq[NQ], o[NQ][16];
+  // value sums on the matrix cores: acc[j] = D tile of channel group j,
+  // row rho = (part, query) = (rho / NQ, rho % NQ) with part 0 the weights'
+  // hi halves, part 1 their lo halves (rows past 2 NQ stay zero), column nl
+  // = channel 8 nl + j; lane (nl, kq) holds rows 4 kq .. 4 kq + 3
+  float Mq[NQ], Lq[NQ];
+  f32x4 acc[8];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     Mq[q] = -INFINITY;
     Lq[q] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[q][e] = 0.0f;
   }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // weights are scaled by 2^(14 - R), R the exponent of the largest value
+  // scale seen so far by the wave (a softmax weight is at most 1), so the
+  // largest lies below 2^15 and binary16 keeps 22 bits of each through its
+  // hi / lo split; R only grows, and the sums are rescaled when it does
+  int R = -110;
 
   // z of this lane's token for query h of each block (-inf past the range)
   auto scores = [&](const Keys& kk, int base, float (&z)[NB]) {
@@ -194,7 +217,15 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
   auto step = [&](const Keys& kk, const Vals& vv, int base) {
     float z[NB];
     scores(kk, base, z);
-    float ws[NB];
+    // the step's largest value scale (both halves hold the same 32 tokens)
+    const float vmax = __builtin_bit_cast(
+        float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, seg_max_f32<32>(kk.vs))));
+    const int E = (int)((__builtin_bit_cast(uint32_t, vmax) >> 23) & 0xFF) - 127;
+    const int Rn = max(R, E);
+    const float up = __builtin_ldexpf(1.0f, R - Rn);        // 1 unless R grew
+    R = Rn;
+    const float f = __builtin_ldexpf(1.0f, 14 - R);
+    float ws[NB], al[NQ];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       // max over the 32 tokens of each half (query 2 b + half)
@@ -202,36 +233,64 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
       halves_u32(__builtin_bit_cast(uint32_t, seg_max_f32<32>(z[b])), mlo, mhi);
       const float mx0 = __builtin_bit_cast(float, mlo), mx1 = __builtin_bit_cast(float, mhi);
       const float Mn0 = __builtin_fmaxf(Mq[2 * b], mx0), Mn1 = __builtin_fmaxf(Mq[2 * b + 1], mx1);
-      const float al0 = __expf(Mq[2 * b] - Mn0), al1 = __expf(Mq[2 * b + 1] - Mn1);
+      al[2 * b] = __expf(Mq[2 * b] - Mn0);
+      al[2 * b + 1] = __expf(Mq[2 * b + 1] - Mn1);
       const float pz = __expf(z[b] - (h ? Mn1 : Mn0));
       uint32_t slo, shi;
       halves_u32(__builtin_bit_cast(uint32_t, seg_sum_f32<32>(pz)), slo, shi);
-      Lq[2 * b] = Lq[2 * b] * al0 + __builtin_bit_cast(float, slo);
-      Lq[2 * b + 1] = Lq[2 * b + 1] * al1 + __builtin_bit_cast(float, shi);
+      Lq[2 * b] = Lq[2 * b] * al[2 * b] + __builtin_bit_cast(float, slo);
+      Lq[2 * b + 1] = Lq[2 * b + 1] * al[2 * b + 1] + __builtin_bit_cast(float, shi);
       Mq[2 * b] = Mn0;
       Mq[2 * b + 1] = Mn1;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        o[2 * b][e] *= al0;
-        o[2 * b + 1][e] *= al1;
-      }
-      ws[b] = pz * kk.vs;
+      ws[b] = pz * kk.vs * f;
     }
+    // rescale: row 4 kq + i of every lane is query (4 kq + i) mod NQ = i mod NQ
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int t = 8 * k + slot;             // value row of this load
-      float cv[16];
+    for (int i = 0; i < 4; ++i) {
+      const float fa = al[i % NQ] * up;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) cv[e] = i8_to_f32(vv.vc[k][e >> 2], e & 3);
+      for (int j = 0; j < 8; ++j) acc[j][i] *= fa;
+    }
+    // weights -> LDS -> A fragment: row nl = (part, query), tokens 8 kq .. + 7
+    __asm__ volatile("" ::: "memory");
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+    for (int b = 0; b < NB; ++b) wst[(2 * b + h) * kGqaChunk + r] = ws[b];
+    __asm__ volatile("" ::: "memory");
+    const int part = nl / NQ, qa = nl % NQ;
+    const f32x4 w0 = *reinterpret_cast<const f32x4*>(wst + qa * kGqaChunk + 8 * kq);
+    const f32x4 w1 = *reinterpret_cast<const f32x4*>(wst + qa * kGqaChunk + 8 * kq + 4);
+    __asm__ volatile("" ::: "memory");
+    f16x8 afr;
 #pragma unroll
-        for (int hq = 0; hq < 2; ++hq) {
-          const float w = __builtin_bit_cast(
-              float, __builtin_amdgcn_ds_bpermute((t + 32 * hq) << 2, __builtin_bit_cast(int, ws[b])));
+    for (int e = 0; e < 8; ++e) {
+      const float v = e < 4 ? w0[e] : w1[e - 4];
+      const float hi = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & 0xFFFFE000u);
+      const float pv = part == 0 ? hi : (part == 1 ? v - hi : 0.0f);
+      afr[e] = __builtin_amdgcn_cvt_pkrtz(pv, 0.0f)[0];
+    }
+    // B fragment of channel group j: codes of tokens 8 kq + e, channel
+    // 8 nl + j, two tokens per register: bytes (b ^ 0x80) under the exponent
+    // of 1024, minus 1152 (exact)
+    uint32_t xw[8][2];
 #pragma unroll
-          for (int e = 0; e < 16; ++e) o[2 * b + hq][e] = __builtin_fmaf(w, cv[e], o[2 * b + hq][e]);
-        }
+    for (int e = 0; e < 8; ++e) {
+      xw[e][0] = vv.vc[e][0] ^ 0x80808080u;
+      xw[e][1] = vv.vc[e][1] ^ 0x80808080u;
+    }
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      f16x8 bfr;
+      const uint32_t sel = 0x0C000C00u | (uint32_t)(j & 3) | ((uint32_t)(4 + (j & 3)) << 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t pr = __builtin_amdgcn_perm(xw[2 * i + 1][j >> 2], xw[2 * i][j >> 2], sel) | 0x64006400u;
+        const h2 hv = __builtin_bit_cast(h2, pr) + bias;
+        bfr[2 * i] = hv[0];
+        bfr[2 * i + 1] = hv[1];
+      }
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr, bfr, acc[j], 0, 0, 0);
     }
   };
 
@@ -275,16 +334,21 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
     }
   }
 
-  // merge the 8 value slots of the wave, then the waves of the workgroup
+  // hi + lo rows of each query (NQ = 4: lanes kq = 0 and 1; NQ = 2: rows
+  // i and i + 2 of lanes kq = 0), unscaled by 2^(R - 14), then the waves of
+  // the workgroup
+  const float unscale = __builtin_ldexpf(1.0f, R - 14);
+  float ov[NQ][8];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q)
+  for (int j = 0; j < 8; ++j)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float v = o[q][e];
-      v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x201F));  // lane ^ 8
-      v += swz_xor16_f32(v);
-      v += xor32_f32(v);
-      o[q][e] = v;
+    for (int q = 0; q < NQ; ++q) {
+      float v;
+      if constexpr (NQ == 4)
+        v = acc[j][q] + swz_xor16_f32(acc[j][q]);
+      else
+        v = acc[j][q] + acc[j][q + 2];
+      ov[q][j] = v * unscale;
     }
   __syncthreads();                           // every lookup of the workgroup is done
   float* wp = wpart + wave * NQ * (D + 2);
@@ -294,9 +358,9 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
       wp[q * (D + 2)] = Mq[q];
       wp[q * (D + 2) + 1] = Lq[q];
     }
-    if (slot == 0) {
+    if (kq == 0) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) wp[q * (D + 2) + 2 + sub * 16 + e] = o[q][e];
+      for (int j = 0; j < 8; ++j) wp[q * (D + 2) + 2 + 8 * nl + j] = ov[q][j];
     }
   }
   __syncthreads();
@@ -349,7 +413,9 @@ DecodeSplit decode_gqa_split(int64_t groups, int64_t T, const DeviceInfo& dev) {
 size_t decode_gqa_lds_bytes(int nb) {
   const size_t tables = (size_t)nb * kGqaBlockBytes;
   const size_t part = (size_t)kGqaWaves * 2 * nb * (kGqaD + 2) * sizeof(float);
-  return std::max(tables, part) + (size_t)2 * nb * kGqaM * sizeof(float);
+  const size_t y = (size_t)2 * nb * kGqaM * sizeof(float);
+  const size_t weights = (size_t)kGqaWaves * 2 * nb * kGqaChunk * sizeof(float);
+  return std::max(tables, part) + y + weights;
 }
 
 hipError_t launch_decode_gqa_pass(const float* y, int64_t groups, int nq_total, int q_off,
