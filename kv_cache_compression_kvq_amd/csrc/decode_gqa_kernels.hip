@@ -47,10 +47,15 @@
 
 namespace kvq {
 
-constexpr int kGqaWaves = 8;
-constexpr int kGqaThreads = 64 * kGqaWaves;
 constexpr int kGqaChunk = 32;                            // tokens per wave step
-constexpr int kGqaBlockTokens = kGqaWaves * kGqaChunk;   // tokens per workgroup step
+// waves per workgroup: the four-query kernel (128 KiB of tables, one
+// workgroup per CU) takes 12 so that 3 waves per SIMD hide the lookups'
+// latency; the two-query kernel (64 KiB) runs two 8-wave workgroups per CU
+#ifndef KVQ_GQA_WAVES2
+#define KVQ_GQA_WAVES2 12
+#endif
+constexpr int gqa_waves(int nb) { return nb == 2 ? KVQ_GQA_WAVES2 : 8; }
+constexpr int kGqaBlockTokens = 8 * kGqaChunk;           // token-range granule
 constexpr int kGqaD = 128, kGqaM = 256;
 constexpr uint32_t kGqaBlockBytes = 65536;               // one table block (two queries)
 
@@ -83,8 +88,8 @@ __device__ void build_pair_tables(const float* ya, const float* yb, float* blk) 
 // [groups * nq_total][m]; this launch takes queries q_off .. q_off + nq_pass
 // - 1 of every group (nq_pass <= 2 NB; the other slots score zero tables and
 // are not written).
-template <int NB>
-__global__ __launch_bounds__(kGqaThreads) __attribute__((amdgpu_waves_per_eu(2)))
+template <int NB, int WAVES = gqa_waves(NB)>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4)))
 void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, int nq_pass,
                        const uint32_t* __restrict__ kbits, const uint16_t* __restrict__ knorms,
                        const int8_t* __restrict__ vcodes, const float* __restrict__ vscales,
@@ -296,10 +301,12 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
 
   // y of the launch's queries first (its wait leaves the first step's loads
   // in flight); dummy query slots get zero tables
-  float yv[NQ / 2];
+  constexpr int TH = 64 * WAVES;
+  constexpr int YK = (NQ * M + TH - 1) / TH;
+  float yv[YK];
 #pragma unroll
-  for (int k = 0; k < NQ / 2; ++k) {
-    const int idx = (int)threadIdx.x + k * kGqaThreads;      // < NQ * M
+  for (int k = 0; k < YK; ++k) {
+    const int idx = min((int)threadIdx.x + k * TH, NQ * M - 1);
     const int q = idx / M;
     const int qc = min(q, nq_pass - 1);
     yv[k] = yall[(g * nq_total + q_off + qc) * M + (idx % M)];
@@ -313,7 +320,8 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
   load_vals(va, first);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int k = 0; k < NQ / 2; ++k) y[threadIdx.x + k * kGqaThreads] = yv[k];
+  for (int k = 0; k < YK; ++k)
+    if ((int)threadIdx.x + k * TH < NQ * M) y[threadIdx.x + k * TH] = yv[k];
   __syncthreads();
 #pragma unroll
   for (int b = 0; b < NB; ++b)
@@ -321,8 +329,9 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
                       reinterpret_cast<float*>(lds_raw + b * kGqaBlockBytes));
   __syncthreads();
   if (first < ntok) {
-    for (int base = first;; base += 2 * kGqaBlockTokens) {
-      const int nb1 = base + kGqaBlockTokens, nb2 = base + 2 * kGqaBlockTokens;
+    constexpr int STEP = WAVES * kGqaChunk;     // tokens per workgroup step
+    for (int base = first;; base += 2 * STEP) {
+      const int nb1 = base + STEP, nb2 = base + 2 * STEP;
       load_keys(kb, nb1);
       step(ka, va, base);
       load_vals(vb, nb1);
@@ -365,27 +374,27 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
   }
   __syncthreads();
   for (int q = 0; q < nq_pass; ++q) {
-    float Mw[kGqaWaves], Ms = -INFINITY;
+    float Mw[WAVES], Ms = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kGqaWaves; ++w) {
+    for (int w = 0; w < WAVES; ++w) {
       Mw[w] = wpart[(w * NQ + q) * (D + 2)];
       Ms = __builtin_fmaxf(Ms, Mw[w]);
     }
-    float sc[kGqaWaves];
+    float sc[WAVES];
 #pragma unroll
-    for (int w = 0; w < kGqaWaves; ++w) sc[w] = (Mw[w] == -INFINITY) ? 0.0f : __expf(Mw[w] - Ms);
+    for (int w = 0; w < WAVES; ++w) sc[w] = (Mw[w] == -INFINITY) ? 0.0f : __expf(Mw[w] - Ms);
     float* out = partials + ((g * nq_total + q_off + q) * splits + sp) * (int64_t)(D + 2);
     if (threadIdx.x == 0) {
       float Ls = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kGqaWaves; ++w) Ls += sc[w] * wpart[(w * NQ + q) * (D + 2) + 1];
+      for (int w = 0; w < WAVES; ++w) Ls += sc[w] * wpart[(w * NQ + q) * (D + 2) + 1];
       out[0] = Ms;
       out[1] = Ls;
     }
-    for (int j = threadIdx.x; j < D; j += kGqaThreads) {
+    for (int j = threadIdx.x; j < D; j += TH) {
       float acc = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kGqaWaves; ++w)
+      for (int w = 0; w < WAVES; ++w)
         if (sc[w] != 0.0f) acc += sc[w] * wpart[(w * NQ + q) * (D + 2) + 2 + j];
       out[2 + j] = acc;
     }
@@ -412,9 +421,10 @@ DecodeSplit decode_gqa_split(int64_t groups, int64_t T, const DeviceInfo& dev) {
 
 size_t decode_gqa_lds_bytes(int nb) {
   const size_t tables = (size_t)nb * kGqaBlockBytes;
-  const size_t part = (size_t)kGqaWaves * 2 * nb * (kGqaD + 2) * sizeof(float);
+  const int waves = nb == 2 ? gqa_waves(2) : gqa_waves(1);
+  const size_t part = (size_t)waves * 2 * nb * (kGqaD + 2) * sizeof(float);
   const size_t y = (size_t)2 * nb * kGqaM * sizeof(float);
-  const size_t weights = (size_t)kGqaWaves * 2 * nb * kGqaChunk * sizeof(float);
+  const size_t weights = (size_t)waves * 2 * nb * kGqaChunk * sizeof(float);
   return std::max(tables, part) + y + weights;
 }
 
@@ -440,13 +450,13 @@ hipError_t launch_decode_gqa_pass(const float* y, int64_t groups, int nq_total, 
     if (nb == 1) {
       e = allow_dynamic_lds(decode_gqa_kernel<1>, lds);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(decode_gqa_kernel<1>, dim3((unsigned)pairs), dim3(kGqaThreads), lds, st,
+      hipLaunchKernelGGL(decode_gqa_kernel<1>, dim3((unsigned)pairs), dim3(64 * gqa_waves(1)), lds, st,
                          yp, nq_total, q_off, nq_pass, kb, kn, vc, vs, T, sp.splits,
                          sp.tokens_per_split, lam, pairs, pp);
     } else {
       e = allow_dynamic_lds(decode_gqa_kernel<2>, lds);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(decode_gqa_kernel<2>, dim3((unsigned)pairs), dim3(kGqaThreads), lds, st,
+      hipLaunchKernelGGL(decode_gqa_kernel<2>, dim3((unsigned)pairs), dim3(64 * gqa_waves(2)), lds, st,
                          yp, nq_total, q_off, nq_pass, kb, kn, vc, vs, T, sp.splits,
                          sp.tokens_per_split, lam, pairs, pp);
     }
