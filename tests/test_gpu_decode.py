@@ -194,6 +194,38 @@ def test_decode_grouped_one_pass(G, nq, T, qscale):
     log(f"[decode-gqa1] worst err / tol = {worst:.3g}")
 
 
+@pytest.mark.parametrize("pattern", ["rising", "falling", "scattered", "zeros"])
+def test_decode_grouped_value_scales_across_binades(pattern):
+    """The one-pass grouped decode sums the values on the matrix cores with
+    binary16 weights scaled by a running power of two (from the largest value
+    scale seen): value scales spanning 2^-40 .. 2^40 that grow along the
+    range (rescaling mid-range), shrink, scatter, or include all-zero value
+    rows; every query checked against the oracle."""
+    rng = np.random.default_rng(len(pattern) * 31)
+    G, nq, T, d, m = 3, 4, 3001, 128, 256
+    k = rng.standard_normal((G, T, d)).astype(np.float16)
+    v = rng.standard_normal((G, T, d)).astype(np.float16)
+    S = rng.standard_normal((m, d)).astype(np.float16)
+    kw, kn, vc, vs = make_cache(k, v, S)
+    ramp = np.linspace(-40.0, 40.0, T)
+    expo = {"rising": ramp, "falling": -ramp, "scattered": rng.uniform(-40, 40, T),
+            "zeros": rng.uniform(-3, 3, T)}[pattern]
+    vs = (np.exp2(expo)[None, :] * rng.uniform(0.5, 1.0, (G, T))).astype(np.float32)
+    if pattern == "zeros":
+        vs[:, rng.integers(0, T, T // 3)] = 0.0
+        vs[1] = 0.0                                    # a head whose values are all zero
+    q = (rng.standard_normal((G, nq, d)) * 2.0).astype(np.float16)
+    lam = 1 / math.sqrt(d)
+    log(f"[decode-gqa-binades] {pattern}")
+    out = down(K.decode_qjl_int8_gqa(up(q), up(S), up(kw), up(kn), up(vc), up(vs), lam))
+    worst = 0.0
+    for j in range(nq):
+        qj = np.ascontiguousarray(q[:, j])
+        ora = OD.decode_qjl_int8(qj, S, kw, kn, vc, vs, lam)
+        worst = max(worst, decode_tolerance_check(out[:, j], qj, S, kw, kn, vc, vs, lam, ora))
+    log(f"[decode-gqa-binades] {pattern}: worst err / tol = {worst:.3g}")
+
+
 def test_decode_grouped_single_query_equals_plain_decode():
     """nq = 1 through the grouped entry point is the plain decode, bit for bit."""
     rng = np.random.default_rng(77)
