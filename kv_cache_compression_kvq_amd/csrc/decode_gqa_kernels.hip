@@ -401,6 +401,206 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Grouped-query QJL scores in one pass (m = 256, fp16 S, d <= 128, 2 .. 4
+// queries per launch): one workgroup per (KV head, token tile) projects its
+// queries (y = S q, the one-query kernels' arithmetic), builds their tables
+// as two pair blocks (the same binary32 entries as the one-query tables),
+// and walks the tile once, each lane scoring one token for one query of
+// each block with the lookups above.  A token t is visited by lane r = t mod
+// 32 with the one-query kernels' summation order, so every score equals,
+// bit for bit, the one-query score of the same query.
+constexpr int kGsWaves = 16;
+constexpr int kGsThreads = 64 * kGsWaves;
+constexpr int kGsStep = kGsWaves * kGqaChunk;            // tokens per workgroup step
+
+template <typename TQ>
+__global__ __launch_bounds__(kGsThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void scores_qjl_gqa_kernel(const TQ* __restrict__ q, int nq_total, int q_off, int nq_pass,
+                           const _Float16* __restrict__ S, int d,
+                           const uint32_t* __restrict__ bits, const uint16_t* __restrict__ norms,
+                           int64_t T, int64_t tiles, int64_t tile_tokens,
+                           float* __restrict__ scores) {
+  constexpr int NB = 2, NQ = 4, M = kGqaM;
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  // tables first, at LDS address 0 (this kernel declares no static
+  // __shared__ data); before they are built the area stages the queries
+  float* qs = reinterpret_cast<float*>(lds_raw);
+  float* y = reinterpret_cast<float*>(lds_raw + NB * kGqaBlockBytes);   // [NQ][M]
+  const int64_t g = blockIdx.x / tiles;
+  const int64_t t0 = (blockIdx.x % tiles) * tile_tokens;
+  const int ntok = (int)std::min<int64_t>(tile_tokens, T - t0);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 31;                   // token of the wave step
+  const int h = lane >> 5;                   // query slot within each block
+  const float c = kSqrtHalfPi / (float)M;
+  const uint32_t* bblk = bits + (g * T + t0) * (M / 32);
+  const uint16_t* nblk = norms + g * T + t0;
+
+  struct Keys {
+    uint32_t wv[8];
+    uint16_t nb;
+  };
+  auto load_keys = [&](Keys& kk, int base) {
+    const int tc = min(base + r, ntok - 1);
+    load_rot_words(bblk + tc * 8, r, kk.wv);
+    kk.nb = ld_stream(nblk + tc);
+  };
+
+  // projections of all the launch's queries at once: 4 waves per query, 64
+  // rows of S each, every row as project16_lite computes it (16 lanes x 8
+  // products, then the 16-lane DPP sum), so y is bit for bit the one-query
+  // kernels' y; dummy query slots get zero tables
+  {
+    static_assert(kGsWaves == 16 && M == 256, "4 waves x 64 rows per query");
+    for (int i = threadIdx.x; i < NQ * 128; i += kGsThreads) {
+      const int j = i >> 7, cch = i & 127;
+      qs[i] = (j < nq_pass && cch < d) ? to_f32(q[(g * nq_total + q_off + j) * d + cch]) : 0.0f;
+    }
+    __syncthreads();
+    const int j = wave >> 2;                   // query of this wave
+    const int rbase = 64 * (wave & 3);
+    const int cl = lane & 15, r4 = lane >> 4;
+    const int cc = min(cl, d / 8 - 1);
+    const bool live_c = 8 * cl < d;
+    float qv[8];
+    const f32x4* p4 = reinterpret_cast<const f32x4*>(qs + j * 128 + 8 * cc);
+    const f32x4 q0 = p4[0], q1 = p4[1];
+    qv[0] = q0[0]; qv[1] = q0[1]; qv[2] = q0[2]; qv[3] = q0[3];
+    qv[4] = q1[0]; qv[5] = q1[1]; qv[6] = q1[2]; qv[7] = q1[3];
+    for (int it0 = 0; it0 < 16; it0 += 4) {
+      f16x8 raw[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        raw[k] = *reinterpret_cast<const f16x8*>(S + (int64_t)(rbase + 4 * (it0 + k) + r4) * d + 8 * cc);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float part = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)raw[k][e], qv[e], part);
+        part = seg_sum_f32<16>(live_c ? part : 0.0f);
+        if (cl == 0) y[j * M + rbase + 4 * (it0 + k) + r4] = j < nq_pass ? part : 0.0f;
+      }
+    }
+  }
+  const int first = wave * kGqaChunk;
+  Keys ka, kb;
+  load_keys(ka, first);
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    build_pair_tables(y + 2 * b * M, y + (2 * b + 1) * M,
+                      reinterpret_cast<float*>(lds_raw + b * kGqaBlockBytes));
+  __syncthreads();
+
+  // per-lane address bytes: byte i of cs = 4 ((r + i) mod 32) + 128 h
+  uint32_t cs[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      v |= (uint32_t)(4 * ((r + 4 * w + b) & 31) + 128 * h) << (8 * b);
+    cs[w] = v;
+  }
+  float* sq = scores + (g * nq_total + q_off) * T + t0;
+  auto score = [&](const Keys& kk, int base) {
+    uint32_t x[8];
+    rot_words(kk.wv, r, x);
+    float acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = 0.0f;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      float v[NB][16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int i = 16 * hf + k;
+        const uint32_t a = __builtin_amdgcn_perm(x[i >> 2], cs[i >> 2],
+                                                 0x0C0C0400u | (uint32_t)(i & 3) | ((uint32_t)(i & 3) << 8));
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          v[b][k] = *(lds_cfloat_ptr)(uintptr_t)(a + (uint32_t)b * kGqaBlockBytes);
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          s0 += v[b][k];
+          s1 += v[b][8 + k];
+        }
+        acc[b] += s0 + s1;
+      }
+    }
+    const float n = (float)__builtin_bit_cast(_Float16, kk.nb);
+    const int t = base + r;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int qj = 2 * b + h;
+      if (t < ntok && qj < nq_pass) sq[(int64_t)qj * T + t] = c * n * acc[b];
+    }
+  };
+  if (first < ntok) {
+    for (int base = first;; base += 2 * kGsStep) {
+      const int nb1 = base + kGsStep, nb2 = base + 2 * kGsStep;
+      load_keys(kb, nb1);
+      score(ka, base);
+      if (nb1 >= ntok) break;
+      load_keys(ka, nb2);
+      score(kb, nb1);
+      if (nb2 >= ntok) break;
+    }
+  }
+}
+
+bool scores_qjl_gqa_supported(int S_f16, int m, int d, int nq) {
+  return S_f16 && m == kGqaM && d >= 8 && d <= 128 && d % 8 == 0 && nq >= 2 && nq <= 4;
+}
+
+size_t scores_qjl_gqa_lds_bytes() {
+  return (size_t)2 * kGqaBlockBytes + (size_t)4 * kGqaM * sizeof(float);
+}
+
+template <typename TQ>
+static hipError_t scores_qjl_gqa_typed(const TQ* q, int64_t groups, int nq, const _Float16* S,
+                                       int d, const uint32_t* bits, const uint16_t* norms,
+                                       int64_t T, float* scores, const DeviceInfo& dev,
+                                       hipStream_t st) {
+  const size_t lds = scores_qjl_gqa_lds_bytes();
+  if (lds > dev.lds_per_block) return hipErrorInvalidConfiguration;
+  hipError_t e = allow_dynamic_lds(scores_qjl_gqa_kernel<TQ>, lds);
+  if (e != hipSuccess) return e;
+  // about one workgroup per CU (one fits beside its 128 KiB of tables),
+  // tiles a multiple of the workgroup step
+  const int64_t splits = std::max<int64_t>(1, ((int64_t)std::max(1, dev.cus) + groups - 1) / groups);
+  int64_t tile = (T + splits - 1) / splits;
+  tile = (tile + kGsStep - 1) / kGsStep * kGsStep;
+  const int64_t tiles = (T + tile - 1) / tile;
+  const int64_t max_groups = std::max<int64_t>(1, (int64_t(1) << 22) / tiles);
+  for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
+    const int64_t gn = std::min(max_groups, groups - g0);
+    hipLaunchKernelGGL(scores_qjl_gqa_kernel<TQ>, dim3((unsigned)(gn * tiles)), dim3(kGsThreads),
+                       lds, st, q + g0 * nq * d, nq, 0, nq, S, d, bits + g0 * T * (kGqaM / 32),
+                       norms + g0 * T, T, tiles, tile, scores + g0 * nq * T);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_scores_qjl_gqa(const void* q, int q_f16, int64_t groups, int nq,
+                                 const _Float16* S, int d, const uint32_t* bits,
+                                 const uint16_t* norms, int64_t T, float* scores,
+                                 const DeviceInfo& dev, hipStream_t st) {
+  if (q_f16)
+    return scores_qjl_gqa_typed(static_cast<const _Float16*>(q), groups, nq, S, d, bits, norms, T,
+                                scores, dev, st);
+  return scores_qjl_gqa_typed(static_cast<const float*>(q), groups, nq, S, d, bits, norms, T, scores,
+                              dev, st);
+}
+
 bool decode_gqa_supported(int m, int d, int nq) { return m == kGqaM && d == kGqaD && nq >= 2; }
 
 // Token split of the one-pass kernel: one workgroup per CU at a time (its

@@ -82,6 +82,16 @@ hipError_t launch_decode_gqa_pass(const float* y, int64_t groups, int nq_total, 
                                   float lam, float* partials, const DecodeSplit& sp,
                                   hipStream_t st);
 
+// One-pass grouped-query QJL scores (decode_gqa_kernels.hip): m = 256, fp16
+// S, d <= 128, 2 .. 4 query heads per KV head; bit-identical to scoring each
+// query alone.
+bool scores_qjl_gqa_supported(int S_f16, int m, int d, int nq);
+size_t scores_qjl_gqa_lds_bytes();
+hipError_t launch_scores_qjl_gqa(const void* q, int q_f16, int64_t groups, int nq,
+                                 const _Float16* S, int d, const uint32_t* bits,
+                                 const uint16_t* norms, int64_t T, float* scores,
+                                 const DeviceInfo& dev, hipStream_t st);
+
 // Device address of the allocation-free decode's scratch array on the
 // current device (kStaticScratchBytes bytes, 256-byte aligned; looked up
 // with hipGetSymbolAddress on the first call per device).

@@ -812,6 +812,9 @@ hipError_t launch_scores_qjl(const void* q, int q_f16, int64_t groups, int nq, c
                              int S_f16, int m, const uint32_t* bits, const uint16_t* norms,
                              int64_t T, int d, float* scores, const DeviceInfo& dev,
                              hipStream_t st) {
+  if (scores_qjl_gqa_supported(S_f16, m, d, nq) && scores_qjl_gqa_lds_bytes() <= dev.lds_per_block)
+    return launch_scores_qjl_gqa(q, q_f16, groups, nq, static_cast<const _Float16*>(S), d, bits,
+                                 norms, T, scores, dev, st);
   if (S_f16) {
     const _Float16* Sp = static_cast<const _Float16*>(S);
     if (q_f16)

@@ -143,16 +143,20 @@ def test_bit_order_matches_fixture_on_gpu():
         assert down(bits, np.uint32).tolist() == want
 
 
-@pytest.mark.parametrize("nq,T,d", [(4, 4100, 128), (8, 999, 64), (2, 9000, 128)])
-def test_grouped_queries_equal_single_query_runs(nq, T, d):
+@pytest.mark.parametrize("qdt", ["f16", "f32"])
+@pytest.mark.parametrize("nq,T,d", [(4, 4100, 128), (8, 999, 64), (2, 9000, 128), (3, 385, 128),
+                                    (4, 1, 128), (2, 17, 32), (3, 20000, 96)])
+def test_grouped_queries_equal_single_query_runs(qdt, nq, T, d):
     """Grouped-query scoring (one pass over a KV head's sign words for all of
-    its queries) gives, bit for bit, what scoring each query alone gives."""
-    rng = np.random.default_rng(nq * T)
+    its queries; for m = 256 and 2 .. 4 queries one workgroup carries all of
+    them through a tile) gives, bit for bit, what scoring each query alone
+    gives."""
+    rng = np.random.default_rng(nq * T + len(qdt))
     G, m = 3, 256
     S = rng.standard_normal((m, d)).astype(np.float16)
     k = rng.standard_normal((G * T, d)).astype(np.float16)
     words, norms = O.qjl_sketch(k, S)
-    q = rng.standard_normal((G, nq, d)).astype(np.float16)
+    q = rng.standard_normal((G, nq, d)).astype(np.float16 if qdt == "f16" else np.float32)
     w, n, Sd = up(words.reshape(G, T, m // 32)), up(norms.reshape(G, T)), up(S)
     grouped = down(K.scores_qjl(up(q), Sd, w, n))
     for j in range(nq):
