@@ -14,8 +14,9 @@ Steps are launched back to back and timed as a block (wall clock, with HIP
 events at its two ends only).  Throughput is scores per second (query-token
 pairs scored per step / time).
 
-Also reported (``components``, sections copy / sweep / llama / qjl /
-residual / gqa): HBM GB/s and roofline fractions of INT8 and INT4 quantize /
+Also reported (``components``, sections copy / tiny / sweep / llama / qjl /
+residual / gqa): the one-head fp32 correctness workload (launch-bound, for
+context), HBM GB/s and roofline fractions of INT8 and INT4 quantize /
 dequantize on the element-count sweep (2^28 and 2^30 fp32), the Llama-7B
 layer (INT8, INT4, per-channel INT8, scores; also as HIP-graph replays), the
 QJL-cache sketch and scores with their HBM stream references, the two-stage
@@ -25,7 +26,11 @@ oracle on bounded samples (the decode on one thread and on every thread,
 the INT8 quantizer on the 2^28 sweep).
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 1000] [--no-components]
+                    [--config {all,tiny,llama7b,sweep,qjl,decode}]
                     [--only SECTIONS] [--no-cpu-baseline]
+
+``--config`` picks one of the five workloads (the decode step alone, or
+the component sections of one workload); the default runs all of them.
 
 The default warm-up (1000 steps, ~0.45 s) brings the GPU's clocks up after
 the seconds of host-side input generation before the timed region: with 3
@@ -58,6 +63,11 @@ def parse_args():
     p.add_argument("--no-components", action="store_true")
     p.add_argument("--only", default=",".join(SECTIONS),
                    help="comma-separated component sections to run (" + ", ".join(SECTIONS) + ")")
+    p.add_argument("--config", default="all", choices=("all",) + tuple(CONFIGS),
+                   help="one workload: tiny (1 head x 512 tokens x 128, fp32), llama7b (one "
+                        "Llama-7B layer's K and V), sweep (2^28 and 2^30 fp32 elements), qjl "
+                        "(8 x 32 x 8192 x 128 QJL key cache, grouped-query variants), decode "
+                        "(the decode step only); all (default) runs every one")
     p.add_argument("--no-graph", action="store_true",
                    help="skip the HIP-graph replay timings (profiling aid)")
     p.add_argument("--no-decode", action="store_true",
@@ -178,7 +188,11 @@ def med(xs):
 
 
 COLD_BYTES = 1 << 30     # rotate inputs over > 1 GiB: 4x the 256 MB last-level cache (MALL)
-SECTIONS = ("copy", "sweep", "llama", "qjl", "residual", "gqa")
+SECTIONS = ("copy", "tiny", "sweep", "llama", "qjl", "residual", "gqa")
+# --config: one workload of the five (the decode step, or a set of component
+# sections); "all" runs everything
+CONFIGS = {"tiny": ("tiny",), "llama7b": ("llama",), "sweep": ("sweep",),
+           "qjl": ("qjl", "residual", "gqa"), "decode": ()}
 
 
 def components(K, si, torch, np, only=SECTIONS, use_graph=True):
@@ -236,6 +250,35 @@ def components(K, si, torch, np, only=SECTIONS, use_graph=True):
         gbs("device_copy_1GiB", 2 * src.numel() * 4,
             [lambda: dsts[next(it_c) % 2].copy_(src)], reps=10)
         del src, dsts
+
+    if "tiny" in only:
+        # the correctness workload, timed for context (launch-bound): fp32 K
+        # and V of one head, 512 tokens x 128; S 256 x 128 and 4 queries, fp32
+        W, T1, d1, m1 = si.W_TINY, 512, 128, 256
+        k1 = torch.from_numpy(si.kv_tensor(W, si.K, 1, 1, T1, d1, "f32")).to(dev).view(T1, d1)
+        v1 = torch.from_numpy(si.kv_tensor(W, si.V, 1, 1, T1, d1, "f32")).to(dev).view(T1, d1)
+        S1 = torch.from_numpy(si.projection(W, m1, d1, "f32")).to(dev)
+        q1 = torch.from_numpy(si.queries(W, 1, 4, d1, "f32")).to(dev)
+        kv1 = torch.stack([k1, v1]).view(-1, d1)
+        c1 = K.quantize_int8(kv1)
+        o1 = like(c1)
+        gbs("tiny_quantize_kv_f32", 2 * T1 * d1 * 4 + 2 * T1 * (d1 + 4),
+            [lambda: K.quantize_int8(kv1, out=o1)], graph=True)
+        od1 = torch.empty_like(kv1)
+        gbs("tiny_dequantize_kv_f32", 2 * T1 * (d1 + 4) + 2 * T1 * d1 * 4,
+            [lambda: K.dequantize_int8(c1[0], c1[1], out=od1)], graph=True)
+        kc1 = (c1[0][:T1].view(1, T1, d1), c1[1][:T1].view(1, T1))
+        os1 = torch.empty((1, 4, T1), dtype=torch.float32, device=dev)
+        gbs("tiny_scores_int8_4x512", T1 * (d1 + 4) + 4 * (d1 * 4 + T1 * 4),
+            [lambda: K.scores_int8(q1, kc1[0], kc1[1], out=os1)], graph=True)
+        sk1 = K.qjl_sketch(k1, S1)
+        osk1 = like(sk1)
+        gbs("tiny_qjl_sketch_f32_m256", T1 * d1 * 4 + T1 * (m1 // 8 + 2) + m1 * d1 * 4,
+            [lambda: K.qjl_sketch(k1, S1, out=osk1)], flops=2.0 * T1 * d1 * m1, graph=True)
+        b1, n1 = sk1[0].view(1, T1, m1 // 32), sk1[1].view(1, T1)
+        gbs("tiny_qjl_scores_4x512", T1 * (m1 // 8 + 2) + 4 * (d1 * 4 + T1 * 4) + m1 * d1 * 4,
+            [lambda: K.scores_qjl(q1, S1, b1, n1, out=os1)], graph=True)
+        del k1, v1, S1, q1, kv1, c1, o1, od1, kc1, os1, sk1, osk1, b1, n1
 
     # INT8 round-trip error on the sweep (fp32 rows, N(0, 1)) and the
     # U(-1, 1) context row: max and mean |dequantize(quantize(x)) - x|
@@ -691,6 +734,10 @@ def main():
     torch.cuda.set_device(0)
 
     only = tuple(x for x in args.only.split(",") if x)
+    if args.config != "all":
+        only = CONFIGS[args.config] + (("copy",) if args.config == "sweep" else ())
+        args.no_decode = args.config != "decode"
+        args.no_components = args.config == "decode"
     bad = [x for x in only if x not in SECTIONS]
     if bad:
         print(f"unknown section(s) {bad}; sections: {', '.join(SECTIONS)}", file=sys.stderr)

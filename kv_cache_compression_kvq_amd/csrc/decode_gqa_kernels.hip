@@ -41,6 +41,7 @@
 #include "kvq_device.h"
 #include "kvq_launch.h"
 #include "kvq_qjl_device.h"
+#include "kvq_qjl_stream.h"
 
 #include <algorithm>
 #include <cmath>
@@ -134,6 +135,9 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
   struct Vals {
     u32x2 vc[8];                             // channels 8 nl .. + 7 of tokens 8 kq + e
   };
+  // (per-lane 16-byte halves: whole-line loads and their lane exchange
+  // measured slower here, where the sign words are a fifth of the bytes and
+  // the vector ALU is the bound)
   auto load_keys = [&](Keys& kk, int base) {
     const int tc = min(base + r, ntok - 1);
     load_rot_words(bblk + tc * 8, r, kk.wv);
@@ -439,12 +443,12 @@ void scores_qjl_gqa_kernel(const TQ* __restrict__ q, int nq_total, int q_off, in
   const uint16_t* nblk = norms + g * T + t0;
 
   struct Keys {
-    uint32_t wv[8];
+    u32x4 wx;                                // sign words, as whole lines
     uint16_t nb;
   };
   auto load_keys = [&](Keys& kk, int base) {
     const int tc = min(base + r, ntok - 1);
-    load_rot_words(bblk + tc * 8, r, kk.wv);
+    kk.wx = issue_rot_words32(bblk, base, ntok - 1, lane);
     kk.nb = ld_stream(nblk + tc);
   };
 
@@ -506,8 +510,9 @@ void scores_qjl_gqa_kernel(const TQ* __restrict__ q, int nq_total, int q_off, in
   }
   float* sq = scores + (g * nq_total + q_off) * T + t0;
   auto score = [&](const Keys& kk, int base) {
-    uint32_t x[8];
-    rot_words(kk.wv, r, x);
+    uint32_t wv[8], x[8];
+    finish_rot_words32(kk.wx, wv);
+    rot_words(wv, r, x);
     float acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = 0.0f;

@@ -28,6 +28,7 @@
 #include "kvq_device.h"
 #include "kvq_launch.h"
 #include "kvq_qjl_device.h"
+#include "kvq_qjl_stream.h"
 
 #include <algorithm>
 #include <cmath>
@@ -618,6 +619,7 @@ hipError_t launch_qjl_sketch(const void* k, int k_f16, int64_t rows, int d, cons
 constexpr int kQjlBatch = 8;
 constexpr int kQjlThreads = 256;
 constexpr int kQjlWideThreads = 512;
+constexpr int kQjlOneQThreads = 1024;   // one query, caches of more than 4096 tokens
 constexpr int kQjlTokPerThread = 16;
 constexpr int kQjlTok = kQjlThreads * kQjlTokPerThread;
 
@@ -629,12 +631,11 @@ __host__ __device__ inline size_t qjl_table_lds_floats(int m) {
   return (size_t)m + (tables > (size_t)kProjQChunk ? tables : (size_t)kProjQChunk);
 }
 
-// TH: threads per workgroup.  ONEQ: one query per group (the query loop is
-// compiled out).  The m = 256 kernels stay under 128 registers so that two
-// workgroups (64 KiB of tables each) share a CU at four waves per SIMD,
-// which hides more of the lookups' LDS latency: the projection holds only
-// four S rows at a time across the token loads, and per-lane token offsets
-// are 32-bit from workgroup-uniform bases.
+// TH: threads per workgroup.  ONEQ: one query per group.  The m = 256
+// kernels stay under 128 registers, i.e. four waves per SIMD (two 512-thread
+// workgroups with 64 KiB of tables each, or one of 1024 threads, per CU),
+// which hides more of the lookups' LDS latency; per-lane token offsets are
+// 32-bit from workgroup-uniform bases.
 template <typename TS, typename TQ, int W, int TH = kQjlThreads, bool ONEQ = false>
 __global__ __launch_bounds__(TH) __attribute__((amdgpu_waves_per_eu(W == 8 ? 4 : 2))) void scores_qjl_kernel(const TQ* __restrict__ q, int nq,
                                                          const TS* __restrict__ S, int m_rt, int d,
@@ -655,38 +656,84 @@ __global__ __launch_bounds__(TH) __attribute__((amdgpu_waves_per_eu(W == 8 ? 4 :
   const float c = kSqrtHalfPi / (float)m;
   if constexpr (W == 8) {
     constexpr int kTile = TH * kQjlBatch;
-    // One workgroup per (group, tile) scores all nq queries of the group
-    // (grouped-query attention: the queries of a KV head share one pass over
-    // its sign words and norms, which stay in registers).  Per query: y = S q
-    // and the byte tables are rebuilt in LDS, then the tokens are scored.
-    // The tokens are requested before the first projection.  The loads are
-    // unconditional (tokens past T re-read the tile's last token and are not
-    // stored): loads under a branch make the compiler wait for each one.
+    // One workgroup per (group, tile): thread i holds tokens i + u TH
+    // (u < kQjlBatch), so a wave's step u is 64 consecutive tokens, read as
+    // whole lines (issue_rot_words64).  Loads are unconditional (tokens past
+    // T re-read the tile's last token and are not stored): loads under a
+    // branch make the compiler wait for each one.
     const int64_t g = blockIdx.x / tiles;
     const int64_t tile = blockIdx.x % tiles;
     const int64_t tbase = tile * kTile;
     const int nlive = (int)std::min<int64_t>(kTile, T - tbase);   // tokens of this tile
     const uint32_t* bg = bits + (g * T + tbase) * words;
     const uint16_t* ng = norms + g * T + tbase;
-    const int r = threadIdx.x & 31;
-    uint32_t wv[kQjlBatch][8];
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 31;
+    const int wfirst = (int)threadIdx.x - lane;   // the wave's first token of step 0
+    RotWords64 rw[kQjlBatch];
     float nv[kQjlBatch];
-    auto load_tokens = [&]() {
+    auto load_step = [&](int u) {
+      const int tb = wfirst + u * TH;
+      issue_rot_words64(bg, tb, nlive - 1, lane, rw[u]);
+      const uint32_t nb = 2u * (uint32_t)min(tb + lane, nlive - 1);   // byte offset
+      nv[u] = (float)__builtin_bit_cast(
+          _Float16, ld_stream(reinterpret_cast<const uint16_t*>(
+                        reinterpret_cast<const unsigned char*>(ng) + nb)));
+    };
+    const TQ* q0 = q + g * nq * d;
+    // (this kernel is launched for fp16 S with d <= 128 only)
+    if constexpr (ONEQ && sizeof(TS) == 2) {
+      // One query: y = S q and the tables first, then the tokens, each wave
+      // requesting step u + 1 before it scores step u.  A CU's vector loads
+      // return in issue order, so S rows requested behind token loads would
+      // wait for HBM: every wave receives its S rows (L2-resident after the
+      // first workgroups) before it requests a token, and one step ahead is
+      // enough to keep HBM busy (more queues the lookups of later waves
+      // behind this wave's loads).
+      QueryProjDirect<TQ, 256 / (TH / 64) / 4> pj;
+      pj.issue(S, q0, d);
+      pj.wait();
+      __builtin_amdgcn_sched_barrier(0);
+      load_step(0);
+      __builtin_amdgcn_sched_barrier(0);
+      pj.finish(y, d);
+      __syncthreads();
+      build_rot_tables(y, lut);
+      __syncthreads();
+      const uint32_t rq = rot_lane_base(lut, r);
+      float* st = scores + g * T + tbase;
 #pragma unroll
       for (int u = 0; u < kQjlBatch; ++u) {
-        const int t = min((int)threadIdx.x + u * TH, nlive - 1);
-        load_rot_words(bg + t * 8, r, wv[u]);
-        nv[u] = (float)__builtin_bit_cast(_Float16, ld_stream(ng + t));
+        if (u + 1 < kQjlBatch) load_step(u + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t w[8];
+        finish_rot_words64(rw[u], w);
+        const float acc = rot_lut_sum(w, r, rq);
+        const int t = wfirst + u * TH + lane;
+        if (t < nlive) st[t] = c * nv[u] * acc;
       }
+      return;
+    }
+    // Several queries of a KV head (grouped-query attention) share one pass
+    // over its sign words and norms, which stay in registers: per query, y
+    // = S q and the byte tables are rebuilt in LDS, then the tokens are
+    // scored.  The tokens are requested once the first query's projection
+    // is done (its S rows then do not wait behind them, and its registers
+    // are free).
+    auto load_tokens = [&]() {
+#pragma unroll
+      for (int u = 0; u < kQjlBatch; ++u) load_step(u);
     };
-    // the words are rotated in place once (rot_words) and serve every query
+    // the words are rotated once (rot_words), back into rw, and serve every
+    // query
     auto rotate_all = [&]() {
 #pragma unroll
       for (int u = 0; u < kQjlBatch; ++u) {
-        uint32_t xr[8];
-        rot_words(wv[u], r, xr);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) wv[u][k] = xr[k];
+        uint32_t w[8], x[8];
+        finish_rot_words64(rw[u], w);
+        rot_words(w, r, x);
+        rw[u].x = u32x4{x[0], x[1], x[2], x[3]};
+        rw[u].y = u32x4{x[4], x[5], x[6], x[7]};
       }
     };
     auto score_all = [&](float* sg) {
@@ -698,28 +745,17 @@ __global__ __launch_bounds__(TH) __attribute__((amdgpu_waves_per_eu(W == 8 ? 4 :
       float* st = sg + tbase;
 #pragma unroll
       for (int u = 0; u < kQjlBatch; ++u) {
-        const int t = (int)threadIdx.x + u * TH;
-        const float acc = rot_lut_sum_rotated(wv[u], rq);
+        const int t = wfirst + u * TH + lane;
+        const uint32_t x[8] = {rw[u].x[0], rw[u].x[1], rw[u].x[2], rw[u].x[3],
+                               rw[u].y[0], rw[u].y[1], rw[u].y[2], rw[u].y[3]};
+        const float acc = rot_lut_sum_rotated(x, rq);
         if (t < nlive) st[t] = c * nv[u] * acc;
       }
     };
-    // query 0 (this kernel is launched for fp16 S with d <= 128 only): its
-    // projection's S rows and query are requested before the tokens, so
-    // that the projection waits for its own loads only (wait counts are in
-    // issue order) while the tokens stream in behind it
-    const TQ* q0 = q + g * nq * d;
     if constexpr (sizeof(TS) == 2) {
-      if (TH == kQjlWideThreads) {
-        QueryProj16<TQ, 8> pj;                 // m = 256 over 8 waves: 8 row groups
-        pj.issue(S, q0, m, d);
-        load_tokens();
-        __builtin_amdgcn_sched_barrier(0);
-        pj.finish(lut, y, m, d);
-      } else {
-        load_tokens();
-        __builtin_amdgcn_sched_barrier(0);
-        project16_lite(S, q0, m, d, lut, y);
-      }
+      project16_lite(S, q0, m, d, lut, y);
+      __builtin_amdgcn_sched_barrier(0);
+      load_tokens();
       __syncthreads();
       build_rot_tables(y, lut);
       __syncthreads();
@@ -770,12 +806,16 @@ static hipError_t scores_qjl_typed(const TQ* q, int64_t groups, int nq, const TS
   // m = 256 with fp16 S and d <= 128: one workgroup per (group, tile) scores
   // all nq queries; else one per (group, query, tile)
   const bool grouped = m == 256 && sizeof(TS) == 2 && d <= 128;
-  // one query: 512-thread workgroups, two per CU; several: 512 threads once
-  // the cache fills their tile (the queries' projections and table builds
-  // are then paid once per 4096 tokens), else 256
+  // one query: 1024-thread workgroups (8192-token tiles, one workgroup per
+  // CU: one projection and one table build per CU) once the cache has more
+  // than 4096 tokens, else 512; several: 512 threads once the cache fills
+  // their tile (the queries' projections and table builds are then paid once
+  // per 4096 tokens), else 256
   const int th = !grouped ? kQjlThreads
-                 : (nq == 1 || T >= (int64_t)kQjlWideThreads * kQjlBatch) ? kQjlWideThreads
-                                                                        : kQjlThreads;
+                 : nq == 1 ? (T > (int64_t)kQjlWideThreads * kQjlBatch ? kQjlOneQThreads
+                                                                        : kQjlWideThreads)
+                 : T >= (int64_t)kQjlWideThreads * kQjlBatch ? kQjlWideThreads
+                                                             : kQjlThreads;
   const int64_t tile_tokens = grouped ? (int64_t)th * kQjlBatch : (int64_t)kQjlTok;
   const int64_t tiles = (T + tile_tokens - 1) / tile_tokens;
   const int64_t per_group = grouped ? tiles : tiles * nq;
@@ -797,7 +837,9 @@ static hipError_t scores_qjl_typed(const TQ* q, int64_t groups, int nq, const TS
     };
     hipError_t e;
     if (grouped && nq == 1)
-      e = launch(scores_qjl_kernel<TS, TQ, 8, kQjlWideThreads, true>, kQjlWideThreads);
+      e = th == kQjlOneQThreads
+              ? launch(scores_qjl_kernel<TS, TQ, 8, kQjlOneQThreads, true>, th)
+              : launch(scores_qjl_kernel<TS, TQ, 8, kQjlWideThreads, true>, th);
     else if (grouped)
       e = th == kQjlWideThreads ? launch(scores_qjl_kernel<TS, TQ, 8, kQjlWideThreads>, th)
                                 : launch(scores_qjl_kernel<TS, TQ, 8>, th);

@@ -50,3 +50,17 @@ def test_committed_traffic_file_matches_the_current_decode_sources():
         t = json.load(fh)
     assert t["source_sha"] == bench.decode_source_hash()
     assert 0.99 < t["hbm_bytes_per_launch"] / t["alg_bytes_per_launch"] < 1.1
+
+
+def test_config_selector_names_known_sections_and_rejects_others():
+    """--config picks one of the five workloads: each maps to component
+    sections the bench knows (the decode step to none), and together they
+    cover every section but the copy context."""
+    assert set(bench.CONFIGS) == {"tiny", "llama7b", "sweep", "qjl", "decode"}
+    named = set()
+    for secs in bench.CONFIGS.values():
+        assert set(secs) <= set(bench.SECTIONS)
+        named |= set(secs)
+    assert named == set(bench.SECTIONS) - {"copy"}
+    r = _run(["--config", "nonesuch"])
+    assert r.returncode == 2 and "invalid choice" in r.stderr
