@@ -126,6 +126,25 @@ def test_scores_shapes(qdt, sdt, nq, T, m, d):
     scores_check(q, S, words.reshape(G, T, m // 32), norms.reshape(G, T), f"scores nq={nq} T={T} m={m}")
 
 
+@pytest.mark.parametrize("qdt", ["f16", "f32"])
+@pytest.mark.parametrize("T,d", [(64, 128), (65, 16), (4095, 64), (4096, 128), (4097, 128),
+                                 (8191, 16), (8192, 128), (8257, 64)])
+def test_one_query_tiles_and_tails(qdt, T, d):
+    """One query per head (fp16 S, m = 256): caches of up to 4096 tokens take
+    512-thread workgroups, longer ones 1024-thread workgroups over 8192-token
+    tiles; every wave step of 64 tokens is read as whole lines and handed to
+    the lanes by a lane exchange.  Tiles that end mid-step, mid-wave and one
+    token past a tile, and d = 16 (lanes past the query's channels), all
+    match the oracle."""
+    rng = np.random.default_rng(T * 7 + d + len(qdt))
+    G, m = 3, 256
+    S = rng.standard_normal((m, d)).astype(np.float16)
+    k = rng.standard_normal((G * T, d)).astype(np.float16)
+    words, norms = O.qjl_sketch(k, S)
+    q = rng.standard_normal((G, 1, d)).astype(np.float16 if qdt == "f16" else np.float32)
+    scores_check(q, S, words.reshape(G, T, m // 32), norms.reshape(G, T), f"one query T={T} d={d}")
+
+
 def test_bit_order_matches_fixture_on_gpu():
     """S = identity: the GPU sign words equal the hand-derived fixture."""
     import os
@@ -145,7 +164,8 @@ def test_bit_order_matches_fixture_on_gpu():
 
 @pytest.mark.parametrize("qdt", ["f16", "f32"])
 @pytest.mark.parametrize("nq,T,d", [(4, 4100, 128), (8, 999, 64), (2, 9000, 128), (3, 385, 128),
-                                    (4, 1, 128), (2, 17, 32), (3, 20000, 96)])
+                                    (4, 1, 128), (2, 17, 32), (3, 20000, 96), (6, 5000, 128),
+                                    (5, 4095, 32)])
 def test_grouped_queries_equal_single_query_runs(qdt, nq, T, d):
     """Grouped-query scoring (one pass over a KV head's sign words for all of
     its queries; for m = 256 and 2 .. 4 queries one workgroup carries all of
