@@ -253,12 +253,20 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
       Mq[2 * b + 1] = Mn1;
       ws[b] = pz * kk.vs * f;
     }
-    // rescale: row 4 kq + i of every lane is query (4 kq + i) mod NQ = i mod NQ
+    // rescale: row 4 kq + i of every lane is query (4 kq + i) mod NQ = i mod NQ;
+    // skipped when every factor is exactly 1 (no query's maximum moved and R
+    // did not grow: the factors are then exp(0) and 2^0), as most steps of a
+    // long range are (multiplying by 1 changes nothing)
+    bool moved = up != 1.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float fa = al[i % NQ] * up;
+    for (int q = 0; q < NQ; ++q) moved |= al[q] != 1.0f;
+    if (moved) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j][i] *= fa;
+      for (int i = 0; i < 4; ++i) {
+        const float fa = al[i % NQ] * up;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j][i] *= fa;
+      }
     }
     // weights -> LDS -> A fragment: row nl = (part, query), tokens 8 kq .. + 7
     __asm__ volatile("" ::: "memory");
