@@ -528,10 +528,18 @@ __global__ __launch_bounds__(kRsThreads) void scores_residual_kernel(
     }
   };
 
+  // the S rows and the query arrive before any token is requested: a CU's
+  // vector loads return in issue order, so rows queued behind token loads
+  // (this wave's or the CU's other waves') would wait for HBM
   QueryProj16<TQ> pj;
   pj.issue(S, q + gq * D, M, D);
+#pragma unroll
+  for (int it = 0; it < 16; ++it) asm volatile("" ::"v"(pj.raw[it]));
+  asm volatile("" ::"v"(pj.qreg));
+  __builtin_amdgcn_sched_barrier(0);
   RsTok<GPL> ka[kRsU];
   load(ka, 0);
+  __builtin_amdgcn_sched_barrier(0);
   pj.finish(qs, y, M, D);
   __syncthreads();
   build_tables32(y, lut);
