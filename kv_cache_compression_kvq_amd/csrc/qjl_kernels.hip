@@ -43,12 +43,23 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // tiles, a multiple of 8 (MT == 0: runtime m, words stored as they are
 // produced).  Each wave
 // owns NT x 32 tokens per iteration and loops over token tiles.
-// Token tiles of 32 per wave iteration: two, or one when d = 256 would
-// otherwise spill.
-template <int KS> constexpr int sketch_nt() { return KS <= 8 ? 2 : 1; }
+// d = 128 with m = 256: one 32-token tile per wave iteration, two in flight,
+// in 768-thread workgroups at three waves per SIMD (144 registers): more
+// waves hide more of the key stream's latency than a second tile per wave
+// does (about 5 % faster, the same words).  Other shapes: token tiles of 32
+// per wave iteration, two, or one when d = 256 would otherwise spill, in
+// 512-thread workgroups at two waves per SIMD.
+template <int KS, int MT> constexpr bool sketch_wide() { return KS == 8 && MT == 8; }
+template <int KS, int MT> constexpr int sketch_nt() {
+  return sketch_wide<KS, MT>() ? 1 : (KS <= 8 ? 2 : 1);
+}
 // Key tiles in flight per wave (a ring of register buffers): four single
 // tiles up to d = 192, two above (four would spill registers).
-template <int KS> constexpr int sketch_ring() { return sketch_nt<KS>() == 1 && KS <= 12 ? 4 : 2; }
+template <int KS, int MT> constexpr int sketch_ring() {
+  return sketch_wide<KS, MT>() ? 2 : (sketch_nt<KS, MT>() == 1 && KS <= 12 ? 4 : 2);
+}
+template <int KS, int MT> constexpr int sketch_threads() { return sketch_wide<KS, MT>() ? 768 : 512; }
+template <int KS, int MT> constexpr int sketch_waves_per_eu() { return sketch_wide<KS, MT>() ? 3 : 2; }
 
 // Sign words of projection tile mt (32 projections) for the NT x 32 tokens
 // of a wave: P = S_tile K^T on fp16 MFMA, then bit = [P >= 0].  Accumulator
@@ -107,7 +118,8 @@ constexpr int kSketchWaves = kSketchThreads / 64;
 // (sign words mt0 .. of words_total per row); S larger than a workgroup's
 // LDS takes several launches, and the one with mt0 == 0 writes the norms.
 template <int KS, int MT>
-__global__ __launch_bounds__(kSketchThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__((sketch_threads<KS, MT>()))
+__attribute__((amdgpu_waves_per_eu((sketch_waves_per_eu<KS, MT>()))))
 void sketch_mfma_kernel(const _Float16* __restrict__ k,
                                                           int64_t rows,
                                                           const _Float16* __restrict__ S,
@@ -115,6 +127,8 @@ void sketch_mfma_kernel(const _Float16* __restrict__ k,
                                                           uint16_t* __restrict__ norms,
                                                           int mt0, int words_total) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
+  constexpr int TH = sketch_threads<KS, MT>();
+  constexpr int kWaves = TH / 64;
   f16x8* sfrag = reinterpret_cast<f16x8*>(lds_raw);
   constexpr int D = KS * 16;
   const int mt_count = MT > 0 ? MT : m_rt / 32;
@@ -128,7 +142,7 @@ void sketch_mfma_kernel(const _Float16* __restrict__ k,
   // S -> LDS in fragment order: fragment (mt, ks), lane l holds
   // S[32 mt + perm(l % 32)][16 ks + 8 (l / 32) .. + 8].
   const int nfrag_lanes = mt_count * KS * 64;
-  for (int idx = tid; idx < nfrag_lanes; idx += kSketchThreads) {
+  for (int idx = tid; idx < nfrag_lanes; idx += TH) {
     const int l = idx & 63;
     const int frag = idx >> 6;
     const int mt = frag / KS, ks = frag % KS;
@@ -137,7 +151,7 @@ void sketch_mfma_kernel(const _Float16* __restrict__ k,
   }
   __syncthreads();
 
-  constexpr int kSketchNT = sketch_nt<KS>();
+  constexpr int kSketchNT = sketch_nt<KS, MT>();
   const int64_t tiles = (rows + 32 * kSketchNT - 1) / (32 * kSketchNT);
 
   // B fragments of one token tile: lane (token j, half h) holds channels
@@ -257,9 +271,9 @@ void sketch_mfma_kernel(const _Float16* __restrict__ k,
   // RING token tiles in flight per wave: a ring of register buffers, each
   // refilled (unconditionally, clamped past the end) right after its tile's
   // multiplies are issued.
-  constexpr int RING = sketch_ring<KS>();
-  const int64_t stride = (int64_t)gridDim.x * kSketchWaves;
-  const int64_t first = (int64_t)blockIdx.x * kSketchWaves + wave;
+  constexpr int RING = sketch_ring<KS, MT>();
+  const int64_t stride = (int64_t)gridDim.x * kWaves;
+  const int64_t first = (int64_t)blockIdx.x * kWaves + wave;
   if (first >= tiles) return;
   f16x8 bq[RING][kSketchNT][KS];
 #pragma unroll
@@ -485,13 +499,15 @@ __global__ __launch_bounds__(256) void sketch_generic_kernel(const T* __restrict
 // (registers and LDS both limit it), each striding over the token tiles.
 template <typename Kernel>
 static hipError_t persistent_blocks(Kernel kernel, size_t lds, int64_t tiles,
-                                    const DeviceInfo& dev, int64_t* blocks) {
+                                    const DeviceInfo& dev, int64_t* blocks,
+                                    int threads = kSketchThreads) {
   hipError_t e = allow_dynamic_lds(kernel, lds);
   if (e != hipSuccess) return e;
   int per_cu = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kSketchThreads, lds);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds);
   if (e != hipSuccess) return e;
-  const int64_t want = (tiles + kSketchWaves - 1) / kSketchWaves;
+  const int waves = threads / 64;
+  const int64_t want = (tiles + waves - 1) / waves;
   const int64_t cap = (int64_t)dev.cus * std::max(1, per_cu);
   *blocks = std::max<int64_t>(1, std::min(want, cap));
   return hipSuccess;
@@ -509,7 +525,8 @@ template <int KS, int MT>
 static hipError_t sketch_mfma_launch(const _Float16* k, int64_t rows, const _Float16* S, int m,
                                      uint32_t* bits, uint16_t* norms, const DeviceInfo& dev,
                                      hipStream_t st) {
-  constexpr int kSketchNT = sketch_nt<KS>();
+  constexpr int kSketchNT = sketch_nt<KS, MT>();
+  constexpr int TH = sketch_threads<KS, MT>();
   const int64_t tiles = (rows + 32 * kSketchNT - 1) / (32 * kSketchNT);
   const int mt_total = m / 32;
   const size_t tile_bytes = (size_t)32 * KS * 16 * sizeof(_Float16);
@@ -518,9 +535,9 @@ static hipError_t sketch_mfma_launch(const _Float16* k, int64_t rows, const _Flo
     const int mtp = std::min(per, mt_total - mt0);
     const size_t lds = (size_t)mtp * tile_bytes;
     int64_t blocks = 0;
-    hipError_t e = persistent_blocks(sketch_mfma_kernel<KS, MT>, lds, tiles, dev, &blocks);
+    hipError_t e = persistent_blocks(sketch_mfma_kernel<KS, MT>, lds, tiles, dev, &blocks, TH);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((sketch_mfma_kernel<KS, MT>), dim3((unsigned)blocks), dim3(kSketchThreads),
+    hipLaunchKernelGGL((sketch_mfma_kernel<KS, MT>), dim3((unsigned)blocks), dim3(TH),
                        lds, st, k, rows, S, 32 * mtp, bits, norms, mt0, mt_total);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
