@@ -41,20 +41,20 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------------------
 // Sketch, fp16 keys on MFMA.  KS = d / 16 K-steps; MT = m / 32 projection
 // tiles, a multiple of 8 (MT == 0: runtime m, words stored as they are
-// produced).  Each wave
-// owns NT x 32 tokens per iteration and loops over token tiles.
-// d = 128 with m = 256: one 32-token tile per wave iteration, two in flight,
-// in 768-thread workgroups at three waves per SIMD (144 registers): more
-// waves hide more of the key stream's latency than a second tile per wave
-// does (about 5 % faster, the same words).  Other shapes: token tiles of 32
-// per wave iteration, two, or one when d = 256 would otherwise spill, in
-// 512-thread workgroups at two waves per SIMD.
+// produced).  Each wave owns NT x 32 tokens per iteration and loops over
+// token tiles.  d = 128 with m = 256: one 32-token tile per wave iteration,
+// two in flight, in 768-thread workgroups at three waves per SIMD (144
+// registers): more waves hide more of the key stream's latency than a second
+// tile per wave does (about 5 % faster, the same words).  Other shapes:
+// token tiles of 32 per wave iteration, two, or one when d = 256 would
+// otherwise spill, in 512-thread workgroups at two waves per SIMD.
 template <int KS, int MT> constexpr bool sketch_wide() { return KS == 8 && MT == 8; }
 template <int KS, int MT> constexpr int sketch_nt() {
   return sketch_wide<KS, MT>() ? 1 : (KS <= 8 ? 2 : 1);
 }
-// Key tiles in flight per wave (a ring of register buffers): four single
-// tiles up to d = 192, two above (four would spill registers).
+// Key tiles in flight per wave (a ring of register buffers): two at d = 128,
+// m = 256; else four single tiles up to d = 192, two above (four would spill
+// registers).
 template <int KS, int MT> constexpr int sketch_ring() {
   return sketch_wide<KS, MT>() ? 2 : (sketch_nt<KS, MT>() == 1 && KS <= 12 ? 4 : 2);
 }
