@@ -182,8 +182,9 @@ def test_scores_shapes(qdt, nq, T, d):
 def test_scores_grouped_queries_matrix_cores(qdt, nq):
     """d = 128 with 2 .. 16 queries per group (the matrix-core score: fp16
     queries as 16 columns, fp32 queries split hi / lo into 8 + 8 columns,
-    so fp32 with 9 and 16 queries takes the vector-ALU kernel), ragged
-    token counts on both sides of the 256- and 1024-token block steps."""
+    so fp32 with 9 and 16 queries takes the vector-ALU kernel; 2 and 3
+    queries take it too below 2^20 rows), ragged token counts on both
+    sides of the 256- and 1024-token block steps."""
     rng = np.random.default_rng(nq * 17 + len(qdt))
     for G, T in ((3, 1), (2, 17), (3, 255), (2, 1025), (5, 4099)):
         x = rng.standard_normal((G * T, 128)).astype(np.float32)
@@ -194,6 +195,23 @@ def test_scores_grouped_queries_matrix_cores(qdt, nq):
         q = q.astype(np.float16 if qdt == "f16" else np.float32)
         sc = down(K.scores_int8(up(q), up(codes), up(scales)))
         assert_int8_scores(sc, q, codes, scales, O.scores_int8(q, codes, scales))
+
+
+@pytest.mark.parametrize("qdt", ["f32", "f16"])
+@pytest.mark.parametrize("nq", [2, 3])
+def test_scores_few_queries_large_cache_matrix_cores(qdt, nq):
+    """2 and 3 queries per group over 2^20 rows or more (the matrix-core
+    score; smaller caches take the vector-ALU kernel), ragged last tile:
+    every score compared with the oracle."""
+    G, T, d = 2, (1 << 19) + 77, 128
+    rng = np.random.default_rng(60 + nq + len(qdt))
+    codes = rng.integers(-127, 128, size=(G, T, d), dtype=np.int8)
+    scales = rng.uniform(1e-3, 5e-2, size=(G, T)).astype(np.float32)
+    q = rng.standard_normal((G, nq, d)).astype(np.float16 if qdt == "f16" else np.float32)
+    log(f"[int8] large-cache scores nq={nq} {qdt}")
+    sc = down(K.scores_int8(up(q), up(codes), up(scales)))
+    worst = FS.int8_scores_every_score(q, codes, scales, sc)
+    log(f"[int8] large-cache scores nq={nq} {qdt}: worst err / scale = {worst:.3g}")
 
 
 @pytest.mark.parametrize("nq", [1, 4])
