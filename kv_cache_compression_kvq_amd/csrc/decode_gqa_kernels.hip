@@ -414,188 +414,306 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
 }
 
 // ---------------------------------------------------------------------------
-// Grouped-query QJL scores in one pass (m = 256, fp16 S, d <= 128, 2 .. 4
-// queries per launch): one workgroup per (KV head, token tile) projects its
-// queries (y = S q, the one-query kernels' arithmetic), builds their tables
-// as two pair blocks (the same binary32 entries as the one-query tables),
-// and walks the tile once, each lane scoring one token for one query of
-// each block with the lookups above.  A token t is visited by lane r = t mod
-// 32 with the one-query kernels' summation order, so every score equals,
-// bit for bit, the one-query score of the same query.
-constexpr int kGsWaves = 16;
-constexpr int kGsThreads = 64 * kGsWaves;
-constexpr int kGsStep = kGsWaves * kGqaChunk;            // tokens per workgroup step
+// Grouped-query QJL scores on the matrix cores (m = 256, fp16 S, d <= 128,
+// 2 .. 8 queries per KV head).  For a tile of 16 tokens and the head's
+// queries, sum_i (2 b_ti - 1) y_i is the product of the tokens' +-1 sign
+// matrix (16 x 256) and the queries' projections (256 x nq), so it runs on
+// v_mfma_f32_16x16x32_f16: the A operand holds the signs as binary16 +-1
+// (exact), column j < 8 of the B operand the binary16 hi part of query j's
+// projection and column j + 8 its lo part, and the two columns' sums are
+// added.  Each projection is scaled by a power of two (exact) so that its
+// largest magnitude lies in [2^14, 2^15); hi is the scaled value with its 13
+// low significand bits cleared, lo the remainder rounded toward zero, so
+// hi + lo is within 2^-21 of the scaled value, relative.  Products are exact
+// and the accumulation is binary32: a score is within a few 2^-21
+// sum_i |y_i| of the exact estimate for the same bits and projection, far
+// inside the 1e-4 ||q|| ||k|| bound.  The cost per token does not grow with
+// the number of queries (the byte-table lookups of the one-query kernel
+// cost 32 per token and query).
+//
+// Signs -> A fragments: lane (t, kq) = (lane % 16, lane / 16) loads bytes
+// 8 kq .. 8 kq + 7 of token t's 32-byte sign row (the 64 lanes read the
+// tile's 512 bytes in one instruction) and at K-step ks reads the 16-byte
+// +-1 expansion of byte 8 kq + ks (bit e -> element e) from an LDS table.
+// The table holds one copy per lane position t, entry (v, t) at 256 v + 16 t,
+// so the 16 lanes of each group read 16 different bank quads whatever the
+// bytes; the address is one byte permute (the token's byte into byte 1, 16 t
+// in byte 0; the table sits at LDS address 0: this kernel declares no static
+// __shared__ data).  MFMA row t, K index 32 ks + 8 kq + e is then projection
+// 8 (8 kq + ks) + e = 64 kq + 8 ks + e, and the B operand holds y there.
+//
+// The projections y = S q run on the same instruction first: each wave takes
+// 16 rows of S (A operand: lane (r, kq) holds channels 32 ks + 8 kq .. + 7 of
+// row r) against all the queries (B operand: column j and j + 8 the hi and
+// lo parts of query j after its own power-of-two scaling), so S is read once
+// per workgroup whatever the number of queries.
+constexpr int kGmWaves = 16;
+constexpr int kGmThreads = 64 * kGmWaves;
+constexpr int kGmMaxNq = 8;
+constexpr int kGmTiles = 4;                                    // 16-token tiles per wave step
+constexpr int kGmStep = kGmWaves * 16 * kGmTiles;              // tokens per workgroup step
+constexpr uint32_t kGmTableBytes = 256u * 16u * 16u;           // 64 KiB
+// LDS: +-1 table | y [8][kGmYs] | q [8][kGmQs] | q scales [8] | y scales [8]
+// (binary32) | the projection's B fragments [4][64] | the scores' B fragments
+// [8][64] (16 bytes each).  The rows of y and q are padded by 8 floats so that
+// the 8 queries' reads at the same offset fall in 8 different bank octets.
+// The B fragments are the same in every wave: each element is computed once,
+// by one thread of the workgroup, and every wave reads them back.
+constexpr int kGmYs = 256 + 8, kGmQs = 128 + 8;
+constexpr size_t kGmLdsBytes = kGmTableBytes + (size_t)(8 * kGmYs + 8 * kGmQs + 16) * sizeof(float) +
+                               (size_t)(4 + 8) * 64 * 16;
+typedef _Float16 gm_f16x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) const f16x8* lds_cf16x8_ptr;
+
+// 2^(14 - e), e the exponent of the largest magnitude (its binary32 bits
+// without the sign); the scaled vector's largest magnitude lies in
+// [2^14, 2^15).
+__device__ __forceinline__ float gm_pow2_scale(uint32_t max_abs_bits) {
+  const int e = max_abs_bits == 0 ? 0 : (int)((max_abs_bits >> 23) & 0xFF) - 127;
+  return __builtin_ldexpf(1.0f, min(14 - e, 126));
+}
+
+// hi = v with its 13 low significand bits cleared, lo = v - hi (exact in
+// binary32) rounded toward zero, both binary16.
+__device__ __forceinline__ void gm_split(float v, _Float16& hi, _Float16& lo) {
+  const float h = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & 0xFFFFE000u);
+  const auto p = __builtin_amdgcn_cvt_pkrtz(h, v - h);
+  hi = p[0];
+  lo = p[1];
+}
+
+// The value of lane ^ 8 (DPP row_ror:8 inside each 16-lane row).
+__device__ __forceinline__ float gm_xor8(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, true));
+}
 
 template <typename TQ>
-__global__ __launch_bounds__(kGsThreads) __attribute__((amdgpu_waves_per_eu(4)))
-void scores_qjl_gqa_kernel(const TQ* __restrict__ q, int nq_total, int q_off, int nq_pass,
-                           const _Float16* __restrict__ S, int d,
-                           const uint32_t* __restrict__ bits, const uint16_t* __restrict__ norms,
-                           int64_t T, int64_t tiles, int64_t tile_tokens,
-                           float* __restrict__ scores) {
-  constexpr int NB = 2, NQ = 4, M = kGqaM;
+__global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void scores_qjl_mfma_kernel(const TQ* __restrict__ q, int nq, const _Float16* __restrict__ S,
+                            int d, const uint32_t* __restrict__ bits,
+                            const uint16_t* __restrict__ norms, int64_t T, int64_t tiles,
+                            int64_t tile_tokens, float* __restrict__ scores) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
-  // tables first, at LDS address 0 (this kernel declares no static
-  // __shared__ data); before they are built the area stages the queries
-  float* qs = reinterpret_cast<float*>(lds_raw);
-  float* y = reinterpret_cast<float*>(lds_raw + NB * kGqaBlockBytes);   // [NQ][M]
+  float* y = reinterpret_cast<float*>(lds_raw + kGmTableBytes);   // [8][kGmYs]
+  float* qs = y + 8 * kGmYs;                                       // [8][kGmQs]
+  float* qscale = qs + 8 * kGmQs;                                  // [8]
+  float* yscale = qscale + 8;                                      // [8]
+  f16x8* bqf = reinterpret_cast<f16x8*>(yscale + 8);               // [4][64]
+  f16x8* byf = bqf + 4 * 64;                                       // [8][64]
   const int64_t g = blockIdx.x / tiles;
   const int64_t t0 = (blockIdx.x % tiles) * tile_tokens;
   const int ntok = (int)std::min<int64_t>(tile_tokens, T - t0);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int r = lane & 31;                   // token of the wave step
-  const int h = lane >> 5;                   // query slot within each block
-  const float c = kSqrtHalfPi / (float)M;
-  const uint32_t* bblk = bits + (g * T + t0) * (M / 32);
+  const int n = lane & 15;                     // A row / B and C column of this lane
+  const int kq = lane >> 4;
+  const uint32_t* bblk = bits + (g * T + t0) * 8;
   const uint16_t* nblk = norms + g * T + t0;
 
-  struct Keys {
-    u32x4 wx;                                // sign words, as whole lines
-    uint16_t nb;
-  };
-  auto load_keys = [&](Keys& kk, int base) {
-    const int tc = min(base + r, ntok - 1);
-    kk.wx = issue_rot_words32(bblk, base, ntok - 1, lane);
-    kk.nb = ld_stream(nblk + tc);
-  };
+  // S rows 16 wave .. + 15 and this thread's query element (loads are
+  // unconditional: chunks and elements past d or nq read a valid address
+  // and are zeroed when used)
+  const int nch = d / 8;                       // 16-byte chunks of an S row
+  f16x8 sa[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    sa[ks] = *reinterpret_cast<const f16x8*>(S + (int64_t)(16 * wave + n) * d +
+                                             8 * min(4 * ks + kq, nch - 1));
+  const int qj = threadIdx.x >> 7, qc = threadIdx.x & 127;
+  const float qv = to_f32(q[(g * nq + min(qj, nq - 1)) * d + min(qc, d - 1)]);
 
-  // projections of all the launch's queries at once: 4 waves per query, 64
-  // rows of S each, every row as project16_lite computes it (16 lanes x 8
-  // products, then the 16-lane DPP sum), so y is bit for bit the one-query
-  // kernels' y; dummy query slots get zero tables
+  // the first step's sign bytes and norms (requested after S and q, which
+  // then do not wait behind them)
+  struct Step {
+    u32x2 w[kGmTiles];                         // bytes 8 kq .. 8 kq + 7 of token n of tile u
+    uint16_t nb;                               // norm of token `lane` of the step
+  };
+  auto load_step = [&](Step& s, int base) {
+#pragma unroll
+    for (int u = 0; u < kGmTiles; ++u) {
+      const int tok = min(base + 16 * u + n, ntok - 1);
+      s.w[u] = ld_stream(reinterpret_cast<const u32x2*>(bblk + (uint32_t)tok * 8u + 2u * (uint32_t)kq));
+    }
+    s.nb = ld_stream(nblk + min(base + lane, ntok - 1));
+  };
+  const int first = wave * 16 * kGmTiles;
+  Step s0, s1;
+  load_step(s0, first);
+
+  qs[qj * kGmQs + qc] = (qj < nq && qc < d) ? qv : 0.0f;
+  // the +-1 table: entry (v, t) at 256 v + 16 t, element e = bit e of v
+  for (int i = threadIdx.x; i < 256 * 16; i += kGmThreads) {
+    const uint32_t v = (uint32_t)i >> 4;
+    u32x4 ent;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      ent[w] = (((v >> (2 * w)) & 1u) ? 0x3C00u : 0xBC00u) |
+               ((((v >> (2 * w + 1)) & 1u) ? 0x3C00u : 0xBC00u) << 16);
+    *reinterpret_cast<u32x4*>(lds_raw + 16 * i) = ent;
+  }
+  __syncthreads();
+  if (wave < kGmMaxNq) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(qs + wave * kGmQs)[lane & 31];
+    uint32_t mx = max(max(abs_bits(a[0]), abs_bits(a[1])), max(abs_bits(a[2]), abs_bits(a[3])));
+    mx = seg_max_u32<64>(mx);
+    if (lane == 0) qscale[wave] = gm_pow2_scale(mx);
+  }
+  __syncthreads();
+
+  // the projection's B fragments: fragment (ks, l) element e is channel
+  // 32 ks + 8 (l / 16) + e of query (l mod 16) mod 8, its hi part for
+  // l mod 16 < 8, its lo part above (two elements per thread)
   {
-    static_assert(kGsWaves == 16 && M == 256, "4 waves x 64 rows per query");
-    for (int i = threadIdx.x; i < NQ * 128; i += kGsThreads) {
-      const int j = i >> 7, cch = i & 127;
-      qs[i] = (j < nq_pass && cch < d) ? to_f32(q[(g * nq_total + q_off + j) * d + cch]) : 0.0f;
-    }
-    __syncthreads();
-    const int j = wave >> 2;                   // query of this wave
-    const int rbase = 64 * (wave & 3);
-    const int cl = lane & 15, r4 = lane >> 4;
-    const int cc = min(cl, d / 8 - 1);
-    const bool live_c = 8 * cl < d;
-    float qv[8];
-    const f32x4* p4 = reinterpret_cast<const f32x4*>(qs + j * 128 + 8 * cc);
-    const f32x4 q0 = p4[0], q1 = p4[1];
-    qv[0] = q0[0]; qv[1] = q0[1]; qv[2] = q0[2]; qv[3] = q0[3];
-    qv[4] = q1[0]; qv[5] = q1[1]; qv[6] = q1[2]; qv[7] = q1[3];
-    for (int it0 = 0; it0 < 16; it0 += 4) {
-      f16x8 raw[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        raw[k] = *reinterpret_cast<const f16x8*>(S + (int64_t)(rbase + 4 * (it0 + k) + r4) * d + 8 * cc);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float part = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)raw[k][e], qv[e], part);
-        part = seg_sum_f32<16>(live_c ? part : 0.0f);
-        if (cl == 0) y[j * M + rbase + 4 * (it0 + k) + r4] = j < nq_pass ? part : 0.0f;
-      }
-    }
+    const int l = threadIdx.x & 63, ks = (threadIdx.x >> 6) & 3, e2 = threadIdx.x >> 8;
+    const int nl = l & 15, j = nl & 7;
+    const float sc = qscale[j];
+    const float* src = qs + j * kGmQs + 32 * ks + 8 * (l >> 4) + 2 * e2;
+    _Float16 h0, l0, h1, l1;
+    gm_split(src[0] * sc, h0, l0);
+    gm_split(src[1] * sc, h1, l1);
+    reinterpret_cast<gm_f16x2*>(bqf + ks * 64 + l)[e2] = nl >= 8 ? gm_f16x2{l0, l1} : gm_f16x2{h0, h1};
   }
-  const int first = wave * kGqaChunk;
-  Keys ka, kb;
-  load_keys(ka, first);
-  __syncthreads();
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-    build_pair_tables(y + 2 * b * M, y + (2 * b + 1) * M,
-                      reinterpret_cast<float*>(lds_raw + b * kGqaBlockBytes));
   __syncthreads();
 
-  // per-lane address bytes: byte i of cs = 4 ((r + i) mod 32) + 128 h
-  uint32_t cs[8];
+  // projections: rows 16 wave + 4 kq + i of every query
+  {
+    const int j = n & 7;
+    const bool lo = n >= 8;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      v |= (uint32_t)(4 * ((r + 4 * w + b) & 31) + 128 * h) << (8 * b);
-    cs[w] = v;
-  }
-  float* sq = scores + (g * nq_total + q_off) * T + t0;
-  auto score = [&](const Keys& kk, int base) {
-    uint32_t wv[8], x[8];
-    finish_rot_words32(kk.wx, wv);
-    rot_words(wv, r, x);
-    float acc[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = 0.0f;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      float v[NB][16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int i = 16 * hf + k;
-        const uint32_t a = __builtin_amdgcn_perm(x[i >> 2], cs[i >> 2],
-                                                 0x0C0C0400u | (uint32_t)(i & 3) | ((uint32_t)(i & 3) << 8));
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-          v[b][k] = *(lds_cfloat_ptr)(uintptr_t)(a + (uint32_t)b * kGqaBlockBytes);
-      }
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          s0 += v[b][k];
-          s1 += v[b][8 + k];
-        }
-        acc[b] += s0 + s1;
-      }
+    for (int ks = 0; ks < 4; ++ks) {
+      const f16x8 a = 4 * ks + kq < nch ? sa[ks] : f16x8{};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bqf[ks * 64 + lane], acc, 0, 0, 0);
     }
-    const float n = (float)__builtin_bit_cast(_Float16, kk.nb);
-    const int t = base + r;
+    const float unsc = 1.0f / qscale[j];       // exact: a power of two
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int qj = 2 * b + h;
-      if (t < ntok && qj < nq_pass) sq[(int64_t)qj * T + t] = c * n * acc[b];
+    for (int i = 0; i < 4; ++i) {
+      const float v = (acc[i] + gm_xor8(acc[i])) * unsc;
+      if (!lo) y[j * kGmYs + 16 * wave + 4 * kq + i] = v;
+    }
+  }
+  __syncthreads();
+  if (wave < kGmMaxNq) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(y + wave * kGmYs)[lane];
+    uint32_t mx = max(max(abs_bits(a[0]), abs_bits(a[1])), max(abs_bits(a[2]), abs_bits(a[3])));
+    mx = seg_max_u32<64>(mx);
+    if (lane == 0) yscale[wave] = gm_pow2_scale(mx);
+  }
+  __syncthreads();
+
+  // B fragments of the scores: fragment (ks, l) element e is projection
+  // 64 (l / 16) + 8 ks + e of query (l mod 16) mod 8, hi part for
+  // l mod 16 < 8, lo part above (four elements per thread)
+  {
+    const int l = threadIdx.x & 63, ks = (threadIdx.x >> 6) & 7, e4 = threadIdx.x >> 9;
+    const int nl = l & 15, j = nl & 7;
+    const float sc = yscale[j];
+    const float* src = y + j * kGmYs + 64 * (l >> 4) + 8 * ks + 4 * e4;
+    f16x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      _Float16 h16, l16;
+      gm_split(src[i] * sc, h16, l16);
+      v[i] = nl >= 8 ? l16 : h16;
+    }
+    reinterpret_cast<f16x4*>(byf + ks * 64 + l)[e4] = v;
+  }
+  __syncthreads();
+  f16x8 by[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) by[ks] = byf[ks * 64 + lane];
+  const float unscale = 1.0f / yscale[n & 7];  // exact: a power of two
+  const float c = kSqrtHalfPi / 256.0f;
+  const bool writer = n < nq;
+  float* sq = scores + (g * nq + (writer ? n : 0)) * T + t0;
+  // whole 16-byte runs of 4 tokens when every query row starts 16-byte aligned
+  const bool vec_out = ((T | t0) & 3) == 0 && ((uintptr_t)scores & 15) == 0;
+  const uint32_t tbyte = 16u * (uint32_t)n;    // byte 0 of this lane's table addresses
+
+  auto score_step = [&](const Step& s, int base) {
+    // norms of this lane's tokens 16 u + 4 kq + i of the step, from the
+    // lanes that loaded them (all requested before the first lookup)
+    const int nstep = __builtin_bit_cast(int, (float)__builtin_bit_cast(_Float16, s.nb));
+    float nt[kGmTiles][4];
+#pragma unroll
+    for (int u = 0; u < kGmTiles; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        nt[u][i] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((16 * u + 4 * kq + i) << 2, nstep));
+#pragma unroll
+    for (int u = 0; u < kGmTiles; ++u) {
+      // the tile's eight sign expansions first, then its eight multiplies
+      f16x8 sg[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const uint32_t a = __builtin_amdgcn_perm(s.w[u][ks >> 2], tbyte,
+                                                 0x0C0C0000u | ((4u + (uint32_t)(ks & 3)) << 8));
+        sg[ks] = *(lds_cf16x8_ptr)(uintptr_t)a;
+      }
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(sg[ks], by[ks], acc, 0, 0, 0);
+      // (the scheduler would otherwise keep one read in flight)
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // MFMA
+      // this lane's tokens: 16 u + 4 kq + i of the step
+      const int tt = base + 16 * u + 4 * kq;
+      f32x4 out;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[i] = ((acc[i] + gm_xor8(acc[i])) * unscale) * (c * nt[u][i]);
+      if (writer) {
+        if (vec_out && tt + 3 < ntok) {
+          *reinterpret_cast<f32x4*>(sq + tt) = out;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (tt + i < ntok) sq[tt + i] = out[i];
+        }
+      }
     }
   };
   if (first < ntok) {
-    for (int base = first;; base += 2 * kGsStep) {
-      const int nb1 = base + kGsStep, nb2 = base + 2 * kGsStep;
-      load_keys(kb, nb1);
-      score(ka, base);
+    for (int base = first;; base += 2 * kGmStep) {
+      const int nb1 = base + kGmStep, nb2 = base + 2 * kGmStep;
+      load_step(s1, nb1);
+      score_step(s0, base);
       if (nb1 >= ntok) break;
-      load_keys(ka, nb2);
-      score(kb, nb1);
+      load_step(s0, nb2);
+      score_step(s1, nb1);
       if (nb2 >= ntok) break;
     }
   }
 }
 
 bool scores_qjl_gqa_supported(int S_f16, int m, int d, int nq) {
-  return S_f16 && m == kGqaM && d >= 8 && d <= 128 && d % 8 == 0 && nq >= 2 && nq <= 4;
+  return S_f16 && m == kGqaM && d >= 8 && d <= 128 && d % 8 == 0 && nq >= 2 && nq <= kGmMaxNq;
 }
 
-size_t scores_qjl_gqa_lds_bytes() {
-  return (size_t)2 * kGqaBlockBytes + (size_t)4 * kGqaM * sizeof(float);
-}
+size_t scores_qjl_gqa_lds_bytes() { return kGmLdsBytes; }
 
 template <typename TQ>
 static hipError_t scores_qjl_gqa_typed(const TQ* q, int64_t groups, int nq, const _Float16* S,
                                        int d, const uint32_t* bits, const uint16_t* norms,
                                        int64_t T, float* scores, const DeviceInfo& dev,
                                        hipStream_t st) {
+  if (T <= 0 || groups <= 0) return hipSuccess;
   const size_t lds = scores_qjl_gqa_lds_bytes();
   if (lds > dev.lds_per_block) return hipErrorInvalidConfiguration;
-  hipError_t e = allow_dynamic_lds(scores_qjl_gqa_kernel<TQ>, lds);
+  hipError_t e = allow_dynamic_lds(scores_qjl_mfma_kernel<TQ>, lds);
   if (e != hipSuccess) return e;
-  // about one workgroup per CU (one fits beside its 128 KiB of tables),
+  // about one workgroup per CU (its 64 KiB table and 16 waves fill one),
   // tiles a multiple of the workgroup step
   const int64_t splits = std::max<int64_t>(1, ((int64_t)std::max(1, dev.cus) + groups - 1) / groups);
   int64_t tile = (T + splits - 1) / splits;
-  tile = (tile + kGsStep - 1) / kGsStep * kGsStep;
+  tile = (tile + kGmStep - 1) / kGmStep * kGmStep;
   const int64_t tiles = (T + tile - 1) / tile;
   const int64_t max_groups = std::max<int64_t>(1, (int64_t(1) << 22) / tiles);
   for (int64_t g0 = 0; g0 < groups; g0 += max_groups) {
     const int64_t gn = std::min(max_groups, groups - g0);
-    hipLaunchKernelGGL(scores_qjl_gqa_kernel<TQ>, dim3((unsigned)(gn * tiles)), dim3(kGsThreads),
-                       lds, st, q + g0 * nq * d, nq, 0, nq, S, d, bits + g0 * T * (kGqaM / 32),
+    hipLaunchKernelGGL(scores_qjl_mfma_kernel<TQ>, dim3((unsigned)(gn * tiles)), dim3(kGmThreads),
+                       lds, st, q + g0 * nq * d, nq, S, d, bits + g0 * T * (kGqaM / 32),
                        norms + g0 * T, T, tiles, tile, scores + g0 * nq * T);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

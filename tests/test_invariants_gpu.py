@@ -277,7 +277,12 @@ def test_qjl_scores_linear_and_permutation(qdt, nq, T):
     norms[:, ::89] = 0
     q = torch.randn(G, nq, d, device=DEV, generator=g).to(F[qdt])
     sc = K.scores_qjl(q, S, bits, norms)
-    same(K.scores_qjl(-q, S, bits, norms), -sc, "scores of -q")
+    # 2 .. 8 queries with fp16 S run on the matrix cores, whose accumulation
+    # is not symmetric under negation; the byte-table kernels' is
+    if qdt == "f16" and 2 <= nq <= 8:
+        close(K.scores_qjl(-q, S, bits, norms), -sc, qjl_mag(q, S, norms), "scores of -q")
+    else:
+        same(K.scores_qjl(-q, S, bits, norms), -sc, "scores of -q")
     same(K.scores_qjl(q * 4, S, bits, norms), sc * 4, "scores of 4 q")
     close(K.scores_qjl(q, S, ~bits, norms), -sc, qjl_mag(q, S, norms),
           "scores of complemented sign words")

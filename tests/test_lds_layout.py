@@ -1,5 +1,6 @@
 """The rotated byte-table lookups of the QJL score, decode and two-stage score
-kernels use a byte permute's result as the LDS address itself, which is
+kernels, and the sign-expansion lookups of the grouped QJL score, use a byte
+permute's result as the LDS address itself, which is
 right only while the tables start at LDS address 0, i.e. while those
 kernels declare no static __shared__ data (dynamic LDS is placed after the
 static part).  This reads the built library's gfx950 code objects and checks
@@ -17,7 +18,7 @@ from kv_cache_compression_kvq_amd import _lib as L
 
 LLVM = "/opt/rocm/llvm/bin"
 ADDRESS_ZERO_KERNELS = ("decode_split_kernel", "scores_qjl_kernel", "scores_residual_kernel",
-                        "decode_gqa_kernel")
+                        "decode_gqa_kernel", "scores_qjl_mfma_kernel")
 
 
 def _tool(name):
