@@ -538,8 +538,9 @@ void scores_qjl_mfma_kernel(const TQ* __restrict__ q, int nq, const _Float16* __
     s.nb = ld_stream(nblk + min(base + lane, ntok - 1));
   };
   const int first = wave * 16 * kGmTiles;
-  Step s0, s1;
+  Step s0, s1, s2;
   load_step(s0, first);
+  load_step(s1, first + kGmStep);
 
   qs[qj * kGmQs + qc] = (qj < nq && qc < d) ? qv : 0.0f;
   // the +-1 table: entry (v, t) at 256 v + 16 t, element e = bit e of v
@@ -553,13 +554,17 @@ void scores_qjl_mfma_kernel(const TQ* __restrict__ q, int nq, const _Float16* __
     *reinterpret_cast<u32x4*>(lds_raw + 16 * i) = ent;
   }
   __syncthreads();
-  if (wave < kGmMaxNq) {
-    const f32x4 a = reinterpret_cast<const f32x4*>(qs + wave * kGmQs)[lane & 31];
-    uint32_t mx = max(max(abs_bits(a[0]), abs_bits(a[1])), max(abs_bits(a[2]), abs_bits(a[3])));
-    mx = seg_max_u32<64>(mx);
-    if (lane == 0) qscale[wave] = gm_pow2_scale(mx);
+  // binary32 queries are scaled per query by a power of two before the
+  // split; binary16 ones split exactly as they are (hi = q, lo = 0)
+  if constexpr (sizeof(TQ) == 4) {
+    if (wave < kGmMaxNq) {
+      const f32x4 a = reinterpret_cast<const f32x4*>(qs + wave * kGmQs)[lane & 31];
+      uint32_t mx = max(max(abs_bits(a[0]), abs_bits(a[1])), max(abs_bits(a[2]), abs_bits(a[3])));
+      mx = seg_max_u32<64>(mx);
+      if (lane == 0) qscale[wave] = gm_pow2_scale(mx);
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // the projection's B fragments: fragment (ks, l) element e is channel
   // 32 ks + 8 (l / 16) + e of query (l mod 16) mod 8, its hi part for
@@ -567,7 +572,7 @@ void scores_qjl_mfma_kernel(const TQ* __restrict__ q, int nq, const _Float16* __
   {
     const int l = threadIdx.x & 63, ks = (threadIdx.x >> 6) & 3, e2 = threadIdx.x >> 8;
     const int nl = l & 15, j = nl & 7;
-    const float sc = qscale[j];
+    const float sc = sizeof(TQ) == 4 ? qscale[j] : 1.0f;
     const float* src = qs + j * kGmQs + 32 * ks + 8 * (l >> 4) + 2 * e2;
     _Float16 h0, l0, h1, l1;
     gm_split(src[0] * sc, h0, l0);
@@ -586,7 +591,7 @@ void scores_qjl_mfma_kernel(const TQ* __restrict__ q, int nq, const _Float16* __
       const f16x8 a = 4 * ks + kq < nch ? sa[ks] : f16x8{};
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bqf[ks * 64 + lane], acc, 0, 0, 0);
     }
-    const float unsc = 1.0f / qscale[j];       // exact: a power of two
+    const float unsc = sizeof(TQ) == 4 ? 1.0f / qscale[j] : 1.0f;   // exact: a power of two
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float v = (acc[i] + gm_xor8(acc[i])) * unsc;
@@ -632,17 +637,15 @@ void scores_qjl_mfma_kernel(const TQ* __restrict__ q, int nq, const _Float16* __
   const uint32_t tbyte = 16u * (uint32_t)n;    // byte 0 of this lane's table addresses
 
   auto score_step = [&](const Step& s, int base) {
-    // norms of this lane's tokens 16 u + 4 kq + i of the step, from the
-    // lanes that loaded them (all requested before the first lookup)
     const int nstep = __builtin_bit_cast(int, (float)__builtin_bit_cast(_Float16, s.nb));
-    float nt[kGmTiles][4];
-#pragma unroll
-    for (int u = 0; u < kGmTiles; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        nt[u][i] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((16 * u + 4 * kq + i) << 2, nstep));
 #pragma unroll
     for (int u = 0; u < kGmTiles; ++u) {
+      // norms of this lane's tokens 16 u + 4 kq + i, from the lanes that
+      // loaded them
+      float nt[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        nt[i] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((16 * u + 4 * kq + i) << 2, nstep));
       // the tile's eight sign expansions first, then its eight multiplies
       f16x8 sg[8];
 #pragma unroll
@@ -662,7 +665,7 @@ void scores_qjl_mfma_kernel(const TQ* __restrict__ q, int nq, const _Float16* __
       const int tt = base + 16 * u + 4 * kq;
       f32x4 out;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) out[i] = ((acc[i] + gm_xor8(acc[i])) * unscale) * (c * nt[u][i]);
+      for (int i = 0; i < 4; ++i) out[i] = ((acc[i] + gm_xor8(acc[i])) * unscale) * (c * nt[i]);
       if (writer) {
         if (vec_out && tt + 3 < ntok) {
           *reinterpret_cast<f32x4*>(sq + tt) = out;
@@ -674,15 +677,19 @@ void scores_qjl_mfma_kernel(const TQ* __restrict__ q, int nq, const _Float16* __
       }
     }
   };
+  // three steps of sign words in flight per wave
   if (first < ntok) {
-    for (int base = first;; base += 2 * kGmStep) {
+    for (int base = first;; base += 3 * kGmStep) {
       const int nb1 = base + kGmStep, nb2 = base + 2 * kGmStep;
-      load_step(s1, nb1);
+      load_step(s2, nb2);
       score_step(s0, base);
       if (nb1 >= ntok) break;
-      load_step(s0, nb2);
+      load_step(s0, base + 3 * kGmStep);
       score_step(s1, nb1);
       if (nb2 >= ntok) break;
+      load_step(s1, base + 4 * kGmStep);
+      score_step(s2, nb2);
+      if (base + 3 * kGmStep >= ntok) break;
     }
   }
 }
