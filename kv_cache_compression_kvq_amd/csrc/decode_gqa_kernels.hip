@@ -8,22 +8,23 @@
 //   sigma_t = sqrt(pi/2)/m * n_t * sum_i (2 b_ti - 1) (S q)_i
 //   out     = sum_t softmax_t(lam * sigma_t) * s_t * c_t
 // Here one workgroup per (KV head, token range) reads the range once and
-// carries up to four of the head's queries through it: byte tables of all
-// four in LDS, four online softmaxes, the four weighted value sums on the
-// matrix cores from each value load.  Heads with more queries take one
-// launch per four.
+// carries up to four of the head's queries through it: the scores of each
+// 32-token wave step on the matrix cores (below), four online softmaxes,
+// the four weighted value sums on the matrix cores from each value load.
+// Heads with more queries take one launch per four.
 //
-// Tables (m = 256: 32 tables of 256 binary32 entries per query): a 64 KiB
-// block holds two queries, row v (256 bytes) = entries T_p[v] of query a
-// (p = 0..31) then of query b.  Two lanes share a token: lane (r, h) =
-// (lane % 32, lane / 32) scores token r of the wave's 32 for query h of each
-// block.  Lane r visits the token's sign bytes in the order p = (r + i) mod
-// 32 (its words rotated once by r), so at step i the 32 lanes of a half read
-// 32 different entries of their rows: columns 32 h + p, one per LDS bank.  The
-// byte address 256 v + 128 h + 4 p is one byte permute of the token's byte v
-// and a per-lane constant byte (4 ((r + i) mod 32) + 128 h, eight registers
-// of them); the second block is the same address plus 64 KiB.
-//
+// Scores, on the matrix cores: for a tile of 16 tokens, sum_i (2 b_ti - 1)
+// y_i for every query is the product of the tokens' +-1 sign matrix
+// (16 x 256) and the queries' projections (256 x NQ): the signs reach the A
+// operand through an LDS table of the 256 byte values' +-1 expansions, the
+// projections are the B operand as binary16 hi / lo parts (column j the hi
+// part of query j, column j + 8 its lo part, after a power-of-two scaling
+// per query), eight v_mfma_f32_16x16x32_f16 per tile.  The step's sums go
+// through a few LDS floats of the wave so that lane (r, h) = (lane % 32,
+// lane / 32) receives token r's score for query 2 b + h (b < NQ / 2), the
+// layout of the softmax below.  (The byte-table lookups used before cost
+// 32 per token and query, which bound the kernel by vector-ALU issue.)
+
 // Values, on the matrix cores: per wave step, o[q][ch] += sum over the 32
 // tokens of w[q][t] c[t][ch] is eight v_mfma_f32_16x16x32_f16 (one per group
 // of 16 channels), the weights w = softmax weight x value scale as the A
@@ -49,48 +50,76 @@
 namespace kvq {
 
 constexpr int kGqaChunk = 32;                            // tokens per wave step
-// waves per workgroup: the four-query kernel (128 KiB of tables, one
-// workgroup per CU) takes 12 so that 3 waves per SIMD hide the lookups'
-// latency; the two-query kernel (64 KiB) runs two 8-wave workgroups per CU
-#ifndef KVQ_GQA_WAVES2
-#define KVQ_GQA_WAVES2 12
-#endif
-constexpr int gqa_waves(int nb) { return nb == 2 ? KVQ_GQA_WAVES2 : 8; }
+// waves per workgroup: the four-query kernel takes 12 (one workgroup per
+// CU, 3 waves per SIMD), the two-query kernel two 8-wave workgroups per CU
+constexpr int gqa_waves(int nb) { return nb == 2 ? 12 : 8; }
 constexpr int kGqaBlockTokens = 8 * kGqaChunk;           // token-range granule
 constexpr int kGqaD = 128, kGqaM = 256;
-constexpr uint32_t kGqaBlockBytes = 65536;               // one table block (two queries)
 
-// Table block of queries a and b (y vectors of 256 values): row v, entry
-// 32 hq + p = T_p[v] of query hq, built from nibble partial sums like the
-// one-query tables (same additions, so the same binary32 entries).
-__device__ void build_pair_tables(const float* ya, const float* yb, float* blk) {
-  for (int task = threadIdx.x; task < 2 * 32 * 16; task += blockDim.x) {
-    const int hq = task >> 9;                  // query of the pair
-    const int p = task & 31;                   // table
-    const int a = (task >> 5) & 15;            // high nibble of v
-    const float* yp = (hq ? yb : ya) + 8 * p;
-    float lo[16];
-    lo[0] = -(((yp[0] + yp[1]) + yp[2]) + yp[3]);
+// --- signs on the matrix cores (shared by the decode and the scores) --------
+//
+// A operand from sign bytes: lane (t, kq) = (lane % 16, lane / 16) holds
+// bytes 8 kq .. 8 kq + 7 of token t's 32-byte sign row and, at K-step ks,
+// reads the 16-byte +-1 expansion of byte 8 kq + ks (bit e -> element e,
+// binary16 +1 / -1) from an LDS table that holds one copy per lane position
+// t: entry (v, t) at 256 v + 16 t, so the 16 lanes of each group read 16
+// different bank quads whatever the bytes.  The address is one byte permute
+// (the byte into byte 1, 16 t in byte 0): the table sits at LDS address 0,
+// and the kernels using it declare no static __shared__ data.  MFMA row t,
+// K index 32 ks + 8 kq + e is then projection 8 (8 kq + ks) + e =
+// 64 kq + 8 ks + e, where the B operand holds the projections.
+constexpr uint32_t kSignTableBytes = 256u * 16u * 16u;         // 64 KiB
+typedef __attribute__((address_space(3))) const f16x8* lds_cf16x8_ptr;
+__device__ __forceinline__ void build_sign_table(unsigned char* lds, int tid, int nthreads) {
+  for (int i = tid; i < 256 * 16; i += nthreads) {
+    const uint32_t v = (uint32_t)i >> 4;
+    u32x4 ent;
 #pragma unroll
-    for (int b = 1; b < 16; ++b) {
-      const int low = b & (-b);
-      const int j = __builtin_ctz(low);
-      lo[b] = lo[b ^ low] + 2.0f * yp[j];
-    }
-    float hi = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hi += ((a >> j) & 1) ? yp[4 + j] : -yp[4 + j];
-#pragma unroll
-    for (int b = 0; b < 16; ++b) blk[(16 * a + b) * 64 + 32 * hq + p] = hi + lo[b];
+    for (int w = 0; w < 4; ++w)
+      ent[w] = (((v >> (2 * w)) & 1u) ? 0x3C00u : 0xBC00u) |
+               ((((v >> (2 * w + 1)) & 1u) ? 0x3C00u : 0xBC00u) << 16);
+    *reinterpret_cast<u32x4*>(lds + 16 * i) = ent;
   }
 }
 
-// NB table blocks (2 NB query slots per launch).  yall: projected queries
+// Expansion of byte ks (0..7) of the lane's 8 sign bytes w; tbyte = 16 t.
+__device__ __forceinline__ f16x8 sign_fragment(const u32x2& w, int ks, uint32_t tbyte) {
+  const uint32_t a = __builtin_amdgcn_perm(w[ks >> 2], tbyte, 0x0C0C0000u | ((4u + (uint32_t)(ks & 3)) << 8));
+  return *(lds_cf16x8_ptr)(uintptr_t)a;
+}
+
+// 2^(14 - e), e the exponent of the largest magnitude (its binary32 bits
+// without the sign); the scaled vector's largest magnitude lies in
+// [2^14, 2^15).
+__device__ __forceinline__ float gm_pow2_scale(uint32_t max_abs_bits) {
+  const int e = max_abs_bits == 0 ? 0 : (int)((max_abs_bits >> 23) & 0xFF) - 127;
+  return __builtin_ldexpf(1.0f, min(14 - e, 126));
+}
+
+// hi = v with its 13 low significand bits cleared, lo = v - hi (exact in
+// binary32) rounded toward zero, both binary16: hi + lo is within 2^-21 of
+// v, relative (2^-24 absolute below binary16's normal range).
+__device__ __forceinline__ void gm_split(float v, _Float16& hi, _Float16& lo) {
+  const float h = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & 0xFFFFE000u);
+  const auto p = __builtin_amdgcn_cvt_pkrtz(h, v - h);
+  hi = p[0];
+  lo = p[1];
+}
+
+// The value of lane ^ 8 (DPP row_ror:8 inside each 16-lane row).
+__device__ __forceinline__ float gm_xor8(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, true));
+}
+
+constexpr int kGqaYs = kGqaM + 8;    // padded row of a projection in LDS
+
+// NQ = 2 NB query slots per launch.  yall: projected queries
 // [groups * nq_total][m]; this launch takes queries q_off .. q_off + nq_pass
-// - 1 of every group (nq_pass <= 2 NB; the other slots score zero tables and
-// are not written).
+// - 1 of every group (nq_pass <= 2 NB; the other slots score against a zero
+// projection and are not written).
 template <int NB, int WAVES = gqa_waves(NB)>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4)))
+// (eight-wave workgroups run two per CU: at most 128 registers)
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES == 8 ? 4 : WAVES / 4)))
 void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, int nq_pass,
                        const uint32_t* __restrict__ kbits, const uint16_t* __restrict__ knorms,
                        const int8_t* __restrict__ vcodes, const float* __restrict__ vscales,
@@ -99,11 +128,11 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
   constexpr int NQ = 2 * NB;
   constexpr int D = kGqaD, M = kGqaM;
   extern __shared__ __align__(16) unsigned char lds_raw[];
-  // tables first, at LDS address 0: the byte permute's result is the
-  // address itself (this kernel declares no static __shared__ data)
-  float* lut = reinterpret_cast<float*>(lds_raw);
-  float* y = reinterpret_cast<float*>(lds_raw + NB * kGqaBlockBytes);   // [NQ][M]
-  float* wpart = lut;                        // [waves][NQ][D + 2], after the last lookup
+  // the sign table first, at LDS address 0 (no static __shared__ data here)
+  float* y = reinterpret_cast<float*>(lds_raw + kSignTableBytes);        // [NQ][kGqaYs]
+  float* yscale = y + NQ * kGqaYs;                                        // [4]
+  f16x8* byf = reinterpret_cast<f16x8*>(yscale + 4);                      // [8][64]
+  float* wpart = reinterpret_cast<float*>(lds_raw);   // [waves][NQ][D + 2], after the last lookup
 
   const int64_t p = blockIdx.x;
   if (p >= pairs) return;
@@ -123,24 +152,27 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
   const uint16_t* nblk = knorms + row0;
   const int8_t* vblk = vcodes + row0 * D + 8 * nl;
   const float* sblk = vscales + row0;
-  // per wave: the step's softmax weights [NQ][32], staged for the matrix cores
-  float* wst = reinterpret_cast<float*>(lds_raw + NB * kGqaBlockBytes + NQ * M * sizeof(float)) +
-               wave * NQ * kGqaChunk;
+  // per wave: the step's softmax weights [NQ][32], staged for the matrix
+  // cores, and its scores [NQ][32], staged for the softmax
+  float* wst = reinterpret_cast<float*>(byf + 8 * 64) + wave * NQ * kGqaChunk;
+  float* zs = reinterpret_cast<float*>(byf + 8 * 64) + (WAVES + wave) * NQ * kGqaChunk;
 
   struct Keys {
-    uint32_t wv[8];
-    uint16_t nb;
-    float vs;
+    u32x2 w[2];                              // sign bytes 8 kq .. + 7 of token 16 u + nl
+    uint16_t nb;                             // norm of token r
+    float vs;                                // value scale of token r
   };
   struct Vals {
     u32x2 vc[8];                             // channels 8 nl .. + 7 of tokens 8 kq + e
   };
-  // (per-lane 16-byte halves: whole-line loads and their lane exchange
-  // measured slower here, where the sign words are a fifth of the bytes and
-  // the vector ALU is the bound)
+  // the step's sign words: each load instruction reads a tile's 16 rows
   auto load_keys = [&](Keys& kk, int base) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tk = min(base + 16 * u + nl, ntok - 1);
+      kk.w[u] = ld_stream(reinterpret_cast<const u32x2*>(bblk + tk * 8 + 2 * kq));
+    }
     const int tc = min(base + r, ntok - 1);
-    load_rot_words(bblk + tc * 8, r, kk.wv);
     kk.nb = ld_stream(nblk + tc);
     kk.vs = ld_stream(sblk + tc);
   };
@@ -153,16 +185,11 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
     }
   };
 
-  // per-lane address bytes: byte i of cs = 4 ((r + i) mod 32) + 128 h
-  uint32_t cs[8];
-#pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      v |= (uint32_t)(4 * ((r + 4 * w + b) & 31) + 128 * h) << (8 * b);
-    cs[w] = v;
-  }
+  // B fragments of the scores (column j < NQ: query j's hi part, j + 8 its
+  // lo part, other columns zero), set up below
+  f16x8 by[8];
+  float yunscale = 1.0f;
+  const uint32_t tbyte = 16u * (uint32_t)nl;
 
   // value sums on the matrix cores: acc[j] = D tile of channel group j,
   // row rho = (part, query) = (rho / NQ, rho % NQ) with part 0 the weights'
@@ -183,42 +210,36 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
   // hi / lo split; R only grows, and the sums are rescaled when it does
   int R = -110;
 
-  // z of this lane's token for query h of each block (-inf past the range)
+  // z of this lane's token r for query 2 b + h (-inf past the range): the
+  // step's two 16-token tiles on the matrix cores, their sums handed to the
+  // softmax layout through the wave's LDS rows zs (LDS operations of one
+  // wave complete in order; the asm statements keep the compiler from
+  // moving them across each other)
   auto scores = [&](const Keys& kk, int base, float (&z)[NB]) {
-    uint32_t x[8];
-    rot_words(kk.wv, r, x);
-    float acc[NB];
+    __asm__ volatile("" ::: "memory");
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = 0.0f;
+    for (int u = 0; u < 2; ++u) {
+      f16x8 sg[8];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      float v[NB][16];
+      for (int ks = 0; ks < 8; ++ks) sg[ks] = sign_fragment(kk.w[u], ks, tbyte);
+      f32x4 a4 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int i = 16 * hf + k;
-        // byte 0: the lane's address byte of step i; byte 1: the token's
-        // byte; bytes 2, 3: zero
-        const uint32_t a = __builtin_amdgcn_perm(x[i >> 2], cs[i >> 2],
-                                                 0x0C0C0400u | (uint32_t)(i & 3) | ((uint32_t)(i & 3) << 8));
+      for (int ks = 0; ks < 8; ++ks) a4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(sg[ks], by[ks], a4, 0, 0, 0);
+      f32x4 sm;
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-          v[b][k] = *(lds_cfloat_ptr)(uintptr_t)(a + (uint32_t)b * kGqaBlockBytes);
-      }
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          s0 += v[b][k];
-          s1 += v[b][8 + k];
-        }
-        acc[b] += s0 + s1;
-      }
+      for (int i = 0; i < 4; ++i) sm[i] = (a4[i] + gm_xor8(a4[i])) * yunscale;
+      // lane (query nl, kq) holds tokens 16 u + 4 kq .. + 3
+      if (nl < NQ) *reinterpret_cast<f32x4*>(zs + nl * kGqaChunk + 16 * u + 4 * kq) = sm;
     }
+    __asm__ volatile("" ::: "memory");
+    float sq[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) sq[b] = zs[(2 * b + h) * kGqaChunk + r];
+    __asm__ volatile("" ::: "memory");
     const bool valid = base + r < ntok;
     const float n = (float)__builtin_bit_cast(_Float16, kk.nb);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) z[b] = valid ? lam * (c * n * acc[b]) : -INFINITY;
+    for (int b = 0; b < NB; ++b) z[b] = valid ? lam * (c * n * sq[b]) : -INFINITY;
   };
 
   // online softmax of the wave step for every query, then the value sums;
@@ -312,7 +333,7 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
   };
 
   // y of the launch's queries first (its wait leaves the first step's loads
-  // in flight); dummy query slots get zero tables
+  // in flight); dummy query slots get a zero projection
   constexpr int TH = 64 * WAVES;
   constexpr int YK = (NQ * M + TH - 1) / TH;
   float yv[YK];
@@ -332,14 +353,43 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
   load_vals(va, first);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int k = 0; k < YK; ++k)
-    if ((int)threadIdx.x + k * TH < NQ * M) y[threadIdx.x + k * TH] = yv[k];
+  for (int k = 0; k < YK; ++k) {
+    const int idx = (int)threadIdx.x + k * TH;
+    if (idx < NQ * M) y[(idx / M) * kGqaYs + idx % M] = yv[k];
+  }
+  build_sign_table(lds_raw, threadIdx.x, TH);
+  __syncthreads();
+  // per-query power-of-two scale of y, then the B fragments, each element
+  // split once by one thread and read back by every wave
+  if (wave < NQ) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(y + wave * kGqaYs)[lane];
+    uint32_t mx = max(max(abs_bits(a[0]), abs_bits(a[1])), max(abs_bits(a[2]), abs_bits(a[3])));
+    mx = seg_max_u32<64>(mx);
+    if (lane == 0) yscale[wave] = gm_pow2_scale(mx);
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 64 * 8 * 2; idx += TH) {
+    // fragment (ks, l) elements 4 e4 .. 4 e4 + 3: projections
+    // 64 (l / 16) + 8 ks + 4 e4 + i of query (l mod 16) mod 8
+    const int l = idx & 63, ks = (idx >> 6) & 7, e4 = idx >> 9;
+    const int nc = l & 15, j = nc & 7;
+    f16x4 v = {(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
+    if (j < NQ) {
+      const float sc = yscale[j];
+      const float* src = y + j * kGqaYs + 64 * (l >> 4) + 8 * ks + 4 * e4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        _Float16 h16, l16;
+        gm_split(src[i] * sc, h16, l16);
+        v[i] = nc >= 8 ? l16 : h16;
+      }
+    }
+    reinterpret_cast<f16x4*>(byf + ks * 64 + l)[e4] = v;
+  }
   __syncthreads();
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
-    build_pair_tables(y + 2 * b * M, y + (2 * b + 1) * M,
-                      reinterpret_cast<float*>(lds_raw + b * kGqaBlockBytes));
-  __syncthreads();
+  for (int ks = 0; ks < 8; ++ks) by[ks] = byf[ks * 64 + lane];
+  if ((nl & 7) < NQ) yunscale = 1.0f / yscale[nl & 7];   // exact: a power of two
   if (first < ntok) {
     constexpr int STEP = WAVES * kGqaChunk;     // tokens per workgroup step
     for (int base = first;; base += 2 * STEP) {
@@ -431,16 +481,8 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
 // the number of queries (the byte-table lookups of the one-query kernel
 // cost 32 per token and query).
 //
-// Signs -> A fragments: lane (t, kq) = (lane % 16, lane / 16) loads bytes
-// 8 kq .. 8 kq + 7 of token t's 32-byte sign row (the 64 lanes read the
-// tile's 512 bytes in one instruction) and at K-step ks reads the 16-byte
-// +-1 expansion of byte 8 kq + ks (bit e -> element e) from an LDS table.
-// The table holds one copy per lane position t, entry (v, t) at 256 v + 16 t,
-// so the 16 lanes of each group read 16 different bank quads whatever the
-// bytes; the address is one byte permute (the token's byte into byte 1, 16 t
-// in byte 0; the table sits at LDS address 0: this kernel declares no static
-// __shared__ data).  MFMA row t, K index 32 ks + 8 kq + e is then projection
-// 8 (8 kq + ks) + e = 64 kq + 8 ks + e, and the B operand holds y there.
+// Signs -> A fragments as described above; the 64 lanes read a tile's
+// 512 bytes of sign words in one instruction.
 //
 // The projections y = S q run on the same instruction first: each wave takes
 // 16 rows of S (A operand: lane (r, kq) holds channels 32 ks + 8 kq .. + 7 of
@@ -452,7 +494,6 @@ constexpr int kGmThreads = 64 * kGmWaves;
 constexpr int kGmMaxNq = 8;
 constexpr int kGmTiles = 4;                                    // 16-token tiles per wave step
 constexpr int kGmStep = kGmWaves * 16 * kGmTiles;              // tokens per workgroup step
-constexpr uint32_t kGmTableBytes = 256u * 16u * 16u;           // 64 KiB
 // LDS: +-1 table | y [8][kGmYs] | q [8][kGmQs] | q scales [8] | y scales [8]
 // (binary32) | the projection's B fragments [4][64] | the scores' B fragments
 // [8][64] (16 bytes each).  The rows of y and q are padded by 8 floats so that
@@ -460,33 +501,9 @@ constexpr uint32_t kGmTableBytes = 256u * 16u * 16u;           // 64 KiB
 // The B fragments are the same in every wave: each element is computed once,
 // by one thread of the workgroup, and every wave reads them back.
 constexpr int kGmYs = 256 + 8, kGmQs = 128 + 8;
-constexpr size_t kGmLdsBytes = kGmTableBytes + (size_t)(8 * kGmYs + 8 * kGmQs + 16) * sizeof(float) +
+constexpr size_t kGmLdsBytes = kSignTableBytes + (size_t)(8 * kGmYs + 8 * kGmQs + 16) * sizeof(float) +
                                (size_t)(4 + 8) * 64 * 16;
 typedef _Float16 gm_f16x2 __attribute__((ext_vector_type(2)));
-
-typedef __attribute__((address_space(3))) const f16x8* lds_cf16x8_ptr;
-
-// 2^(14 - e), e the exponent of the largest magnitude (its binary32 bits
-// without the sign); the scaled vector's largest magnitude lies in
-// [2^14, 2^15).
-__device__ __forceinline__ float gm_pow2_scale(uint32_t max_abs_bits) {
-  const int e = max_abs_bits == 0 ? 0 : (int)((max_abs_bits >> 23) & 0xFF) - 127;
-  return __builtin_ldexpf(1.0f, min(14 - e, 126));
-}
-
-// hi = v with its 13 low significand bits cleared, lo = v - hi (exact in
-// binary32) rounded toward zero, both binary16.
-__device__ __forceinline__ void gm_split(float v, _Float16& hi, _Float16& lo) {
-  const float h = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & 0xFFFFE000u);
-  const auto p = __builtin_amdgcn_cvt_pkrtz(h, v - h);
-  hi = p[0];
-  lo = p[1];
-}
-
-// The value of lane ^ 8 (DPP row_ror:8 inside each 16-lane row).
-__device__ __forceinline__ float gm_xor8(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, true));
-}
 
 template <typename TQ>
 __global__ __launch_bounds__(kGmThreads) __attribute__((amdgpu_waves_per_eu(4)))
@@ -495,7 +512,7 @@ void scores_qjl_mfma_kernel(const TQ* __restrict__ q, int nq, const _Float16* __
                             const uint16_t* __restrict__ norms, int64_t T, int64_t tiles,
                             int64_t tile_tokens, float* __restrict__ scores) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
-  float* y = reinterpret_cast<float*>(lds_raw + kGmTableBytes);   // [8][kGmYs]
+  float* y = reinterpret_cast<float*>(lds_raw + kSignTableBytes);   // [8][kGmYs]
   float* qs = y + 8 * kGmYs;                                       // [8][kGmQs]
   float* qscale = qs + 8 * kGmQs;                                  // [8]
   float* yscale = qscale + 8;                                      // [8]
@@ -543,16 +560,7 @@ void scores_qjl_mfma_kernel(const TQ* __restrict__ q, int nq, const _Float16* __
   load_step(s1, first + kGmStep);
 
   qs[qj * kGmQs + qc] = (qj < nq && qc < d) ? qv : 0.0f;
-  // the +-1 table: entry (v, t) at 256 v + 16 t, element e = bit e of v
-  for (int i = threadIdx.x; i < 256 * 16; i += kGmThreads) {
-    const uint32_t v = (uint32_t)i >> 4;
-    u32x4 ent;
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-      ent[w] = (((v >> (2 * w)) & 1u) ? 0x3C00u : 0xBC00u) |
-               ((((v >> (2 * w + 1)) & 1u) ? 0x3C00u : 0xBC00u) << 16);
-    *reinterpret_cast<u32x4*>(lds_raw + 16 * i) = ent;
-  }
+  build_sign_table(lds_raw, threadIdx.x, kGmThreads);
   __syncthreads();
   // binary32 queries are scaled per query by a power of two before the
   // split; binary16 ones split exactly as they are (hi = q, lo = 0)
@@ -649,11 +657,7 @@ void scores_qjl_mfma_kernel(const TQ* __restrict__ q, int nq, const _Float16* __
       // the tile's eight sign expansions first, then its eight multiplies
       f16x8 sg[8];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const uint32_t a = __builtin_amdgcn_perm(s.w[u][ks >> 2], tbyte,
-                                                 0x0C0C0000u | ((4u + (uint32_t)(ks & 3)) << 8));
-        sg[ks] = *(lds_cf16x8_ptr)(uintptr_t)a;
-      }
+      for (int ks = 0; ks < 8; ++ks) sg[ks] = sign_fragment(s.w[u], ks, tbyte);
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
@@ -758,12 +762,12 @@ DecodeSplit decode_gqa_split(int64_t groups, int64_t T, const DeviceInfo& dev) {
 }
 
 size_t decode_gqa_lds_bytes(int nb) {
-  const size_t tables = (size_t)nb * kGqaBlockBytes;
-  const int waves = nb == 2 ? gqa_waves(2) : gqa_waves(1);
-  const size_t part = (size_t)waves * 2 * nb * (kGqaD + 2) * sizeof(float);
-  const size_t y = (size_t)2 * nb * kGqaM * sizeof(float);
-  const size_t weights = (size_t)waves * 2 * nb * kGqaChunk * sizeof(float);
-  return std::max(tables, part) + y + weights;
+  const int nq = 2 * nb;
+  const int waves = gqa_waves(nb);
+  // the partial sums at the end reuse the sign table's space
+  static_assert((size_t)12 * 4 * (kGqaD + 2) * sizeof(float) <= kSignTableBytes, "partials fit");
+  return (size_t)kSignTableBytes + ((size_t)nq * kGqaYs + 4) * sizeof(float) + 8 * 64 * 16 +
+         (size_t)2 * waves * nq * kGqaChunk * sizeof(float);
 }
 
 hipError_t launch_decode_gqa_pass(const float* y, int64_t groups, int nq_total, int q_off,
