@@ -105,7 +105,9 @@ def test_decode_full_size_every_group():
     oracle (sign bits within the band, norms within one ulp, value codes and
     scales bit-exact).  The full-size decode (the bench's launch) then runs
     on the GPU-built cache, and the oracle, fed the same cache, checks the
-    output of every one of the 512 groups."""
+    output of every one of the 512 groups; then the grouped-query decode of
+    4 queries for each of the first 128 heads (the bench's grouped shape),
+    every (head, query) output."""
     W = si.W_DECODE
     B, H, T, d, m = 16, 32, 32768, 128, 256
     G = B * H
@@ -141,6 +143,21 @@ def test_decode_full_size_every_group():
     worst = FS.decode_every_group(q, S, kw.reshape(G, T, m // 32), kn.reshape(G, T),
                                   vc.reshape(G, T, d), vs.reshape(G, T), lam, out)
     log(f"[decode] full size: all {G} groups within tolerance; worst err / tol = {worst:.3g}")
+    # grouped-query decode at the bench's grouped shape on the same cache:
+    # 128 KV heads x 32768 tokens, 4 queries per head, every (head, query)
+    Gk, nq = 128, 4
+    q4 = si.queries(W, Gk, nq, d, "f16")
+    log("[decode] full size: grouped decode, 128 KV heads x 4 queries")
+    out4 = down(K.decode_qjl_int8_gqa(up(q4), Sd, kbits.view(G, T, m // 32)[:Gk],
+                                      knorms.view(G, T)[:Gk], vcodes.view(G, T, d)[:Gk],
+                                      vscales.view(G, T)[:Gk], lam))
+    assert np.all(np.isfinite(out4))
+    for j in range(nq):
+        worst = FS.decode_every_group(np.ascontiguousarray(q4[:, j]), S, kw.reshape(G, T, m // 32)[:Gk],
+                                      kn.reshape(G, T)[:Gk], vc.reshape(G, T, d)[:Gk],
+                                      vs.reshape(G, T)[:Gk], lam, np.ascontiguousarray(out4[:, j]))
+        log(f"[decode] full size: grouped query {j}: all {Gk} heads within tolerance; "
+            f"worst err / tol = {worst:.3g}")
 
 
 # --- grouped-query attention: nq query heads per KV head -------------------------

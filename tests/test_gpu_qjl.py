@@ -59,7 +59,8 @@ def test_qjl_cache_full_size_every_row_and_group():
     checked against the oracle's (bits may differ only inside the 1e-4 band)
     and every norm within one binary16 ulp; then the oracle scores every
     group against the GPU-built bits and norms (identical inputs to the
-    estimator) and every score is checked."""
+    estimator) and every score is checked, for one query per head and for
+    four (the grouped kernel)."""
     W = si.W_QJL_CACHE
     B, H, T, d, m = 8, 32, 8192, 128, 256
     G = B * H
@@ -77,6 +78,13 @@ def test_qjl_cache_full_size_every_row_and_group():
         f"{ulps} norms one ulp apart")
     worst = FS.qjl_scores_every_group(q, S, wg.reshape(G, T, m // 32), ng.reshape(G, T), sc)
     log(f"[qjl] full size: every score checked; worst err / tol = {worst:.3g}")
+    # four queries per KV head (the grouped kernel on the matrix cores), the
+    # bench's grouped-query workload on the same GPU-built cache
+    q4 = si.queries(W, G, 4, d, "f16")
+    log("[qjl] full size: grouped scores, 4 queries per head")
+    sc4 = down(K.scores_qjl(up(q4), Sd, bits.view(G, T, m // 32), norms.view(G, T)))
+    worst = FS.qjl_scores_every_group(q4, S, wg.reshape(G, T, m // 32), ng.reshape(G, T), sc4)
+    log(f"[qjl] full size: every grouped score checked; worst err / tol = {worst:.3g}")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
