@@ -247,7 +247,10 @@ kvq_status kvq_qjl_sketch(const void* k, kvq_dtype k_dt, int64_t rows, int32_t d
  * estimate of the inner product).  With y = S q (binary32, not quantized):
  *   scores[g, j, t] = sqrt(pi/2) / m * norm_{g,t} * sum_i (2 b_{g,t,i} - 1) * y_i
  * Given identical bits and norms, agrees with the exact value within
- * 1e-4 * ||q|| * norm_{g,t}.
+ * 1e-4 * ||q|| * norm_{g,t}.  With 2 .. 8 queries, m = 256, binary16 S and
+ * d <= 128 the head's queries are scored together on the matrix cores (the
+ * results then differ from nq single-query calls by rounding, within that
+ * bound); otherwise each query's scores equal a single-query call's.
  *
  * q      [groups, nq, d] (q_dt);  S [m, d] (S_dt; KVQ_F32 or KVQ_F16)
  * bits   [groups, T, m / 32] uint32;  norms [groups, T] binary16 patterns
