@@ -195,13 +195,15 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
   // row rho = (part, query) = (rho / NQ, rho % NQ) with part 0 the weights'
   // hi halves, part 1 their lo halves (rows past 2 NQ stay zero), column nl
   // = channel 8 nl + j; lane (nl, kq) holds rows 4 kq .. 4 kq + 3
-  float Mq[NQ], Lq[NQ];
+  // Mq: running maxima (per query, the same in every lane); Ll: this lane's
+  // share of the softmax denominators (its tokens, query 2 b + h), summed
+  // over the lanes once at the end
+  float Mq[NQ], Ll[NB];
   f32x4 acc[8];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    Mq[q] = -INFINITY;
-    Lq[q] = 0.0f;
-  }
+  for (int q = 0; q < NQ; ++q) Mq[q] = -INFINITY;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) Ll[b] = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   // weights are scaled by 2^(14 - R), R the exponent of the largest value
@@ -247,31 +249,45 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
   auto step = [&](const Keys& kk, const Vals& vv, int base) {
     float z[NB];
     scores(kk, base, z);
-    // the step's largest value scale (both halves hold the same 32 tokens)
-    const float vmax = __builtin_bit_cast(
-        float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, seg_max_f32<32>(kk.vs))));
-    const int E = (int)((__builtin_bit_cast(uint32_t, vmax) >> 23) & 0xFF) - 127;
-    const int Rn = max(R, E);
+    // the step's largest value scale (both halves hold the same 32 tokens),
+    // reduced across the wave only when some lane's scale has a larger
+    // exponent than R (otherwise max(R, E) is R)
+    int Rn = R;
+    if (__ballot((int)((__builtin_bit_cast(uint32_t, kk.vs) >> 23) & 0xFF) - 127 > R) != 0) {
+      const float vmax = __builtin_bit_cast(
+          float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, seg_max_f32<32>(kk.vs))));
+      Rn = max(R, (int)((__builtin_bit_cast(uint32_t, vmax) >> 23) & 0xFF) - 127);
+    }
     const float up = __builtin_ldexpf(1.0f, R - Rn);        // 1 unless R grew
     R = Rn;
     const float f = __builtin_ldexpf(1.0f, 14 - R);
+    // the step's maxima, reduced across the wave only when some score
+    // exceeds its query's running maximum (otherwise they stay, and every
+    // factor al is exp(0) = 1)
+    bool zgrow = false;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) zgrow |= z[b] > (h ? Mq[2 * b + 1] : Mq[2 * b]);
     float ws[NB], al[NQ];
 #pragma unroll
+    for (int q = 0; q < NQ; ++q) al[q] = 1.0f;
+    if (__ballot(zgrow) != 0) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        // max over the 32 tokens of each half (query 2 b + half)
+        uint32_t mlo, mhi;
+        halves_u32(__builtin_bit_cast(uint32_t, seg_max_f32<32>(z[b])), mlo, mhi);
+        const float Mn0 = __builtin_fmaxf(Mq[2 * b], __builtin_bit_cast(float, mlo));
+        const float Mn1 = __builtin_fmaxf(Mq[2 * b + 1], __builtin_bit_cast(float, mhi));
+        al[2 * b] = __expf(Mq[2 * b] - Mn0);
+        al[2 * b + 1] = __expf(Mq[2 * b + 1] - Mn1);
+        Mq[2 * b] = Mn0;
+        Mq[2 * b + 1] = Mn1;
+      }
+    }
+#pragma unroll
     for (int b = 0; b < NB; ++b) {
-      // max over the 32 tokens of each half (query 2 b + half)
-      uint32_t mlo, mhi;
-      halves_u32(__builtin_bit_cast(uint32_t, seg_max_f32<32>(z[b])), mlo, mhi);
-      const float mx0 = __builtin_bit_cast(float, mlo), mx1 = __builtin_bit_cast(float, mhi);
-      const float Mn0 = __builtin_fmaxf(Mq[2 * b], mx0), Mn1 = __builtin_fmaxf(Mq[2 * b + 1], mx1);
-      al[2 * b] = __expf(Mq[2 * b] - Mn0);
-      al[2 * b + 1] = __expf(Mq[2 * b + 1] - Mn1);
-      const float pz = __expf(z[b] - (h ? Mn1 : Mn0));
-      uint32_t slo, shi;
-      halves_u32(__builtin_bit_cast(uint32_t, seg_sum_f32<32>(pz)), slo, shi);
-      Lq[2 * b] = Lq[2 * b] * al[2 * b] + __builtin_bit_cast(float, slo);
-      Lq[2 * b + 1] = Lq[2 * b + 1] * al[2 * b + 1] + __builtin_bit_cast(float, shi);
-      Mq[2 * b] = Mn0;
-      Mq[2 * b + 1] = Mn1;
+      const float pz = __expf(z[b] - (h ? Mq[2 * b + 1] : Mq[2 * b]));
+      Ll[b] = Ll[b] * (h ? al[2 * b + 1] : al[2 * b]) + pz;
       ws[b] = pz * kk.vs * f;
     }
     // rescale: row 4 kq + i of every lane is query (4 kq + i) mod NQ = i mod NQ;
@@ -408,6 +424,15 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
   // hi + lo rows of each query (NQ = 4: lanes kq = 0 and 1; NQ = 2: rows
   // i and i + 2 of lanes kq = 0), unscaled by 2^(R - 14), then the waves of
   // the workgroup
+  // the softmax denominators: each half's 32 lanes hold query 2 b + half
+  float Lq[NQ];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    uint32_t slo, shi;
+    halves_u32(__builtin_bit_cast(uint32_t, seg_sum_f32<32>(Ll[b])), slo, shi);
+    Lq[2 * b] = __builtin_bit_cast(float, slo);
+    Lq[2 * b + 1] = __builtin_bit_cast(float, shi);
+  }
   const float unscale = __builtin_ldexpf(1.0f, R - 14);
   float ov[NQ][8];
 #pragma unroll
