@@ -553,17 +553,18 @@ void scores_qjl_mfma_kernel(const TQ* __restrict__ q, int nq, const _Float16* __
   const uint32_t* bblk = bits + (g * T + t0) * 8;
   const uint16_t* nblk = norms + g * T + t0;
 
-  // S rows 16 wave .. + 15 and this thread's query element (loads are
-  // unconditional: chunks and elements past d or nq read a valid address
-  // and are zeroed when used)
+  // this thread's query element, then S rows 16 wave .. + 15 (the first
+  // barrier waits for the query only; S is needed from the projection on).
+  // Loads are unconditional: chunks and elements past d or nq read a valid
+  // address and are zeroed when used.
+  const int qj = threadIdx.x >> 7, qc = threadIdx.x & 127;
+  const float qv = to_f32(q[(g * nq + min(qj, nq - 1)) * d + min(qc, d - 1)]);
   const int nch = d / 8;                       // 16-byte chunks of an S row
   f16x8 sa[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
     sa[ks] = *reinterpret_cast<const f16x8*>(S + (int64_t)(16 * wave + n) * d +
                                              8 * min(4 * ks + kq, nch - 1));
-  const int qj = threadIdx.x >> 7, qc = threadIdx.x & 127;
-  const float qv = to_f32(q[(g * nq + min(qj, nq - 1)) * d + min(qc, d - 1)]);
 
   // the first step's sign bytes and norms (requested after S and q, which
   // then do not wait behind them)
@@ -584,8 +585,8 @@ void scores_qjl_mfma_kernel(const TQ* __restrict__ q, int nq, const _Float16* __
   load_step(s0, first);
   load_step(s1, first + kGmStep);
 
-  qs[qj * kGmQs + qc] = (qj < nq && qc < d) ? qv : 0.0f;
   build_sign_table(lds_raw, threadIdx.x, kGmThreads);
+  qs[qj * kGmQs + qc] = (qj < nq && qc < d) ? qv : 0.0f;
   __syncthreads();
   // binary32 queries are scaled per query by a power of two before the
   // split; binary16 ones split exactly as they are (hi = q, lo = 0)
