@@ -527,7 +527,7 @@ constexpr int kGmStep = kGmWaves * 16 * kGmTiles;              // tokens per wor
 // by one thread of the workgroup, and every wave reads them back.
 constexpr int kGmYs = 256 + 8, kGmQs = 128 + 8;
 constexpr size_t kGmLdsBytes = kSignTableBytes + (size_t)(8 * kGmYs + 8 * kGmQs + 16) * sizeof(float) +
-                               (size_t)(4 + 8) * 64 * 16;
+                               (size_t)(4 + 8) * 64 * 16 + 16;   // + the step counter
 typedef _Float16 gm_f16x2 __attribute__((ext_vector_type(2)));
 
 template <typename TQ>
@@ -543,6 +543,7 @@ void scores_qjl_mfma_kernel(const TQ* __restrict__ q, int nq, const _Float16* __
   float* yscale = qscale + 8;                                      // [8]
   f16x8* bqf = reinterpret_cast<f16x8*>(yscale + 8);               // [4][64]
   f16x8* byf = bqf + 4 * 64;                                       // [8][64]
+  int* next_step = reinterpret_cast<int*>(byf + 8 * 64);           // steps handed out
   const int64_t g = blockIdx.x / tiles;
   const int64_t t0 = (blockIdx.x % tiles) * tile_tokens;
   const int ntok = (int)std::min<int64_t>(tile_tokens, T - t0);
@@ -566,8 +567,7 @@ void scores_qjl_mfma_kernel(const TQ* __restrict__ q, int nq, const _Float16* __
     sa[ks] = *reinterpret_cast<const f16x8*>(S + (int64_t)(16 * wave + n) * d +
                                              8 * min(4 * ks + kq, nch - 1));
 
-  // the first step's sign bytes and norms (requested after S and q, which
-  // then do not wait behind them)
+  // a wave step: 64 tokens' sign bytes and norms
   struct Step {
     u32x2 w[kGmTiles];                         // bytes 8 kq .. 8 kq + 7 of token n of tile u
     uint16_t nb;                               // norm of token `lane` of the step
@@ -580,13 +580,28 @@ void scores_qjl_mfma_kernel(const TQ* __restrict__ q, int nq, const _Float16* __
     }
     s.nb = ld_stream(nblk + min(base + lane, ntok - 1));
   };
-  const int first = wave * 16 * kGmTiles;
+  // The tile's 64-token steps: wave w takes steps w and w + 16 first, then
+  // claims the next free step from an LDS counter each time it requests
+  // one, so waves that the scheduler serves faster score more steps (with a
+  // fixed share per wave the last wave of a workgroup ended ~6 us after the
+  // first).  The first two steps are requested now, behind the query
+  // elements and S rows (a CU returns its vector loads in issue order);
+  // requesting them after the first barrier instead delayed the set-up by
+  // the issue of all the waves' token loads at once.
+  const int nsteps = (ntok + 16 * kGmTiles - 1) / (16 * kGmTiles);
+  auto claim = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(next_step, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  int a0 = wave, a1 = wave + kGmWaves, a2;
   Step s0, s1, s2;
-  load_step(s0, first);
-  load_step(s1, first + kGmStep);
+  load_step(s0, 16 * kGmTiles * a0);
+  load_step(s1, 16 * kGmTiles * a1);
 
   build_sign_table(lds_raw, threadIdx.x, kGmThreads);
   qs[qj * kGmQs + qc] = (qj < nq && qc < d) ? qv : 0.0f;
+  if (threadIdx.x == 0) *next_step = 2 * kGmWaves;
   __syncthreads();
   // binary32 queries are scaled per query by a power of two before the
   // split; binary16 ones split exactly as they are (hi = q, lo = 0)
@@ -707,20 +722,21 @@ void scores_qjl_mfma_kernel(const TQ* __restrict__ q, int nq, const _Float16* __
       }
     }
   };
-  // three steps of sign words in flight per wave
-  if (first < ntok) {
-    for (int base = first;; base += 3 * kGmStep) {
-      const int nb1 = base + kGmStep, nb2 = base + 2 * kGmStep;
-      load_step(s2, nb2);
-      score_step(s0, base);
-      if (nb1 >= ntok) break;
-      load_step(s0, base + 3 * kGmStep);
-      score_step(s1, nb1);
-      if (nb2 >= ntok) break;
-      load_step(s1, base + 4 * kGmStep);
-      score_step(s2, nb2);
-      if (base + 3 * kGmStep >= ntok) break;
-    }
+  // three steps of sign words in flight per wave; claims only grow, so the
+  // first step past the tile ends the wave's work
+  for (;;) {
+    a2 = claim();
+    load_step(s2, 16 * kGmTiles * a2);
+    if (a0 >= nsteps) break;
+    score_step(s0, 16 * kGmTiles * a0);
+    a0 = claim();
+    load_step(s0, 16 * kGmTiles * a0);
+    if (a1 >= nsteps) break;
+    score_step(s1, 16 * kGmTiles * a1);
+    a1 = claim();
+    load_step(s1, 16 * kGmTiles * a1);
+    if (a2 >= nsteps) break;
+    score_step(s2, 16 * kGmTiles * a2);
   }
 }
 
