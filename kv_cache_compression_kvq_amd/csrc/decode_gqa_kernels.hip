@@ -156,6 +156,7 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
   // cores, and its scores [NQ][32], staged for the softmax
   float* wst = reinterpret_cast<float*>(byf + 8 * 64) + wave * NQ * kGqaChunk;
   float* zs = reinterpret_cast<float*>(byf + 8 * 64) + (WAVES + wave) * NQ * kGqaChunk;
+  int* next_step = reinterpret_cast<int*>(byf + 8 * 64) + 2 * WAVES * NQ * kGqaChunk;   // steps handed out
 
   struct Keys {
     u32x2 w[2];                              // sign bytes 8 kq .. + 7 of token 16 u + nl
@@ -374,6 +375,7 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
     if (idx < NQ * M) y[(idx / M) * kGqaYs + idx % M] = yv[k];
   }
   build_sign_table(lds_raw, threadIdx.x, TH);
+  if (threadIdx.x == 0) *next_step = WAVES;
   __syncthreads();
   // per-query power-of-two scale of y, then the B fragments, each element
   // split once by one thread and read back by every wave
@@ -406,18 +408,30 @@ void decode_gqa_kernel(const float* __restrict__ yall, int nq_total, int q_off, 
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) by[ks] = byf[ks * 64 + lane];
   if ((nl & 7) < NQ) yunscale = 1.0f / yscale[nl & 7];   // exact: a power of two
-  if (first < ntok) {
-    constexpr int STEP = WAVES * kGqaChunk;     // tokens per workgroup step
-    for (int base = first;; base += 2 * STEP) {
-      const int nb1 = base + STEP, nb2 = base + 2 * STEP;
-      load_keys(kb, nb1);
-      step(ka, va, base);
-      load_vals(vb, nb1);
-      if (nb1 >= ntok) break;
-      load_keys(ka, nb2);
-      step(kb, vb, nb1);
-      load_vals(va, nb2);
-      if (nb2 >= ntok) break;
+  // 32-token steps of the range: wave w takes step w first, then claims the
+  // next free step from an LDS counter when it requests one (the next
+  // step's keys are requested before the current step is scored, its values
+  // after), so waves that the scheduler serves faster take more steps; the
+  // partials of the waves are merged below whatever tokens each one saw
+  const int nsteps = (ntok + kGqaChunk - 1) / kGqaChunk;
+  auto claim = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(next_step, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  int sa = wave, sb;
+  if (sa < nsteps) {
+    for (;;) {
+      sb = claim();
+      load_keys(kb, kGqaChunk * sb);
+      step(ka, va, kGqaChunk * sa);
+      load_vals(vb, kGqaChunk * sb);
+      if (sb >= nsteps) break;
+      sa = claim();
+      load_keys(ka, kGqaChunk * sa);
+      step(kb, vb, kGqaChunk * sb);
+      load_vals(va, kGqaChunk * sa);
+      if (sa >= nsteps) break;
     }
   }
 
@@ -809,7 +823,7 @@ size_t decode_gqa_lds_bytes(int nb) {
   // the partial sums at the end reuse the sign table's space
   static_assert((size_t)12 * 4 * (kGqaD + 2) * sizeof(float) <= kSignTableBytes, "partials fit");
   return (size_t)kSignTableBytes + ((size_t)nq * kGqaYs + 4) * sizeof(float) + 8 * 64 * 16 +
-         (size_t)2 * waves * nq * kGqaChunk * sizeof(float);
+         (size_t)2 * waves * nq * kGqaChunk * sizeof(float) + 16;   // + the step counter
 }
 
 hipError_t launch_decode_gqa_pass(const float* y, int64_t groups, int nq_total, int q_off,
