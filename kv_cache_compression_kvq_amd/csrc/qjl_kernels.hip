@@ -149,6 +149,10 @@ void sketch_mfma_kernel(const _Float16* __restrict__ k,
     const int srow = 32 * (mt0 + mt) + sketch_row_perm(l & 31);
     sfrag[idx] = *reinterpret_cast<const f16x8*>(S + (int64_t)srow * D + 16 * ks + 8 * (l >> 5));
   }
+  // tiles handed out so far (after the S fragments)
+  int* next_tile = reinterpret_cast<int*>(sfrag + nfrag_lanes);
+  constexpr int RING = sketch_ring<KS, MT>();
+  if (tid == 0) *next_tile = RING * kWaves;
   __syncthreads();
 
   constexpr int kSketchNT = sketch_nt<KS, MT>();
@@ -268,24 +272,54 @@ void sketch_mfma_kernel(const _Float16* __restrict__ k,
     }
   };
 
-  // RING token tiles in flight per wave: a ring of register buffers, each
-  // refilled (unconditionally, clamped past the end) right after its tile's
-  // multiplies are issued.
-  constexpr int RING = sketch_ring<KS, MT>();
-  const int64_t stride = (int64_t)gridDim.x * kWaves;
-  const int64_t first = (int64_t)blockIdx.x * kWaves + wave;
-  if (first >= tiles) return;
+  // A workgroup takes a contiguous range of the tiles; its waves take tiles
+  // w, w + W, ... (W waves, RING of them each) first, then claim the next
+  // free tile of the range from an LDS counter as they refill a buffer, so
+  // waves that the scheduler serves faster take more tiles (with a fixed
+  // stride per wave the last tiles of a workgroup ran on a few waves).  RING
+  // token tiles in flight per wave: a ring of register buffers, each
+  // refilled (unconditionally, clamped past the range) right after its
+  // tile's multiplies are issued; claims only grow, so a wave stops at its
+  // first tile past the range.
+  const int64_t per_wg = (tiles + gridDim.x - 1) / gridDim.x;
+  const int64_t wg_first = (int64_t)blockIdx.x * per_wg;
+  const int64_t wg_count = std::min<int64_t>(per_wg, tiles - wg_first);
+  if (wg_count <= 0) return;
+  auto claim = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(next_tile, 1);
+    return (int64_t)__builtin_amdgcn_readfirstlane(v);
+  };
   f16x8 bq[RING][kSketchNT][KS];
+  int64_t idx[RING];
 #pragma unroll
-  for (int r = 0; r < RING; ++r) load(bq[r], std::min(first + r * stride, tiles - 1));
-  for (int64_t t0 = first;; t0 += RING * stride) {
-#pragma unroll
-    for (int r = 0; r < RING; ++r) {
-      const int64_t t = t0 + r * stride;
-      process(bq[r], t);
-      if (t + stride >= tiles) return;
-      load(bq[r], std::min(t + RING * stride, tiles - 1));
+  for (int r = 0; r < RING; ++r) {
+    idx[r] = wave + r * kWaves;
+    load(bq[r], wg_first + std::min(idx[r], wg_count - 1));
+  }
+  // the slots in order, each refilled right after its tile is processed
+  // (written out: the buffers are indexed by constants only)
+  static_assert(RING == 2 || RING == 4, "ring of 2 or 4 tiles");
+  if (idx[0] >= wg_count) return;
+  for (;;) {
+    process(bq[0], wg_first + idx[0]);
+    idx[0] = claim();
+    load(bq[0], wg_first + std::min(idx[0], wg_count - 1));
+    if (idx[1] >= wg_count) return;
+    process(bq[1], wg_first + idx[1]);
+    idx[1] = claim();
+    load(bq[1], wg_first + std::min(idx[1], wg_count - 1));
+    if constexpr (RING == 4) {
+      if (idx[2] >= wg_count) return;
+      process(bq[2], wg_first + idx[2]);
+      idx[2] = claim();
+      load(bq[2], wg_first + std::min(idx[2], wg_count - 1));
+      if (idx[3] >= wg_count) return;
+      process(bq[3], wg_first + idx[3]);
+      idx[3] = claim();
+      load(bq[3], wg_first + std::min(idx[3], wg_count - 1));
     }
+    if (idx[0] >= wg_count) return;
   }
 }
 
@@ -530,10 +564,10 @@ static hipError_t sketch_mfma_launch(const _Float16* k, int64_t rows, const _Flo
   const int64_t tiles = (rows + 32 * kSketchNT - 1) / (32 * kSketchNT);
   const int mt_total = m / 32;
   const size_t tile_bytes = (size_t)32 * KS * 16 * sizeof(_Float16);
-  const int per = MT > 0 ? MT : tiles_per_pass(mt_total, tile_bytes, dev.lds_per_block);
+  const int per = MT > 0 ? MT : tiles_per_pass(mt_total, tile_bytes, dev.lds_per_block - 16);
   for (int mt0 = 0; mt0 < mt_total; mt0 += per) {
     const int mtp = std::min(per, mt_total - mt0);
-    const size_t lds = (size_t)mtp * tile_bytes;
+    const size_t lds = (size_t)mtp * tile_bytes + 16;   // S fragments + the tile counter
     int64_t blocks = 0;
     hipError_t e = persistent_blocks(sketch_mfma_kernel<KS, MT>, lds, tiles, dev, &blocks, TH);
     if (e != hipSuccess) return e;
@@ -585,7 +619,7 @@ constexpr int kSketchMfmaMaxD = 256;
 hipError_t launch_qjl_sketch(const void* k, int k_f16, int64_t rows, int d, const void* S, int m,
                              uint32_t* bits, uint16_t* norms, const DeviceInfo& dev,
                              hipStream_t st) {
-  if (k_f16 && d == 128 && m == 256 && dev.lds_per_block >= (size_t)m * d * sizeof(_Float16))
+  if (k_f16 && d == 128 && m == 256 && dev.lds_per_block >= (size_t)m * d * sizeof(_Float16) + 16)
     return sketch_mfma_launch<8, 8>(static_cast<const _Float16*>(k), rows,
                                     static_cast<const _Float16*>(S), m, bits, norms, dev, st);
   switch (d) {
