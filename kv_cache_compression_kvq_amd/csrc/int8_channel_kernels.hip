@@ -126,56 +126,61 @@ __global__ __launch_bounds__(kChThreads) void channel_scale_kernel(
   scales[idx] = __builtin_bit_cast(float, a) / 127.0f;
 }
 
-// One code for a channel's divisor: the quotient by reciprocal, divided
-// only where it could round differently (as the per-row quantizer: for a
-// divisor in [2^-120, 2^120], |x * rcp(s) - RN32(x / s)| < 2.7e-5 since
-// |x / s| <= 127 + 2^-16, so the codes agree unless x * rcp(s) lies within
-// 2^-14 of a half-integer).
-__device__ __forceinline__ uint32_t channel_code(float x, float sdiv, float r, bool divide) {
-  const float q = x * r;
-  float c = __builtin_rintf(q);
-  if (divide || __builtin_fabsf(q - c) > 0.5f - 0x1p-14f) {
-    __asm__ volatile("");
-    c = __builtin_rintf(x / sdiv);
-  }
-  return (uint32_t)(int)__builtin_amdgcn_fmed3f(c, -128.0f, 127.0f) & 0xFFu;
-}
-
-// Codes of one 16-byte chunk of a row (N channels).
+// Codes of one 16-byte chunk of a row (N channels, each with its own
+// divisor sd and reciprocal rc): the quotients by reciprocal, and the
+// divisions for the whole chunk where any of them could round differently
+// (as the per-row quantizer: for a divisor in [2^-120, 2^120],
+// |x * rcp(s) - RN32(x / s)| < 2.7e-5 since |x / s| <= 127 + 2^-16, so the
+// codes agree unless x * rcp(s) lies within 2^-14 of a half-integer), or
+// where a channel's reciprocal is not trusted.  The division is the
+// definition, so dividing a whole chunk changes no code; one decision per
+// chunk keeps the common path free of per-element branches.
 template <typename T, int N = ChChunk<T>::N>
 __device__ __forceinline__ typename ChChunk<T>::Codes channel_codes(const typename ChChunk<T>::V& v,
                                                                    const float (&sd)[N],
                                                                    const float (&rc)[N],
-                                                                   const bool (&dv)[N]) {
-  typename ChChunk<T>::Codes out;
-  if constexpr (N == 4) {
-    uint32_t w = 0;
+                                                                   bool untrusted) {
+  float c[N];
+  float dmax = 0.0f;  // largest |q - rint(q)| of the chunk (a NaN q counts as 0)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w |= channel_code(v[e], sd[e], rc[e], dv[e]) << (8 * e);
-    out = w;
-  } else {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w |= channel_code((float)v[4 * h + e], sd[4 * h + e], rc[4 * h + e], dv[4 * h + e]) << (8 * e);
-      out[h] = w;
-    }
+  for (int e = 0; e < N; ++e) {
+    const float q = (float)v[e] * rc[e];
+    c[e] = __builtin_rintf(q);
+    dmax = __builtin_fmaxf(dmax, __builtin_fabsf(q - c[e]));
   }
-  return out;
+  if (untrusted || dmax > 0.5f - 0x1p-14f) {
+    // (an opaque statement keeps the divisions behind the branch)
+    __asm__ volatile("");
+#pragma unroll
+    for (int e = 0; e < N; ++e) c[e] = __builtin_rintf((float)v[e] / sd[e]);
+  }
+  uint32_t w[N / 4];
+#pragma unroll
+  for (int h = 0; h < N / 4; ++h) {
+    w[h] = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[h] |= ((uint32_t)(int)__builtin_amdgcn_fmed3f(c[4 * h + e], -128.0f, 127.0f) & 0xFFu) << (8 * e);
+  }
+  if constexpr (N == 4) {
+    return w[0];
+  } else {
+    return u32x2{w[0], w[1]};
+  }
 }
 
 // Divisors of N consecutive channels from their scales: a zero scale
-// divides by 1; reciprocals outside [2^-120, 2^120] are not trusted.
+// divides by 1; reciprocals of divisors outside [2^-120, 2^120] are not
+// trusted (`untrusted` is set if any of the N is).
 template <int N>
 __device__ __forceinline__ void channel_divisors(const float* s, float (&sd)[N], float (&rc)[N],
-                                                 bool (&dv)[N]) {
+                                                 bool& untrusted) {
+  untrusted = false;
 #pragma unroll
   for (int e = 0; e < N; ++e) {
     sd[e] = (s[e] == 0.0f) ? 1.0f : s[e];
     rc[e] = __builtin_amdgcn_rcpf(sd[e]);
-    dv[e] = !(sd[e] >= 0x1p-120f && sd[e] <= 0x1p120f);
+    untrusted |= !(sd[e] >= 0x1p-120f && sd[e] <= 0x1p120f);
   }
 }
 
@@ -195,15 +200,15 @@ __global__ __launch_bounds__(kChThreads) void channel_quantize_kernel(
   int8_t* cg = codes + (g * Ttok + t0) * d;
   const float* sg = scales + g * d;
   auto encode = [&](const typename C::V& v, const float (&sd)[N], const float (&rc)[N],
-                    const bool (&dv)[N]) { return channel_codes<T>(v, sd, rc, dv); };
-  auto divisors = [&](int chunk, float (&sd)[N], float (&rc)[N], bool (&dv)[N]) {
+                    bool dv) { return channel_codes<T>(v, sd, rc, dv); };
+  auto divisors = [&](int chunk, float (&sd)[N], float (&rc)[N], bool& dv) {
     channel_divisors<N>(sg + chunk * N, sd, rc, dv);
   };
   if (kChThreads % cpr == 0) {
     const int chunk = threadIdx.x % cpr;
     const int step = kChThreads / cpr;
     float sd[N], rc[N];
-    bool dv[N];
+    bool dv;
     divisors(chunk, sd, rc, dv);
     for (int r = threadIdx.x / cpr; r < nrows; r += 4 * step) {
       typename C::V v[4];
@@ -223,7 +228,7 @@ __global__ __launch_bounds__(kChThreads) void channel_quantize_kernel(
     for (int idx = threadIdx.x; idx < nrows * cpr; idx += kChThreads) {
       const int rr = idx / cpr, chunk = idx % cpr;
       float sd[N], rc[N];
-      bool dv[N];
+      bool dv;
       divisors(chunk, sd, rc, dv);
       const typename C::V v = *reinterpret_cast<const typename C::V*>(xg + (int64_t)rr * d + chunk * N);
       *reinterpret_cast<typename C::Codes*>(cg + (int64_t)rr * d + chunk * N) = encode(v, sd, rc, dv);
@@ -302,7 +307,7 @@ __global__ __launch_bounds__(kChResThreads) void channel_quantize_resident_kerne
   }
   __syncthreads();
   float sd[N], rc[N];
-  bool dv[N];
+  bool dv;
   channel_divisors<N>(wsc[h], sd, rc, dv);
   int8_t* cg = codes + g * Ttok * d + chunk * N;
 #pragma unroll
