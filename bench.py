@@ -179,6 +179,9 @@ def stream_probe():
     lib.kvqprobe_stream_rw.restype = c_int
     lib.kvqprobe_stream_rw.argtypes = [c_void_p, c_int64, c_int, c_void_p, c_int, c_void_p, c_int,
                                        c_void_p]
+    lib.kvqprobe_sketch_layout.restype = c_int
+    lib.kvqprobe_sketch_layout.argtypes = [c_void_p, c_int64, c_int, c_void_p, c_void_p, c_int,
+                                           c_void_p]
     return lib
 
 
@@ -428,7 +431,22 @@ def components(K, si, torch, np, only=SECTIONS, use_graph=True):
         src32 = [a[: R * 32] for a in src]
         gbs("stream_ref_read32_B_per_row", R * 32,
             [lambda a=a: run_probe(a, 1, None, 0) for a in src32], graph=True)
-        del src, src32, dst, sink
+        # the sketch's memory side alone: its grid, 32-row wave tiles, ring of
+        # two and writes (32 B words + 2 B norm per row), no multiplies; the
+        # keys read in the matrix-core operand layout (32 rows x 32 B per
+        # load instruction, as the sketch reads them) or as whole lines
+        nrm = torch.empty(R, dtype=torch.int16, device=dev)
+        ncu = torch.cuda.get_device_properties(0).multi_processor_count
+
+        def run_layout(a, layout):
+            rc = probe.kvqprobe_sketch_layout(a.data_ptr(), R, layout, dst.data_ptr(), nrm.data_ptr(),
+                                              ncu, torch.cuda.current_stream().cuda_stream)
+            assert rc == 0, rc
+
+        for layout, nm in ((0, "operand_layout"), (1, "whole_lines"), (2, "whole_lines_nt")):
+            gbs(f"stream_ref_sketch_grid_{nm}", R * (256 + 32 + 2),
+                [lambda a=a, layout=layout: run_layout(a, layout) for a in src])
+        del src, src32, dst, sink, nrm
         kks = [kk] + [kk.clone() for _ in range(ncopies(R * d * 2) - 1)]
         sk = [K.qjl_sketch(t, S) for t in kks]
         osk = like(sk[0])
