@@ -15,7 +15,8 @@
 //      into the code buffer, which is free until pass 3 (the partials need
 //      4 * ceil(T / kChSlab) <= T bytes per channel; for T <= kChSlab pass 1
 //      writes the scales directly and pass 2 is skipped);
-//   2. per (group, channel): the max over the slabs' partials, the scale;
+//   2. per (group, 64-channel block): the max over the slabs' partials, the
+//      scale;
 //   3. per (group, slab): the codes (the keys are read a second time).
 // Heads of at most kChResMaxT tokens take one launch instead: a workgroup
 // per (group, 32-byte column of the rows) holds its column of every token
@@ -105,25 +106,43 @@ __global__ __launch_bounds__(kChThreads) void channel_absmax_kernel(
   }
 }
 
-// Pass 2: scale of channel c of group g from the slabs' maxima.
-__global__ __launch_bounds__(kChThreads) void channel_scale_kernel(
-    const uint32_t* __restrict__ partials, int64_t groups, int d, int64_t nslab,
-    float* __restrict__ scales) {
-  const int64_t idx = (int64_t)blockIdx.x * kChThreads + threadIdx.x;
-  if (idx >= groups * d) return;
-  const int64_t g = idx / d;
-  const int c = (int)(idx % d);
-  const uint32_t* p = partials + g * nslab * d + c;
+// Pass 2: scales of 64 channels of one group from the slabs' maxima.  A
+// workgroup per (group, 64-channel block): lane l takes channel 64 b + l
+// (each wave instruction reads 256 consecutive bytes of one slab's row of
+// maxima), the 16 waves take every 16th slab with 8 slabs' loads in flight,
+// and the waves' maxima meet in LDS; so a head of nslab slabs costs about
+// nslab / 128 memory round trips instead of nslab / 8.
+constexpr int kChScaleThreads = 1024;
+constexpr int kChScaleWaves = kChScaleThreads / 64;
+
+__global__ __launch_bounds__(kChScaleThreads) void channel_scale_kernel(
+    const uint32_t* __restrict__ partials, int d, int64_t nslab, float* __restrict__ scales) {
+  __shared__ uint32_t red[kChScaleWaves][64];
+  const int nb = (d + 63) / 64;
+  const int64_t g = blockIdx.x / nb;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = (int)(blockIdx.x % nb) * 64 + lane;
   uint32_t a = 0;
-  // 8 slabs' loads in flight at a time (past the last slab: the last one again)
-  for (int64_t s0 = 0; s0 < nslab; s0 += 8) {
-    uint32_t v[8];
+  if (c < d) {
+    const uint32_t* p = partials + g * nslab * d + c;
+    for (int64_t s0 = w; s0 < nslab; s0 += 8 * kChScaleWaves) {
+      uint32_t v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = p[std::min<int64_t>(s0 + u, nslab - 1) * d];
+      for (int u = 0; u < 8; ++u) {
+        const int64_t sl = s0 + (int64_t)u * kChScaleWaves;
+        v[u] = sl < nslab ? p[sl * d] : 0u;
+      }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) a = max(a, v[u]);
+      for (int u = 0; u < 8; ++u) a = max(a, v[u]);
+    }
   }
-  scales[idx] = __builtin_bit_cast(float, a) / 127.0f;
+  red[w][lane] = a;
+  __syncthreads();
+  if (w == 0 && c < d) {
+#pragma unroll
+    for (int i = 1; i < kChScaleWaves; ++i) a = max(a, red[i][lane]);
+    scales[g * d + c] = __builtin_bit_cast(float, a) / 127.0f;
+  }
 }
 
 // Codes of one 16-byte chunk of a row (N channels, each with its own
@@ -363,9 +382,8 @@ static hipError_t quantize_channel_typed(const T* x, int64_t groups, int64_t Tto
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (nslab > 1) {
-      const int64_t n = ng * d;
-      hipLaunchKernelGGL(channel_scale_kernel, dim3((unsigned)((n + kChThreads - 1) / kChThreads)),
-                         dim3(kChThreads), 0, st, pp, ng, d, nslab, sp);
+      hipLaunchKernelGGL(channel_scale_kernel, dim3((unsigned)(ng * ((d + 63) / 64))),
+                         dim3(kChScaleThreads), 0, st, pp, d, nslab, sp);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
